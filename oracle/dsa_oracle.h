@@ -1,0 +1,36 @@
+/* Plain CPU oracle of the DSA hot path (test infrastructure only; see dsa_oracle.c).
+ * All tensors are dense row-major; bf16 values are passed as their uint16 bit patterns,
+ * fp8 values as OCP e4m3 bytes.  Every function returns 0 on success, nonzero on a bad
+ * argument.  `kv_len` may be NULL (every sequence holds Tk keys). */
+#ifndef DSA_ORACLE_H
+#define DSA_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+double oracle_bf16_to_double(uint16_t h);
+double oracle_e4m3_to_double(uint8_t b);
+/* q [B][Tq][H][D], k [B][Tk][D], w [B][Tq][H] -> scores float [B][Tq][ld] */
+int oracle_index_scores(const uint16_t* q, const uint16_t* k, const uint16_t* w,
+                        const int32_t* kv_len, int B, int Tq, int Tk, int H, int D,
+                        float* scores, int64_t ld, int nthreads);
+/* scores [B][Tq][ld] -> idx int32 [B][Tq][k] (ascending, -1 padded) */
+int oracle_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk,
+                int k, int32_t* idx, int nthreads);
+/* q bf16 [B][Tq][H][Dqk]; kv bf16 or e4m3 [B][Tk][Hkv][Dqk]; kv_scale [B][Tk] (fp8 only);
+ * v bf16 [B][Tk][Hkv][Dv] or NULL (V = kv[..., :Dv]); idx [B][Tq][k]
+ * -> out double [B][Tq][H][Dv], lse double [B][Tq][H] (may be NULL) */
+int oracle_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
+                       int kv_fp8, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv,
+                       int Dqk, int Dv, int k, double sm_scale, double* out, double* lse,
+                       int nthreads);
+/* Rows `rows[0..nrows)` of one prefill sequence (query t sees keys 0..t), streamed row by
+ * row through scores, top-k and MLA attention (Hkv = 1, V = kv[..., :Dv]). */
+int oracle_dsa_rows(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w_idx,
+                    const uint16_t* q, const void* kv, const float* kv_scale, int kv_fp8,
+                    const int32_t* rows, int nrows, int Tk, int H_I, int d_I, int H, int Dqk,
+                    int Dv, int k, double sm_scale, int32_t* idx_out, double* out, int nthreads);
+#ifdef __cplusplus
+}
+#endif
+#endif
