@@ -1,0 +1,224 @@
+"""DeepSeek Sparse Attention hot path for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in include/dsa.h (libdsa.so, built in-tree by
+`deepseek_sparse_attention_amd.build`).  Every step runs in the library's HIP kernels;
+this module only passes device pointers, sizes and torch's current stream, and turns a
+non-OK status into DSAError.  There is no CPU fallback: without the built library (or on
+a machine without a gfx950 GPU) the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DSAError", "lib", "abi_version", "index_scores", "topk", "sparse_attn", "layer_stack",
+    "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
+    "KV_BF16", "KV_FP8_E4M3", "CACHE_PREFILLED", "OP_SCORES", "OP_TOPK", "OP_ATTN", "OP_STACK",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+KV_BF16, KV_FP8_E4M3 = 0, 1
+OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK = 0, 1, 2, 3
+CACHE_PREFILLED = 1
+_STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_PATTERN",
+           "DSA_ERR_WORKSPACE", "DSA_ERR_LAUNCH", "DSA_ERR_DEVICE"]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = _STATUS[status] if 0 <= status < len(_STATUS) else str(status)
+        super().__init__(f"{name}: {message}")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Tq", ctypes.c_int), ("Tk", ctypes.c_int),
+                ("H_I", ctypes.c_int), ("d_I", ctypes.c_int),
+                ("H", ctypes.c_int), ("Hkv", ctypes.c_int), ("Dqk", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("k", ctypes.c_int), ("sm_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int),
+                ("kv_len", ctypes.c_void_p)]
+
+
+class LayerIO(ctypes.Structure):
+    _fields_ = [("q_idx", ctypes.c_void_p), ("k_idx", ctypes.c_void_p), ("w_idx", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdsa.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m deepseek_sparse_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, U, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_float,
+                               ctypes.c_size_t)
+        L.dsa_abi_version.restype = I
+        L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_status_string.argtypes = [I]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P, I64, P]
+        L.dsa_topk.argtypes = [P, I64, P, I, I, I, I, P, P, SZ, P]
+        L.dsa_sparse_attn.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, F, P, P, P, SZ, P]
+        L.dsa_layer_stack.argtypes = [ctypes.c_char_p, I, P, ctypes.POINTER(Shape), P, U, P, SZ, P]
+        L.dsa_workspace_size.argtypes = [ctypes.POINTER(Shape), I]
+        L.dsa_workspace_size.restype = SZ
+        L.dsa_stack_chunk_rows.argtypes = [ctypes.POINTER(Shape)]
+        L.dsa_stack_chunk_rows.restype = I
+        L.dsa_check_pattern.argtypes = [ctypes.c_char_p, I, U]
+        L.dsa_pattern_from_freq.argtypes = [I, I, ctypes.c_char_p]
+        for f in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_stack", "dsa_check_pattern",
+                  "dsa_pattern_from_freq"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DSAError(status, lib().dsa_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+
+
+def abi_version() -> int:
+    return lib().dsa_abi_version()
+
+
+def index_scores(q_idx, k_idx, w_idx, kv_len=None, scores=None, ld=None, stream=None):
+    """dsa_index_scores: returns the fp32 score tensor [B, Tq, ld] (entries s > p untouched)."""
+    B, Tq, H_I, d_I = q_idx.shape
+    Tk = k_idx.shape[1]
+    ld = Tk if ld is None else ld
+    if scores is None:
+        scores = torch.full((B, Tq, ld), float("-inf"), dtype=torch.float32, device=q_idx.device)
+    _check(lib().dsa_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(kv_len), B, Tq, Tk, H_I, d_I,
+                                  _ptr(scores), ld, _stream(stream)))
+    return scores
+
+
+def topk(scores, k, Tk=None, kv_len=None, idx=None, stream=None):
+    """dsa_topk: int32 [B, Tq, k] ascending, -1 padded."""
+    B, Tq, ld = scores.shape
+    Tk = ld if Tk is None else Tk
+    if idx is None:
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device=scores.device)
+    _check(lib().dsa_topk(_ptr(scores), ld, _ptr(kv_len), B, Tq, Tk, k, _ptr(idx), None, 0, _stream(stream)))
+    return idx
+
+
+def _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, H_I=16, d_I=64, kv_len=None):
+    return Shape(B, Tq, Tk, H_I, d_I, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, _ptr(kv_len))
+
+
+def workspace_size(shape: Shape, op: int) -> int:
+    return lib().dsa_workspace_size(ctypes.byref(shape), op)
+
+
+def stack_chunk_rows(shape: Shape) -> int:
+    return lib().dsa_stack_chunk_rows(ctypes.byref(shape))
+
+
+def _workspace(nbytes, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, lse=None, want_lse=True,
+                ws=None, stream=None):
+    """dsa_sparse_attn: returns (out bf16 [B,Tq,H,Dv], lse fp32 [B,Tq,H] or None)."""
+    B, Tq, H, Dqk = q.shape
+    Tk, Hkv = kv.shape[1], kv.shape[2]
+    fp8 = kv.dtype == torch.uint8
+    if v is not None:
+        Dv = v.shape[3]
+    elif Dv is None:
+        raise ValueError("Dv is required when V is taken from the kv rows")
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, Tq, H, Dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
+    kvd = KV_FP8_E4M3 if fp8 else KV_BF16
+    shp = _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kvd)
+    nbytes = workspace_size(shp, OP_ATTN)
+    ws = _workspace(nbytes, q.device, ws)
+    _check(lib().dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(v), kvd, _ptr(idx), B, Tq, Tk, H, Hkv,
+                                 Dqk, Dv, k, sm_scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+    return out, lse
+
+
+def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=None, prefilled=False,
+                H_I=None, d_I=None, ws=None, want_lse=True, stream=None):
+    """dsa_layer_stack over `layers` (dicts with q/kv[/v/kv_scale] and, on F layers, q_idx/k_idx/w_idx).
+
+    Returns (outs, lses, index_cache).  Output tensors are allocated unless a layer dict
+    carries "out"/"lse".
+    """
+    n = len(layers)
+    L0 = layers[0]
+    B, Tq, H, Dqk = L0["q"].shape
+    Tk, Hkv = L0["kv"].shape[1], L0["kv"].shape[2]
+    fp8 = L0["kv"].dtype == torch.uint8
+    if L0.get("v") is not None:
+        Dv = L0["v"].shape[3]
+    elif Dv is None:
+        raise ValueError("Dv is required when V is taken from the kv rows")
+    f0 = next((L for c, L in zip(pattern, layers) if c == "F"), None)
+    if f0 is not None:
+        H_I, d_I = f0["q_idx"].shape[2], f0["q_idx"].shape[3]
+    H_I, d_I = H_I or 16, d_I or 64
+    dev = L0["q"].device
+    kvd = KV_FP8_E4M3 if fp8 else KV_BF16
+    shp = _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kvd, H_I, d_I, kv_len)
+    if index_cache is None:
+        index_cache = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+    ios = (LayerIO * n)()
+    outs, lses = [], []
+    for i, L in enumerate(layers):
+        o = L.get("out")
+        if o is None:
+            o = torch.empty((B, Tq, H, Dv), dtype=torch.bfloat16, device=dev)
+        ls = L.get("lse")
+        if ls is None and want_lse:
+            ls = torch.empty((B, Tq, H), dtype=torch.float32, device=dev)
+        outs.append(o)
+        lses.append(ls)
+        ios[i] = LayerIO(_ptr(L.get("q_idx")), _ptr(L.get("k_idx")), _ptr(L.get("w_idx")), _ptr(L["q"]),
+                         _ptr(L["kv"]), _ptr(L.get("kv_scale")), _ptr(L.get("v")), _ptr(o), _ptr(ls))
+    nbytes = workspace_size(shp, OP_STACK)
+    ws = _workspace(nbytes, dev, ws)
+    _check(lib().dsa_layer_stack(pattern.encode(), n, ios, ctypes.byref(shp), _ptr(index_cache),
+                                 CACHE_PREFILLED if prefilled else 0, _ptr(ws), nbytes, _stream(stream)))
+    return outs, lses, index_cache
+
+
+def check_pattern(pattern: str, n_layers: int = None, prefilled: bool = False) -> None:
+    n = len(pattern) if n_layers is None else n_layers
+    _check(lib().dsa_check_pattern(pattern.encode(), n, CACHE_PREFILLED if prefilled else 0))
+
+
+def pattern_from_freq(freq: int, n_layers: int) -> str:
+    buf = ctypes.create_string_buffer(max(0, n_layers) + 1)
+    _check(lib().dsa_pattern_from_freq(freq, n_layers, buf))
+    return buf.value.decode()

@@ -1,0 +1,265 @@
+// C ABI of the DSA library: argument checks, workspace planning and the IndexCache layer
+// stack.  Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "dsa.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+dsa_status launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Score chunk of the layer stack: at most this many bytes of fp32 score rows at a time.
+constexpr int64_t kChunkBytes = int64_t(128) << 20;
+
+int64_t stack_ld(int Tk) { return ((int64_t)Tk + 63) / 64 * 64; }
+
+int chunk_rows(const dsa_shape& s) {
+  const int64_t per_row = (int64_t)std::max(1, s.B) * stack_ld(s.Tk) * 4;
+  int64_t rows = std::max<int64_t>(1, kChunkBytes / std::max<int64_t>(1, per_row));
+  if (rows >= 64) rows = rows / 64 * 64;
+  return (int)std::min<int64_t>(rows, std::max(1, s.Tq));
+}
+
+dsa_status check_indexer(const void* q, const void* k, const void* w, int B, int Tq, int Tk, int H_I, int d_I,
+                         const float* scores, int64_t ld) {
+  if (B < 0 || Tq < 0 || Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
+  if (H_I < 1 || d_I < 1) return fail(DSA_ERR_SHAPE, "H_I and d_I must be >= 1");
+  if (ld < Tk) return fail(DSA_ERR_SHAPE, "ld must be >= Tk");
+  if (!dsa::indexer_supported(H_I, d_I))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer supports H_I in {1,2,4,8,16} and d_I in {16,32,64,128}");
+  if ((int64_t)B * Tq == 0) return DSA_OK;
+  if (!q || !k || !w || !scores) return fail(DSA_ERR_NULL, "q_idx, k_idx, w_idx and scores are required");
+  return DSA_OK;
+}
+
+dsa_status check_topk(const float* scores, int64_t ld, int B, int Tq, int Tk, int k, const int32_t* idx) {
+  if (B < 0 || Tq < 0 || Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
+  if (k < 1) return fail(DSA_ERR_SHAPE, "k must be >= 1");
+  if (ld < Tk) return fail(DSA_ERR_SHAPE, "ld must be >= Tk");
+  if (k > dsa::kTopkMaxK) return fail(DSA_ERR_UNSUPPORTED, "k must be <= 4096");
+  if (Tk > dsa::kTopkMaxTk) return fail(DSA_ERR_UNSUPPORTED, "Tk must be <= 2^24");
+  if ((int64_t)B * Tq == 0) return DSA_OK;
+  if (!scores || !idx) return fail(DSA_ERR_NULL, "scores and idx are required");
+  return DSA_OK;
+}
+
+dsa_status check_attn(const dsa::AttnArgs& a, size_t ws_bytes) {
+  if (a.B < 0 || a.Tq < 0 || a.Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
+  if (a.H < 1 || a.Hkv < 1 || a.Dqk < 1 || a.Dv < 1 || a.k < 1)
+    return fail(DSA_ERR_SHAPE, "H, Hkv, Dqk, Dv and k must be >= 1");
+  if (a.H % a.Hkv) return fail(DSA_ERR_SHAPE, "H must be a multiple of Hkv");
+  if (!a.v && a.Dv > a.Dqk) return fail(DSA_ERR_SHAPE, "Dv > Dqk needs a separate v");
+  if (!isfinite(a.sm_scale)) return fail(DSA_ERR_SHAPE, "sm_scale must be finite");
+  if (a.fp8 && a.v) return fail(DSA_ERR_UNSUPPORTED, "fp8 rows need V taken from kv (v = NULL)");
+  if (!dsa::attn_mla_supported(a) && !dsa::attn_mha_supported(a))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "supported: MLA (Hkv=1, Dqk=576, Dv=512, v=NULL, H%16==0, k<=65536, bf16/fp8) or "
+                "multi-head (Hkv=H<=16, Dqk=Dv=32, bf16, v given, k<=4096)");
+  if ((int64_t)a.B * a.Tq == 0) return DSA_OK;
+  if (!a.q || !a.kv || !a.idx || !a.out) return fail(DSA_ERR_NULL, "q, kv, idx and out are required");
+  if (a.fp8 && !a.kv_scale) return fail(DSA_ERR_NULL, "kv_scale is required for fp8 rows");
+  const size_t need = dsa::attn_workspace_bytes(a.B, a.Tq, a.H, a.Dv, a.k, dsa::attn_mla_supported(a));
+  if (need && (!a.ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "attention workspace too small: need " + std::to_string(need) + " bytes");
+  return DSA_OK;
+}
+
+dsa::AttnArgs attn_args(const void* q, const void* kv, const float* kv_scale, const void* v, dsa_kv_dtype kv_dtype,
+                        const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv, int Dqk, int Dv, int k,
+                        float sm_scale, void* out, float* lse, void* ws) {
+  dsa::AttnArgs a;
+  a.q = (const uint16_t*)q;
+  a.kv = kv;
+  a.kv_scale = kv_scale;
+  a.v = (const uint16_t*)v;
+  a.fp8 = kv_dtype == DSA_KV_FP8_E4M3;
+  a.idx = idx;
+  a.B = B;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.Dqk = Dqk;
+  a.Dv = Dv;
+  a.k = k;
+  a.sm_scale = sm_scale;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.ws = ws;
+  return a;
+}
+
+bool valid_kv_dtype(dsa_kv_dtype d) { return d == DSA_KV_BF16 || d == DSA_KV_FP8_E4M3; }
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_PATTERN: return "DSA_ERR_PATTERN";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH";
+    case DSA_ERR_DEVICE: return "DSA_ERR_DEVICE";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_idx, const int32_t* kv_len, int B,
+                            int Tq, int Tk, int H_I, int d_I, float* scores, int64_t ld, void* stream) {
+  dsa_status st = check_indexer(q_idx, k_idx, w_idx, B, Tq, Tk, H_I, d_I, scores, ld);
+  if (st != DSA_OK || (int64_t)B * Tq == 0 || Tk == 0) return st;
+  dsa::IndexerArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, kv_len, B, Tq, Tk,
+                     H_I, d_I, 0, Tq, scores, ld, (int64_t)Tq * ld};
+  return launch_status(dsa::launch_index_scores(a, as_stream(stream)), "dsa_index_scores");
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk, int k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  dsa_status st = check_topk(scores, ld, B, Tq, Tk, k, idx);
+  if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
+  dsa::TopkArgs a{scores, ld, (int64_t)Tq * ld, kv_len, B, Tq, Tk, k, 0, Tq, idx};
+  return launch_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk");
+}
+
+dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
+                           dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv, int Dqk,
+                           int Dv, int k, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!valid_kv_dtype(kv_dtype)) return fail(DSA_ERR_SHAPE, "unknown kv dtype");
+  dsa::AttnArgs a = attn_args(q, kv, kv_scale, v, kv_dtype, idx, B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, out, lse, ws);
+  dsa_status st = check_attn(a, ws_bytes);
+  if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
+  return launch_status(dsa::launch_sparse_attn(a, as_stream(stream)), "dsa_sparse_attn");
+}
+
+dsa_status dsa_check_pattern(const char* pattern, int n_layers, unsigned flags) {
+  if (!pattern) return fail(DSA_ERR_NULL, "pattern is required");
+  if (n_layers < 0) return fail(DSA_ERR_PATTERN, "n_layers must be >= 0");
+  const size_t len = strnlen(pattern, (size_t)n_layers + 1);
+  if (len != (size_t)n_layers) return fail(DSA_ERR_PATTERN, "pattern length must equal n_layers");
+  for (int i = 0; i < n_layers; ++i)
+    if (pattern[i] != 'F' && pattern[i] != 'S')
+      return fail(DSA_ERR_PATTERN, "pattern character " + std::to_string(i) + " is not 'F' or 'S'");
+  if (n_layers > 0 && pattern[0] == 'S' && !(flags & DSA_CACHE_PREFILLED))
+    return fail(DSA_ERR_PATTERN, "a leading 'S' layer has no cached indices (set DSA_CACHE_PREFILLED)");
+  return DSA_OK;
+}
+
+dsa_status dsa_pattern_from_freq(int freq, int n_layers, char* out) {
+  if (!out) return fail(DSA_ERR_NULL, "out is required");
+  if (freq < 1 || n_layers < 0) return fail(DSA_ERR_PATTERN, "freq must be >= 1 and n_layers >= 0");
+  for (int i = 0; i < n_layers; ++i) out[i] = (i % freq == 0) ? 'F' : 'S';
+  out[n_layers] = '\0';
+  return DSA_OK;
+}
+
+int dsa_stack_chunk_rows(const dsa_shape* shape) { return shape ? chunk_rows(*shape) : 1; }
+
+size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
+  if (!s || s->B < 0 || s->Tq < 0 || s->Tk < 0 || s->H < 1 || s->Dv < 1 || s->k < 1) return 0;
+  const bool mla = s->Hkv == 1 && s->Dqk == 576 && s->Dv == 512;
+  switch (op) {
+    case DSA_OP_SCORES:
+    case DSA_OP_TOPK: return 0;
+    case DSA_OP_ATTN: return dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
+    case DSA_OP_STACK: {
+      const size_t scores = (size_t)s->B * chunk_rows(*s) * stack_ld(s->Tk) * sizeof(float);
+      return align_up(scores) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
+    }
+  }
+  return 0;
+}
+
+dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers, const dsa_shape* shape,
+                           int32_t* index_cache, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  if (!shape) return fail(DSA_ERR_NULL, "shape is required");
+  dsa_status st = dsa_check_pattern(pattern, n_layers, flags);
+  if (st != DSA_OK) return st;
+  if (n_layers > 0 && !layers) return fail(DSA_ERR_NULL, "layers is required");
+  const dsa_shape& s = *shape;
+  if (!valid_kv_dtype(s.kv_dtype)) return fail(DSA_ERR_SHAPE, "unknown kv dtype");
+  // validate every layer before enqueueing anything
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_io& L = layers[l];
+    const std::string at = " (layer " + std::to_string(l) + ")";
+    if (pattern[l] == 'F') {
+      // the score rows live in the workspace, which is checked below
+      const float* ws_scores = reinterpret_cast<const float*>(&s);
+      st = check_indexer(L.q_idx, L.k_idx, L.w_idx, s.B, s.Tq, s.Tk, s.H_I, s.d_I, ws_scores, stack_ld(s.Tk));
+      if (st != DSA_OK) return fail(st, g_last_error + at);
+      st = check_topk(ws_scores, stack_ld(s.Tk), s.B, s.Tq, s.Tk, s.k, index_cache);
+      if (st != DSA_OK) return fail(st, g_last_error + at);
+    }
+    dsa::AttnArgs a = attn_args(L.q, L.kv, L.kv_scale, L.v, s.kv_dtype, index_cache, s.B, s.Tq, s.Tk, s.H, s.Hkv,
+                                s.Dqk, s.Dv, s.k, s.sm_scale, L.out, L.lse, ws);
+    st = check_attn(a, (size_t)-1);
+    if (st != DSA_OK) return fail(st, g_last_error + at);
+  }
+  if ((int64_t)s.B * s.Tq == 0 || n_layers == 0) return DSA_OK;
+  if (!index_cache) return fail(DSA_ERR_NULL, "index_cache is required");
+  const size_t need = dsa_workspace_size(shape, DSA_OP_STACK);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "stack workspace too small: need " + std::to_string(need) + " bytes");
+
+  const int Tc = chunk_rows(s);
+  const int64_t ld = stack_ld(s.Tk);
+  float* scores = reinterpret_cast<float*>(ws);
+  void* attn_ws = reinterpret_cast<char*>(ws) + align_up((size_t)s.B * Tc * ld * sizeof(float));
+  hipStream_t strm = as_stream(stream);
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_io& L = layers[l];
+    if (pattern[l] == 'F' && s.Tk > 0) {
+      for (int r0 = 0; r0 < s.Tq; r0 += Tc) {
+        const int n = std::min(Tc, s.Tq - r0);
+        dsa::IndexerArgs ia{(const uint16_t*)L.q_idx, (const uint16_t*)L.k_idx, (const uint16_t*)L.w_idx, s.kv_len,
+                            s.B, s.Tq, s.Tk, s.H_I, s.d_I, r0, n, scores, ld, (int64_t)Tc * ld};
+        st = launch_status(dsa::launch_index_scores(ia, strm), "dsa_layer_stack: indexer");
+        if (st != DSA_OK) return st;
+        dsa::TopkArgs ta{scores, ld, (int64_t)Tc * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, index_cache};
+        st = launch_status(dsa::launch_topk(ta, strm), "dsa_layer_stack: top-k");
+        if (st != DSA_OK) return st;
+      }
+    } else if (pattern[l] == 'F') {  // no keys at all: every row selects nothing
+      dsa::TopkArgs ta{scores, ld, 0, s.kv_len, s.B, s.Tq, s.Tk, s.k, 0, s.Tq, index_cache};
+      st = launch_status(dsa::launch_topk(ta, strm), "dsa_layer_stack: top-k");
+      if (st != DSA_OK) return st;
+    }
+    dsa::AttnArgs a = attn_args(L.q, L.kv, L.kv_scale, L.v, s.kv_dtype, index_cache, s.B, s.Tq, s.Tk, s.H, s.Hkv,
+                                s.Dqk, s.Dv, s.k, s.sm_scale, L.out, L.lse, attn_ws);
+    st = launch_status(dsa::launch_sparse_attn(a, strm), "dsa_layer_stack: attention");
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

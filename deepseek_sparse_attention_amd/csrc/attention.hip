@@ -1,0 +1,453 @@
+// Attention restricted to each query's selected keys, on gfx950.
+//
+//   out[h] = sum_s softmax_s(sm_scale * q[h] . K[s]) V[s],  s over the row's index list
+//
+// MLA form (DeepSeek-V2-Lite-Chat SIQ card, "Measured": one 576-wide latent row per token,
+// 512 compressed-KV values then 64 rotary values; V = the first 512 values of the same
+// row).  A workgroup serves one query row and 16 heads.  Per tile of 64 selected keys the
+// gathered rows are staged once in LDS and used twice: as K (all 576 columns) for
+// S = Q K^T with the 16 heads as the MFMA M dimension, and as V (columns 0..511) for
+// O += P V, read transposed straight from LDS with ds_read_b64_tr_b16.  The 4 waves split
+// the keys of a tile for Q K^T and the 512 value columns for P V; softmax statistics are
+// exchanged through LDS (online softmax in base 2).  The next tile's gather is issued into
+// registers before the current tile is computed.  fp8 (OCP e4m3) rows are widened to bf16
+// exactly while staged; their per-token scale multiplies the logit and the probability.
+// Decode rows (few queries) split the key list over workgroups and merge the partial
+// results by log-sum-exp in a second kernel, in a fixed order.
+//
+// Multi-head form (DSA ablation card: 4 heads of width 32, RoPE'd inputs): one wave per
+// head, logits in LDS, three fixed-order passes.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kDqk = 576, kDv = 512;
+constexpr int kTile = 64;              // keys per tile
+constexpr int kPitch = kDqk * 2 + 16;  // LDS row pitch in bytes (1168: 16-B skew per row)
+constexpr int kPPitch = kTile * 2 + 16;  // P tile pitch in bytes (144)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool FP8>
+struct TileStage;
+
+template <>
+struct TileStage<false> {  // bf16 rows: 72 chunks of 16 B
+  static constexpr int kChunks = kTile * (kDqk * 2 / 16) / 256;  // 18 per thread
+  u32x4 r[kChunks];
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int ch = tid + 256 * c, key = ch / 72, part = ch % 72;
+      *reinterpret_cast<u32x4*>(lds + key * kPitch + part * 16) = r[c];
+    }
+  }
+};
+
+template <>
+struct TileStage<true> {  // e4m3 rows: 36 chunks of 16 B, widened to bf16 (exact)
+  static constexpr int kChunks = kTile * (kDqk / 16) / 256;  // 9 per thread
+  u32x4 r[kChunks];
+  template <bool HI>
+  __device__ __forceinline__ static uint32_t widen2(uint32_t word) {
+    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+    // e4m3 values are exact in bf16: the low 16 bits of the fp32 pattern are zero
+    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int ch = tid + 256 * c, key = ch / 36, part = ch % 36;
+      u32x4 lo, hi;
+      lo[0] = widen2<false>(r[c][0]);
+      lo[1] = widen2<true>(r[c][0]);
+      lo[2] = widen2<false>(r[c][1]);
+      lo[3] = widen2<true>(r[c][1]);
+      hi[0] = widen2<false>(r[c][2]);
+      hi[1] = widen2<true>(r[c][2]);
+      hi[2] = widen2<false>(r[c][3]);
+      hi[3] = widen2<true>(r[c][3]);
+      uint8_t* dst = lds + key * kPitch + part * 32;
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 16) = hi;
+    }
+  }
+};
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                                                          const float* __restrict__ kv_scale,
+                                                          const int32_t* __restrict__ idx, int Tq, int Tk, int H, int k,
+                                                          float scale_log2, int tiles_per_split,
+                                                          uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                          float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t ps[16 * kPPitch];
+  __shared__ float red_m[4][16], red_l[4][16];
+  __shared__ float tile_scale[kTile];
+  __shared__ int tile_valid[kTile];
+  __shared__ int jmax_red[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int HG = H >> 4;
+  const int64_t rowh = blockIdx.x;  // (b*Tq + t)*HG + hg
+  const int64_t row = rowh / HG;
+  const int hg = (int)(rowh % HG);
+  const int b = (int)(row / Tq);
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int32_t* ix = idx + row * k;
+  const uint8_t* kvb = kv + (int64_t)b * Tk * (FP8 ? kDqk : kDqk * 2);
+
+  // extent of the index list that holds valid entries
+  int jm = -1;
+  for (int j = tid; j < k; j += 256) {
+    const int s = ix[j];
+    if (s >= 0 && s < Tk) jm = j;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
+  if (lane == 0) jmax_red[wave] = jm;
+  __syncthreads();
+  jm = max(max(jmax_red[0], jmax_red[1]), max(jmax_red[2], jmax_red[3]));
+  const int ntiles = (jm + kTile) / kTile;  // tiles covering entries 0..jm
+  const int t_begin = split * tiles_per_split;
+  const int t_end = min(ntiles, t_begin + tiles_per_split);
+
+  // Q as the A operand of 16x16x32: lane = head (lane%16), 8 dims per k-step
+  const int hl = lane & 15, gq = lane >> 4;
+  bf16x8 qa[kDqk / 32];
+  {
+    const uint16_t* qp = q + (row * H + hg * 16 + hl) * kDqk + gq * 8;
+#pragma unroll
+    for (int s = 0; s < kDqk / 32; ++s) qa[s] = as_bf16x8(ld16(qp + s * 32));
+  }
+
+  f32x4 o_acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+
+  TileStage<FP8> stage;
+  int my_s = 0;
+  float my_scale = 1.f;
+  auto fetch_meta = [&](int t) {  // thread < 64 owns key tid of the tile
+    if (tid < kTile) {
+      const int j = t * kTile + tid;
+      my_s = (j < k) ? ix[j] : -1;
+      my_scale = 1.f;
+      if (my_s >= 0 && my_s < Tk) {
+        if (FP8) my_scale = kv_scale[(int64_t)b * Tk + my_s];
+      } else {
+        my_s = -1;
+      }
+    }
+  };
+  // entries past k are never read: a partial last tile repeats entry k-1 (masked later)
+  // rows are gathered with range-checked buffer loads: 32-bit offsets, one VGPR each
+  constexpr uint32_t kRowBytes = FP8 ? kDqk : kDqk * 2;
+  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kvb, (uint32_t)Tk * kRowBytes);
+  auto safe_load = [&](int t) {
+    const int j0 = t * kTile;
+    constexpr int per = FP8 ? 36 : 72;
+#pragma unroll
+    for (int c = 0; c < TileStage<FP8>::kChunks; ++c) {
+      const int ch = tid + 256 * c, key = ch / per, part = ch % per;
+      int s = ix[min(j0 + key, k - 1)];
+      s = (s >= 0 && s < Tk) ? s : 0;
+      stage.r[c] = buf_load_16(kv_rs, (uint32_t)s * kRowBytes + part * 16, 0);
+    }
+  };
+
+  if (t_begin < t_end) {
+    safe_load(t_begin);
+    fetch_meta(t_begin);
+  }
+  for (int t = t_begin; t < t_end; ++t) {
+    __syncthreads();  // previous tile fully consumed
+    stage.store(kvs, tid);
+    if (tid < kTile) {
+      tile_valid[tid] = my_s >= 0;
+      tile_scale[tid] = my_scale;
+    }
+    __syncthreads();
+    if (t + 1 < t_end) {
+      safe_load(t + 1);
+      fetch_meta(t + 1);
+    }
+
+    // ---- S = Q K^T for keys 16*wave .. 16*wave+15 of the tile
+    const int kl = 16 * wave + hl;  // this lane's key (B column)
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* krow = kvs + kl * kPitch + gq * 16;
+#pragma unroll
+    for (int s = 0; s < kDqk / 32; ++s) {
+      bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + s * 64));
+      sacc = mfma16(qa[s], kb, sacc);
+    }
+    const bool kvalid = tile_valid[kl] != 0;
+    const float ksc = tile_scale[kl];
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = kvalid ? sacc[i] * (ksc * scale_log2) : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float wm = group16_max(sv[i]);
+      if (hl == 0) red_m[wave][gq * 4 + i] = wm;
+    }
+    __syncthreads();
+    float alpha[4], pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = gq * 4 + i;
+      const float tm = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+      const float mn = fmaxf(m_run[i], tm);
+      alpha[i] = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[i] - mn);
+      pv[i] = (sv[i] == -INFINITY) ? 0.f : fast_exp2(sv[i] - mn);
+      m_run[i] = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ws = group16_sum(pv[i]);
+      if (hl == 0) red_l[wave][gq * 4 + i] = ws;
+      // P (times the fp8 row scale for V) as bf16: row = head, column = key
+      *reinterpret_cast<uint16_t*>(ps + (gq * 4 + i) * kPPitch + kl * 2) = f32_to_bf16_bits(pv[i] * ksc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = gq * 4 + i;
+      l_run[i] = l_run[i] * alpha[i] + (((red_l[0][h] + red_l[1][h]) + red_l[2][h]) + red_l[3][h]);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o_acc[n][i] *= alpha[i];
+
+    // ---- O[:, wave*128 .. +128] += P V
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ps + hl * kPPitch + (ks * 32 + gq * 8) * 2));
+      const int kb0 = ks * 32 + gq * 8 + (hl >> 2);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int col = wave * 128 + n * 16 + 4 * (hl & 3);
+        const i16x4 v0 = lds_read_tr16(kvs + kb0 * kPitch + col * 2);
+        const i16x4 v1 = lds_read_tr16(kvs + (kb0 + 4) * kPitch + col * 2);
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o_acc[n] = mfma16(pa, __builtin_bit_cast(bf16x8, vv), o_acc[n]);
+      }
+    }
+  }
+
+  // ---- results: lane holds O[head gq*4+i][wave*128 + n*16 + hl]
+  if (nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = hg * 16 + gq * 4 + i;
+      const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
+      uint16_t* op = out + (row * H + h) * kDv + wave * 128 + hl;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) op[n * 16] = f32_to_bf16_bits(o_acc[n][i] * inv);
+      if (lse && wave == 0 && hl == 0)
+        lse[row * H + h] = l_run[i] > 0.f ? (m_run[i] + __log2f(l_run[i])) * kLn2 : -INFINITY;
+    }
+  } else {
+    const int64_t nrowh = (int64_t)gridDim.x * 16;  // (row, head) pairs over all rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rh = rowh * 16 + gq * 4 + i;
+      float* po = part_o + ((int64_t)split * nrowh + rh) * kDv + wave * 128 + hl;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) po[n * 16] = o_acc[n][i];
+      if (wave == 0 && hl == 0) {
+        part_ml[((int64_t)split * nrowh + rh) * 2 + 0] = m_run[i];
+        part_ml[((int64_t)split * nrowh + rh) * 2 + 1] = l_run[i];
+      }
+    }
+  }
+}
+
+// Merge split-key partial results (fixed split order).  One workgroup per (row, head).
+__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                          int nsplit, int64_t nrowh, int H, uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int64_t rh = blockIdx.x;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[((int64_t)s * nrowh + rh) * 2]);
+  float l = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = part_ml[((int64_t)s * nrowh + rh) * 2];
+    if (ms != -INFINITY) l += part_ml[((int64_t)s * nrowh + rh) * 2 + 1] * fast_exp2(ms - m);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  for (int d = threadIdx.x; d < kDv; d += blockDim.x) {
+    float o = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = part_ml[((int64_t)s * nrowh + rh) * 2];
+      if (ms != -INFINITY) o += part_o[((int64_t)s * nrowh + rh) * kDv + d] * fast_exp2(ms - m);
+    }
+    out[rh * kDv + d] = f32_to_bf16_bits(o * inv);
+  }
+  if (lse && threadIdx.x == 0) lse[rh] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// Multi-head form: Dqk = Dv = 32, Hkv = H, one wave per head (heads strided over 4 waves),
+// logits of up to kMhaMaxK selected keys kept in LDS.
+constexpr int kMhaD = 32;
+constexpr int kMhaMaxK = 4096;
+
+__global__ __launch_bounds__(256) void mha_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kk,
+                                                       const uint16_t* __restrict__ vv, const int32_t* __restrict__ idx,
+                                                       int Tq, int Tk, int H, int k, float scale_log2,
+                                                       uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float zb[4][kMhaMaxK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int b = (int)(row / Tq);
+  const int32_t* ix = idx + row * k;
+  float* z = zb[wave];
+  // every wave runs the same number of rounds, so the barriers below are uniform
+  for (int h0 = 0; h0 < H; h0 += 4) {
+    const int h = h0 + wave;
+    const bool active = h < H;
+    float m = -INFINITY, l = 0.f;
+    if (active) {
+      float qf[kMhaD];
+      const uint16_t* qp = q + (row * H + h) * kMhaD;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 w4 = ld16(qp + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[c * 8 + 2 * e] = __uint_as_float(w4[e] << 16);
+          qf[c * 8 + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
+      }
+      for (int j = lane; j < k; j += 64) {
+        const int s = ix[j];
+        float zz = -INFINITY;
+        if (s >= 0 && s < Tk) {
+          const uint16_t* kp = kk + (((int64_t)b * Tk + s) * H + h) * kMhaD;
+          float dot = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4 w4 = ld16(kp + c * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dot = fmaf(qf[c * 8 + 2 * e], __uint_as_float(w4[e] << 16), dot);
+              dot = fmaf(qf[c * 8 + 2 * e + 1], __uint_as_float(w4[e] & 0xFFFF0000u), dot);
+            }
+          }
+          zz = dot * scale_log2;
+        }
+        z[j] = zz;
+        m = fmaxf(m, zz);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      for (int j = lane; j < k; j += 64) {
+        const float p = (z[j] == -INFINITY) ? 0.f : fast_exp2(z[j] - m);
+        z[j] = p;
+        l += p;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+    }
+    __syncthreads();  // probabilities written by other lanes are read below
+    if (active) {
+      // P V: lane -> (column d = lane % 32, half = lane / 32), keys of that parity
+      const int d = lane & 31, half = lane >> 5;
+      float o = 0.f;
+      for (int j = half; j < k; j += 2) {
+        const float p = z[j];
+        if (p != 0.f) {
+          const int s = ix[j];
+          o = fmaf(p, bf16_bits_to_f32(vv[(((int64_t)b * Tk + s) * H + h) * kMhaD + d]), o);
+        }
+      }
+      o += __shfl_xor(o, 32, 64);
+      if (half == 0) out[(row * H + h) * kMhaD + d] = f32_to_bf16_bits(l > 0.f ? o / l : 0.f);
+      if (lse && lane == 0) lse[row * H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();  // z is reused by the next round
+  }
+}
+
+}  // namespace
+
+bool attn_mla_supported(const AttnArgs& a) {
+  // the gather addresses a sequence's rows with 32-bit byte offsets
+  const int64_t seq_bytes = (int64_t)a.Tk * (a.fp8 ? kDqk : kDqk * 2);
+  return a.Hkv == 1 && a.Dqk == kDqk && a.Dv == kDv && a.v == nullptr && a.H % 16 == 0 && a.H > 0 && a.k >= 1 &&
+         a.k <= 65536 && seq_bytes < (int64_t(1) << 32);
+}
+
+bool attn_mha_supported(const AttnArgs& a) {
+  return !a.fp8 && a.Hkv == a.H && a.H >= 1 && a.H <= 16 && a.Dqk == kMhaD && a.Dv == kMhaD && a.v != nullptr &&
+         a.k >= 1 && a.k <= kMhaMaxK;
+}
+
+int attn_mla_splits(int B, int Tq, int H, int k) {
+  const int64_t wgs = (int64_t)B * Tq * (H / 16);
+  const int tiles = (k + kTile - 1) / kTile;
+  if (wgs >= 512) return 1;
+  int s = (int)std::min<int64_t>(tiles, (1024 + wgs - 1) / std::max<int64_t>(1, wgs));
+  if (s <= 1) return 1;
+  const int per = (tiles + s - 1) / s;
+  return (tiles + per - 1) / per;
+}
+
+size_t attn_workspace_bytes(int B, int Tq, int H, int Dv, int k, bool mla) {
+  if (!mla) return 0;
+  const int s = attn_mla_splits(B, Tq, H, k);
+  if (s <= 1) return 0;
+  const size_t nrowh = (size_t)B * Tq * H;
+  return (size_t)s * nrowh * ((size_t)Dv + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.Tq;
+  if (rows == 0) return hipSuccess;
+  if (attn_mla_supported(a)) {
+    const float sl2 = a.sm_scale * kLog2e;
+    const int tiles = (a.k + kTile - 1) / kTile;
+    const int nsplit = attn_mla_splits(a.B, a.Tq, a.H, a.k);
+    const int per = (tiles + nsplit - 1) / nsplit;
+    const int64_t nrowh = rows * a.H;
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
+    if (nsplit > 1) {
+      part_o = reinterpret_cast<float*>(a.ws);
+      part_ml = part_o + (size_t)nsplit * nrowh * kDv;
+    }
+    dim3 grid((unsigned)(rows * (a.H / 16)), nsplit);
+    if (a.fp8)
+      hipLaunchKernelGGL(mla_attn_kernel<true>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale, a.idx,
+                         a.Tq, a.Tk, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+    else
+      hipLaunchKernelGGL(mla_attn_kernel<false>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr, a.idx,
+                         a.Tq, a.Tk, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit == 1) return e;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)nrowh), dim3(256), 0, st, part_o, part_ml, nsplit, nrowh,
+                       a.H, a.out, a.lse);
+    return hipGetLastError();
+  }
+  if (attn_mha_supported(a)) {
+    hipLaunchKernelGGL(mha_attn_kernel, dim3((unsigned)rows), dim3(256), 0, st, a.q, (const uint16_t*)a.kv, a.v,
+                       a.idx, a.Tq, a.Tk, a.H, a.k, a.sm_scale * kLog2e, a.out, a.lse);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

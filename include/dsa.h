@@ -1,0 +1,181 @@
+/*
+ * dsa.h - C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD Instinct MI355X
+ * (gfx950).  Plain C99: no HIP or torch types.  Streams are passed as `void*` holding a
+ * hipStream_t (NULL = the default stream).
+ *
+ * The path (as the source pages describe DSA):
+ *   1. lightning-indexer scores  I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j] . k_I[s]) over causal
+ *      keys s <= t ("DSA ablation model card", model list: a ReLU indexer with a few small
+ *      heads selects each query's top keys; its parameter count fixes one indexer key per
+ *      token, shared by the heads);
+ *   2. a per-query causal top-k (k = 512 on that card; 2048 on the "DSV2-Lite-IndexCache-
+ *      Sparse-1250" card, intro), where a query with fewer than k causal keys keeps all of
+ *      them (ablation card, "Benchmarks" note);
+ *   3. softmax attention over the selected keys only, in multi-head form or in the MLA
+ *      latent form (one shared 576-wide row per token: 512 compressed-KV values then 64
+ *      rotary values, "DeepSeek-V2-Lite-Chat SIQ K4/K3" card, "Measured"; V = the first
+ *      512 values of the same row);
+ *   4. IndexCache reuse across layers: 'F' layers compute and store the top-k indices, 'S'
+ *      layers attend with the indices handed down the stack ("IndexCache" vLLM feature
+ *      doc, "How It Works"; pattern semantics from its "Configuration Reference").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, in device memory the caller allocated; the library
+ *     never allocates, frees or synchronizes.  All work is enqueued in order on `stream`.
+ *     Inputs must stay valid until that work completes.  Outputs must not alias inputs.
+ *   - bf16 tensors hold IEEE bfloat16 values; fp8 tensors hold OCP e4m3 ("e4m3fn") bytes.
+ *   - Positions: sequence b holds L_b = kv_len[b] keys (kv_len: device int32[B], or NULL
+ *     meaning L_b = Tk for every b).  Query row i of the Tq rows of sequence b sits at
+ *     position p = L_b - Tq + i and may attend keys 0..p (its own key included).  Prefill:
+ *     Tq = Tk = T.  Decode: Tq = 1, kv_len = cache lengths.  Values of kv_len are clamped
+ *     to [0, Tk] on the device; rows with p < 0 have no candidates.
+ *   - Errors: arguments are checked on the host before anything is enqueued; a status
+ *     other than DSA_OK means nothing ran.  DSA_ERR_LAUNCH reports a failed kernel launch
+ *     (work enqueued before it in the same call may have run).  Device faults surface at
+ *     the caller's next synchronization.  dsa_last_error() gives a message for the calling
+ *     thread's last failure.
+ *   - Determinism: identical inputs and shapes give bit-identical outputs (fixed reduction
+ *     orders, no floating-point atomics), whatever chunk size the library picks.
+ *   - Thread safety: re-entrant; concurrent calls on different streams need separate
+ *     workspaces.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+  DSA_ERR_UNSUPPORTED = 3, /* a valid shape this build has no kernel for */
+  DSA_ERR_PATTERN = 4,     /* bad F/S pattern */
+  DSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than dsa_workspace_size() */
+  DSA_ERR_LAUNCH = 6,      /* a HIP launch failed */
+  DSA_ERR_DEVICE = 7       /* no usable gfx950 device / HIP runtime error */
+} dsa_status;
+
+typedef enum { DSA_KV_BF16 = 0, DSA_KV_FP8_E4M3 = 1 } dsa_kv_dtype;
+
+typedef enum { DSA_OP_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_ATTN = 2, DSA_OP_STACK = 3 } dsa_op;
+
+/* flags of dsa_layer_stack */
+#define DSA_CACHE_PREFILLED 1u /* index_cache already holds indices: a leading 'S' may reuse them */
+
+int dsa_abi_version(void);
+const char* dsa_last_error(void);
+const char* dsa_status_string(dsa_status s);
+
+/*
+ * Lightning-indexer scores (step 1).
+ *   q_idx  bf16 [B][Tq][H_I][d_I]  per-query indexer heads
+ *   k_idx  bf16 [B][Tk][d_I]       one indexer key per token, shared by all heads
+ *   w_idx  bf16 [B][Tq][H_I]       per-query head weights
+ *   scores fp32 [B][Tq][ld], ld >= Tk: for every row, entries s = 0..p are written with
+ *          I[t,s] (fp32 accumulation of the bf16 products, ReLU per head, then the weighted
+ *          head sum in head order); entries s > p are not written.
+ * Supported: H_I in {1,2,4,8,16}, d_I in {16,32,64,128}, Tk <= 2^31 - 1.
+ */
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_idx,
+                            const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I,
+                            float* scores, int64_t ld, void* stream);
+
+/*
+ * Causal top-k (step 2).
+ *   scores fp32 [B][Tq][ld]: only entries 0..p of each row are read.
+ *   idx    int32 [B][Tq][k]: if p+1 <= k, the keys 0..p; otherwise the k keys of largest
+ *          score, equal scores resolved toward the lower key index, -0.0 equal to +0.0;
+ *          either way sorted ascending and padded with -1 up to k entries.
+ * Scores must not be NaN.  Supported: 1 <= k <= 4096, Tk <= 65536 (rows kept in
+ * registers) or Tk <= 2^24 (rows re-read per pass).  ws/ws_bytes: reserved, may be NULL/0.
+ */
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk,
+                    int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Attention restricted to the selected keys (step 3).
+ *   q     bf16 [B][Tq][H][Dqk]
+ *   kv    [B][Tk][Hkv][Dqk], bf16 (DSA_KV_BF16) or e4m3 bytes (DSA_KV_FP8_E4M3)
+ *   kv_scale fp32 [B][Tk] for fp8 (key row value = e4m3 value * kv_scale[b][s]); else NULL
+ *   v     bf16 [B][Tk][Hkv][Dv], or NULL: V is kv[..., 0:Dv] (MLA shared latent row)
+ *   idx   int32 [B][Tq][k]: key indices per query row, shared by all heads; entries
+ *         outside [0, Tk) (e.g. the -1 padding) are skipped
+ *   out   bf16 [B][Tq][H][Dv] = sum_s softmax_s(sm_scale * q[h].K[s]) V[s] over valid s
+ *         (0 for a row with no valid entry); head h reads kv head h*Hkv/H
+ *   lse   fp32 [B][Tq][H] natural-log sum-exp of the scaled logits (-inf if none), or NULL
+ *   ws    device workspace of at least dsa_workspace_size(shape, DSA_OP_ATTN) bytes (may be
+ *         NULL when that size is 0); used for split-key partial results
+ * Supported: MLA (Hkv = 1, Dqk = 576, Dv = 512, v = NULL, H a multiple of 16, bf16 or fp8)
+ * and multi-head (Hkv = H <= 16, Dqk = Dv = 32, bf16, v given); 1 <= k <= 65536.
+ */
+dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
+                           dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk, int H,
+                           int Hkv, int Dqk, int Dv, int k, float sm_scale, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Shape of one layer of a stack (all layers share it). */
+typedef struct {
+  int B, Tq, Tk;        /* sequences, query rows per sequence, keys per sequence */
+  int H_I, d_I;         /* indexer heads and width */
+  int H, Hkv, Dqk, Dv;  /* attention heads, kv heads, q/k width, v width */
+  int k;                /* top-k budget */
+  float sm_scale;       /* softmax scale (e.g. 1/sqrt(Dqk)); not fixed by the pages */
+  dsa_kv_dtype kv_dtype;
+  const int32_t* kv_len; /* device int32[B] or NULL */
+} dsa_shape;
+
+/* Per-layer tensors (layouts as in the calls above).  q_idx/k_idx/w_idx are read on 'F'
+ * layers only and may be NULL on 'S' layers. */
+typedef struct {
+  const void* q_idx;
+  const void* k_idx;
+  const void* w_idx;
+  const void* q;
+  const void* kv;
+  const float* kv_scale;
+  const void* v;
+  void* out;
+  float* lse;
+} dsa_layer_io;
+
+/*
+ * IndexCache layer stack (step 4 around steps 1-3).
+ *   pattern  host string of n_layers characters, 'F' (full) or 'S' (shared)
+ *   layers   host array [n_layers]
+ *   index_cache int32 [B][Tq][k] device buffer handed down the stack: an 'F' layer overwrites
+ *            it with its own top-k indices, every layer then attends with it as it stands.
+ *            A leading 'S' is rejected unless flags has DSA_CACHE_PREFILLED.
+ *   ws       at least dsa_workspace_size(shape, DSA_OP_STACK) bytes: one chunk of score rows
+ *            (the full Tq x Tk score matrix is never held) plus the attention workspace.
+ */
+dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers,
+                           const dsa_shape* shape, int32_t* index_cache, unsigned flags, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs for `shape` (0 if none); 0 also for an invalid shape. */
+size_t dsa_workspace_size(const dsa_shape* shape, dsa_op op);
+
+/* Query rows per score chunk that dsa_layer_stack uses for `shape` (>= 1). */
+int dsa_stack_chunk_rows(const dsa_shape* shape);
+
+/* Check an F/S pattern: DSA_OK, or DSA_ERR_PATTERN (wrong length, a character other than
+ * 'F'/'S', or a leading 'S' without DSA_CACHE_PREFILLED). */
+dsa_status dsa_check_pattern(const char* pattern, int n_layers, unsigned flags);
+
+/* The pattern of index_topk_freq = freq ("compute on 1/freq of layers", IndexCache doc,
+ * "Configuration Reference"): layer i is 'F' iff i % freq == 0.  out: n_layers + 1 chars
+ * (NUL-terminated).  freq = 1 gives all 'F' (IndexCache off). */
+dsa_status dsa_pattern_from_freq(int freq, int n_layers, char* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

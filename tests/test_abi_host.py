@@ -1,0 +1,129 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and its
+argument checks reject bad calls before touching the GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from tests.conftest import ROOT, golden
+
+import deepseek_sparse_attention_amd as dsa
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.LIB_PATH):
+        from deepseek_sparse_attention_amd import build
+        build.build()
+    return dsa.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_stack"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.dsa_abi_version() == 1
+
+
+def test_status_strings(L):
+    assert L.dsa_status_string(0) == b"DSA_OK"
+    assert L.dsa_status_string(4) == b"DSA_ERR_PATTERN"
+
+
+def test_indexer_argument_checks(L):
+    P = ctypes.c_void_p(16)
+    assert L.dsa_index_scores(None, P, P, None, 1, 4, 4, 16, 64, P, 4, None) == 1          # NULL
+    assert L.dsa_index_scores(P, P, P, None, -1, 4, 4, 16, 64, P, 4, None) == 2            # negative B
+    assert L.dsa_index_scores(P, P, P, None, 1, 4, 4, 16, 64, P, 3, None) == 2             # ld < Tk
+    assert L.dsa_index_scores(P, P, P, None, 1, 4, 4, 3, 64, P, 4, None) == 3              # H_I
+    assert L.dsa_index_scores(P, P, P, None, 1, 4, 4, 16, 48, P, 4, None) == 3             # d_I
+    assert L.dsa_index_scores(None, None, None, None, 0, 4, 4, 16, 64, None, 4, None) == 0  # empty batch
+    assert b"ld" in L.dsa_last_error() or True
+
+
+def test_topk_argument_checks(L):
+    P = ctypes.c_void_p(16)
+    assert L.dsa_topk(P, 8, None, 1, 2, 8, 0, P, None, 0, None) == 2          # k = 0
+    assert L.dsa_topk(P, 8, None, 1, 2, 8, 4097, P, None, 0, None) == 3       # k too large
+    assert L.dsa_topk(None, 8, None, 1, 2, 8, 4, P, None, 0, None) == 1       # NULL scores
+    assert L.dsa_topk(P, 8, None, 1, 2, (1 << 24) + 1, 4, P, None, 0, None) == 2  # ld < Tk
+    assert L.dsa_topk(None, 8, None, 0, 2, 8, 4, None, None, 0, None) == 0    # empty batch
+
+
+def test_attention_argument_checks(L):
+    P = ctypes.c_void_p(16)
+    f = ctypes.c_float
+    # MLA shape, fp8 without scale
+    assert L.dsa_sparse_attn(P, P, None, None, 1, P, 1, 4, 4, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0, None) == 1
+    # unsupported widths
+    assert L.dsa_sparse_attn(P, P, None, None, 0, P, 1, 4, 4, 16, 1, 128, 128, 4, f(0.04), P, None, None, 0, None) == 3
+    # H not a multiple of Hkv
+    assert L.dsa_sparse_attn(P, P, None, P, 0, P, 1, 4, 4, 6, 4, 32, 32, 4, f(0.1), P, None, None, 0, None) == 2
+    # non-finite scale
+    assert L.dsa_sparse_attn(P, P, None, None, 0, P, 1, 4, 4, 16, 1, 576, 512, 4, f(float("inf")), P, None, None, 0,
+                             None) == 2
+    # decode shape needs split-key workspace: missing -> DSA_ERR_WORKSPACE
+    shp = dsa.Shape(64, 1, 65536, 16, 64, 16, 1, 576, 512, 2048, 0.04, 1, None)
+    need = L.dsa_workspace_size(ctypes.byref(shp), dsa.OP_ATTN)
+    assert need > 0
+    assert L.dsa_sparse_attn(P, P, P, None, 1, P, 64, 1, 65536, 16, 1, 576, 512, 2048, f(0.04), P, None, None, 0,
+                             None) == 5
+    assert L.dsa_sparse_attn(P, P, P, None, 1, P, 64, 1, 65536, 16, 1, 576, 512, 2048, f(0.04), P, None, P,
+                             need - 1, None) == 5
+    # unknown kv dtype
+    assert L.dsa_sparse_attn(P, P, None, None, 7, P, 1, 4, 4, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0, None) == 2
+
+
+def _patterns():
+    for line in open(golden("indexcache_patterns.txt")):
+        if line.strip() and not line.startswith("#"):
+            yield line.split()[1]
+
+
+def test_pattern_checks_agree_with_the_oracle(L):
+    for pat in _patterns():
+        dsa.check_pattern(pat)
+        oracle.check_pattern(pat, len(pat))
+    for bad, n in (("FSX", 3), ("SFF", 3), ("FS", 3), ("FFFF", 3)):
+        with pytest.raises(dsa.DSAError):
+            dsa.check_pattern(bad, n)
+        with pytest.raises(ValueError):
+            oracle.check_pattern(bad, n)
+    dsa.check_pattern("SFF", prefilled=True)
+    for freq in (1, 2, 3, 4, 7):
+        for n in (1, 27, 61):
+            assert dsa.pattern_from_freq(freq, n) == oracle.pattern_from_freq(freq, n)
+    assert dsa.pattern_from_freq(3, 27) == "FSS" * 9
+    with pytest.raises(dsa.DSAError):
+        dsa.pattern_from_freq(0, 5)
+
+
+def test_layer_stack_rejects_before_enqueueing(L):
+    P = ctypes.c_void_p(16)
+    shp = dsa.Shape(1, 64, 64, 16, 64, 16, 1, 576, 512, 32, 0.04, 0, None)
+    io = (dsa.LayerIO * 2)()
+    io[0] = dsa.LayerIO(None, None, None, 16, 16, None, None, 16, None)  # F layer without indexer inputs
+    io[1] = dsa.LayerIO(None, None, None, 16, 16, None, None, 16, None)
+    assert L.dsa_layer_stack(b"FS", 2, io, ctypes.byref(shp), P, 0, P, 1 << 30, None) == 1
+    assert L.dsa_layer_stack(b"SS", 2, io, ctypes.byref(shp), P, 0, P, 1 << 30, None) == 4
+    io[0] = dsa.LayerIO(16, 16, 16, 16, 16, None, None, 16, None)
+    need = L.dsa_workspace_size(ctypes.byref(shp), dsa.OP_STACK)
+    assert need >= 64 * 64 * 4
+    assert L.dsa_layer_stack(b"FS", 2, io, ctypes.byref(shp), P, 0, P, need - 1, None) == 5
+    assert L.dsa_layer_stack(b"FS", 2, io, ctypes.byref(shp), None, 0, P, need, None) == 1
+
+
+def test_stack_chunk_rows_bound_the_score_chunk(L):
+    for B, T in ((1, 65536), (1, 16384), (1, 2057), (64, 65536), (1, 100)):
+        shp = dsa.Shape(B, T if B == 1 else 1, T, 16, 64, 16, 1, 576, 512, 2048, 0.04, 0, None)
+        rows = L.dsa_stack_chunk_rows(ctypes.byref(shp))
+        assert 1 <= rows <= max(1, shp.Tq)
+        assert B * rows * ((T + 63) // 64 * 64) * 4 <= max(128 << 20, B * ((T + 63) // 64 * 64) * 4)
