@@ -1,0 +1,249 @@
+"""Throughput of the DSA hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the
+lightning-indexer scores, the causal top-k and the sparse MLA attention of one DSA layer
+at T=65536, k=2048 (dsa_layer_stack with pattern "F": query chunks of scores -> top-k
+into the index buffer -> attention over the selected keys).  The JSON line also carries
+the batched-decode step (64 sequences x 65536 cached tokens, fp8 latent cache, FSS over
+three layers), a roofline entry for the dominant kernel timed with HIP events on the
+stream it runs on, per-kernel event timings, and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "query tokens/sec through indexer+top-k+sparse attn, T=65536 k=2048; decode tok/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--T", type=int, default=65536, help="prefill length (default: the named workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference dispatch for HBM counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "deepseek_sparse_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import deepseek_sparse_attention_amd as dsa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.workload("D", T=args.T)
+    T, k = w.T, w.k
+    log(f"generating workload {w.name} T={T} on the GPU")
+    layer = synth.layer_inputs(w, 0, device=dev)
+    kv_len = None
+    idx_cache = torch.empty((1, T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, T, w.H, w.Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, T, w.H), dtype=torch.float32, device=dev)
+    layer["out"], layer["lse"] = out, lse
+    shp = dsa._shape(1, T, T, w.H, w.Hkv, w.Dqk, w.Dv, k, w.scale(), dsa.KV_BF16, w.H_I, w.d_I)
+    ws = torch.empty(max(1, dsa.workspace_size(shp, dsa.OP_STACK)), dtype=torch.uint8, device=dev)
+
+    def step():
+        dsa.layer_stack("F", [layer], k, w.scale(), Dv=w.Dv, index_cache=idx_cache, ws=ws)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+    value = T / (dt / args.steps)
+    log(f"prefill: {ms_step:.2f} ms/step, {value:.0f} q-tok/s")
+
+    # ---- per-kernel event timings on the library's stream (torch's current stream)
+    stream = torch.cuda.current_stream()
+    reps = max(1, args.steps)
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+    attn_ms = timed(lambda: dsa.sparse_attn(layer["q"], layer["kv"], idx_cache, w.scale(), Dv=w.Dv, out=out, lse=lse))
+    Tc = dsa.stack_chunk_rows(shp)
+    ld = (T + 63) // 64 * 64
+    chunk = torch.empty((1, Tc, ld), dtype=torch.float32, device=dev)
+    chunk_idx = torch.empty((1, Tc, k), dtype=torch.int32, device=dev)
+    starts = list(range(0, T, Tc))
+    kvl = [torch.tensor([r0 + min(Tc, T - r0)], dtype=torch.int32, device=dev) for r0 in starts]
+
+    def indexer_all():
+        for r0, kl in zip(starts, kvl):
+            n = min(Tc, T - r0)
+            dsa.index_scores(layer["q_idx"][:, r0:r0 + n], layer["k_idx"], layer["w_idx"][:, r0:r0 + n], kv_len=kl,
+                             scores=chunk[:, :n], ld=ld)
+
+    def topk_all():
+        for r0, kl in zip(starts, kvl):
+            n = min(Tc, T - r0)
+            dsa.topk(chunk[:, :n], k, Tk=r0 + n, kv_len=kl, idx=chunk_idx[:, :n])
+
+    indexer_ms = timed(indexer_all)
+    topk_ms = timed(topk_all)  # (on the last chunk's scores: same row lengths per chunk)
+
+    # ---- roofline of the dominant kernel (sparse MLA attention)
+    sel = k * T - k * (k - 1) // 2 if T >= k else T * (T + 1) // 2
+    attn_bytes = sel * w.Dqk * 2 + T * w.H * w.Dqk * 2 + T * k * 4 + T * w.H * w.Dv * 2 + T * w.H * 4
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(PROFILES, "mla_attn_t65536_k2048_traffic.json")
+    if os.path.exists(tfile) and T == 65536:
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash("attention.hip", "common.hpp"):
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"kernel": "mla_attn_kernel<bf16>", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": attn_bytes, "ms_per_launch": round(attn_ms, 3)}
+    pairs = T * (T + 1) // 2
+    idx_flops = 2 * w.H_I * w.d_I * pairs
+    kernels = {
+        "indexer": {"ms": round(indexer_ms, 3), "tflops": round(idx_flops / (indexer_ms * 1e-3) / 1e12, 1),
+                    "frac_mfma_bf16": round(idx_flops / (indexer_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "topk": {"ms": round(topk_ms, 3),
+                 "gbs": round((pairs * 4 + T * k * 4) / (topk_ms * 1e-3) / 1e9, 1)},
+        "sparse_attn": {"ms": round(attn_ms, 3), "gbs_logical": round(achieved, 1)},
+    }
+    log(f"kernels: {kernels}")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": 1, "T": T, "k": k, "pattern": "F", "indexer": f"{w.H_I}x{w.d_I}",
+                   "heads": w.H, "dqk": w.Dqk, "dv": w.Dv, "chunk_rows": Tc},
+        "roofline": roofline, "kernels": kernels,
+    }
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = a.numel() * 4
+        del a, b
+
+    # ---- batched decode: 64 x 65536 fp8 cache, FSS over 3 layers
+    if not args.no_decode:
+        del chunk, chunk_idx
+        e = synth.workload("E")
+        log(f"generating decode workload {e.name}")
+        kc = synth.decode_indexer_cache(e, device=dev)
+        dl = []
+        for l in range(3):
+            d = synth.decode_layer_inputs(e, l, device=dev)
+            if "q_idx" in d:
+                d["k_idx"] = kc
+            dl.append(d)
+        klen = torch.full((e.B,), e.T, dtype=torch.int32, device=dev)
+        dcache = torch.empty((e.B, 1, e.k), dtype=torch.int32, device=dev)
+        dshp = dsa._shape(e.B, 1, e.T, e.H, 1, e.Dqk, e.Dv, e.k, e.scale(), dsa.KV_FP8_E4M3, e.H_I, e.d_I, klen)
+        dws = torch.empty(max(1, dsa.workspace_size(dshp, dsa.OP_STACK)), dtype=torch.uint8, device=dev)
+        for L in dl:
+            L["out"] = torch.empty((e.B, 1, e.H, e.Dv), dtype=torch.bfloat16, device=dev)
+            L["lse"] = torch.empty((e.B, 1, e.H), dtype=torch.float32, device=dev)
+
+        def dstep():
+            dsa.layer_stack(e.pattern, dl, e.k, e.scale(), Dv=e.Dv, kv_len=klen, index_cache=dcache, ws=dws)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        dsteps = max(args.steps, 10)
+        t0 = time.perf_counter()
+        for _ in range(dsteps):
+            dstep()
+        torch.cuda.synchronize()
+        ddt = (time.perf_counter() - t0) / dsteps
+        dbytes = e.B * e.T * e.d_I * 2 + e.B * e.T * 4 + 3 * e.B * e.k * (e.Dqk + 4)
+        result["decode"] = {"workload": e.name, "value": round(e.B / ddt, 1), "unit": "tokens/s",
+                            "ms_per_step": round(ddt * 1e3, 4), "steps": dsteps, "pattern": e.pattern,
+                            "algorithmic_bytes": dbytes, "gbs": round(dbytes / ddt / 1e9, 1)}
+        log(f"decode: {ddt * 1e3:.3f} ms/step, {e.B / ddt:.0f} tok/s")
+        del kc, dl
+
+    # ---- CPU oracle on a bounded, evenly spread sample of the same prefill rows
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+
+        stride = max(1, T // args.cpu_rows)
+        rows = np.arange(stride // 2, T, stride, dtype=np.int32)[: args.cpu_rows]
+        host = {x: layer[x].cpu() for x in ("q_idx", "k_idx", "w_idx", "q", "kv")}
+        nthreads = oracle.default_threads()
+        log(f"oracle on {len(rows)} rows with {nthreads} threads")
+        t0 = time.perf_counter()
+        ridx, rout = oracle.dsa_rows(host["q_idx"][0], host["k_idx"][0], host["w_idx"][0], host["q"][0],
+                                     host["kv"][0], rows, k, w.scale(), Dv=w.Dv, nthreads=nthreads)
+        cdt = time.perf_counter() - t0
+        # the sample spreads evenly over positions, so rows/s estimates the whole layer's rate
+        got_out = out[0, torch.from_numpy(rows).long().to(dev)].double().cpu().numpy()
+        got_idx = idx_cache[0, torch.from_numpy(rows).long().to(dev)].cpu().numpy()
+        same_sets = float(np.mean([len(np.intersect1d(a[a >= 0], b[b >= 0])) / max(1, (b >= 0).sum())
+                                   for a, b in zip(got_idx, ridx)]))
+        result["cpu_baseline"] = {
+            "value": round(len(rows) / cdt, 3), "unit": "query tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{len(rows)} query rows of the T={T} layer (every {stride}th position), "
+                      f"scores+top-k+attention in fp64, {cdt:.1f} s wall",
+            "sample_check": {"max_abs_out_diff": float(np.max(np.abs(got_out - rout))),
+                             "index_set_agreement": round(same_sets, 6)},
+        }
+        log(f"oracle: {len(rows) / cdt:.2f} rows/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
