@@ -25,42 +25,57 @@ namespace dsa {
 namespace {
 
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kTile = 64;              // keys per tile
-constexpr int kPitch = kDqk * 2 + 16;  // LDS row pitch in bytes (1168: 16-B skew per row)
-constexpr int kPPitch = kTile * 2 + 16;  // P tile pitch in bytes (144)
+constexpr int kTile = 32;                // selected keys per tile
+constexpr int kPitch = kDqk * 2 + 16;    // LDS row pitch in bytes (1168: 16-B skew per row)
+constexpr int kPPitch = kTile * 2 + 16;  // P tile pitch in bytes (80)
+constexpr int kQSteps = kDqk / 32 / 2;   // MFMA k-steps of Q K^T per wave (half of 18)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Gather of one tile: wave w fetches tile keys 8w..8w+7; lane l owns key 8w + l/8 and the
+// 16-byte parts l%8, l%8+8, ... of its row, so every load instruction reads eight full
+// 128-byte lines.  Rows go through registers into LDS (bf16; fp8 widened exactly).
 template <bool FP8>
 struct TileStage;
 
 template <>
-struct TileStage<false> {  // bf16 rows: 72 chunks of 16 B
-  static constexpr int kChunks = kTile * (kDqk * 2 / 16) / 256;  // 18 per thread
+struct TileStage<false> {  // bf16 row: 72 parts of 16 B, 9 per lane
+  static constexpr int kChunks = 9;
+  static constexpr uint32_t kRowBytes = kDqk * 2;
   u32x4 r[kChunks];
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int s, int part0) {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int ch = tid + 256 * c, key = ch / 72, part = ch % 72;
-      *reinterpret_cast<u32x4*>(lds + key * kPitch + part * 16) = r[c];
-    }
+    for (int c = 0; c < kChunks; ++c) r[c] = buf_load_16(rs, (uint32_t)s * kRowBytes + (part0 + 8 * c) * 16, 0);
+  }
+  __device__ __forceinline__ void store(uint8_t* lds_row, int part0) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) *reinterpret_cast<u32x4*>(lds_row + (part0 + 8 * c) * 16) = r[c];
   }
 };
 
 template <>
-struct TileStage<true> {  // e4m3 rows: 36 chunks of 16 B, widened to bf16 (exact)
-  static constexpr int kChunks = kTile * (kDqk / 16) / 256;  // 9 per thread
+struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
+  static constexpr int kChunks = 5;
+  static constexpr uint32_t kRowBytes = kDqk;
   u32x4 r[kChunks];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int s, int part0) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int part = part0 + 8 * c;
+      if (part < 36) r[c] = buf_load_16(rs, (uint32_t)s * kRowBytes + part * 16, 0);
+    }
+  }
   template <bool HI>
   __device__ __forceinline__ static uint32_t widen2(uint32_t word) {
     f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
     // e4m3 values are exact in bf16: the low 16 bits of the fp32 pattern are zero
     return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+  __device__ __forceinline__ void store(uint8_t* lds_row, int part0) const {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int ch = tid + 256 * c, key = ch / 36, part = ch % 36;
+      const int part = part0 + 8 * c;
+      if (part >= 36) continue;
       u32x4 lo, hi;
       lo[0] = widen2<false>(r[c][0]);
       lo[1] = widen2<true>(r[c][0]);
@@ -70,7 +85,7 @@ struct TileStage<true> {  // e4m3 rows: 36 chunks of 16 B, widened to bf16 (exac
       hi[1] = widen2<true>(r[c][2]);
       hi[2] = widen2<false>(r[c][3]);
       hi[3] = widen2<true>(r[c][3]);
-      uint8_t* dst = lds + key * kPitch + part * 32;
+      uint8_t* dst = lds_row + part * 32;
       *reinterpret_cast<u32x4*>(dst) = lo;
       *reinterpret_cast<u32x4*>(dst + 16) = hi;
     }
@@ -84,11 +99,11 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
                                                           float scale_log2, int tiles_per_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t ps[16 * kPPitch];
-  __shared__ float red_m[4][16], red_l[4][16];
-  __shared__ float tile_scale[kTile];
-  __shared__ int tile_valid[kTile];
+  __shared__ __attribute__((aligned(16))) float sbuf[4][4][64];  // partial S per wave, accumulator layout
+  __shared__ float tile_scale[2][kTile];
+  __shared__ int tile_valid[2][kTile];
   __shared__ int jmax_red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -99,13 +114,14 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   const int b = (int)(row / Tq);
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int32_t* ix = idx + row * k;
-  const uint8_t* kvb = kv + (int64_t)b * Tk * (FP8 ? kDqk : kDqk * 2);
+  constexpr uint32_t kRowBytes = TileStage<FP8>::kRowBytes;
+  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + (int64_t)b * Tk * kRowBytes, (uint32_t)Tk * kRowBytes);
 
   // extent of the index list that holds valid entries
   int jm = -1;
   for (int j = tid; j < k; j += 256) {
-    const int s = ix[j];
-    if (s >= 0 && s < Tk) jm = j;
+    const int sj = ix[j];
+    if (sj >= 0 && sj < Tk) jm = j;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
@@ -116,14 +132,23 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   const int t_begin = split * tiles_per_split;
   const int t_end = min(ntiles, t_begin + tiles_per_split);
 
-  // Q as the A operand of 16x16x32: lane = head (lane%16), 8 dims per k-step
+  // roles: Q K^T of key half kh (tile keys 16kh..16kh+15) over k-step half ksh
   const int hl = lane & 15, gq = lane >> 4;
-  bf16x8 qa[kDqk / 32];
+  const int kh = wave >> 1, ksh = wave & 1;
+  bf16x8 qa[kQSteps];
   {
-    const uint16_t* qp = q + (row * H + hg * 16 + hl) * kDqk + gq * 8;
+    const uint16_t* qp = q + (row * H + hg * 16 + hl) * kDqk + (ksh * kQSteps) * 32 + gq * 8;
 #pragma unroll
-    for (int s = 0; s < kDqk / 32; ++s) qa[s] = as_bf16x8(ld16(qp + s * 32));
+    for (int s = 0; s < kQSteps; ++s) qa[s] = as_bf16x8(ld16(qp + s * 32));
   }
+  // gather: this lane's key of the tile and its first 16-byte part
+  const int gk = 8 * wave + (lane >> 3), part0 = lane & 7;
+  const bool key_owner = (lane & 7) == 0;
+  auto entry = [&](int t) -> int {  // validated key index of this lane's entry in tile t, or -1
+    const int j = t * kTile + gk;
+    const int sj = j < k ? ix[j] : -1;
+    return (sj >= 0 && sj < Tk) ? sj : -1;
+  };
 
   f32x4 o_acc[8];
 #pragma unroll
@@ -136,111 +161,93 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   }
 
   TileStage<FP8> stage;
-  int my_s = 0;
-  float my_scale = 1.f;
-  auto fetch_meta = [&](int t) {  // thread < 64 owns key tid of the tile
-    if (tid < kTile) {
-      const int j = t * kTile + tid;
-      my_s = (j < k) ? ix[j] : -1;
-      my_scale = 1.f;
-      if (my_s >= 0 && my_s < Tk) {
-        if (FP8) my_scale = kv_scale[(int64_t)b * Tk + my_s];
-      } else {
-        my_s = -1;
-      }
-    }
-  };
-  // entries past k are never read: a partial last tile repeats entry k-1 (masked later)
-  // rows are gathered with range-checked buffer loads: 32-bit offsets, one VGPR each
-  constexpr uint32_t kRowBytes = FP8 ? kDqk : kDqk * 2;
-  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kvb, (uint32_t)Tk * kRowBytes);
-  auto safe_load = [&](int t) {
-    const int j0 = t * kTile;
-    constexpr int per = FP8 ? 36 : 72;
-#pragma unroll
-    for (int c = 0; c < TileStage<FP8>::kChunks; ++c) {
-      const int ch = tid + 256 * c, key = ch / per, part = ch % per;
-      int s = ix[min(j0 + key, k - 1)];
-      s = (s >= 0 && s < Tk) ? s : 0;
-      stage.r[c] = buf_load_16(kv_rs, (uint32_t)s * kRowBytes + part * 16, 0);
-    }
-  };
-
+  int s_cur = -1, s_next = -1;
+  float sc_cur = 1.f;
   if (t_begin < t_end) {
-    safe_load(t_begin);
-    fetch_meta(t_begin);
+    s_cur = entry(t_begin);
+    stage.load(kv_rs, max(s_cur, 0), part0);
+    if (FP8 && key_owner && s_cur >= 0) sc_cur = kv_scale[(int64_t)b * Tk + s_cur];
+    if (t_begin + 1 < t_end) s_next = entry(t_begin + 1);
   }
   for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();  // previous tile fully consumed
-    stage.store(kvs, tid);
-    if (tid < kTile) {
-      tile_valid[tid] = my_s >= 0;
-      tile_scale[tid] = my_scale;
+    const int buf = (t - t_begin) & 1;
+    uint8_t* kvb = kvs[buf];
+    stage.store(kvb + gk * kPitch, part0);
+    if (key_owner) {
+      tile_valid[buf][gk] = s_cur >= 0;
+      tile_scale[buf][gk] = sc_cur;
     }
-    __syncthreads();
+    __syncthreads();  // tile t staged (the other buffer may still be read by PV of t-1)
     if (t + 1 < t_end) {
-      safe_load(t + 1);
-      fetch_meta(t + 1);
+      s_cur = s_next;
+      stage.load(kv_rs, max(s_cur, 0), part0);
+      sc_cur = 1.f;
+      if (FP8 && key_owner && s_cur >= 0) sc_cur = kv_scale[(int64_t)b * Tk + s_cur];
+      s_next = (t + 2 < t_end) ? entry(t + 2) : -1;
     }
 
-    // ---- S = Q K^T for keys 16*wave .. 16*wave+15 of the tile
-    const int kl = 16 * wave + hl;  // this lane's key (B column)
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* krow = kvs + kl * kPitch + gq * 16;
+    // ---- partial S = Q K^T over this wave's k-steps, keys 16kh .. 16kh+15
+    {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = kvb + (16 * kh + hl) * kPitch + (ksh * kQSteps) * 64 + gq * 16;
 #pragma unroll
-    for (int s = 0; s < kDqk / 32; ++s) {
-      bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + s * 64));
-      sacc = mfma16(qa[s], kb, sacc);
+      for (int s = 0; s < kQSteps; ++s) {
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + s * 64));
+        sacc = mfma16(qa[s], kb, sacc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sbuf[wave][i][lane] = sacc[i];
     }
-    const bool kvalid = tile_valid[kl] != 0;
-    const float ksc = tile_scale[kl];
-    float sv[4];
+    __syncthreads();  // partial sums visible
+
+    // ---- logits of all 32 keys (lane: key hl of each half, heads gq*4+i), softmax update
+    float sv[2][4];
+    float ksc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = kvalid ? sacc[i] * (ksc * scale_log2) : -INFINITY;
+    for (int h = 0; h < 2; ++h) {
+      const int key = 16 * h + hl;
+      const bool valid = tile_valid[buf][key] != 0;
+      ksc[h] = tile_scale[buf][key];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sfull = sbuf[2 * h][i][lane] + sbuf[2 * h + 1][i][lane];
+        sv[h][i] = valid ? sfull * (ksc[h] * scale_log2) : -INFINITY;
+      }
+    }
+    float alpha[4], pv[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float wm = group16_max(sv[i]);
-      if (hl == 0) red_m[wave][gq * 4 + i] = wm;
-    }
-    __syncthreads();
-    float alpha[4], pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = gq * 4 + i;
-      const float tm = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+      const float tm = fmaxf(group16_max(sv[0][i]), group16_max(sv[1][i]));
       const float mn = fmaxf(m_run[i], tm);
       alpha[i] = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[i] - mn);
-      pv[i] = (sv[i] == -INFINITY) ? 0.f : fast_exp2(sv[i] - mn);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pv[h][i] = (sv[h][i] == -INFINITY) ? 0.f : fast_exp2(sv[h][i] - mn);
+      l_run[i] = l_run[i] * alpha[i] + (group16_sum(pv[0][i]) + group16_sum(pv[1][i]));
       m_run[i] = mn;
     }
+    // P (times the fp8 row scale for V) as bf16, row = head, column = key; each wave
+    // writes 8 keys of one half
+    if ((hl >> 3) == ksh) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ws = group16_sum(pv[i]);
-      if (hl == 0) red_l[wave][gq * 4 + i] = ws;
-      // P (times the fp8 row scale for V) as bf16: row = head, column = key
-      *reinterpret_cast<uint16_t*>(ps + (gq * 4 + i) * kPPitch + kl * 2) = f32_to_bf16_bits(pv[i] * ksc);
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint16_t*>(ps + (gq * 4 + i) * kPPitch + (16 * kh + hl) * 2) =
+            f32_to_bf16_bits(pv[kh][i] * ksc[kh]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = gq * 4 + i;
-      l_run[i] = l_run[i] * alpha[i] + (((red_l[0][h] + red_l[1][h]) + red_l[2][h]) + red_l[3][h]);
-    }
+    __syncthreads();  // P visible
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o_acc[n][i] *= alpha[i];
 
-    // ---- O[:, wave*128 .. +128] += P V
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ps + hl * kPPitch + (ks * 32 + gq * 8) * 2));
-      const int kb0 = ks * 32 + gq * 8 + (hl >> 2);
+    // ---- O[:, wave*128 .. +128] += P V  (V read transposed from the staged rows)
+    {
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ps + hl * kPPitch + gq * 16));
+      const int kb0 = gq * 8 + (hl >> 2);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const int col = wave * 128 + n * 16 + 4 * (hl & 3);
-        const i16x4 v0 = lds_read_tr16(kvs + kb0 * kPitch + col * 2);
-        const i16x4 v1 = lds_read_tr16(kvs + (kb0 + 4) * kPitch + col * 2);
+        const i16x4 v0 = lds_read_tr16(kvb + kb0 * kPitch + col * 2);
+        const i16x4 v1 = lds_read_tr16(kvb + (kb0 + 4) * kPitch + col * 2);
         typedef short i16x8 __attribute__((ext_vector_type(8)));
         const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         o_acc[n] = mfma16(pa, __builtin_bit_cast(bf16x8, vv), o_acc[n]);
@@ -397,10 +404,11 @@ bool attn_mha_supported(const AttnArgs& a) {
 }
 
 int attn_mla_splits(int B, int Tq, int H, int k) {
+  // few rows (decode): split each row's key list so ~512 workgroups (2 per CU) run
   const int64_t wgs = (int64_t)B * Tq * (H / 16);
   const int tiles = (k + kTile - 1) / kTile;
-  if (wgs >= 512) return 1;
-  int s = (int)std::min<int64_t>(tiles, (1024 + wgs - 1) / std::max<int64_t>(1, wgs));
+  if (wgs >= 256) return 1;
+  int s = (int)std::min<int64_t>(tiles, (512 + wgs - 1) / std::max<int64_t>(1, wgs));
   if (s <= 1) return 1;
   const int per = (tiles + s - 1) / s;
   return (tiles + per - 1) / per;
