@@ -44,8 +44,8 @@ dsa_status check_indexer(const void* q, const void* k, const void* w, int B, int
   if (B < 0 || Tq < 0 || Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
   if (H_I < 1 || d_I < 1) return fail(DSA_ERR_SHAPE, "H_I and d_I must be >= 1");
   if (ld < Tk) return fail(DSA_ERR_SHAPE, "ld must be >= Tk");
-  if (!dsa::indexer_supported(H_I, d_I))
-    return fail(DSA_ERR_UNSUPPORTED, "indexer supports H_I in {1,2,4,8,16} and d_I in {16,32,64,128}");
+  if (!dsa::indexer_supported(H_I, d_I, ld))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer supports H_I in {1,2,4,8,16}, d_I in {16,32,64,128}, ld <= 2^22");
   if ((int64_t)B * Tq == 0) return DSA_OK;
   if (!q || !k || !w || !scores) return fail(DSA_ERR_NULL, "q_idx, k_idx, w_idx and scores are required");
   return DSA_OK;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   __shared__ int tile_valid[2][kTile];
   __shared__ int jmax_red[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int HG = H >> 4;
   const int64_t rowh = blockIdx.x;  // (b*Tq + t)*HG + hg
   const int64_t row = rowh / HG;
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void mha_attn_kernel(const uint16_t* __restric
                                                        int Tq, int Tk, int H, int k, float scale_log2,
                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ float zb[4][kMhaMaxK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int64_t row = blockIdx.x;
   const int b = (int)(row / Tq);
   const int32_t* ix = idx + row * k;

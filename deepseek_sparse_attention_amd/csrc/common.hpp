@@ -23,6 +23,9 @@ __device__ __forceinline__ int64_t seq_len(const int32_t* kv_len, int b, int Tk)
   return L < 0 ? 0 : (L > Tk ? Tk : L);
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
@@ -52,6 +55,12 @@ __device__ __forceinline__ u32x4 buf_load_16(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+__device__ __forceinline__ void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
+}
+// A byte offset no buffer range reaches (ranges here stay below 2 GiB): the store is dropped.
+constexpr uint32_t kOffNone = 0x80000000u;
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -77,6 +86,61 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
 }
 
+// ---- DPP (data-parallel primitives) on GFX9: lane permutations inside 16-lane rows,
+// executed by the VALU without an LDS round trip.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {  // lanes without a source read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-wide min / max / sum of a uint32, returned as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  v = max(v, dpp<kDppRowRor4>(v));
+  v = max(v, dpp<kDppRowRor8>(v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowRor4>(v);
+  v += dpp<kDppRowRor8>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+// Inclusive prefix sum over the 64 lanes (lane order); *total gets the wave's sum.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  v += dpp<kDppRowShr1>(v);
+  v += dpp<kDppRowShr2>(v);
+  v += dpp<kDppRowShr4>(v);
+  v += dpp<kDppRowShr8>(v);  // inclusive scan inside each 16-lane row
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  v += (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+  *total = r0 + r1 + r2 + r3;
+  return v;
+}
+
+// Order LDS accesses of one wave: its own earlier LDS writes are visible to its later
+// LDS reads from any lane (LDS instructions of a wave complete in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Wave-wide reductions over the 16 lanes of a row group (lanes with equal l/16).
 __device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
@@ -88,6 +152,11 @@ __device__ __forceinline__ float group16_sum(float v) {
   for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
   return v;
 }
+
+// max(x, 0) as one integer max on the bit pattern: negative floats (sign bit set) are
+// negative int32 and become +0.0, non-negative floats stay.  A float max would first
+// canonicalize x, an extra instruction per element.  Inputs here are finite.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   constexpr int QPL = 16 / H_I;          // queries per lane (per tile)
   constexpr int KS = D_I / 16;           // MFMA k-steps over the indexer width
   constexpr int QB = 4 * kQP * QPT;      // queries per workgroup
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int b = blockIdx.z;
   const int64_t L = seq_len(kv_len, b, Tk);
   const int64_t pos_base = L - Tq + row0;  // position of chunk row r is pos_base + r
@@ -39,67 +39,94 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   if (pmax < 0 || seg0 > pmax) return;
   const int64_t seg_end = min((int64_t)min((int64_t)Tk, seg0 + key_seg), pmax + 1);
 
+  // Range-checked views: rows past the chunk read as zero, keys past Tk read as zero,
+  // and score stores outside this wave's rows are dropped.
+  const uint16_t* qw = q + ((int64_t)b * Tq + row0 + wrow0) * H_I * D_I;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(qw, (uint32_t)wrows * H_I * D_I * 2);
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
+  float* sw = scores + (int64_t)b * score_bstride + (int64_t)wrow0 * ld;
+  const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(sw, (uint32_t)(wrows * ld * 4));
+
   // A operand: lane row m = lane%32 <-> (query, head) such that D lane group g = lane/32
   // holds all heads of queries g*QPL .. g*QPL+QPL-1 of the tile.
   const int m = lane & 31;
-  const int mi = (m >> 3) * 4 + (m & 3);         // accumulator slot of row m
-  const int mq = ((m >> 2) & 1) * QPL + mi / H_I; // query within tile
-  const int mh = mi % H_I;                        // head
-  const int kh = (lane >> 5) * 8;                 // k offset of this lane within a k-step
+  const int mi = (m >> 3) * 4 + (m & 3);          // accumulator slot of row m
+  const int mq = ((m >> 2) & 1) * QPL + mi / H_I;  // query within tile
+  const int mh = mi % H_I;                         // head
+  const int kh = (lane >> 5) * 8;                  // k offset of this lane within a k-step
   bf16x8 a[kQP][KS];
 #pragma unroll
   for (int t = 0; t < kQP; ++t) {
-    const int r = wrow0 + t * QPT + mq;
-    const bool ok = r < nrows;
-    const uint16_t* src = q + (((int64_t)b * Tq + row0 + (ok ? r : 0)) * H_I + mh) * D_I + kh;
+    const uint32_t off = (uint32_t)(((t * QPT + mq) * H_I + mh) * D_I + kh) * 2;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = ok ? ld16(src + s * 16) : u32x4{0, 0, 0, 0};
-      a[t][s] = as_bf16x8(v);
-    }
+    for (int s = 0; s < KS; ++s) a[t][s] = as_bf16x8(buf_load_16(q_rs, off + s * 32, 0));
   }
-  // head weights of the lane's queries (fp32), and their positions
+  // head weights of the lane's queries (fp32), their positions and score-row offsets
+  // (positions and keys fit in 32 bits: Tk <= ld <= 2^22)
   const int g = lane >> 5;
+  const __amdgpu_buffer_rsrc_t w_rs =
+      make_rsrc(w + ((int64_t)b * Tq + row0 + wrow0) * H_I, (uint32_t)wrows * H_I * 2);
   float wt[kQP][16];
-  int64_t qpos[kQP][QPL];
-  int qrow[kQP][QPL];
+  int qpos[kQP][QPL];
+  uint32_t qoff[kQP][QPL];
 #pragma unroll
   for (int t = 0; t < kQP; ++t) {
 #pragma unroll
     for (int qq = 0; qq < QPL; ++qq) {
-      const int r = wrow0 + t * QPT + g * QPL + qq;
-      const bool ok = r < nrows;
-      qrow[t][qq] = ok ? r : -1;
-      qpos[t][qq] = ok ? pos_base + r : -1;
+      const int r = t * QPT + g * QPL + qq;  // row within the wave
+      qpos[t][qq] = r < wrows ? (int)(pos_base + wrow0 + r) : -1;
+      qoff[t][qq] = (uint32_t)(r * ld) * 4u;
+      if constexpr (H_I == 1) {  // a lone bf16 weight: 2-byte aligned only
+        const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b16(w_rs, r * 2, 0, 0);
+        wt[t][qq] = __uint_as_float(bits << 16);
+      } else {  // head pairs: 4-byte aligned
 #pragma unroll
-      for (int h = 0; h < H_I; ++h)
-        wt[t][qq * H_I + h] = ok ? bf16_bits_to_f32(w[((int64_t)b * Tq + row0 + r) * H_I + h]) : 0.f;
+        for (int h = 0; h < H_I; h += 2) {
+          const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(w_rs, (r * H_I + h) * 2, 0, 0);
+          wt[t][qq * H_I + h] = __uint_as_float(bits << 16);
+          wt[t][qq * H_I + h + 1] = __uint_as_float(bits & 0xFFFF0000u);
+        }
+      }
     }
   }
 
   const int col = lane & 31;
-  const uint16_t* kbase = k + (int64_t)b * Tk * D_I + kh;
-  float* sbase = scores + (int64_t)b * score_bstride;
-  for (int64_t s0 = seg0; s0 < seg_end; s0 += 32) {
-    const int64_t key = min(s0 + col, (int64_t)Tk - 1);
-    bf16x8 bk[KS];
+  const int kend = (int)seg_end;
+  // byte offset of this lane's key row slice; advances 32 keys per tile
+  uint32_t koff = (uint32_t)(((int)seg0 + col) * D_I + kh) * 2;
+  constexpr uint32_t kTileBytes = 32 * D_I * 2;
+  auto load_keys = [&](bf16x8 (&bk)[KS]) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) bk[s] = as_bf16x8(ld16(kbase + key * D_I + s * 16));
-    const int64_t skey = s0 + col;
+    for (int s = 0; s < KS; ++s) bk[s] = as_bf16x8(buf_load_16(k_rs, koff + s * 32, 0));
+    koff += kTileBytes;
+  };
+  auto tile = [&](int s0, const bf16x8 (&bk)[KS]) {
+    const int skey = s0 + col;
 #pragma unroll
     for (int t = 0; t < kQP; ++t) {
-      if (t * QPT >= wrows) break;
       f32x16 acc = {};
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = mfma32(a[t][s], bk[s], acc);
 #pragma unroll
       for (int qq = 0; qq < QPL; ++qq) {
-        float tot = wt[t][qq * H_I] * fmaxf(acc[qq * H_I], 0.f);
+        float tot = wt[t][qq * H_I] * relu(acc[qq * H_I]);
 #pragma unroll
-        for (int h = 1; h < H_I; ++h) tot = fmaf(wt[t][qq * H_I + h], fmaxf(acc[qq * H_I + h], 0.f), tot);
-        if (skey <= qpos[t][qq] && skey < seg_end) sbase[(int64_t)qrow[t][qq] * ld + skey] = tot;
+        for (int h = 1; h < H_I; ++h) tot = fmaf(wt[t][qq * H_I + h], relu(acc[qq * H_I + h]), tot);
+        // tiles never cross a segment edge, so the causal bound is the only mask
+        buf_store_f32(tot, s_rs, skey <= qpos[t][qq] ? qoff[t][qq] + (uint32_t)skey * 4u : kOffNone, 0);
       }
     }
+  };
+  // two key tiles per trip, ping-ponging the prefetch buffers (no register copies);
+  // prefetches past the segment read keys nobody stores, or zeros past Tk
+  bf16x8 b0[KS], b1[KS];
+  load_keys(b0);
+  for (int s0 = (int)seg0; s0 < kend; s0 += 64) {
+    load_keys(b1);
+    tile(s0, b0);
+    if (s0 + 32 >= kend) break;
+    load_keys(b0);
+    tile(s0 + 32, b1);
   }
 }
 
@@ -123,9 +150,10 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
 
 }  // namespace
 
-bool indexer_supported(int H_I, int d_I) {
+bool indexer_supported(int H_I, int d_I, int64_t ld) {
+  // a wave's score rows (kQP * 32/H_I of them) are addressed with 32-bit byte offsets
   return (H_I == 1 || H_I == 2 || H_I == 4 || H_I == 8 || H_I == 16) &&
-         (d_I == 16 || d_I == 32 || d_I == 64 || d_I == 128);
+         (d_I == 16 || d_I == 32 || d_I == 64 || d_I == 128) && ld <= kIndexerMaxLd;
 }
 
 hipError_t launch_index_scores(const IndexerArgs& A, hipStream_t st) {

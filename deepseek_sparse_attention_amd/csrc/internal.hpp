@@ -20,7 +20,8 @@ struct IndexerArgs {
   float* scores;
   int64_t ld, score_bstride;
 };
-bool indexer_supported(int H_I, int d_I);
+constexpr int64_t kIndexerMaxLd = int64_t(1) << 22;
+bool indexer_supported(int H_I, int d_I, int64_t ld);
 hipError_t launch_index_scores(const IndexerArgs& a, hipStream_t st);
 
 // Top-k for rows [row0, row0 + nrows): score row r of sequence b at

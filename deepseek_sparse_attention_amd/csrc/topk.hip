@@ -35,25 +35,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
 // Exclusive prefix sum over the workgroup in thread order; also returns the total.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t incl = wave_incl_scan(v, lane);
-  if (lane == 63) red[wid] = incl;
+  uint32_t wsum;
+  const uint32_t incl = wave_incl_scan_u32(v, &wsum);
+  if (lane == 0) red[wid] = wsum;
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NWAVES; ++i) {
-    uint32_t r = red[i];
+    const uint32_t r = red[i];
     pre += (i < wid) ? r : 0u;
     tot += r;
   }
@@ -251,6 +243,366 @@ __global__ __launch_bounds__(NT, 1) void topk_kernel(const float* __restrict__ s
   }
 }
 
+// Rows of up to one segment (65536 keys), keys in registers (64 per thread).
+//
+// 1. A sample of 8 keys per thread (slots spread over the whole row) is histogrammed to
+//    pick a threshold T0 expected to keep about 2k keys.
+// 2. Each thread marks its keys >= T0 in a 64-bit mask; one block scan of the mask counts
+//    gives every thread its place in an LDS candidate list (no atomics).
+// 3. If k <= #candidates <= kCandCap, one wave runs an exact radix select on the list and
+//    marks the kept keys (> K*) and the ties (== K*) in LDS bitmaps.  Otherwise (a poor
+//    sample, or massive ties) the whole workgroup runs the exact radix select over the
+//    registers.
+// 4. The bitmaps are emitted in position order from a block-wide prefix count.
+constexpr int kCandCap = 8192;
+constexpr int kSamples = 8;  // per thread
+
+// Top-down search of hist[0..NBINS) by one wave: the bin holding the `need`-th largest
+// count, and the count strictly above it (both wave-uniform).
+__device__ __forceinline__ void wave_find_bin_from_top(const uint32_t* hist, uint32_t need, uint32_t& bin,
+                                                       uint32_t& above) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = NBINS / 64;  // 32 bins per lane, lane 0 holds the top ones
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum += hist[NBINS - 1 - (lane * PER + i)];
+  uint32_t total;
+  const uint32_t incl = wave_incl_scan_u32(sum, &total);
+  // the lane whose 32 bins hold the need-th count (exactly one: counts are cumulative)
+  const uint64_t hit = __ballot(incl - sum < need && need <= incl);
+  const int L = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : 0);
+  const uint32_t preL = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
+  // spread that lane's bins over lanes 0..31 and scan them
+  const uint32_t c = lane < PER ? hist[NBINS - 1 - (L * PER + lane)] : 0u;
+  uint32_t t2;
+  const uint32_t incl2 = preL + wave_incl_scan_u32(c, &t2);
+  const uint64_t hit2 = __ballot(lane < PER && incl2 - c < need && need <= incl2);
+  const int i2 = hit2 ? (int)__builtin_ctzll(hit2) : 0;
+  uint32_t my_bin = 0xFFFFFFFFu, my_above = 0;
+  if (lane == i2) {
+    my_bin = NBINS - 1 - (L * PER + i2);
+    my_above = incl2 - c;
+  }
+  bin = wave_min_u32(my_bin);  // exactly one lane found it
+  above = wave_min_u32(my_bin == bin ? my_above : 0xFFFFFFFFu);
+}
+
+__global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restrict__ scores, int64_t ld,
+                                                          int64_t score_bstride, const int32_t* __restrict__ kv_len,
+                                                          int Tq, int Tk, int k, int row0, int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[NBINS];
+  __shared__ __attribute__((aligned(8))) uint32_t sel_bits[SEG_WORDS];
+  __shared__ __attribute__((aligned(8))) uint32_t tie_bits[SEG_WORDS];
+  __shared__ uint32_t cand_key[kCandCap + 1];  // last slot absorbs non-candidate writes
+  __shared__ int32_t cand_pos[kCandCap + 1];
+  __shared__ uint32_t red[3 * NWAVES];
+  __shared__ uint32_t state[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int64_t L = seq_len(kv_len, b, Tk);
+  const int64_t p = L - Tq + row0 + r;
+  int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * k;
+  if (p + 1 <= k) {  // every causal key (or none), then padding
+    for (int j = tid; j < k; j += NT) out[j] = (j <= p) ? j : -1;
+    return;
+  }
+  if (p + 1 > SEG) return;  // launched only for rows that fit
+  const int n = (int)(p + 1);
+  const int nj = (n + NT - 1) / NT;  // item slots in use (uniform)
+
+  // ---- keys: batched range-checked loads (slots past the row read 0 and are zeroed)
+  const float* row = scores + (int64_t)b * score_bstride + (int64_t)r * ld;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)n * 4u);
+  uint32_t keys[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) keys[j] = __float_as_uint(buf_load_f32(rs, tid * 4u, (uint32_t)(NT * 4 * j)));
+  // slots are handled in blocks of 8 (8192 positions); a block past the row is skipped
+  // with one uniform branch (per-slot branches would pin 64 conditions in scalar registers)
+  constexpr int JB = 8;
+#pragma unroll
+  for (int jb = 0; jb < ITEMS / JB; ++jb) {
+    if (jb * JB < nj) {
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = jb * JB + jj;
+        // order-preserving map; adding +0 first turns -0 into +0, so the two tie
+        const uint32_t u = __float_as_uint(__uint_as_float(keys[j]) + 0.0f);
+        const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+        keys[j] = (tid + NT * j < n) ? key : 0u;  // 0 marks "no candidate"
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) keys[jb * JB + jj] = 0u;
+    }
+  }
+  for (int i = tid; i < SEG_WORDS; i += NT) {
+    sel_bits[i] = 0;
+    tie_bits[i] = 0;
+  }
+  for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+
+  // ---- 1. sample: thread t takes slots (t % 8) + 8m, m = 0..7
+  uint32_t smp[kSamples];
+#pragma unroll
+  for (int m = 0; m < kSamples; ++m) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v = ((tid & 7) == q) ? keys[8 * m + q] : v;
+    smp[m] = v;
+  }
+  uint32_t smin = 0xFFFFFFFFu, smax = 0u, scount = 0;
+#pragma unroll
+  for (int m = 0; m < kSamples; ++m) {
+    smin = min(smin, smp[m] - 1u);  // 0 (no candidate) wraps to the top and drops out
+    smax = max(smax, smp[m]);
+    scount += smp[m] != 0u;
+  }
+  smin = wave_min_u32(smin);
+  smax = wave_max_u32(smax);
+  scount = wave_sum_u32(scount);
+  if (lane == 0) {
+    red[wave] = smin;
+    red[NWAVES + wave] = smax;
+    red[2 * NWAVES + wave] = scount;
+  }
+  __syncthreads();
+  smin = red[0];
+  smax = red[NWAVES];
+  scount = red[2 * NWAVES];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) {
+    smin = min(smin, red[i]);
+    smax = max(smax, red[NWAVES + i]);
+    scount += red[2 * NWAVES + i];
+  }
+  smin += 1u;
+  const uint32_t sspan = smax - smin;
+  const int sshift = sspan == 0 ? 0 : max(0, 32 - __clz(sspan) - BIN_BITS);
+#pragma unroll
+  for (int m = 0; m < kSamples; ++m)
+    if (smp[m]) atomicAdd(&hist[(smp[m] - smin) >> sshift], 1u);
+  __syncthreads();
+  if (wave == 0) {
+    // aim at about twice k keys: the bin where the sampled count from the top reaches
+    // 2k * (samples / n)
+    uint32_t target = (uint32_t)min((uint64_t)scount, ((uint64_t)2 * k * scount + n - 1) / n);
+    target = max(target, 1u);
+    uint32_t bin, above;
+    wave_find_bin_from_top(hist, target, bin, above);
+    if (lane == 0) state[0] = smin + (bin << sshift);
+  }
+  __syncthreads();
+  const uint32_t t0 = state[0];  // >= smin >= 1
+
+  // ---- 2. candidates: keys >= t0, placed by one block scan of per-thread counts
+  uint32_t ccount = 0;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) ccount += keys[j] >= t0;
+  uint32_t c0;
+  const uint32_t cbase = block_excl_scan(ccount, red, c0);
+
+  uint32_t need = (uint32_t)k;
+  uint32_t kstar;
+  if (c0 >= (uint32_t)k && c0 <= (uint32_t)kCandCap) {
+    // (t0 re-read after the scan's barriers: the compares are redone here rather than
+    // 64 results kept live across the scan)
+    const uint32_t t0c = state[0];
+    uint32_t off = cbase, cmax = 0;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const bool c = keys[j] >= t0c;
+      const uint32_t slot = c ? off : (uint32_t)kCandCap;
+      cand_key[slot] = keys[j];
+      cand_pos[slot] = tid + NT * j;
+      off += c;
+      cmax = max(cmax, keys[j]);
+    }
+    cmax = wave_max_u32(cmax);
+    for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+    if (lane == 0) red[2 * NWAVES + wave] = cmax;
+    if (tid == 0) state[2] = 0;  // members of the threshold bin
+    __syncthreads();
+    cmax = red[2 * NWAVES];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) cmax = max(cmax, red[2 * NWAVES + i]);
+    // block-wide radix passes over the list until the threshold bin is small
+    uint32_t lo = t0c, hi = cmax;
+    int sh = (hi == lo) ? 0 : max(0, 32 - __clz(hi - lo) - BIN_BITS);
+    uint32_t m;
+    for (;;) {
+      for (uint32_t c = tid; c < c0; c += NT) {
+        const uint32_t key = cand_key[c];
+        if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sh], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_from_top(hist, need, bin, above);
+        if (lane == 0) {
+          state[0] = bin;
+          state[1] = above;
+          state[3] = hist[bin];
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = state[0];
+      m = state[3];
+      const uint32_t blo = lo + (bin << sh);
+      const uint32_t bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)hi);
+      // keys above the threshold bin are kept
+      for (uint32_t c = tid; c < c0; c += NT) {
+        const uint32_t key = cand_key[c];
+        if (key > bhi && key <= hi) {
+          const int e = cand_pos[c];
+          atomicOr(&sel_bits[e >> 5], 1u << (e & 31));
+        }
+      }
+      need -= state[1];
+      lo = blo;
+      hi = bhi;
+      if (sh == 0 || m <= 64) break;
+      sh = max(0, sh - BIN_BITS);
+      for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+      __syncthreads();
+    }
+    if (sh > 0 || m <= 64) {
+      // the threshold bin's m <= 64 members: rank them exactly (score, then position)
+      // in one wave and keep the first `need`
+      __shared__ uint32_t mem_key[64];
+      __shared__ int32_t mem_pos[64];
+      for (uint32_t c = tid; c < c0; c += NT) {
+        const uint32_t key = cand_key[c];
+        if (key >= lo && key <= hi) {
+          const uint32_t slot = atomicAdd(&state[2], 1u);
+          mem_key[slot] = key;
+          mem_pos[slot] = cand_pos[c];
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const uint32_t mk = lane < (int)m ? mem_key[lane] : 0u;
+        const int32_t mp = lane < (int)m ? mem_pos[lane] : 0x7FFFFFFF;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < m; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
+          const int32_t pj = __builtin_amdgcn_readlane(mp, (int)j);
+          rank += (kj > mk) || (kj == mk && pj < mp);
+        }
+        if (lane < (int)m && rank < need) atomicOr(&sel_bits[mp >> 5], 1u << (mp & 31));
+      }
+      need = 0;  // every kept key is in sel_bits
+    } else {
+      // a threshold bin of one key value held by more than 64 candidates: its members
+      // are ties; keep the first `need` by position
+      kstar = lo;
+      for (uint32_t c = tid; c < c0; c += NT) {
+        const uint32_t key = cand_key[c];
+        if (key == kstar) {
+          const int e = cand_pos[c];
+          atomicOr(&tie_bits[e >> 5], 1u << (e & 31));
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    // exact radix select over the registers, by the whole workgroup
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      kmin = min(kmin, keys[j] - 1u);
+      kmax = max(kmax, keys[j]);
+    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+      red[wave] = kmin;
+      red[NWAVES + wave] = kmax;
+    }
+    __syncthreads();
+    kmin = red[0];
+    kmax = red[NWAVES];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) {
+      kmin = min(kmin, red[i]);
+      kmax = max(kmax, red[NWAVES + i]);
+    }
+    kmin += 1u;
+    uint32_t lo = kmin, hi = kmax;
+    int sh = (kmax == kmin) ? 0 : max(0, 32 - __clz(kmax - kmin) - BIN_BITS);
+    for (;;) {
+      for (int i = tid; i < NBINS; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t key = keys[j];
+        if (key && key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sh], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_from_top(hist, need, bin, above);
+        if (lane == 0) {
+          state[0] = bin;
+          state[1] = above;
+        }
+      }
+      __syncthreads();
+      need -= state[1];
+      lo += state[0] << sh;
+      if (sh == 0) break;
+      hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
+      sh = max(0, sh - BIN_BITS);
+      __syncthreads();
+    }
+    kstar = lo;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const uint32_t key = keys[j];
+      const int e = tid + NT * j;
+      if (key > kstar) atomicOr(&sel_bits[e >> 5], 1u << (e & 31));
+      else if (key == kstar && key) atomicOr(&tie_bits[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+  }
+  // need = ties (key == kstar) to keep, lowest positions first; k - need keys > kstar
+
+  // ---- 4. emission in position order: thread t owns positions 64t .. 64t+63
+  constexpr int WPT = SEG_WORDS / NT;  // 2 bitmap words per thread
+  uint32_t sw[WPT], tw[WPT];
+  uint32_t cs = 0, ct = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    sw[i] = sel_bits[tid * WPT + i];
+    tw[i] = tie_bits[tid * WPT + i];
+    cs += __popc(sw[i]);
+    ct += __popc(tw[i]);
+  }
+  // one scan for both counts: kept-above count (< 4096) in the high bits, ties below
+  uint32_t tot;
+  const uint32_t packed = block_excl_scan((cs << 17) | ct, red, tot);
+  uint32_t sp = packed >> 17, tp = packed & 0x1FFFFu;
+  const int pos0 = tid * WPT * 32;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t m = sw[i] | tw[i];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      const int32_t pos = pos0 + i * 32 + bit;
+      // slots stay below k by construction; the guard keeps a violated invariant in-row
+      if ((sw[i] >> bit) & 1u) {
+        const uint32_t slot = sp + min(tp, need);
+        if (slot < (uint32_t)k) out[slot] = pos;
+        ++sp;
+      } else {
+        if (tp < need && sp + tp < (uint32_t)k) out[sp + tp] = pos;
+        ++tp;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
@@ -258,7 +610,7 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   dim3 grid(A.nrows, A.B);
   // rows see at most Tk keys: up to one segment they are kept in registers
   if (A.Tk <= SEG)
-    hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len, A.Tq,
+    hipLaunchKernelGGL(topk_fast_kernel, grid, dim3(NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len, A.Tq,
                        A.Tk, A.k, A.row0, A.idx);
   else
     hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len, A.Tq,

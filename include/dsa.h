@@ -81,7 +81,7 @@ const char* dsa_status_string(dsa_status s);
  *   scores fp32 [B][Tq][ld], ld >= Tk: for every row, entries s = 0..p are written with
  *          I[t,s] (fp32 accumulation of the bf16 products, ReLU per head, then the weighted
  *          head sum in head order); entries s > p are not written.
- * Supported: H_I in {1,2,4,8,16}, d_I in {16,32,64,128}, Tk <= 2^31 - 1.
+ * Supported: H_I in {1,2,4,8,16}, d_I in {16,32,64,128}, ld <= 2^22.
  */
 dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_idx,
                             const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I,

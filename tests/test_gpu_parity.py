@@ -112,6 +112,17 @@ def test_topk_ties_signed_zeros_and_short_rows():
     assert np.array_equal(got, ref)
 
 
+def test_topk_threshold_bin_larger_than_candidate_list():
+    # >4096 equal scores straddle the threshold: the register fallback path
+    rng = np.random.default_rng(8)
+    T = 9000
+    s = np.zeros((1, 24, T), np.float32)
+    s[0, :, ::7] = rng.standard_normal((24, (T + 6) // 7)).astype(np.float32)
+    s[0, ::3] *= -1.0  # some rows hold only negatives besides the zeros
+    got, ref = _topk_case(s, 2048, kv_len=[T])
+    assert np.array_equal(got, ref)
+
+
 def test_topk_long_rows_from_indexer_scores():
     print("topk on GPU indexer scores (workload D shape, T=9000)", flush=True)
     w = synth.workload("D", T=9000)
