@@ -27,7 +27,6 @@ namespace {
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kTile = 32;                // selected keys per tile
 constexpr int kPitch = kDqk * 2 + 16;    // LDS row pitch in bytes (1168: 16-B skew per row)
-constexpr int kPPitch = kTile * 2 + 16;  // P tile pitch in bytes (80)
 constexpr int kQSteps = kDqk / 32 / 2;   // MFMA k-steps of Q K^T per wave (half of 18)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -100,8 +99,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t ps[16 * kPPitch];
-  __shared__ __attribute__((aligned(16))) float sbuf[4][4][64];  // partial S per wave, accumulator layout
+  __shared__ __attribute__((aligned(16))) float sbuf[4][4][64];  // partial S^T per wave, accumulator layout
   __shared__ float tile_scale[2][kTile];
   __shared__ int tile_valid[2][kTile];
   __shared__ int jmax_red[4];
@@ -132,14 +130,16 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   const int t_begin = split * tiles_per_split;
   const int t_end = min(ntiles, t_begin + tiles_per_split);
 
-  // roles: Q K^T of key half kh (tile keys 16kh..16kh+15) over k-step half ksh
+  // Lane roles.  hl = lane % 16 is this lane's head in S^T and O^T; gq = lane / 16 picks
+  // which 4 keys of each 16-key half it holds (keys 4gq..4gq+3 and 16+4gq..16+4gq+3).
+  // Wave roles in S^T = K Q^T: key half kh (tile keys 16kh..16kh+15), k-step half ksh.
   const int hl = lane & 15, gq = lane >> 4;
   const int kh = wave >> 1, ksh = wave & 1;
-  bf16x8 qa[kQSteps];
+  bf16x8 qb[kQSteps];  // Q^T as the B operand: column = head hl, 8 dims per k-step
   {
     const uint16_t* qp = q + (row * H + hg * 16 + hl) * kDqk + (ksh * kQSteps) * 32 + gq * 8;
 #pragma unroll
-    for (int s = 0; s < kQSteps; ++s) qa[s] = as_bf16x8(ld16(qp + s * 32));
+    for (int s = 0; s < kQSteps; ++s) qb[s] = as_bf16x8(ld16(qp + s * 32));
   }
   // gather: this lane's key of the tile and its first 16-byte part
   const int gk = 8 * wave + (lane >> 3), part0 = lane & 7;
@@ -150,15 +150,10 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     return (sj >= 0 && sj < Tk) ? sj : -1;
   };
 
-  f32x4 o_acc[8];
+  f32x4 o_acc[8];  // O^T: rows = dims wave*128 + n*16 + 4gq + i, column = head hl
 #pragma unroll
   for (int n = 0; n < 8; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.f;
-  }
+  float m_run = -INFINITY, l_run = 0.f;
 
   TileStage<FP8> stage;
   int s_cur = -1, s_next = -1;
@@ -186,99 +181,97 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
       s_next = (t + 2 < t_end) ? entry(t + 2) : -1;
     }
 
-    // ---- partial S = Q K^T over this wave's k-steps, keys 16kh .. 16kh+15
+    // ---- partial S^T = K Q^T over this wave's k-steps, keys 16kh .. 16kh+15
     {
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
       const uint8_t* krow = kvb + (16 * kh + hl) * kPitch + (ksh * kQSteps) * 64 + gq * 16;
 #pragma unroll
       for (int s = 0; s < kQSteps; ++s) {
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + s * 64));
-        sacc = mfma16(qa[s], kb, sacc);
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + s * 64));
+        sacc = mfma16(ka, qb[s], sacc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sbuf[wave][i][lane] = sacc[i];
     }
     __syncthreads();  // partial sums visible
 
-    // ---- logits of all 32 keys (lane: key hl of each half, heads gq*4+i), softmax update
-    float sv[2][4];
-    float ksc[2];
+    // ---- logits of the lane's 8 keys for head hl, online softmax in base 2
+    float sv[8], ksc[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int key = 16 * h + hl;
-      const bool valid = tile_valid[buf][key] != 0;
-      ksc[h] = tile_scale[buf][key];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const int key = 16 * h + 4 * gq + i;
+        ksc[4 * h + i] = tile_scale[buf][key];
         const float sfull = sbuf[2 * h][i][lane] + sbuf[2 * h + 1][i][lane];
-        sv[h][i] = valid ? sfull * (ksc[h] * scale_log2) : -INFINITY;
+        sv[4 * h + i] = tile_valid[buf][key] ? sfull * (ksc[4 * h + i] * scale_log2) : -INFINITY;
       }
     }
-    float alpha[4], pv[2][4];
+    float tm = sv[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float tm = fmaxf(group16_max(sv[0][i]), group16_max(sv[1][i]));
-      const float mn = fmaxf(m_run[i], tm);
-      alpha[i] = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[i] - mn);
+    for (int e = 1; e < 8; ++e) tm = fmaxf(tm, sv[e]);
+    tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    const float mn = fmaxf(m_run, tm);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
+    float pv[8], ts = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) pv[h][i] = (sv[h][i] == -INFINITY) ? 0.f : fast_exp2(sv[h][i] - mn);
-      l_run[i] = l_run[i] * alpha[i] + (group16_sum(pv[0][i]) + group16_sum(pv[1][i]));
-      m_run[i] = mn;
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = (sv[e] == -INFINITY) ? 0.f : fast_exp2(sv[e] - mn);
+      ts += pv[e];
     }
-    // P (times the fp8 row scale for V) as bf16, row = head, column = key; each wave
-    // writes 8 keys of one half
-    if ((hl >> 3) == ksh) {
+    ts += __shfl_xor(ts, 16, 64);
+    ts += __shfl_xor(ts, 32, 64);
+    l_run = l_run * alpha + ts;
+    m_run = mn;
+    // P^T as the B operand: k-slot e of group gq <-> key 4gq+e (e<4), 16+4gq+(e-4) (e>=4);
+    // probabilities carry the fp8 row scale for V
+    u32x4 pw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint16_t*>(ps + (gq * 4 + i) * kPPitch + (16 * kh + hl) * 2) =
-            f32_to_bf16_bits(pv[kh][i] * ksc[kh]);
-    }
-    __syncthreads();  // P visible
+    for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(pv[2 * e] * ksc[2 * e], pv[2 * e + 1] * ksc[2 * e + 1]);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o_acc[n][i] *= alpha[i];
+      for (int i = 0; i < 4; ++i) o_acc[n][i] *= alpha;
 
-    // ---- O[:, wave*128 .. +128] += P V  (V read transposed from the staged rows)
+    // ---- O^T[dims wave*128 .. +128] += V^T P^T  (V read transposed from the staged rows)
     {
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ps + hl * kPPitch + gq * 16));
-      const int kb0 = gq * 8 + (hl >> 2);
+      const int kb0 = 4 * gq + (hl >> 2);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const int col = wave * 128 + n * 16 + 4 * (hl & 3);
         const i16x4 v0 = lds_read_tr16(kvb + kb0 * kPitch + col * 2);
-        const i16x4 v1 = lds_read_tr16(kvb + (kb0 + 4) * kPitch + col * 2);
+        const i16x4 v1 = lds_read_tr16(kvb + (kb0 + 16) * kPitch + col * 2);
         typedef short i16x8 __attribute__((ext_vector_type(8)));
         const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o_acc[n] = mfma16(pa, __builtin_bit_cast(bf16x8, vv), o_acc[n]);
+        o_acc[n] = mfma16(__builtin_bit_cast(bf16x8, vv), pb, o_acc[n]);
       }
     }
   }
 
-  // ---- results: lane holds O[head gq*4+i][wave*128 + n*16 + hl]
+  // ---- results: lane holds O[head hl][wave*128 + n*16 + 4gq + i]
+  const int h = hg * 16 + hl;
   if (nsplit == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* op = out + (row * H + h) * kDv + wave * 128 + 4 * gq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = hg * 16 + gq * 4 + i;
-      const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
-      uint16_t* op = out + (row * H + h) * kDv + wave * 128 + hl;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) op[n * 16] = f32_to_bf16_bits(o_acc[n][i] * inv);
-      if (lse && wave == 0 && hl == 0)
-        lse[row * H + h] = l_run[i] > 0.f ? (m_run[i] + __log2f(l_run[i])) * kLn2 : -INFINITY;
+    for (int n = 0; n < 8; ++n) {
+      const uint32_t lo = pack_bf16x2(o_acc[n][0] * inv, o_acc[n][1] * inv);
+      const uint32_t hi = pack_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
+      *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
     }
+    if (lse && wave == 0 && gq == 0) lse[row * H + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t nrowh = (int64_t)gridDim.x * 16;  // (row, head) pairs over all rows
+    const int64_t rh = rowh * 16 + hl;
+    float* po = part_o + ((int64_t)split * nrowh + rh) * kDv + wave * 128 + 4 * gq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t rh = rowh * 16 + gq * 4 + i;
-      float* po = part_o + ((int64_t)split * nrowh + rh) * kDv + wave * 128 + hl;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) po[n * 16] = o_acc[n][i];
-      if (wave == 0 && hl == 0) {
-        part_ml[((int64_t)split * nrowh + rh) * 2 + 0] = m_run[i];
-        part_ml[((int64_t)split * nrowh + rh) * 2 + 1] = l_run[i];
-      }
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<float4*>(po + n * 16) = make_float4(o_acc[n][0], o_acc[n][1], o_acc[n][2], o_acc[n][3]);
+    if (wave == 0 && gq == 0) {
+      part_ml[((int64_t)split * nrowh + rh) * 2 + 0] = m_run;
+      part_ml[((int64_t)split * nrowh + rh) * 2 + 1] = l_run;
     }
   }
 }
