@@ -28,6 +28,66 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+TRAFFIC_FILE = os.path.join(PROFILES, "mla_attn_t65536_k2048_traffic.txt")
+
+
+def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
+    """Turn two rocprofv3 --pmc runs of `bench.py --copy-calibration` (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into the HBM bytes per launch of the sparse-attention
+    kernel, each counter scaled by what it reads for the plain 1 GiB device copy."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        attn = [float(r["Counter_Value"]) for r in rows if "mla_attn_kernel<false>" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+                or "copy_kernel" in r["Kernel_Name"]]
+        return attn, copy
+
+    fa, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    wa, wc = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = 1 << 30
+    f_scale = copy_bytes / (max(fc) * 1024.0)  # the copy reads 1 GiB
+    w_scale = copy_bytes / (max(wc) * 1024.0)  # and writes 1 GiB
+    f_bytes = sum(fa) / len(fa) * 1024.0 * f_scale
+    w_bytes = sum(wa) / len(wa) * 1024.0 * w_scale
+    lines = [
+        "# HBM traffic of mla_attn_kernel<bf16> (T=65536, k=2048, 16 heads, 576/512) per launch",
+        "# made by:",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch_D -o fetch -- "
+        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --copy-calibration",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write_D -o write -- "
+        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --copy-calibration",
+        "#   python3 bench.py --summarize-traffic <fetch csv> <write csv>",
+        f"attn_dispatches: {len(fa)}",
+        f"fetch_kib_per_launch: {sum(fa) / len(fa):.1f}",
+        f"write_kib_per_launch: {sum(wa) / len(wa):.1f}",
+        f"copy_fetch_kib: {max(fc):.1f}",
+        f"copy_write_kib: {max(wc):.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"hbm_bytes_per_launch: {int(f_bytes + w_bytes)}",
+        f"source_hash: {source_hash('attention.hip', 'common.hpp')}",
+    ]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed summary, if the kernel source is unchanged."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if line.strip() and not line.startswith("#") and ":" in line:
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_hash") != source_hash("attention.hip", "common.hpp"):
+        return None
+    return int(kv["hbm_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -39,6 +99,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference dispatch for HBM counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs and exit")
     return ap.parse_args()
 
 
@@ -56,6 +118,9 @@ def source_hash(*names):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
@@ -135,13 +200,7 @@ def main():
     sel = k * T - k * (k - 1) // 2 if T >= k else T * (T + 1) // 2
     attn_bytes = sel * w.Dqk * 2 + T * w.H * w.Dqk * 2 + T * k * 4 + T * w.H * w.Dv * 2 + T * w.H * 4
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = None
-    tfile = os.path.join(PROFILES, "mla_attn_t65536_k2048_traffic.json")
-    if os.path.exists(tfile) and T == 65536:
-        with open(tfile) as f:
-            tr = json.load(f)
-        if tr.get("source_hash") == source_hash("attention.hip", "common.hpp"):
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = read_traffic() if T == 65536 else None
     roofline = {"kernel": "mla_attn_kernel<bf16>", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": attn_bytes, "ms_per_launch": round(attn_ms, 3)}
@@ -166,8 +225,8 @@ def main():
         "roofline": roofline, "kernels": kernels,
     }
 
-    if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    if args.copy_calibration:  # a plain 1 GiB device copy: reference dispatch for HBM counters
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
