@@ -26,14 +26,27 @@ namespace {
 
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kTile = 32;                // selected keys per tile
-constexpr int kPitch = kDqk * 2 + 16;    // LDS row pitch in bytes (1168: 16-B skew per row)
+constexpr int kRowB = kDqk * 2;          // staged bf16 row: 1152 B = 72 chunks of 16 B
 constexpr int kQSteps = kDqk / 32 / 2;   // MFMA k-steps of Q K^T per wave (half of 18)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// LDS rows are XOR-swizzled in 16-byte chunks: chunk c of row r sits at c ^ swz(r).
+// swz maps any 8 consecutive rows to 8 distinct values (the K reads of Q K^T touch one
+// chunk of 8 rows at a time) and rows 4m..4m+3 to {0,2,4,6} plus one shared low bit (the
+// transposed V reads touch 2 adjacent chunks of 4 such rows), so both read patterns
+// spread over all 32 banks.  Chunks stay inside their aligned group of 8 (72 = 9 x 8).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int lds_off(int r, int chunk) { return r * kRowB + ((chunk ^ swz(r)) << 4); }
+
 // Gather of one tile: wave w fetches tile keys 8w..8w+7; lane l owns key 8w + l/8 and the
 // 16-byte parts l%8, l%8+8, ... of its row, so every load instruction reads eight full
 // 128-byte lines.  Rows go through registers into LDS (bf16; fp8 widened exactly).
+// Row offsets use a 24-bit multiply (rows < 2^24 here): a 64-bit multiply-add would read an
+// undefined high addend register and could force a wait on an unrelated load.  A missing
+// row (s < 0) is read at an offset past the buffer range: zeros, no memory access.  Every
+// part is loaded unconditionally, so all paths issue the same loads and the compiler's
+// load-count waits stay exact.
 template <bool FP8>
 struct TileStage;
 
@@ -42,13 +55,16 @@ struct TileStage<false> {  // bf16 row: 72 parts of 16 B, 9 per lane
   static constexpr int kChunks = 9;
   static constexpr uint32_t kRowBytes = kDqk * 2;
   u32x4 r[kChunks];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int s, int part0) {
+  int s = -1;      // key index of this lane's entry (-1: none)
+  float sc = 1.f;  // its scale (fp8 only)
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int part0) {
+    const uint32_t base = s >= 0 ? __umul24((uint32_t)s, kRowBytes) + part0 * 16 : kOffNone;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) r[c] = buf_load_16(rs, (uint32_t)s * kRowBytes + (part0 + 8 * c) * 16, 0);
+    for (int c = 0; c < kChunks; ++c) r[c] = buf_load_16(rs, base + 128 * c, 0);
   }
-  __device__ __forceinline__ void store(uint8_t* lds_row, int part0) const {
+  __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) *reinterpret_cast<u32x4*>(lds_row + (part0 + 8 * c) * 16) = r[c];
+    for (int c = 0; c < kChunks; ++c) *reinterpret_cast<u32x4*>(lds + lds_off(key, part0 + 8 * c)) = r[c];
   }
 };
 
@@ -57,11 +73,15 @@ struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
   static constexpr int kChunks = 5;
   static constexpr uint32_t kRowBytes = kDqk;
   u32x4 r[kChunks];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int s, int part0) {
+  int s = -1;
+  float sc = 1.f;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int part0) {
+    const uint32_t base = s >= 0 ? __umul24((uint32_t)s, kRowBytes) + part0 * 16 : kOffNone;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int part = part0 + 8 * c;
-      if (part < 36) r[c] = buf_load_16(rs, (uint32_t)s * kRowBytes + part * 16, 0);
+      // part part0 + 8c; the fifth exists for part0 < 4 only (36 parts)
+      const uint32_t off = (c < 4 || part0 < 4) ? base + 128 * c : kOffNone;
+      r[c] = buf_load_16(rs, off, 0);
     }
   }
   template <bool HI>
@@ -70,7 +90,7 @@ struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
     // e4m3 values are exact in bf16: the low 16 bits of the fp32 pattern are zero
     return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
   }
-  __device__ __forceinline__ void store(uint8_t* lds_row, int part0) const {
+  __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int part = part0 + 8 * c;
@@ -84,9 +104,8 @@ struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
       hi[1] = widen2<true>(r[c][2]);
       hi[2] = widen2<false>(r[c][3]);
       hi[3] = widen2<true>(r[c][3]);
-      uint8_t* dst = lds_row + part * 32;
-      *reinterpret_cast<u32x4*>(dst) = lo;
-      *reinterpret_cast<u32x4*>(dst + 16) = hi;
+      *reinterpret_cast<u32x4*>(lds + lds_off(key, 2 * part)) = lo;  // bf16 chunks 2p, 2p+1
+      *reinterpret_cast<u32x4*>(lds + lds_off(key, 2 * part + 1)) = hi;
     }
   }
 };
@@ -98,10 +117,10 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
                                                           float scale_log2, int tiles_per_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) float sbuf[4][4][64];  // partial S^T per wave, accumulator layout
-  __shared__ float tile_scale[2][kTile];
-  __shared__ int tile_valid[2][kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kTile * kRowB];
+  __shared__ __attribute__((aligned(16))) f32x4 sbuf[4][64];           // partial S^T per wave and lane
+  __shared__ __attribute__((aligned(16))) float tile_bias[2][kTile];   // 0 for a valid key, -inf otherwise
+  __shared__ __attribute__((aligned(16))) float tile_scale[2][kTile];  // fp8 row scales
   __shared__ int jmax_red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -144,10 +163,24 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   // gather: this lane's key of the tile and its first 16-byte part
   const int gk = 8 * wave + (lane >> 3), part0 = lane & 7;
   const bool key_owner = (lane & 7) == 0;
-  auto entry = [&](int t) -> int {  // validated key index of this lane's entry in tile t, or -1
+  // Index entries are fetched two tiles ahead of the rows they name, as unconditional
+  // buffer loads (past the list or past this split: the range check returns 0), and
+  // validated only when the row gather is issued: waiting on a load retires every older
+  // load too, so an index consumed right after its load would drain the row prefetch.
+  const __amdgpu_buffer_rsrc_t ix_rs = make_rsrc(ix, (uint32_t)k * 4);
+  const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(FP8 ? kv_scale + (int64_t)b * Tk : nullptr, FP8 ? (uint32_t)Tk * 4 : 0u);
+  auto raw_entry = [&](int t) -> int {
     const int j = t * kTile + gk;
-    const int sj = j < k ? ix[j] : -1;
-    return (sj >= 0 && sj < Tk) ? sj : -1;
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, t < t_end ? j * 4 : (int)kOffNone, 0, 0);
+  };
+  auto valid_entry = [&](int t, int raw) -> int {  // key index of this lane's entry in tile t, or -1
+    const int lim = (t < t_end && t * kTile + gk < k) ? Tk : 0;  // the raw value is always read
+    return (uint32_t)raw < (uint32_t)lim ? raw : -1;
+  };
+  auto fetch = [&](TileStage<FP8>& st, int s_idx) {  // issue the gather of one tile
+    st.s = s_idx;
+    st.load(kv_rs, part0);
+    if (FP8) st.sc = buf_load_f32(sc_rs, s_idx >= 0 ? (uint32_t)s_idx * 4 : kOffNone, 0);
   };
 
   f32x4 o_acc[8];  // O^T: rows = dims wave*128 + n*16 + 4gq + i, column = head hl
@@ -155,100 +188,105 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   for (int n = 0; n < 8; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  TileStage<FP8> stage;
-  int s_cur = -1, s_next = -1;
-  float sc_cur = 1.f;
-  if (t_begin < t_end) {
-    s_cur = entry(t_begin);
-    stage.load(kv_rs, max(s_cur, 0), part0);
-    if (FP8 && key_owner && s_cur >= 0) sc_cur = kv_scale[(int64_t)b * Tk + s_cur];
-    if (t_begin + 1 < t_end) s_next = entry(t_begin + 1);
-  }
-  for (int t = t_begin; t < t_end; ++t) {
+  auto tile = [&](int t, TileStage<FP8>& st, int& nx) {  // nx: raw index entry of tile t+2
     const int buf = (t - t_begin) & 1;
     uint8_t* kvb = kvs[buf];
-    stage.store(kvb + gk * kPitch, part0);
+    st.store(kvb, gk, part0);
     if (key_owner) {
-      tile_valid[buf][gk] = s_cur >= 0;
-      tile_scale[buf][gk] = sc_cur;
+      tile_bias[buf][gk] = st.s >= 0 ? 0.f : -INFINITY;
+      if (FP8) tile_scale[buf][gk] = st.sc;
     }
     __syncthreads();  // tile t staged (the other buffer may still be read by PV of t-1)
-    if (t + 1 < t_end) {
-      s_cur = s_next;
-      stage.load(kv_rs, max(s_cur, 0), part0);
-      sc_cur = 1.f;
-      if (FP8 && key_owner && s_cur >= 0) sc_cur = kv_scale[(int64_t)b * Tk + s_cur];
-      s_next = (t + 2 < t_end) ? entry(t + 2) : -1;
+    // refill this stage with tile t+2; its index entry arrived with tile t's rows
+    {
+      const int s2 = valid_entry(t + 2, nx);
+      nx = raw_entry(t + 4);
+      fetch(st, s2);
     }
 
     // ---- partial S^T = K Q^T over this wave's k-steps, keys 16kh .. 16kh+15
     {
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = kvb + (16 * kh + hl) * kPitch + (ksh * kQSteps) * 64 + gq * 16;
+      const int krow = 16 * kh + hl;
 #pragma unroll
       for (int s = 0; s < kQSteps; ++s) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + s * 64));
+        const int chunk = (ksh * kQSteps + s) * 4 + gq;
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kvb + lds_off(krow, chunk)));
         sacc = mfma16(ka, qb[s], sacc);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sbuf[wave][i][lane] = sacc[i];
+      sbuf[wave][lane] = sacc;
     }
     __syncthreads();  // partial sums visible
 
     // ---- logits of the lane's 8 keys for head hl, online softmax in base 2
+    // (the lane's keys 16h+4gq .. +3 are contiguous: one 16-byte LDS read per half)
     float sv[8], ksc[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const f32x4 pa = sbuf[2 * h][lane], pb2 = sbuf[2 * h + 1][lane];
+      const f32x4 bias = *reinterpret_cast<const f32x4*>(&tile_bias[buf][16 * h + 4 * gq]);
+      f32x4 kscv = {1.f, 1.f, 1.f, 1.f};
+      if (FP8) kscv = *reinterpret_cast<const f32x4*>(&tile_scale[buf][16 * h + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 16 * h + 4 * gq + i;
-        ksc[4 * h + i] = tile_scale[buf][key];
-        const float sfull = sbuf[2 * h][i][lane] + sbuf[2 * h + 1][i][lane];
-        sv[4 * h + i] = tile_valid[buf][key] ? sfull * (ksc[4 * h + i] * scale_log2) : -INFINITY;
+        ksc[4 * h + i] = kscv[i];
+        const float sfull = pa[i] + pb2[i];
+        sv[4 * h + i] = __builtin_fmaf(sfull, FP8 ? kscv[i] * scale_log2 : scale_log2, bias[i]);  // -inf if masked
       }
     }
-    float tm = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) tm = fmaxf(tm, sv[e]);
-    tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    tm = rows_max(tm);
     const float mn = fmaxf(m_run, tm);
-    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
-    float pv[8], ts = 0.f;
+    // exp2(-inf) = 0 covers masked keys and a first valid tile; only a head with no valid
+    // key yet (mn = -inf) needs a finite reference to avoid -inf - -inf
+    const float mref = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m_run - mref);
+    float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = (sv[e] == -INFINITY) ? 0.f : fast_exp2(sv[e] - mn);
-      ts += pv[e];
-    }
-    ts += __shfl_xor(ts, 16, 64);
-    ts += __shfl_xor(ts, 32, 64);
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sv[e] - mref);
+    const float ts = rows_sum(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
     l_run = l_run * alpha + ts;
     m_run = mn;
     // P^T as the B operand: k-slot e of group gq <-> key 4gq+e (e<4), 16+4gq+(e-4) (e>=4);
     // probabilities carry the fp8 row scale for V
     u32x4 pw;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(pv[2 * e] * ksc[2 * e], pv[2 * e + 1] * ksc[2 * e + 1]);
+    for (int e = 0; e < 4; ++e)
+      pw[e] = FP8 ? cvt_bf16x2(pv[2 * e] * ksc[2 * e], pv[2 * e + 1] * ksc[2 * e + 1]) : cvt_bf16x2(pv[2 * e], pv[2 * e + 1]);
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    if (__ballot(alpha != 1.f)) {  // rescale only when some head's running max moved
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o_acc[n][i] *= alpha;
+      for (int n = 0; n < 8; ++n) o_acc[n] *= alpha;
+    }
 
     // ---- O^T[dims wave*128 .. +128] += V^T P^T  (V read transposed from the staged rows)
     {
-      const int kb0 = 4 * gq + (hl >> 2);
+      const int r0 = 4 * gq + (hl >> 2);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const int col = wave * 128 + n * 16 + 4 * (hl & 3);
-        const i16x4 v0 = lds_read_tr16(kvb + kb0 * kPitch + col * 2);
-        const i16x4 v1 = lds_read_tr16(kvb + (kb0 + 16) * kPitch + col * 2);
+        const int dim = wave * 128 + n * 16 + 4 * (hl & 3);  // 4 dims = 8 bytes
+        const int chunk = dim >> 3, half = (dim & 7) * 2;
+        const i16x4 v0 = lds_read_tr16(kvb + lds_off(r0, chunk) + half);
+        const i16x4 v1 = lds_read_tr16(kvb + lds_off(r0 + 16, chunk) + half);
         typedef short i16x8 __attribute__((ext_vector_type(8)));
         const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         o_acc[n] = mfma16(__builtin_bit_cast(bf16x8, vv), pb, o_acc[n]);
       }
     }
+  };
+
+  // prologue: index entries of tiles t_begin .. t_begin+3, rows of the first two in flight
+  TileStage<FP8> st0, st1;
+  const int e0 = raw_entry(t_begin), e1 = raw_entry(t_begin + 1);
+  int nx0 = raw_entry(t_begin + 2), nx1 = raw_entry(t_begin + 3);
+  fetch(st0, valid_entry(t_begin, e0));
+  fetch(st1, valid_entry(t_begin + 1, e1));
+  int t = t_begin;
+  for (; t + 1 < t_end; t += 2) {
+    tile(t, st0, nx0);
+    tile(t + 1, st1, nx1);
   }
+  if (t < t_end) tile(t, st0, nx0);
 
   // ---- results: lane holds O[head hl][wave*128 + n*16 + 4gq + i]
   const int h = hg * 16 + hl;
@@ -257,8 +295,8 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     uint16_t* op = out + (row * H + h) * kDv + wave * 128 + 4 * gq;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const uint32_t lo = pack_bf16x2(o_acc[n][0] * inv, o_acc[n][1] * inv);
-      const uint32_t hi = pack_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
+      const uint32_t lo = cvt_bf16x2(o_acc[n][0] * inv, o_acc[n][1] * inv);
+      const uint32_t hi = cvt_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
       *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
     }
     if (lse && wave == 0 && gq == 0) lse[row * H + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;

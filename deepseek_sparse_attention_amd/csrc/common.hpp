@@ -132,6 +132,30 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, uint32_t* tot
   return v;
 }
 
+// Reductions across the four 16-lane rows of a wave for lanes with the same lane % 16,
+// with the gfx950 lane-swap instructions (VALU, no LDS round trip):
+// permlane16_swap(x, x) yields rows {r0,r0,r2,r2} and {r1,r1,r3,r3};
+// permlane32_swap(x, x) yields halves {lo,lo} and {hi,hi}.
+__device__ __forceinline__ float rows_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // (row 2i) + (row 2i+1), same order in both
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// fp32 -> bf16 pair with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));  // one packed convert
+}
+
 // Order LDS accesses of one wave: its own earlier LDS writes are visible to its later
 // LDS reads from any lane (LDS instructions of a wave complete in order).
 __device__ __forceinline__ void wave_lds_sync() {
