@@ -16,7 +16,13 @@ namespace dsa {
 
 namespace {
 
-constexpr int kQP = 4;  // query tiles per wave
+// Query tiles per wave: as many (up to four) as fit the register file without spilling,
+// next to the weights and three key tiles.
+template <int H_I, int D_I>
+constexpr int query_tiles() {
+  if (D_I <= 32 || (D_I == 64 && H_I >= 8)) return 4;
+  return (D_I == 64 && H_I >= 2) || H_I >= 8 ? 2 : 1;
+}
 
 template <int H_I, int D_I>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
@@ -26,6 +32,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   constexpr int QPT = 32 / H_I;          // queries per MFMA tile
   constexpr int QPL = 16 / H_I;          // queries per lane (per tile)
   constexpr int KS = D_I / 16;           // MFMA k-steps over the indexer width
+  constexpr int kQP = query_tiles<H_I, D_I>();
   constexpr int QB = 4 * kQP * QPT;      // queries per workgroup
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int b = blockIdx.z;
@@ -61,21 +68,16 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) a[t][s] = as_bf16x8(buf_load_16(q_rs, off + s * 32, 0));
   }
-  // head weights of the lane's queries (fp32), their positions and score-row offsets
-  // (positions and keys fit in 32 bits: Tk <= ld <= 2^22)
+  // head weights of the lane's queries (fp32)
   const int g = lane >> 5;
   const __amdgpu_buffer_rsrc_t w_rs =
       make_rsrc(w + ((int64_t)b * Tq + row0 + wrow0) * H_I, (uint32_t)wrows * H_I * 2);
   float wt[kQP][16];
-  int qpos[kQP][QPL];
-  uint32_t qoff[kQP][QPL];
 #pragma unroll
   for (int t = 0; t < kQP; ++t) {
 #pragma unroll
     for (int qq = 0; qq < QPL; ++qq) {
       const int r = t * QPT + g * QPL + qq;  // row within the wave
-      qpos[t][qq] = r < wrows ? (int)(pos_base + wrow0 + r) : -1;
-      qoff[t][qq] = (uint32_t)(r * ld) * 4u;
       if constexpr (H_I == 1) {  // a lone bf16 weight: 2-byte aligned only
         const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b16(w_rs, r * 2, 0, 0);
         wt[t][qq] = __uint_as_float(bits << 16);
@@ -90,6 +92,13 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     }
   }
 
+  // Row r = t*QPT + g*QPL + qq of the wave sits at position pos0 + r and score offset
+  // r*ld*4; only the lane part (g*QPL) lives in registers (positions and keys fit in 32
+  // bits: Tk <= ld <= 2^22).  Rows past the chunk need no mask: their score offsets fall
+  // outside the store range and are dropped.
+  const int pos0 = (int)(pos_base + wrow0) + g * QPL;
+  const uint32_t off0 = (uint32_t)(g * QPL * ld) * 4u;
+  const uint32_t row_bytes = (uint32_t)ld * 4u;
   const int col = lane & 31;
   const int kend = (int)seg_end;
   // byte offset of this lane's key row slice; advances 32 keys per tile
@@ -113,26 +122,39 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
 #pragma unroll
         for (int h = 1; h < H_I; ++h) tot = fmaf(wt[t][qq * H_I + h], relu(acc[qq * H_I + h]), tot);
         // tiles never cross a segment edge, so the causal bound is the only mask
-        buf_store_f32(tot, s_rs, skey <= qpos[t][qq] ? qoff[t][qq] + (uint32_t)skey * 4u : kOffNone, 0);
+        const int rr = t * QPT + qq;  // row offset from the lane's first row (a constant)
+        buf_store_f32(tot, s_rs, skey - rr <= pos0 ? off0 + (uint32_t)rr * row_bytes + (uint32_t)skey * 4u : kOffNone, 0);
       }
     }
   };
-  // two key tiles per trip, ping-ponging the prefetch buffers (no register copies);
-  // prefetches past the segment read keys nobody stores, or zeros past Tk
-  bf16x8 b0[KS], b1[KS];
+  // Key tiles are prefetched two tiles ahead through three rotating register buffers, and
+  // each tile's prefetch is issued before its score stores: stores count in the same
+  // in-order memory counter as loads, so a load issued behind them would wait for them too.
+  // Prefetches past the segment read keys nobody stores, or zeros past Tk.
+  bf16x8 b0[KS], b1[KS], b2[KS];
   load_keys(b0);
-  for (int s0 = (int)seg0; s0 < kend; s0 += 64) {
-    load_keys(b1);
+  load_keys(b1);
+  int s0 = (int)seg0;
+  for (; s0 + 64 < kend; s0 += 96) {
+    load_keys(b2);
     tile(s0, b0);
-    if (s0 + 32 >= kend) break;
     load_keys(b0);
     tile(s0 + 32, b1);
+    load_keys(b1);
+    tile(s0 + 64, b2);
+  }
+  // at most three tiles left: b0 and b1 hold the next two
+  if (s0 < kend) {
+    load_keys(b2);
+    tile(s0, b0);
+    if (s0 + 32 < kend) tile(s0 + 32, b1);
+    if (s0 + 64 < kend) tile(s0 + 64, b2);
   }
 }
 
 template <int H_I, int D_I>
 hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
-  constexpr int QB = 4 * kQP * (32 / H_I);
+  constexpr int QB = 4 * query_tiles<H_I, D_I>() * (32 / H_I);
   const int qblocks = (A.nrows + QB - 1) / QB;
   // keys any row of the chunk can see (kv_len <= Tk)
   const int64_t maxkeys = std::min<int64_t>(A.Tk, (int64_t)A.Tk - A.Tq + A.row0 + A.nrows);
@@ -151,7 +173,7 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
 }  // namespace
 
 bool indexer_supported(int H_I, int d_I, int64_t ld) {
-  // a wave's score rows (kQP * 32/H_I of them) are addressed with 32-bit byte offsets
+  // a wave's score rows (at most 4 * 32/H_I of them) are addressed with 32-bit byte offsets
   return (H_I == 1 || H_I == 2 || H_I == 4 || H_I == 8 || H_I == 16) &&
          (d_I == 16 || d_I == 32 || d_I == 64 || d_I == 128) && ld <= kIndexerMaxLd;
 }

@@ -126,4 +126,4 @@ def test_stack_chunk_rows_bound_the_score_chunk(L):
         shp = dsa.Shape(B, T if B == 1 else 1, T, 16, 64, 16, 1, 576, 512, 2048, 0.04, 0, None)
         rows = L.dsa_stack_chunk_rows(ctypes.byref(shp))
         assert 1 <= rows <= max(1, shp.Tq)
-        assert B * rows * ((T + 63) // 64 * 64) * 4 <= max(128 << 20, B * ((T + 63) // 64 * 64) * 4)
+        assert B * rows * ((T + 63) // 64 * 64) * 4 <= max(1 << 30, B * ((T + 63) // 64 * 64) * 4)
