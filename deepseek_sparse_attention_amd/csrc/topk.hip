@@ -603,13 +603,419 @@ __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restric
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Streaming top-k for rows of up to 65536 keys: 256 threads per row and few registers, so
+// several rows share a CU and one row's loads overlap another's selection.
+//
+// 1. Threshold: 4096 scores from 32 blocks of 128 positions spread over the row are
+//    binned (2048 bins over their range); the low edge of the bin holding the m-th
+//    largest sample, m = alpha*k*4096/n, keeps about alpha*k keys (alpha = 1.4 for k = 2048).
+// 2. Filter: one coalesced 16-byte-per-lane pass over the row appends every key >= the
+//    threshold to an LDS candidate list.  Each wave fills its own quarter of the list from
+//    a wave-uniform counter (ballots place the lanes), so no atomic sits on the path.
+// 3. If k <= candidates <= capacity, the k largest keys of the whole row are exactly the k
+//    largest candidates (every key at or above the k-th largest passed the filter), and a
+//    radix select over the list marks them in position bitmaps.  Otherwise (a misleading
+//    sample, or massive ties) an exact radix select streams the row from global memory.
+// 4. The bitmaps are emitted in position order from a block-wide prefix count.
+constexpr int ST_NT = 256;
+constexpr int ST_NW = ST_NT / 64;
+constexpr int ST_CAP = 4096;                    // candidate list entries
+constexpr int ST_WCAP = ST_CAP / ST_NW;         // entries per wave (1024)
+constexpr int ST_SBLK = 32, ST_SLEN = 128;      // sampled blocks and their length
+constexpr int ST_SAMPLES = ST_SBLK * ST_SLEN;   // 4096, 16 per thread
+constexpr int ST_WPT = SEG_WORDS / ST_NT;       // 8 bitmap words per thread
+constexpr int ST_U = 8;                         // 16-byte loads in flight per thread
+
+__device__ __forceinline__ uint32_t st_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t wsum;
+  const uint32_t incl = wave_incl_scan_u32(v, &wsum);
+  if (lane == 0) red[wid] = wsum;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < ST_NW; ++i) {
+    const uint32_t r = red[i];
+    pre += (i < wid) ? r : 0u;
+    tot += r;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + incl - v;
+}
+
+// min and max over the workgroup (one barrier pair)
+__device__ __forceinline__ void st_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    red[wid] = mn;
+    red[ST_NW + wid] = mx;
+  }
+  __syncthreads();
+  mn = red[0];
+  mx = red[ST_NW];
+#pragma unroll
+  for (int i = 1; i < ST_NW; ++i) {
+    mn = min(mn, red[i]);
+    mx = max(mx, red[ST_NW + i]);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t st_key(float f) {
+  // order-preserving map; adding +0 first turns -0 into +0, so the two tie
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+__global__ __launch_bounds__(ST_NT, 3) void topk_stream_kernel(const float* __restrict__ scores, int64_t ld,
+                                                              int64_t score_bstride, const int32_t* __restrict__ kv_len,
+                                                              int Tq, int Tk, int k, int row0, int32_t* __restrict__ idx) {
+  // 41 KB of LDS: three rows per CU.  The tie bitmap reuses the histogram, which is
+  // cleared once the last histogram pass is done.
+  __shared__ uint32_t hist[NBINS];
+  __shared__ uint32_t sel_bits[SEG_WORDS];
+  uint32_t* const tie_bits = hist;
+  static_assert(NBINS == SEG_WORDS, "tie bitmap aliases the histogram");
+  __shared__ uint32_t cand_key[ST_CAP];
+  __shared__ uint16_t cand_pos[ST_CAP];  // positions < 65536
+  __shared__ uint32_t mem_key[64];
+  __shared__ int32_t mem_pos[64];
+  __shared__ uint32_t red[2 * ST_NW];
+  __shared__ uint32_t state[4];
+  __shared__ uint32_t wcount[ST_NW];  // candidates each wave appended
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int64_t L = seq_len(kv_len, b, Tk);
+  const int64_t p = L - Tq + row0 + r;
+  int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * k;
+  if (p + 1 <= k) {  // every causal key (or none), then padding
+    for (int j = tid; j < k; j += ST_NT) out[j] = (j <= p) ? j : -1;
+    return;
+  }
+  if (p + 1 > SEG) return;  // launched only for rows that fit
+  const int n = (int)(p + 1);
+  // slot c of the list is in use iff it lies below its wave's count
+  auto in_list = [&](int c) { return (uint32_t)(c % ST_WCAP) < wcount[c / ST_WCAP]; };
+  const float* row = scores + (int64_t)b * score_bstride + (int64_t)r * ld;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)n * 4u);
+  // four scores at pos0 .. pos0+3 (pos0 a multiple of 4): one 16-byte load where the row
+  // is 16-byte aligned (ld is free in the API), and dword loads for a group that crosses
+  // the end of the row, so no load depends on how a partly out-of-range access is handled
+  const bool al16 = ((uintptr_t)row & 15u) == 0;
+  auto load4 = [&](int pos0) -> u32x4 {
+    u32x4 v;
+    if (al16 && pos0 + 4 <= n) {
+      v = buf_load_16(rs, (uint32_t)pos0 * 4u, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(buf_load_f32(rs, (uint32_t)(pos0 + e) * 4u, 0));
+    }
+    return v;
+  };
+
+  for (int i = tid; i < SEG_WORDS; i += ST_NT) sel_bits[i] = 0;
+  for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+  if (tid < 4) state[tid] = 0;
+
+  // ---- 1. threshold from the sample (rows that fit the list keep every key)
+  uint32_t theta = 1u;  // every key is >= 1
+  if (n > ST_CAP) {
+    const int blk = tid >> 3, sub = (tid & 7) * 16;
+    const int base = (int)(((int64_t)blk * (n - ST_SLEN)) / (ST_SBLK - 1)) & ~3;  // base + 128 <= n
+    uint32_t sk[16];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const u32x4 v = load4(base + sub + 4 * qd);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sk[4 * qd + e] = st_key(__uint_as_float(v[e]));
+    }
+    uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      smin = min(smin, sk[i]);
+      smax = max(smax, sk[i]);
+    }
+    st_minmax(smin, smax, red);  // (its barriers also order the clears above)
+    const int sh = smax == smin ? 0 : max(0, 32 - __clz(smax - smin) - BIN_BITS);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) atomicAdd(&hist[(sk[i] - smin) >> sh], 1u);
+    __syncthreads();
+    const float alpha = fminf(1.5f, 0.7f * ST_CAP / (float)k);
+    const uint32_t m = max(1u, (uint32_t)min((int64_t)ST_SAMPLES,
+                                             (int64_t)ceilf(alpha * (float)k * (float)ST_SAMPLES / (float)n)));
+    if (wave == 0) {
+      uint32_t bin, above;
+      wave_find_bin_from_top(hist, m, bin, above);
+      if (lane == 0) {
+        state[0] = bin;
+        state[1] = above;
+      }
+    }
+    __syncthreads();
+    // second pass inside that bin: the threshold lands within 2^(sh-11) keys of the m-th
+    // largest sample (a bin edge alone could keep half again as many candidates)
+    const uint32_t blo = smin + (state[0] << sh);
+    const uint32_t bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)smax);
+    const uint32_t m2 = m - state[1];
+    theta = blo;
+    if (sh > 0) {
+      for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+      __syncthreads();
+      const int sh2 = max(0, sh - BIN_BITS);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (sk[i] >= blo && sk[i] <= bhi) atomicAdd(&hist[(sk[i] - blo) >> sh2], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_from_top(hist, m2, bin, above);
+        if (lane == 0) state[0] = blo + (bin << sh2);
+      }
+      __syncthreads();
+      theta = state[0];
+    }
+    for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+    __syncthreads();
+    if (tid == 0) state[0] = 0;
+  }
+  __syncthreads();
+
+  // ---- 2. filter: keys >= theta go to this wave's part of the candidate list
+  {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
+    const int nit = (n + 4 * ST_NT - 1) / (4 * ST_NT);
+    uint32_t wcnt = 0;  // wave-uniform
+    for (int it0 = 0; it0 < nit; it0 += ST_U) {
+      u32x4 v[ST_U];
+#pragma unroll
+      for (int u = 0; u < ST_U; ++u) v[u] = load4((it0 + u) * 4 * ST_NT + 4 * tid);  // past n: zeros
+#pragma unroll
+      for (int u = 0; u < ST_U; ++u) {
+        if (it0 + u >= nit) break;  // uniform
+        const int pos0 = (it0 + u) * 4 * ST_NT + 4 * tid;
+        uint32_t key[4];
+        uint64_t bal[4];
+        uint32_t tot = 0, pre[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          key[e] = (pos0 + e < n) ? st_key(__uint_as_float(v[u][e])) : 0u;
+          bal[e] = __ballot(key[e] >= theta);
+          pre[e] = tot + (uint32_t)__popcll(bal[e] & lt);
+          tot += (uint32_t)__popcll(bal[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t slot = wcnt + pre[e];
+          if (key[e] >= theta && slot < (uint32_t)ST_WCAP) {
+            cand_key[wave * ST_WCAP + slot] = key[e];
+            cand_pos[wave * ST_WCAP + slot] = (uint16_t)(pos0 + e);
+          }
+        }
+        wcnt += tot;
+      }
+    }
+    if (lane == 0) wcount[wave] = min(wcnt, (uint32_t)ST_WCAP);
+    if (lane == 0) red[wave] = wcnt;
+  }
+  __syncthreads();
+  uint32_t c0 = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int i = 0; i < ST_NW; ++i) {
+    c0 += red[i];
+    overflow |= red[i] > (uint32_t)ST_WCAP;
+  }
+  __syncthreads();
+  if (tid == 0) state[2] = 0;  // members of the final bin (exact ranking)
+
+  // ---- 3. exact selection
+  uint32_t need = (uint32_t)k;
+  if (c0 >= (uint32_t)k && !overflow) {
+    uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
+    for (int c = tid; c < ST_CAP; c += ST_NT)
+      if (in_list(c)) cmax = max(cmax, cand_key[c]);
+    st_minmax(cmin, cmax, red);
+    uint32_t lo = theta, hi = cmax;
+    int sh = (hi == lo) ? 0 : max(0, 32 - __clz(hi - lo) - BIN_BITS);
+    uint32_t m;
+    for (;;) {
+      for (int c = tid; c < ST_CAP; c += ST_NT) {
+        const uint32_t key = cand_key[c];
+        if (in_list(c) && key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sh], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_from_top(hist, need, bin, above);
+        if (lane == 0) {
+          state[0] = bin;
+          state[1] = above;
+          state[3] = hist[bin];
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = state[0];
+      m = state[3];
+      const uint32_t blo = lo + (bin << sh);
+      const uint32_t bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)hi);
+      // keys above the threshold bin are kept
+      for (int c = tid; c < ST_CAP; c += ST_NT) {
+        const uint32_t key = cand_key[c];
+        if (in_list(c) && key > bhi && key <= hi) {
+          const int e = cand_pos[c];
+          atomicOr(&sel_bits[e >> 5], 1u << (e & 31));
+        }
+      }
+      need -= state[1];
+      lo = blo;
+      hi = bhi;
+      if (sh == 0 || m <= 64) break;
+      sh = max(0, sh - BIN_BITS);
+      for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+      __syncthreads();
+    }
+    __syncthreads();  // last histogram reads done: it becomes the (empty) tie bitmap
+    for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+    __syncthreads();
+    if (sh > 0 || m <= 64) {
+      // the final bin's m <= 64 members: rank them exactly (score, then position) in one
+      // wave and keep the first `need`
+      for (int c = tid; c < ST_CAP; c += ST_NT) {
+        const uint32_t key = cand_key[c];
+        if (in_list(c) && key >= lo && key <= hi) {
+          const uint32_t slot = atomicAdd(&state[2], 1u);
+          mem_key[slot] = key;
+          mem_pos[slot] = cand_pos[c];
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const uint32_t mk = lane < (int)m ? mem_key[lane] : 0u;
+        const int32_t mp = lane < (int)m ? mem_pos[lane] : 0x7FFFFFFF;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < m; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
+          const int32_t pj = __builtin_amdgcn_readlane(mp, (int)j);
+          rank += (kj > mk) || (kj == mk && pj < mp);
+        }
+        if (lane < (int)m && rank < need) atomicOr(&sel_bits[mp >> 5], 1u << (mp & 31));
+      }
+      need = 0;  // every kept key is in sel_bits
+    } else {
+      // a final bin of one key value held by more than 64 candidates: its members are
+      // ties; keep the first `need` by position
+      const uint32_t kstar = lo;
+      for (int c = tid; c < ST_CAP; c += ST_NT) {
+        if (in_list(c) && cand_key[c] == kstar) {
+          const int e = cand_pos[c];
+          atomicOr(&tie_bits[e >> 5], 1u << (e & 31));
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    // exact radix select over the whole row, re-read from global memory for each pass:
+    // three passes of 11, 11 and 10 bits from the top of the key
+    uint32_t lo = 1u, hi = 0xFFFFFFFFu;
+    int sh = 32 - BIN_BITS;
+    for (;;) {
+      for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+      __syncthreads();
+      for (int pos0 = 4 * tid; pos0 < n; pos0 += 4 * ST_NT) {
+        const u32x4 v = load4(pos0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = (pos0 + e < n) ? st_key(__uint_as_float(v[e])) : 0u;
+          if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sh], 1u);
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_from_top(hist, need, bin, above);
+        if (lane == 0) {
+          state[0] = bin;
+          state[1] = above;
+        }
+      }
+      __syncthreads();
+      need -= state[1];
+      lo += state[0] << sh;
+      if (sh == 0) break;
+      hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
+      sh = max(0, sh - BIN_BITS);
+      __syncthreads();
+    }
+    __syncthreads();  // last histogram reads done: it becomes the (empty) tie bitmap
+    for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
+    __syncthreads();
+    const uint32_t kstar = lo;
+    for (int pos0 = 4 * tid; pos0 < n; pos0 += 4 * ST_NT) {
+      const u32x4 v = load4(pos0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = pos0 + e;
+        const uint32_t key = (pos < n) ? st_key(__uint_as_float(v[e])) : 0u;
+        if (key > kstar) atomicOr(&sel_bits[pos >> 5], 1u << (pos & 31));
+        else if (key == kstar && key) atomicOr(&tie_bits[pos >> 5], 1u << (pos & 31));
+      }
+    }
+    __syncthreads();
+  }
+  // need = ties (key == kstar) to keep, lowest positions first; k - need keys above
+
+  // ---- 4. emission in position order: thread t owns positions 256t .. 256t+255
+  uint32_t sw[ST_WPT], tw[ST_WPT];
+  uint32_t cs = 0, ct = 0;
+#pragma unroll
+  for (int i = 0; i < ST_WPT; ++i) {
+    sw[i] = sel_bits[tid * ST_WPT + i];
+    tw[i] = tie_bits[tid * ST_WPT + i];
+    cs += __popc(sw[i]);
+    ct += __popc(tw[i]);
+  }
+  // one scan for both counts: kept-above count (< 4096) in the high bits, ties below
+  uint32_t tot;
+  const uint32_t packed = st_excl_scan((cs << 17) | ct, red, tot);
+  uint32_t sp = packed >> 17, tp = packed & 0x1FFFFu;
+  const int pbase = tid * ST_WPT * 32;
+#pragma unroll
+  for (int i = 0; i < ST_WPT; ++i) {
+    uint32_t mm = sw[i] | tw[i];
+    while (mm) {
+      const int bit = __ffs(mm) - 1;
+      mm &= mm - 1;
+      const int32_t pos = pbase + i * 32 + bit;
+      // slots stay below k by construction; the guard keeps a violated invariant in-row
+      if ((sw[i] >> bit) & 1u) {
+        const uint32_t slot = sp + min(tp, need);
+        if (slot < (uint32_t)k) out[slot] = pos;
+        ++sp;
+      } else {
+        if (tp < need && sp + tp < (uint32_t)k) out[sp + tp] = pos;
+        ++tp;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.nrows <= 0 || A.B <= 0) return hipSuccess;
   dim3 grid(A.nrows, A.B);
   // rows see at most Tk keys: up to one segment they are kept in registers
-  if (A.Tk <= SEG)
+  // Many rows: the streaming kernel (256 threads, two rows per CU); few rows (decode):
+  // 1024 threads per row keep the chip busy.
+  if (A.Tk <= SEG && (int64_t)A.nrows * A.B >= 1024)
+    hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(ST_NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len,
+                       A.Tq, A.Tk, A.k, A.row0, A.idx);
+  else if (A.Tk <= SEG)
     hipLaunchKernelGGL(topk_fast_kernel, grid, dim3(NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len, A.Tq,
                        A.Tk, A.k, A.row0, A.idx);
   else
