@@ -609,7 +609,7 @@ __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restric
 //
 // 1. Threshold: 4096 scores from 32 blocks of 128 positions spread over the row are
 //    binned (2048 bins over their range); the low edge of the bin holding the m-th
-//    largest sample, m = alpha*k*4096/n, keeps about alpha*k keys (alpha = 1.4 for k = 2048).
+//    largest sample, m = alpha*k*4096/n, keeps about alpha*k keys (alpha = 1.3 for k = 2048).
 // 2. Filter: one coalesced 16-byte-per-lane pass over the row appends every key >= the
 //    threshold to an LDS candidate list.  Each wave fills its own quarter of the list from
 //    a wave-uniform counter (ballots place the lanes), so no atomic sits on the path.
@@ -620,8 +620,8 @@ __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restric
 // 4. The bitmaps are emitted in position order from a block-wide prefix count.
 constexpr int ST_NT = 256;
 constexpr int ST_NW = ST_NT / 64;
-constexpr int ST_CAP = 4096;                    // candidate list entries
-constexpr int ST_WCAP = ST_CAP / ST_NW;         // entries per wave (1024)
+constexpr int ST_CAP = 3840;                    // candidate list entries
+constexpr int ST_WCAP = ST_CAP / ST_NW;         // entries per wave (960)
 constexpr int ST_SBLK = 32, ST_SLEN = 128;      // sampled blocks and their length
 constexpr int ST_SAMPLES = ST_SBLK * ST_SLEN;   // 4096, 16 per thread
 constexpr int ST_WPT = SEG_WORDS / ST_NT;       // 8 bitmap words per thread
@@ -671,10 +671,10 @@ __device__ __forceinline__ uint32_t st_key(float f) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-__global__ __launch_bounds__(ST_NT, 3) void topk_stream_kernel(const float* __restrict__ scores, int64_t ld,
+__global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __restrict__ scores, int64_t ld,
                                                               int64_t score_bstride, const int32_t* __restrict__ kv_len,
                                                               int Tq, int Tk, int k, int row0, int32_t* __restrict__ idx) {
-  // 41 KB of LDS: three rows per CU.  The tie bitmap reuses the histogram, which is
+  // 40 KB of LDS: four rows per CU.  The tie bitmap reuses the histogram, which is
   // cleared once the last histogram pass is done.
   __shared__ uint32_t hist[NBINS];
   __shared__ uint32_t sel_bits[SEG_WORDS];
