@@ -74,6 +74,104 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     print("\n".join(lines))
 
 
+STATS_FILE = os.path.join(PROFILES, "prefill_t65536_k2048_kernel_stats.txt")
+
+
+def summarize_stats(stats_csv, out_path=STATS_FILE):
+    """Turn the kernel_stats.csv of a `rocprofv3 --kernel-trace --stats` run of the default
+    bench command into the per-kernel summary kept with the repository (the library's
+    kernels; torch's own input-generation kernels only enter the total)."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    total_ns = sum(float(r["TotalDurationNs"]) for r in rows)
+    ours = [r for r in rows if "dsa::" in r["Name"]]
+    ours.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [
+        "# rocprofv3 kernel-trace summary: one T=65536, k=2048 DSA layer (workload mla_t65536_k2048_sink)",
+        "# plus the 64 x 65536 fp8 decode step (FSS over 3 layers), on one MI355X",
+        "# command (from the repository root):",
+        "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_D -o trace -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   python3 bench.py --summarize-stats gpurun_out/trace_D/trace_kernel_stats.csv",
+        "# calls: 1 warmup + 3 timed layer_stack steps + 3 event-timed launches of each kernel group",
+        "# (the indexer and top-k run once per query chunk), then the decode steps.",
+        "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel",
+        "",
+    ]
+    for r in ours:
+        short = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} {float(r['MinNs']) / 1e3:10.1f} "
+                     f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['TotalDurationNs']) / 1e6:10.2f} "
+                     f"{100 * float(r['TotalDurationNs']) / total_ns:6.2f}%  {short}")
+    lines += ["", f"# all kernels (incl. torch's input generation): {total_ns / 1e6:.1f} ms"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def run_configs(steps, warmup):
+    """One timed step of each workload (A-E) through dsa_layer_stack, one JSON line each:
+    the per-config measurements (the default run's single line is the headline)."""
+    import torch
+
+    import synth
+    import deepseek_sparse_attention_amd as dsa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def selected(T, k):
+        return k * T - k * (k - 1) // 2 if T >= k else T * (T + 1) // 2
+
+    for key in "ABCDE":
+        w = synth.workload(key)
+        if w.decode:
+            kc = synth.decode_indexer_cache(w, device=dev)
+            layers = []
+            for l in range(len(w.pattern)):
+                d = synth.decode_layer_inputs(w, l, device=dev)
+                if "q_idx" in d:
+                    d["k_idx"] = kc
+                layers.append(d)
+            klen = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
+            cache = torch.empty((w.B, 1, w.k), dtype=torch.int32, device=dev)
+            ms = timed(lambda: dsa.layer_stack(w.pattern, layers, w.k, w.scale(), Dv=w.Dv, kv_len=klen,
+                                               index_cache=cache))
+            nF = w.pattern.count("F")
+            nbytes = nF * w.B * w.T * (w.d_I * 2 + 4) + len(w.pattern) * w.B * w.k * (w.Dqk + 4)
+            line = {"config": key, "workload": w.name, "ms_per_step": round(ms, 4), "value": round(w.B / (ms * 1e-3), 1),
+                    "unit": "tokens/s", "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        else:
+            layers = [synth.layer_inputs(w, l, device=dev) for l in range(len(w.pattern))]
+            cache = torch.empty((w.B, w.T, w.k), dtype=torch.int32, device=dev)
+            ms = timed(lambda: dsa.layer_stack(w.pattern, layers, w.k, w.scale(), Dv=w.Dv, index_cache=cache))
+            nF, nL = w.pattern.count("F"), len(w.pattern)
+            row = w.Hkv * (w.Dqk + (w.Dv if not w.mla else 0)) * 2  # gathered bytes per selected key
+            gather = nL * selected(w.T, w.k) * row
+            flops = nF * 2 * w.H_I * w.d_I * w.T * (w.T + 1) // 2
+            line = {"config": key, "workload": w.name, "layers": nL, "pattern": w.pattern,
+                    "ms_per_step": round(ms, 3), "value": round(w.T / (ms * 1e-3), 1), "unit": "query tokens/s",
+                    "gather_bytes": gather, "gather_gbs": round(gather / (ms * 1e-3) / 1e9, 1),
+                    "indexer_flops": flops}
+        print(json.dumps(line), flush=True)
+        del layers, cache
+        torch.cuda.empty_cache()
+
+
 def read_traffic():
     """HBM bytes per launch from the committed summary, if the kernel source is unchanged."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -96,11 +194,15 @@ def parse():
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: the named workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference dispatch for HBM counters)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--configs", action="store_true",
+                    help="time one step of each workload A-E (one JSON line each) instead of the headline")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="write the per-kernel summary from a rocprofv3 kernel_stats.csv and exit")
     return ap.parse_args()
 
 
@@ -121,9 +223,15 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
+    if args.configs:
+        run_configs(args.steps, args.warmup)
+        return
 
     import torch
 
