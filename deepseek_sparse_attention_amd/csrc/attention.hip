@@ -135,20 +135,11 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   constexpr uint32_t kRowBytes = TileStage<FP8>::kRowBytes;
   const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + (int64_t)b * Tk * kRowBytes, (uint32_t)Tk * kRowBytes);
 
-  // extent of the index list that holds valid entries
-  int jm = -1;
-  for (int j = tid; j < k; j += 256) {
-    const int sj = ix[j];
-    if (sj >= 0 && sj < Tk) jm = j;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
-  if (lane == 0) jmax_red[wave] = jm;
-  __syncthreads();
-  jm = max(max(jmax_red[0], jmax_red[1]), max(jmax_red[2], jmax_red[3]));
-  const int ntiles = (jm + kTile) / kTile;  // tiles covering entries 0..jm
+  // This split's tiles.  Index entries are validated against its nominal range; the scan
+  // below only trims trailing tiles that hold no valid entry, so it can run while the first
+  // loads are in flight (it used to sit in front of them as one more memory round trip).
   const int t_begin = split * tiles_per_split;
-  const int t_end = min(ntiles, t_begin + tiles_per_split);
+  const int t_lim = min((k + kTile - 1) / kTile, t_begin + tiles_per_split);
 
   // Lane roles.  hl = lane % 16 is this lane's head in S^T and O^T; gq = lane / 16 picks
   // which 4 keys of each 16-key half it holds (keys 4gq..4gq+3 and 16+4gq..16+4gq+3).
@@ -172,10 +163,10 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(FP8 ? kv_scale + (int64_t)b * Tk : nullptr, FP8 ? (uint32_t)Tk * 4 : 0u);
   auto raw_entry = [&](int t) -> int {
     const int j = t * kTile + gk;
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, t < t_end ? j * 4 : (int)kOffNone, 0, 0);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, t < t_lim ? j * 4 : (int)kOffNone, 0, 0);
   };
   auto valid_entry = [&](int t, int raw) -> int {  // key index of this lane's entry in tile t, or -1
-    const int lim = (t < t_end && t * kTile + gk < k) ? Tk : 0;  // the raw value is always read
+    const int lim = (t < t_lim && t * kTile + gk < k) ? Tk : 0;  // the raw value is always read
     return (uint32_t)raw < (uint32_t)lim ? raw : -1;
   };
   auto fetch = [&](TileStage<FP8>& st, int s_idx) {  // issue the gather of one tile
@@ -183,6 +174,26 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     st.load(kv_rs, part0);
     if (FP8) st.sc = buf_load_f32(sc_rs, s_idx >= 0 ? (uint32_t)s_idx * 4 : kOffNone, 0);
   };
+
+  // prologue: index entries of tiles t_begin .. t_begin+3, rows of the first two in flight
+  TileStage<FP8> st0, st1;
+  const int e0 = raw_entry(t_begin), e1 = raw_entry(t_begin + 1);
+  int nx0 = raw_entry(t_begin + 2), nx1 = raw_entry(t_begin + 3);
+  fetch(st0, valid_entry(t_begin, e0));
+  fetch(st1, valid_entry(t_begin + 1, e1));
+
+  // extent of the index list that holds valid entries: the loop ends after its last tile
+  int jm = -1;
+  for (int j = tid; j < k; j += 256) {
+    const int sj = ix[j];
+    if (sj >= 0 && sj < Tk) jm = j;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
+  if (lane == 0) jmax_red[wave] = jm;
+  __syncthreads();
+  jm = max(max(jmax_red[0], jmax_red[1]), max(jmax_red[2], jmax_red[3]));
+  const int t_end = min((jm + kTile) / kTile, t_lim);  // tiles covering entries 0..jm
 
   f32x4 o_acc[8];  // O^T: rows = dims wave*128 + n*16 + 4gq + i, column = head hl
 #pragma unroll
@@ -276,12 +287,6 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     }
   };
 
-  // prologue: index entries of tiles t_begin .. t_begin+3, rows of the first two in flight
-  TileStage<FP8> st0, st1;
-  const int e0 = raw_entry(t_begin), e1 = raw_entry(t_begin + 1);
-  int nx0 = raw_entry(t_begin + 2), nx1 = raw_entry(t_begin + 3);
-  fetch(st0, valid_entry(t_begin, e0));
-  fetch(st1, valid_entry(t_begin + 1, e1));
   int t = t_begin;
   for (; t + 1 < t_end; t += 2) {
     tile(t, st0, nx0);
