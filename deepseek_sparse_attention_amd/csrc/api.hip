@@ -42,6 +42,9 @@ int chunk_rows(const dsa_shape& s) {
   return (int)std::min<int64_t>(rows, std::max(1, s.Tq));
 }
 
+// The kernels move bf16 / fp8 rows in 16-byte pieces and fp32 / int32 values in 4-byte ones.
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
 dsa_status check_indexer(const void* q, const void* k, const void* w, int B, int Tq, int Tk, int H_I, int d_I,
                          const float* scores, int64_t ld) {
   if (B < 0 || Tq < 0 || Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
@@ -51,6 +54,8 @@ dsa_status check_indexer(const void* q, const void* k, const void* w, int B, int
     return fail(DSA_ERR_UNSUPPORTED, "indexer supports H_I in {1,2,4,8,16}, d_I in {16,32,64,128}, ld <= 2^22");
   if ((int64_t)B * Tq == 0) return DSA_OK;
   if (!q || !k || !w || !scores) return fail(DSA_ERR_NULL, "q_idx, k_idx, w_idx and scores are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, H_I == 1 ? 2 : 4) || !aligned(scores, 4))
+    return fail(DSA_ERR_UNSUPPORTED, "q_idx and k_idx must be 16-byte aligned, w_idx 4-byte (2 for H_I=1), scores 4-byte");
   return DSA_OK;
 }
 
@@ -62,6 +67,7 @@ dsa_status check_topk(const float* scores, int64_t ld, int B, int Tq, int Tk, in
   if (Tk > dsa::kTopkMaxTk) return fail(DSA_ERR_UNSUPPORTED, "Tk must be <= 2^24");
   if ((int64_t)B * Tq == 0) return DSA_OK;
   if (!scores || !idx) return fail(DSA_ERR_NULL, "scores and idx are required");
+  if (!aligned(scores, 4) || !aligned(idx, 4)) return fail(DSA_ERR_UNSUPPORTED, "scores and idx must be 4-byte aligned");
   return DSA_OK;
 }
 
@@ -80,6 +86,9 @@ dsa_status check_attn(const dsa::AttnArgs& a, size_t ws_bytes) {
   if ((int64_t)a.B * a.Tq == 0) return DSA_OK;
   if (!a.q || !a.kv || !a.idx || !a.out) return fail(DSA_ERR_NULL, "q, kv, idx and out are required");
   if (a.fp8 && !a.kv_scale) return fail(DSA_ERR_NULL, "kv_scale is required for fp8 rows");
+  if (!aligned(a.q, 16) || !aligned(a.kv, 16) || !aligned(a.v, 16) || !aligned(a.out, 16) || !aligned(a.ws, 16) ||
+      !aligned(a.idx, 4) || !aligned(a.kv_scale, 4) || !aligned(a.lse, 4))
+    return fail(DSA_ERR_UNSUPPORTED, "q, kv, v, out and ws must be 16-byte aligned; idx, kv_scale and lse 4-byte");
   const size_t need = dsa::attn_workspace_bytes(a.B, a.Tq, a.H, a.Dv, a.k, dsa::attn_mla_supported(a));
   if (need && (!a.ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "attention workspace too small: need " + std::to_string(need) + " bytes");

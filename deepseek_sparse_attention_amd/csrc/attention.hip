@@ -182,9 +182,9 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   fetch(st0, valid_entry(t_begin, e0));
   fetch(st1, valid_entry(t_begin + 1, e1));
 
-  // extent of the index list that holds valid entries: the loop ends after its last tile
+  // extent of this split's entries that are valid: the loop ends after its last tile
   int jm = -1;
-  for (int j = tid; j < k; j += 256) {
+  for (int j = t_begin * kTile + tid; j < min(k, t_lim * kTile); j += 256) {
     const int sj = ix[j];
     if (sj >= 0 && sj < Tk) jm = j;
   }
@@ -320,28 +320,42 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   }
 }
 
-// Merge split-key partial results (fixed split order).  One workgroup per (row, head).
+// Merge split-key partial results (fixed split order).  One workgroup per (row, 4 heads),
+// one wave per head: lane s holds split s's (m, l) (up to 64 splits), the wave reduces
+// them, and each lane then sums 8 output dims over the splits with 16-byte loads.
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                           int nsplit, int64_t nrowh, int H, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const int64_t rh = blockIdx.x;
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[((int64_t)s * nrowh + rh) * 2]);
-  float l = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = part_ml[((int64_t)s * nrowh + rh) * 2];
-    if (ms != -INFINITY) l += part_ml[((int64_t)s * nrowh + rh) * 2 + 1] * fast_exp2(ms - m);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int64_t rh = (int64_t)blockIdx.x * 4 + wave;  // (row, head)
+  if (rh >= nrowh) return;
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < nsplit) {
+    ms = part_ml[((int64_t)lane * nrowh + rh) * 2];
+    ls = part_ml[((int64_t)lane * nrowh + rh) * 2 + 1];
   }
+  float m = ms;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);  // this lane's split weight
+  float l = ls * wgt;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);  // butterfly: same order in every lane
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  for (int d = threadIdx.x; d < kDv; d += blockDim.x) {
-    float o = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = part_ml[((int64_t)s * nrowh + rh) * 2];
-      if (ms != -INFINITY) o += part_o[((int64_t)s * nrowh + rh) * kDv + d] * fast_exp2(ms - m);
-    }
-    out[rh * kDv + d] = f32_to_bf16_bits(o * inv);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* po = part_o + rh * kDv + lane * 8;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float w = __shfl(wgt, sp, 64);
+    const float4 a0 = *reinterpret_cast<const float4*>(po + (int64_t)sp * nrowh * kDv);
+    const float4 a1 = *reinterpret_cast<const float4*>(po + (int64_t)sp * nrowh * kDv + 4);
+    acc[0] += a0.x * w; acc[1] += a0.y * w; acc[2] += a0.z * w; acc[3] += a0.w * w;
+    acc[4] += a1.x * w; acc[5] += a1.y * w; acc[6] += a1.z * w; acc[7] += a1.w * w;
   }
-  if (lse && threadIdx.x == 0) lse[rh] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  uint32_t pk[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pk[e] = cvt_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<uint4*>(out + rh * kDv + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  if (lse && lane == 0) lse[rh] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 // Multi-head form: Dqk = Dv = 32, Hkv = H, one wave per head (heads strided over 4 waves),
@@ -445,7 +459,8 @@ int attn_mla_splits(int B, int Tq, int H, int k) {
   const int64_t wgs = (int64_t)B * Tq * (H / 16);
   const int tiles = (k + kTile - 1) / kTile;
   if (wgs >= 256) return 1;
-  int s = (int)std::min<int64_t>(tiles, (512 + wgs - 1) / std::max<int64_t>(1, wgs));
+  // (at most 64: the merge holds one split per lane)
+  int s = (int)std::min<int64_t>(std::min(tiles, 64), (512 + wgs - 1) / std::max<int64_t>(1, wgs));
   if (s <= 1) return 1;
   const int per = (tiles + s - 1) / s;
   return (tiles + per - 1) / per;
@@ -483,8 +498,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
                          a.Tq, a.Tk, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)nrowh), dim3(256), 0, st, part_o, part_ml, nsplit, nrowh,
-                       a.H, a.out, a.lse);
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((nrowh + 3) / 4)), dim3(256), 0, st, part_o, part_ml, nsplit,
+                       nrowh, a.H, a.out, a.lse);
     return hipGetLastError();
   }
   if (attn_mha_supported(a)) {

@@ -24,6 +24,9 @@
  *     never allocates, frees or synchronizes.  All work is enqueued in order on `stream`.
  *     Inputs must stay valid until that work completes.  Outputs must not alias inputs.
  *   - bf16 tensors hold IEEE bfloat16 values; fp8 tensors hold OCP e4m3 ("e4m3fn") bytes.
+ *   - Alignment: bf16 and fp8 tensors and workspaces start on 16-byte boundaries, fp32 and
+ *     int32 tensors on 4-byte ones (w_idx: 4, or 2 when H_I = 1); otherwise the call
+ *     returns DSA_ERR_UNSUPPORTED.  Row pitches follow from the dense layouts.
  *   - Positions: sequence b holds L_b = kv_len[b] keys (kv_len: device int32[B], or NULL
  *     meaning L_b = Tk for every b).  Query row i of the Tq rows of sequence b sits at
  *     position p = L_b - Tq + i and may attend keys 0..p (its own key included).  Prefill:

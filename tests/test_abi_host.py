@@ -82,6 +82,24 @@ def test_attention_argument_checks(L):
     assert L.dsa_sparse_attn(P, P, None, None, 7, P, 1, 4, 4, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0, None) == 2
 
 
+def test_alignment_checks(L):
+    P = ctypes.c_void_p(16)   # 16-byte aligned
+    U = ctypes.c_void_p(24)   # 8-byte aligned only
+    H = ctypes.c_void_p(18)   # 2-byte aligned only
+    f = ctypes.c_float
+    assert L.dsa_index_scores(U, P, P, None, 1, 4, 4, 16, 64, P, 4, None) == 3    # q_idx
+    assert L.dsa_index_scores(P, U, P, None, 1, 4, 4, 16, 64, P, 4, None) == 3    # k_idx
+    assert L.dsa_index_scores(P, P, H, None, 1, 4, 4, 16, 64, P, 4, None) == 3    # w_idx, H_I = 16
+    assert L.dsa_topk(H, 8, None, 1, 2, 8, 4, P, None, 0, None) == 3              # scores
+    assert L.dsa_topk(P, 8, None, 1, 2, 8, 4, H, None, 0, None) == 3              # idx
+    mla = (1, 4, 4, 16, 1, 576, 512, 4, f(0.04))
+    assert L.dsa_sparse_attn(U, P, None, None, 0, P, *mla, P, None, None, 0, None) == 3   # q
+    assert L.dsa_sparse_attn(P, U, None, None, 0, P, *mla, P, None, None, 0, None) == 3   # kv
+    assert L.dsa_sparse_attn(P, P, None, None, 0, H, *mla, P, None, None, 0, None) == 3   # idx
+    assert L.dsa_sparse_attn(P, P, None, None, 0, P, *mla, U, None, None, 0, None) == 3   # out
+    assert b"aligned" in L.dsa_last_error()
+
+
 def _patterns():
     for line in open(golden("indexcache_patterns.txt")):
         if line.strip() and not line.startswith("#"):
