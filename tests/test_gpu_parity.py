@@ -52,6 +52,21 @@ def test_indexer_integer_inputs_bit_exact(H_I, d_I, T):
     assert np.all(np.isneginf(got[~c]))  # untouched (the binding pre-fills -inf)
 
 
+@pytest.mark.parametrize("d_I,Tq,Tk", [(64, 1, 5000), (32, 3, 777), (128, 8, 1500)])
+def test_indexer_few_rows_integer_inputs_bit_exact(d_I, Tq, Tk):
+    # a few query rows per sequence (decode shapes) take the key-streaming kernel
+    print(f"indexer few rows d_I={d_I} Tq={Tq} Tk={Tk}", flush=True)
+    d = synth.integer_indexer_inputs(3, Tk, 16, d_I, seed=7000 + d_I, qk_max=1, w_max=2)
+    q, w = d["q_idx"][:, -Tq:].contiguous(), d["w_idx"][:, -Tq:].contiguous()
+    kv_len = [Tk, Tk - 37, Tq + 5]
+    ref = oracle.index_scores(q, d["k_idx"], w, kv_len=kv_len)
+    kl = torch.tensor(kv_len, dtype=torch.int32, device=DEV)
+    got = _host(dsa.index_scores(q.to(DEV), d["k_idx"].to(DEV), w.to(DEV), kv_len=kl)).numpy()
+    c = _causal(3, Tq, Tk, kv_len)
+    assert np.array_equal(got[c], ref[c])
+    assert np.all(np.isneginf(got[~c]))  # untouched (the binding pre-fills -inf)
+
+
 @pytest.mark.parametrize("key,T", [("A", 3072), ("B", 2057), ("D", 700)])
 def test_indexer_scores_within_tolerance(key, T):
     print(f"indexer workload {key} T={T}", flush=True)
