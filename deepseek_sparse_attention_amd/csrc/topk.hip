@@ -607,22 +607,30 @@ __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restric
 // Streaming top-k for rows of up to 65536 keys: 256 threads per row and few registers, so
 // several rows share a CU and one row's loads overlap another's selection.
 //
-// 1. Threshold: 4096 scores from 32 blocks of 128 positions spread over the row are
-//    binned (2048 bins over their range); the low edge of the bin holding the m-th
-//    largest sample, m = alpha*k*4096/n, keeps about alpha*k keys (alpha = 1.3 for k = 2048).
+// 1. Threshold: 4096 scores from 256 blocks of 16 positions spread over the row are binned
+//    twice (2048 bins over their range, then inside the chosen bin); the m-th largest
+//    sample, m = alpha*k*4096/n, is a threshold expected to keep about alpha*k keys
+//    (alpha = 1.31 for k = 2048).
 // 2. Filter: one coalesced 16-byte-per-lane pass over the row appends every key >= the
 //    threshold to an LDS candidate list.  Each wave fills its own quarter of the list from
 //    a wave-uniform counter (ballots place the lanes), so no atomic sits on the path.
 // 3. If k <= candidates <= capacity, the k largest keys of the whole row are exactly the k
 //    largest candidates (every key at or above the k-th largest passed the filter), and a
-//    radix select over the list marks them in position bitmaps.  Otherwise (a misleading
-//    sample, or massive ties) an exact radix select streams the row from global memory.
+//    radix select over the list marks them in position bitmaps.  A sample that misjudged
+//    the row (too few candidates, or an overflowing list: scores with positional structure
+//    can do that) has its rank m rescaled by the count the filter saw, and the filter runs
+//    again, up to three passes in all; after that an exact radix select streams the row
+//    from global memory.
 // 4. The bitmaps are emitted in position order from a block-wide prefix count.
 constexpr int ST_NT = 256;
 constexpr int ST_NW = ST_NT / 64;
-constexpr int ST_CAP = 3840;                    // candidate list entries
-constexpr int ST_WCAP = ST_CAP / ST_NW;         // entries per wave (960)
-constexpr int ST_SBLK = 32, ST_SLEN = 128;      // sampled blocks and their length
+constexpr int ST_CAP = 3584;                    // candidate list entries
+constexpr int ST_WCAP = ST_CAP / ST_NW;         // entries per wave (896)
+constexpr int ST_DUMMY = ST_CAP;                // + 256 slots where lanes without a candidate write
+// Rows up to this length keep every key: wave w takes positions 256w .. 256w+255 of each
+// 1024, so its part of the list then holds at most 3*256 + 128 = ST_WCAP of them.
+constexpr int ST_KEEP = (ST_WCAP / 256) * 4 * 256 + ST_WCAP % 256;
+constexpr int ST_SBLK = 256, ST_SLEN = 16;      // sampled blocks (one per thread) and their length
 constexpr int ST_SAMPLES = ST_SBLK * ST_SLEN;   // 4096, 16 per thread
 constexpr int ST_WPT = SEG_WORDS / ST_NT;       // 8 bitmap words per thread
 constexpr int ST_U = 8;                         // 16-byte loads in flight per thread
@@ -680,8 +688,8 @@ __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __re
   __shared__ uint32_t sel_bits[SEG_WORDS];
   uint32_t* const tie_bits = hist;
   static_assert(NBINS == SEG_WORDS, "tie bitmap aliases the histogram");
-  __shared__ uint32_t cand_key[ST_CAP];
-  __shared__ uint16_t cand_pos[ST_CAP];  // positions < 65536
+  __shared__ uint32_t cand_key[ST_CAP + 256];
+  __shared__ uint16_t cand_pos[ST_CAP + 256];  // positions < 65536
   __shared__ uint32_t mem_key[64];
   __shared__ int32_t mem_pos[64];
   __shared__ uint32_t red[2 * ST_NW];
@@ -722,32 +730,34 @@ __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __re
   for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
   if (tid < 4) state[tid] = 0;
 
-  // ---- 1. threshold from the sample (rows that fit the list keep every key)
-  uint32_t theta = 1u;  // every key is >= 1
-  if (n > ST_CAP) {
-    const int blk = tid >> 3, sub = (tid & 7) * 16;
-    const int base = (int)(((int64_t)blk * (n - ST_SLEN)) / (ST_SBLK - 1)) & ~3;  // base + 128 <= n
-    uint32_t sk[16];
+  // ---- 1. the sample: thread t reads the 16 scores of block t (rows up to ST_KEEP keys
+  // keep every key and need no sample)
+  uint32_t sk[16];
+  uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+  int ssh = 0;  // bin shift of the sample's range
+  if (n > ST_KEEP) {
+    const int base = (int)(((int64_t)tid * (n - ST_SLEN)) / (ST_SBLK - 1)) & ~3;  // base + 16 <= n
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
-      const u32x4 v = load4(base + sub + 4 * qd);
+      const u32x4 v = load4(base + 4 * qd);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sk[4 * qd + e] = st_key(__uint_as_float(v[e]));
     }
-    uint32_t smin = 0xFFFFFFFFu, smax = 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       smin = min(smin, sk[i]);
       smax = max(smax, sk[i]);
     }
     st_minmax(smin, smax, red);  // (its barriers also order the clears above)
-    const int sh = smax == smin ? 0 : max(0, 32 - __clz(smax - smin) - BIN_BITS);
+    ssh = smax == smin ? 0 : max(0, 32 - __clz(smax - smin) - BIN_BITS);
+  }
+  // The m-th largest sample, within 2^(ssh-11) keys (two histogram passes; a bin edge alone
+  // could keep half again as many candidates).  The histogram is zero before and after.
+  auto threshold = [&](uint32_t m) -> uint32_t {
+    const int sh = ssh;
 #pragma unroll
     for (int i = 0; i < 16; ++i) atomicAdd(&hist[(sk[i] - smin) >> sh], 1u);
     __syncthreads();
-    const float alpha = fminf(1.5f, 0.7f * ST_CAP / (float)k);
-    const uint32_t m = max(1u, (uint32_t)min((int64_t)ST_SAMPLES,
-                                             (int64_t)ceilf(alpha * (float)k * (float)ST_SAMPLES / (float)n)));
     if (wave == 0) {
       uint32_t bin, above;
       wave_find_bin_from_top(hist, m, bin, above);
@@ -757,12 +767,10 @@ __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __re
       }
     }
     __syncthreads();
-    // second pass inside that bin: the threshold lands within 2^(sh-11) keys of the m-th
-    // largest sample (a bin edge alone could keep half again as many candidates)
     const uint32_t blo = smin + (state[0] << sh);
     const uint32_t bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)smax);
     const uint32_t m2 = m - state[1];
-    theta = blo;
+    uint32_t th = blo;
     if (sh > 0) {
       for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
       __syncthreads();
@@ -777,60 +785,87 @@ __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __re
         if (lane == 0) state[0] = blo + (bin << sh2);
       }
       __syncthreads();
-      theta = state[0];
+      th = state[0];
     }
     for (int i = tid; i < NBINS; i += ST_NT) hist[i] = 0;
     __syncthreads();
-    if (tid == 0) state[0] = 0;
-  }
-  __syncthreads();
+    return th;
+  };
 
-  // ---- 2. filter: keys >= theta go to this wave's part of the candidate list
-  {
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
+  // ---- 2. filter: keys >= theta go to this wave's part of the candidate list.  Every lane
+  // stores every step (no branches): a lane without a candidate writes a dummy slot of its
+  // own past the list.  A slot past the wave's part is clamped to its last entry: that only
+  // happens on overflow, and an overflowing list is not used.  Returns the count of keys
+  // >= theta (all of them, also past the capacity); `overflow`: some wave's part overflowed.
+  bool overflow = false;
+  auto filter = [&](uint32_t theta) -> uint32_t {
     const int nit = (n + 4 * ST_NT - 1) / (4 * ST_NT);
-    uint32_t wcnt = 0;  // wave-uniform
+    const int nfull = n / (4 * ST_NT);  // steps whose 1024 positions all lie in the row
+    uint32_t wcnt = 0;                  // wave-uniform
+    const int dslot = ST_DUMMY + wave * 64 + lane;
+    auto step = [&](const u32x4& v, int pos0, bool tail) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t key = st_key(__uint_as_float(v[e]));
+        if (tail) key = (pos0 + e < n) ? key : 0u;
+        const bool c = key >= theta;
+        const uint64_t bal = __ballot(c);
+        const uint32_t slot =
+            wcnt + tot + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        int at = c ? wave * ST_WCAP + (int)min(slot, (uint32_t)ST_WCAP - 1u) : dslot;
+        asm volatile("" : "+v"(at));  // keep the select: one store per array, not two masked ones
+        cand_key[at] = key;
+        cand_pos[at] = (uint16_t)(pos0 + e);
+        tot += (uint32_t)__popcll(bal);
+      }
+      wcnt += tot;
+    };
     for (int it0 = 0; it0 < nit; it0 += ST_U) {
       u32x4 v[ST_U];
+      if (al16 && it0 + ST_U <= nfull) {  // uniform: whole 16-byte groups inside the row
 #pragma unroll
-      for (int u = 0; u < ST_U; ++u) v[u] = load4((it0 + u) * 4 * ST_NT + 4 * tid);  // past n: zeros
+        for (int u = 0; u < ST_U; ++u) v[u] = buf_load_16(rs, (uint32_t)((it0 + u) * 4 * ST_NT + 4 * tid) * 4u, 0);
 #pragma unroll
-      for (int u = 0; u < ST_U; ++u) {
-        if (it0 + u >= nit) break;  // uniform
-        const int pos0 = (it0 + u) * 4 * ST_NT + 4 * tid;
-        uint32_t key[4];
-        uint64_t bal[4];
-        uint32_t tot = 0, pre[4];
+        for (int u = 0; u < ST_U; ++u) step(v[u], (it0 + u) * 4 * ST_NT + 4 * tid, false);
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          key[e] = (pos0 + e < n) ? st_key(__uint_as_float(v[u][e])) : 0u;
-          bal[e] = __ballot(key[e] >= theta);
-          pre[e] = tot + (uint32_t)__popcll(bal[e] & lt);
-          tot += (uint32_t)__popcll(bal[e]);
-        }
+        for (int u = 0; u < ST_U; ++u) v[u] = load4((it0 + u) * 4 * ST_NT + 4 * tid);  // past n: zeros
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t slot = wcnt + pre[e];
-          if (key[e] >= theta && slot < (uint32_t)ST_WCAP) {
-            cand_key[wave * ST_WCAP + slot] = key[e];
-            cand_pos[wave * ST_WCAP + slot] = (uint16_t)(pos0 + e);
-          }
-        }
-        wcnt += tot;
+        for (int u = 0; u < ST_U; ++u)
+          if (it0 + u < nit) step(v[u], (it0 + u) * 4 * ST_NT + 4 * tid, true);
       }
     }
-    if (lane == 0) wcount[wave] = min(wcnt, (uint32_t)ST_WCAP);
-    if (lane == 0) red[wave] = wcnt;
-  }
-  __syncthreads();
-  uint32_t c0 = 0;
-  bool overflow = false;
+    if (lane == 0) {
+      wcount[wave] = min(wcnt, (uint32_t)ST_WCAP);
+      red[wave] = wcnt;
+    }
+    __syncthreads();
+    uint32_t cnt = 0;
+    overflow = false;
 #pragma unroll
-  for (int i = 0; i < ST_NW; ++i) {
-    c0 += red[i];
-    overflow |= red[i] > (uint32_t)ST_WCAP;
+    for (int i = 0; i < ST_NW; ++i) {
+      cnt += red[i];
+      overflow |= red[i] > (uint32_t)ST_WCAP;
+    }
+    __syncthreads();
+    return cnt;
+  };
+
+  uint32_t c0;
+  if (n <= ST_KEEP) {
+    c0 = filter(1u);  // every key is >= 1
+  } else {
+    const float alpha = fminf(1.5f, 0.75f * ST_CAP / (float)k);
+    float m = fminf((float)ST_SAMPLES, ceilf(alpha * (float)k * (float)ST_SAMPLES / (float)n));
+    for (int attempt = 0;; ++attempt) {  // uniform: every quantity below is the workgroup's
+      c0 = filter(threshold((uint32_t)fmaxf(1.f, m)));
+      if ((c0 >= (uint32_t)k && !overflow) || attempt == 2) break;
+      // rescale the sample rank by what the filter saw
+      const float target = alpha * (float)k;
+      m = fminf((float)ST_SAMPLES, fmaxf(1.f, ceilf(m * target / fmaxf(1.f, (float)c0))));
+    }
   }
-  __syncthreads();
   if (tid == 0) state[2] = 0;  // members of the final bin (exact ranking)
 
   // ---- 3. exact selection
@@ -838,9 +873,12 @@ __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __re
   if (c0 >= (uint32_t)k && !overflow) {
     uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
     for (int c = tid; c < ST_CAP; c += ST_NT)
-      if (in_list(c)) cmax = max(cmax, cand_key[c]);
+      if (in_list(c)) {
+        cmin = min(cmin, cand_key[c]);
+        cmax = max(cmax, cand_key[c]);
+      }
     st_minmax(cmin, cmax, red);
-    uint32_t lo = theta, hi = cmax;
+    uint32_t lo = cmin, hi = cmax;
     int sh = (hi == lo) ? 0 : max(0, 32 - __clz(hi - lo) - BIN_BITS);
     uint32_t m;
     for (;;) {

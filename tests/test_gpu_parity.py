@@ -138,6 +138,47 @@ def test_topk_threshold_bin_larger_than_candidate_list():
     assert np.array_equal(got, ref)
 
 
+def _sampled_positions(n):
+    # the blocks the many-row top-k samples to set its threshold: 256 blocks of 16 positions
+    bases = ((np.arange(256) * (n - 16)) // 255) & ~3
+    return (bases[:, None] + np.arange(16)[None, :]).ravel()
+
+
+def test_topk_many_rows_misleading_sample_retries():
+    # 1024 rows (the many-row kernel); only the sampled positions carry large scores, so the
+    # first threshold keeps far fewer than k keys and the filter must run again
+    print("topk many rows, misleading sample", flush=True)
+    rng = np.random.default_rng(21)
+    Tq, Tk = 1024, 32768
+    s = rng.standard_normal((1, Tq, Tk)).astype(np.float32)
+    for i in range(Tq):
+        n = Tk - Tq + i + 1
+        s[0, i, _sampled_positions(n)] += 10.0
+    got, ref = _topk_case(s, 2048)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_many_rows_massive_ties_take_the_exact_path():
+    # three distinct values (and signed zeros): the candidate list overflows on every try
+    print("topk many rows, massive ties", flush=True)
+    rng = np.random.default_rng(22)
+    Tq, Tk = 1024, 20000
+    s = rng.integers(0, 3, size=(1, Tq, Tk)).astype(np.float32)
+    s[s == 0] = np.where(rng.random(np.count_nonzero(s == 0)) < 0.5, -0.0, 0.0).astype(np.float32)
+    got, ref = _topk_case(s, 2048)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_many_rows_short_and_kept_whole():
+    # rows of 1977 .. 3000 keys: shorter than k (all kept) or short enough to keep every key
+    print("topk many rows, short rows", flush=True)
+    rng = np.random.default_rng(23)
+    Tq, Tk = 1024, 3000
+    s = rng.standard_normal((1, Tq, Tk)).astype(np.float32)
+    got, ref = _topk_case(s, 2048)
+    assert np.array_equal(got, ref)
+
+
 def test_topk_long_rows_from_indexer_scores():
     print("topk on GPU indexer scores (workload D shape, T=9000)", flush=True)
     w = synth.workload("D", T=9000)
