@@ -17,7 +17,7 @@ namespace dsa {
 namespace {
 
 // Query tiles per wave: as many (up to four) as fit the register file without spilling,
-// next to the weights and three key tiles.
+// next to the weights and the key pipeline (two tiles of rows, two of operands).
 template <int H_I, int D_I>
 constexpr int query_tiles() {
   if (D_I <= 32 || (D_I == 64 && H_I >= 8)) return 4;
@@ -101,13 +101,37 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   const uint32_t row_bytes = (uint32_t)ld * 4u;
   const int col = lane & 31;
   const int kend = (int)seg_end;
-  // byte offset of this lane's key row slice; advances 32 keys per tile
-  uint32_t koff = (uint32_t)(((int)seg0 + col) * D_I + kh) * 2;
+  // Key tiles pass through a private LDS buffer of the wave: global loads then read whole
+  // key rows (KPI keys of D_I*2 bytes per instruction) rather than 32 keys x 16 bytes in the
+  // MFMA operand layout, and the operand comes back with one ds_read_b128 per k-step.  Only
+  // this wave touches its buffer and LDS operations of one wave complete in order, so no
+  // barrier is needed.
   constexpr uint32_t kTileBytes = 32 * D_I * 2;
-  auto load_keys = [&](bf16x8 (&bk)[KS]) {
+  constexpr int CPK = D_I / 8;   // 16-byte chunks per key row
+  constexpr int KPI = 64 / CPK;  // keys per load instruction
+  constexpr int NLD = 32 / KPI;  // load instructions per tile
+  __shared__ __attribute__((aligned(16))) uint8_t wks[4][2][kTileBytes];
+  uint8_t* const wk0 = wks[wave][0];
+  uint8_t* const wk1 = wks[wave][1];
+  // chunk c of key j sits at chunk position c ^ ((j/2) mod 8): the row-wise writes and the
+  // operand reads (32 keys, one chunk each) both spread over all banks
+  auto kl_off = [](int key, int chunk) {
+    return key * (D_I * 2) + ((chunk ^ ((key >> 1) & (CPK < 8 ? CPK - 1 : 7))) << 4);
+  };
+  const int lk = lane / CPK, lc = lane % CPK;
+  uint32_t gkoff = (uint32_t)(((int)seg0 + lk) * D_I + lc * 8) * 2;
+  auto gload = [&](u32x4 (&gr)[NLD]) {  // keys past Tk read as zero
 #pragma unroll
-    for (int s = 0; s < KS; ++s) bk[s] = as_bf16x8(buf_load_16(k_rs, koff + s * 32, 0));
-    koff += kTileBytes;
+    for (int i = 0; i < NLD; ++i) gr[i] = buf_load_16(k_rs, gkoff + i * KPI * D_I * 2, 0);
+    gkoff += kTileBytes;
+  };
+  auto lstore = [&](uint8_t* wk, const u32x4 (&gr)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(wk + kl_off(i * KPI + lk, lc)) = gr[i];
+  };
+  auto lread = [&](const uint8_t* wk, bf16x8 (&bk)[KS]) {  // B operand: key col, dims 16s + 8g
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bk[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(wk + kl_off(col, 2 * s + g)));
   };
   auto tile = [&](int s0, const bf16x8 (&bk)[KS]) {
     const int skey = s0 + col;
@@ -127,28 +151,26 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
       }
     }
   };
-  // Key tiles are prefetched two tiles ahead through three rotating register buffers, and
-  // each tile's prefetch is issued before its score stores: stores count in the same
-  // in-order memory counter as loads, so a load issued behind them would wait for them too.
-  // Prefetches past the segment read keys nobody stores, or zeros past Tk.
-  bf16x8 b0[KS], b1[KS], b2[KS];
-  load_keys(b0);
-  load_keys(b1);
-  int s0 = (int)seg0;
-  for (; s0 + 64 < kend; s0 += 96) {
-    load_keys(b2);
-    tile(s0, b0);
-    load_keys(b0);
-    tile(s0 + 32, b1);
-    load_keys(b1);
-    tile(s0 + 64, b2);
-  }
-  // at most three tiles left: b0 and b1 hold the next two
-  if (s0 < kend) {
-    load_keys(b2);
-    tile(s0, b0);
-    if (s0 + 32 < kend) tile(s0 + 32, b1);
-    if (s0 + 64 < kend) tile(s0 + 64, b2);
+  // Pipeline: global rows of the next two tiles in flight in registers, the next tile's
+  // operand read from LDS while the current tile computes.  Loads past the segment read
+  // keys nobody stores, or zeros past Tk.
+  u32x4 G0[NLD], G1[NLD];
+  bf16x8 B0[KS], B1[KS];
+  gload(G0);  // tile 0
+  gload(G1);  // tile 1
+  lstore(wk0, G0);
+  gload(G0);  // tile 2
+  lread(wk0, B0);
+  for (int s0 = (int)seg0; s0 < kend; s0 += 64) {
+    lstore(wk1, G1);  // tile j+1
+    gload(G1);        // tile j+3
+    tile(s0, B0);
+    lread(wk1, B1);
+    if (s0 + 32 >= kend) break;
+    lstore(wk0, G0);  // tile j+2
+    gload(G0);        // tile j+4
+    tile(s0 + 32, B1);
+    lread(wk0, B0);
   }
 }
 
@@ -160,8 +182,9 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   const int64_t maxkeys = std::min<int64_t>(A.Tk, (int64_t)A.Tk - A.Tq + A.row0 + A.nrows);
   if (qblocks == 0 || maxkeys <= 0) return hipSuccess;
   const int64_t tiles = (maxkeys + 31) / 32;
-  // enough workgroups to fill the chip: aim at ~1024 workgroups per launch
-  int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, 1024 / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
+  // Aim at ~2048 workgroups per launch: twice what the chip holds at once, with segments
+  // short enough that the causal tail of a launch stays small.
+  int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, 2048 / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
   int64_t seg_tiles = (tiles + segs - 1) / segs;
   segs = (tiles + seg_tiles - 1) / seg_tiles;
   dim3 grid(qblocks, (unsigned)segs, A.B);
