@@ -14,17 +14,18 @@ import os
 import torch
 
 __all__ = [
-    "DSAError", "lib", "abi_version", "index_scores", "topk", "sparse_attn", "layer_stack",
+    "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "layer_stack",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
-    "KV_BF16", "KV_FP8_E4M3", "CACHE_PREFILLED", "OP_SCORES", "OP_TOPK", "OP_ATTN", "OP_STACK",
+    "KV_BF16", "KV_FP8_E4M3", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
+    "OP_STACK", "OP_INDEX_TOPK",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 KV_BF16, KV_FP8_E4M3 = 0, 1
-OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK = 0, 1, 2, 3
-CACHE_PREFILLED = 1
+OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK, OP_INDEX_TOPK = 0, 1, 2, 3, 4
+CACHE_PREFILLED, STACK_UNFUSED = 1, 2
 _STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_PATTERN",
            "DSA_ERR_WORKSPACE", "DSA_ERR_LAUNCH", "DSA_ERR_DEVICE"]
 
@@ -68,6 +69,7 @@ def lib():
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P, I64, P]
         L.dsa_topk.argtypes = [P, I64, P, I, I, I, I, P, P, SZ, P]
+        L.dsa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, SZ, P]
         L.dsa_sparse_attn.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, F, P, P, P, SZ, P]
         L.dsa_layer_stack.argtypes = [ctypes.c_char_p, I, P, ctypes.POINTER(Shape), P, U, P, SZ, P]
         L.dsa_workspace_size.argtypes = [ctypes.POINTER(Shape), I]
@@ -76,7 +78,7 @@ def lib():
         L.dsa_stack_chunk_rows.restype = I
         L.dsa_check_pattern.argtypes = [ctypes.c_char_p, I, U]
         L.dsa_pattern_from_freq.argtypes = [I, I, ctypes.c_char_p]
-        for f in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_stack", "dsa_check_pattern",
+        for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_layer_stack", "dsa_check_pattern",
                   "dsa_pattern_from_freq"):
             getattr(L, f).restype = I
         _lib = L
@@ -121,6 +123,20 @@ def topk(scores, k, Tk=None, kv_len=None, idx=None, stream=None):
     if idx is None:
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=scores.device)
     _check(lib().dsa_topk(_ptr(scores), ld, _ptr(kv_len), B, Tq, Tk, k, _ptr(idx), None, 0, _stream(stream)))
+    return idx
+
+
+def index_topk(q_idx, k_idx, w_idx, k, kv_len=None, oversample=0.0, idx=None, ws=None, stream=None):
+    """dsa_index_topk: int32 [B, Tq, k], the indices index_scores + topk would give."""
+    B, Tq, H_I, d_I = q_idx.shape
+    Tk = k_idx.shape[1]
+    if idx is None:
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+    shp = _shape(B, Tq, Tk, 1, 1, 1, 1, k, 1.0, KV_BF16, H_I, d_I, kv_len)
+    nbytes = workspace_size(shp, OP_INDEX_TOPK)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    _check(lib().dsa_index_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(kv_len), B, Tq, Tk, H_I, d_I, k,
+                                float(oversample), _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
     return idx
 
 
@@ -169,11 +185,11 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, 
 
 
 def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=None, prefilled=False,
-                H_I=None, d_I=None, ws=None, want_lse=True, stream=None):
+                H_I=None, d_I=None, ws=None, want_lse=True, unfused=False, stream=None):
     """dsa_layer_stack over `layers` (dicts with q/kv[/v/kv_scale] and, on F layers, q_idx/k_idx/w_idx).
 
     Returns (outs, lses, index_cache).  Output tensors are allocated unless a layer dict
-    carries "out"/"lse".
+    carries "out"/"lse".  unfused: 'F' layers take the score-chunk route (STACK_UNFUSED).
     """
     n = len(layers)
     L0 = layers[0]
@@ -209,7 +225,8 @@ def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=
     nbytes = workspace_size(shp, OP_STACK)
     ws = _workspace(nbytes, dev, ws)
     _check(lib().dsa_layer_stack(pattern.encode(), n, ios, ctypes.byref(shp), _ptr(index_cache),
-                                 CACHE_PREFILLED if prefilled else 0, _ptr(ws), nbytes, _stream(stream)))
+                                 (CACHE_PREFILLED if prefilled else 0) | (STACK_UNFUSED if unfused else 0),
+                                 _ptr(ws), nbytes, _stream(stream)))
     return outs, lses, index_cache
 
 

@@ -42,6 +42,65 @@ int chunk_rows(const dsa_shape& s) {
   return (int)std::min<int64_t>(rows, std::max(1, s.Tq));
 }
 
+// Route of dsa_index_topk: the fused kernels over chunks of `rows` query rows (candidate
+// lists instead of score rows), or the score kernel + top-k over score chunks.  The fused
+// kernels give every wave whole rows, so a launch needs many rows to balance (rows of all
+// lengths at once): the whole Tq in one chunk up to kFusedBytes of workspace.
+constexpr size_t kFusedBytes = size_t(8) << 30;
+constexpr int64_t kFusedMinRows = 1024;
+
+struct IndexTopkPlan {
+  bool fused;
+  int rows;     // query rows per chunk
+  size_t ws;    // workspace bytes
+};
+
+IndexTopkPlan plan_index_topk(const dsa_shape& s, bool force_unfused) {
+  IndexTopkPlan P;
+  P.fused = !force_unfused && dsa::index_topk_fused_supported(s.H_I, s.d_I, s.k) &&
+            (int64_t)std::max(0, s.B) * std::max(0, s.Tq) >= kFusedMinRows;
+  if (P.fused) {
+    const size_t per_row = std::max<size_t>(1, dsa::fused_layout(s.B, 1, s.Tk).bytes);
+    int64_t rows = std::max<int64_t>(1, (int64_t)(kFusedBytes / per_row));
+    if (rows >= 64) rows = rows / 64 * 64;
+    P.rows = (int)std::min<int64_t>(rows, std::max(1, s.Tq));
+    P.ws = dsa::fused_layout(s.B, P.rows, s.Tk).bytes;
+  } else {
+    P.rows = chunk_rows(s);
+    P.ws = (size_t)std::max(0, s.B) * P.rows * stack_ld(s.Tk) * sizeof(float);
+  }
+  return P;
+}
+
+// Indices of rows [0, Tq) of every sequence by the planned route.
+dsa_status run_index_topk(const IndexTopkPlan& P, const void* q_idx, const void* k_idx, const void* w_idx,
+                          const dsa_shape& s, float oversample, int32_t* idx, void* ws, hipStream_t strm,
+                          const char* who) {
+  for (int r0 = 0; r0 < s.Tq; r0 += P.rows) {
+    const int n = std::min(P.rows, s.Tq - r0);
+    if (P.fused) {
+      dsa::IndexTopkArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, s.kv_len,
+                           s.B, s.Tq, s.Tk, s.H_I, s.d_I, s.k, r0, n, oversample, idx, ws};
+      dsa_status st = launch_status(dsa::launch_index_topk(a, strm), who);
+      if (st != DSA_OK) return st;
+    } else {
+      const int64_t ld = stack_ld(s.Tk);
+      float* scores = reinterpret_cast<float*>(ws);
+      if (s.Tk > 0) {
+        dsa::IndexerArgs ia{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, s.kv_len,
+                            s.B, s.Tq, s.Tk, s.H_I, s.d_I, r0, n, scores, ld, (int64_t)P.rows * ld};
+        dsa_status st = launch_status(dsa::launch_index_scores(ia, strm), who);
+        if (st != DSA_OK) return st;
+      }
+      // (no keys at all: every row selects nothing, and top-k reads no score)
+      dsa::TopkArgs ta{scores, ld, (int64_t)P.rows * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, idx};
+      dsa_status st = launch_status(dsa::launch_topk(ta, strm), who);
+      if (st != DSA_OK) return st;
+    }
+  }
+  return DSA_OK;
+}
+
 // The kernels move bf16 / fp8 rows in 16-byte pieces and fp32 / int32 values in 4-byte ones.
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
@@ -163,6 +222,32 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int 
   return launch_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk");
 }
 
+dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx, const int32_t* kv_len, int B,
+                          int Tq, int Tk, int H_I, int d_I, int k, float oversample, int32_t* idx, void* ws,
+                          size_t ws_bytes, void* stream) {
+  dsa_shape s{};
+  s.B = B;
+  s.Tq = Tq;
+  s.Tk = Tk;
+  s.H_I = H_I;
+  s.d_I = d_I;
+  s.k = k;
+  s.kv_len = kv_len;
+  // the score rows, when used, live in the workspace (checked below)
+  const float* ws_scores = reinterpret_cast<const float*>(&s);
+  dsa_status st = check_indexer(q_idx, k_idx, w_idx, B, Tq, Tk, H_I, d_I, ws_scores, stack_ld(Tk));
+  if (st != DSA_OK) return st;
+  st = check_topk(ws_scores, stack_ld(Tk), B, Tq, Tk, k, idx);
+  if (st != DSA_OK) return st;
+  if (!isfinite(oversample)) return fail(DSA_ERR_SHAPE, "oversample must be finite");
+  if ((int64_t)B * Tq == 0) return DSA_OK;
+  const IndexTopkPlan P = plan_index_topk(s, false);
+  if (P.ws && (!ws || ws_bytes < P.ws))
+    return fail(DSA_ERR_WORKSPACE, "index_topk workspace too small: need " + std::to_string(P.ws) + " bytes");
+  if (!aligned(ws, 16)) return fail(DSA_ERR_UNSUPPORTED, "ws must be 16-byte aligned");
+  return run_index_topk(P, q_idx, k_idx, w_idx, s, oversample, idx, ws, as_stream(stream), "dsa_index_topk");
+}
+
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
                            dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv, int Dqk,
                            int Dv, int k, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
@@ -204,9 +289,11 @@ size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
     case DSA_OP_SCORES:
     case DSA_OP_TOPK: return 0;
     case DSA_OP_ATTN: return dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
+    case DSA_OP_INDEX_TOPK: return plan_index_topk(*s, false).ws;
     case DSA_OP_STACK: {
-      const size_t scores = (size_t)s->B * chunk_rows(*s) * stack_ld(s->Tk) * sizeof(float);
-      return align_up(scores) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
+      // either route of the 'F' layers fits (DSA_STACK_UNFUSED picks the score chunks)
+      const size_t sel = std::max(plan_index_topk(*s, false).ws, plan_index_topk(*s, true).ws);
+      return align_up(sel) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
     }
   }
   return 0;
@@ -243,27 +330,14 @@ dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "stack workspace too small: need " + std::to_string(need) + " bytes");
 
-  const int Tc = chunk_rows(s);
-  const int64_t ld = stack_ld(s.Tk);
-  float* scores = reinterpret_cast<float*>(ws);
-  void* attn_ws = reinterpret_cast<char*>(ws) + align_up((size_t)s.B * Tc * ld * sizeof(float));
+  const IndexTopkPlan P = plan_index_topk(s, (flags & DSA_STACK_UNFUSED) != 0);
+  const size_t sel = std::max(plan_index_topk(s, false).ws, plan_index_topk(s, true).ws);
+  void* attn_ws = reinterpret_cast<char*>(ws) + align_up(sel);
   hipStream_t strm = as_stream(stream);
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer_io& L = layers[l];
-    if (pattern[l] == 'F' && s.Tk > 0) {
-      for (int r0 = 0; r0 < s.Tq; r0 += Tc) {
-        const int n = std::min(Tc, s.Tq - r0);
-        dsa::IndexerArgs ia{(const uint16_t*)L.q_idx, (const uint16_t*)L.k_idx, (const uint16_t*)L.w_idx, s.kv_len,
-                            s.B, s.Tq, s.Tk, s.H_I, s.d_I, r0, n, scores, ld, (int64_t)Tc * ld};
-        st = launch_status(dsa::launch_index_scores(ia, strm), "dsa_layer_stack: indexer");
-        if (st != DSA_OK) return st;
-        dsa::TopkArgs ta{scores, ld, (int64_t)Tc * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, index_cache};
-        st = launch_status(dsa::launch_topk(ta, strm), "dsa_layer_stack: top-k");
-        if (st != DSA_OK) return st;
-      }
-    } else if (pattern[l] == 'F') {  // no keys at all: every row selects nothing
-      dsa::TopkArgs ta{scores, ld, 0, s.kv_len, s.B, s.Tq, s.Tk, s.k, 0, s.Tq, index_cache};
-      st = launch_status(dsa::launch_topk(ta, strm), "dsa_layer_stack: top-k");
+    if (pattern[l] == 'F') {
+      st = run_index_topk(P, L.q_idx, L.k_idx, L.w_idx, s, 0.f, index_cache, ws, strm, "dsa_layer_stack: index/top-k");
       if (st != DSA_OK) return st;
     }
     dsa::AttnArgs a = attn_args(L.q, L.kv, L.kv_scale, L.v, s.kv_dtype, index_cache, s.B, s.Tq, s.Tk, s.H, s.Hkv,

@@ -1,0 +1,538 @@
+// Fused lightning indexer -> causal top-k on gfx950: the selection runs on the scores while
+// the indexer produces them, so no fp32 score row is written to or read back from memory.
+//
+// What is computed is exactly what the indexer followed by top-k computes (DSA ablation card,
+// model list: ReLU indexer; DSV2-Lite IndexCache card, intro: causal selection of k keys;
+// DSA ablation card, "Benchmarks": short rows keep every key; lower index wins a tie,
+// -0 == +0).  Every score comes from the shared per-wave core (indexer_core.hpp), so it is
+// the same fp32 value the score kernel would store, and the selection is exact:
+//
+// 1. sample:    each wave scores its rows against ~1/16 of their keys (whole 32-key tiles
+//               spread evenly over the keys every row of the wave can see);
+// 2. threshold: per row, a score expected to be exceeded by about alpha*k keys (alpha
+//               ~1.65 at k = 2048): the m-th largest sample, m = alpha*k*samples/n;
+// 3. filter:    each wave scores its rows against all their keys and appends every score at
+//               or above its row's threshold, with its key index, to the row's candidate
+//               list (through a small LDS ring, flushed in 32- or 64-entry blocks).  A wave
+//               owns whole rows, so a list needs no atomics and comes out in key order;
+// 4. select:    per row, if the list holds at least k and at most kFusedCap entries it holds
+//               the whole top-k (every key at or above the k-th largest score passed the
+//               threshold test, which is monotone in the score); a radix select over the
+//               list finds the k-th largest key and the ties to keep, and the kept entries
+//               are written in list order, i.e. ascending key index;
+// 5. exact:     rows whose list was too short or overflowed are redone from scratch: one
+//               workgroup recomputes the row's scores in each of five passes (three radix
+//               histogram passes, a count pass and an emission pass).  With the default
+//               alpha this path is astronomically rare; it keeps the result exact anyway.
+#include "indexer_core.hpp"
+#include "internal.hpp"
+#include "selection.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int FZ_CAP = kFusedCap;      // candidate entries per row
+constexpr int FZ_NT = 256;
+constexpr int FZ_NW = FZ_NT / 64;
+constexpr int FZ_EPT = FZ_CAP / FZ_NT;  // list entries per thread in the select kernel
+constexpr int FZ_KEEP = FZ_CAP;         // rows of up to this many keys keep every key
+static_assert(FZ_CAP % FZ_NT == 0 && FZ_CAP % 64 == 0, "list blocks");
+
+// Threshold score of a key from the order-preserving map (keys from finite scores map back
+// to finite floats).
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Block-wide min / max of the valid keys (every thread passes its partial values).
+__device__ __forceinline__ void fz_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    red[wid] = mn;
+    red[FZ_NW + wid] = mx;
+  }
+  __syncthreads();
+  mn = red[0];
+  mx = red[FZ_NW];
+#pragma unroll
+  for (int i = 1; i < FZ_NW; ++i) {
+    mn = min(mn, red[i]);
+    mx = max(mx, red[FZ_NW + i]);
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup in thread order; also returns the total.
+__device__ __forceinline__ uint32_t fz_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t wsum;
+  const uint32_t incl = wave_incl_scan_u32(v, &wsum);
+  if (lane == 0) red[wid] = wsum;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < FZ_NW; ++i) {
+    const uint32_t r = red[i];
+    pre += (i < wid) ? r : 0u;
+    tot += r;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + incl - v;
+}
+
+template <int H_I, int D_I>
+using FzWave = IdxWave<H_I, D_I, idx_query_tiles<H_I, D_I>()>;
+
+// Rows of a wave / workgroup and the wave geometry shared by the sample and filter kernels.
+struct FzRows {
+  int64_t pos_base;  // position of chunk row r is pos_base + r
+  int wrow0, wrows;  // the wave's first chunk row and row count
+  int64_t p_first, p_last;
+};
+
+template <int ROWS>
+__device__ __forceinline__ bool fz_rows(const int32_t* kv_len, int Tq, int Tk, int row0, int nrows, int nblocks,
+                                        FzRows& R) {
+  const int wave = wave_id();
+  const int64_t L = seq_len(kv_len, blockIdx.z, Tk);
+  R.pos_base = L - Tq + row0;
+  const int blk = nblocks - 1 - (int)blockIdx.x;  // blocks with the longest rows first
+  R.wrow0 = blk * 4 * ROWS + wave * ROWS;
+  if (R.wrow0 >= nrows) return false;
+  R.wrows = min(ROWS, nrows - R.wrow0);
+  R.p_first = R.pos_base + R.wrow0;
+  R.p_last = R.p_first + R.wrows - 1;
+  return true;
+}
+
+// ---- 1. sample scores (as order keys) of ~1/16 of the keys of each row
+template <int H_I, int D_I>
+__global__ __launch_bounds__(256, 2) void fz_sample_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ w,
+                                                           const int32_t* __restrict__ kv_len, int Tq, int Tk,
+                                                           int row0, int nrows, int nblocks, uint32_t* __restrict__ smp,
+                                                           int smax, int32_t* __restrict__ ns) {
+  using W = FzWave<H_I, D_I>;
+  __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
+  FzRows R;
+  if (!fz_rows<W::ROWS>(kv_len, Tq, Tk, row0, nrows, nblocks, R)) return;
+  if (R.p_last + 1 <= FZ_KEEP) return;  // every row of the wave keeps all its keys
+  const int b = blockIdx.z, lane = threadIdx.x & 63;
+  // the keys every row of the wave sees: 0 .. p_first (p_first + 1 > FZ_KEEP - 16 >= 512)
+  const int span = (int)(R.p_first + 1);
+  const int nst = fz_sample_tiles(span);
+  const int step = span / nst, half = step / 2 - 16;  // tile j is centred in [j*step, (j+1)*step)
+  const int64_t rbase = (int64_t)b * nrows + R.wrow0;
+  if (lane < R.wrows) ns[rbase + lane] = nst * 32;
+  W wv;
+  wv.load(q + ((int64_t)b * Tq + row0 + R.wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + R.wrow0) * H_I, R.wrows);
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
+  // rows past the wave's count fall outside the store range and are dropped
+  const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(smp + rbase * smax, (uint32_t)(R.wrows * smax * 4));
+  const int col = wv.col;
+  wv.run(k_rs, wks[wave_id()], nst, [&](int j) { return min(max(j * step + half, 0), span - 32); },
+         [&](int j, int, int t, int qq, float tot) {
+           const uint32_t off = (uint32_t)(wv.row_of(t, qq) * smax + j * 32 + col) * 4u;
+           __builtin_amdgcn_raw_buffer_store_b32(sel_key(tot), s_rs, (int)off, 0, 0);
+         });
+}
+
+// ---- 2. per-row threshold: the m-th largest sample (to within a fine histogram bin below
+// it), m = alpha*k*samples/n; rows that keep every key get -inf
+__global__ __launch_bounds__(FZ_NT) void fz_threshold_kernel(const uint32_t* __restrict__ smp, int smax,
+                                                             const int32_t* __restrict__ ns,
+                                                             const int32_t* __restrict__ kv_len, int Tq, int Tk,
+                                                             int row0, int nrows, int topk, float alpha,
+                                                             float* __restrict__ thr) {
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t red[2 * FZ_NW];
+  __shared__ uint32_t state[2];
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int64_t n = seq_len(kv_len, b, Tk) - Tq + row0 + r + 1;
+  const int64_t rowi = (int64_t)b * nrows + r;
+  if (n <= FZ_KEEP) {
+    if (tid == 0) thr[rowi] = -__builtin_inff();
+    return;
+  }
+  const int nsr = ns[rowi];  // <= 32 * kFusedMaxSampleTiles = 16 per thread
+  const uint32_t m = (uint32_t)fminf((float)nsr, fmaxf(1.f, ceilf(alpha * (float)topk * (float)nsr / (float)n)));
+  constexpr int PER = 32 * kFusedMaxSampleTiles / FZ_NT;
+  uint32_t key[PER];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  const uint32_t* srow = smp + rowi * smax;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + FZ_NT * i;
+    key[i] = e < nsr ? srow[e] : 0u;  // 0: no sample (every real key is >= 1)
+    if (key[i]) {
+      mn = min(mn, key[i]);
+      mx = max(mx, key[i]);
+    }
+  }
+  for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
+  fz_minmax(mn, mx, red);  // (its barriers also order the clear)
+  const int sh = sel_shift(mn, mx);
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (key[i]) atomicAdd(&hist[(key[i] - mn) >> sh], 1u);
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bin, above;
+    wave_find_bin_from_top(hist, m, bin, above);
+    if (lane == 0) {
+      state[0] = bin;
+      state[1] = above;
+    }
+  }
+  __syncthreads();
+  const uint32_t blo = mn + (state[0] << sh);
+  const uint32_t bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)mx);
+  const uint32_t m2 = m - state[1];
+  uint32_t th = blo;
+  if (sh > 0) {  // refine inside the bin: a bin edge alone could pass many more keys
+    for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
+    __syncthreads();
+    const int sh2 = sel_shift(blo, bhi);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (key[i] >= blo && key[i] <= bhi) atomicAdd(&hist[(key[i] - blo) >> sh2], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t bin, above;
+      wave_find_bin_from_top(hist, m2, bin, above);
+      if (lane == 0) state[0] = blo + (bin << sh2);
+    }
+    __syncthreads();
+    th = state[0];
+  }
+  // at least m samples have keys >= th, so the filter's count is near alpha*k
+  if (tid == 0) thr[rowi] = key_to_float(th);
+}
+
+// ---- 3. scores of every causal key, filtered into per-row candidate lists
+template <int H_I, int D_I>
+__global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ w,
+                                                           const int32_t* __restrict__ kv_len, int Tq, int Tk,
+                                                           int row0, int nrows, int nblocks, int topk,
+                                                           const float* __restrict__ thr, uint32_t* __restrict__ cnt,
+                                                           uint2* __restrict__ list) {
+  using W = FzWave<H_I, D_I>;
+  constexpr int ROWS = W::ROWS;
+  constexpr int RING = ROWS <= 8 ? 128 : 64;  // ring entries per row (8 KB per wave)
+  constexpr int HALF = RING / 2;              // flush block; a tile adds <= 32 per row
+  static_assert(HALF >= 32 && ROWS * RING <= 1024, "ring size");
+  __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
+  __shared__ uint2 rings[4][ROWS * RING];
+  FzRows R;
+  if (!fz_rows<ROWS>(kv_len, Tq, Tk, row0, nrows, nblocks, R)) return;
+  if (R.p_last + 1 <= topk) return;  // every row keeps all its keys: nothing to select
+  const int b = blockIdx.z, lane = threadIdx.x & 63;
+  const int64_t rbase = (int64_t)b * nrows + R.wrow0;
+  uint2* const ring = rings[wave_id()];
+  W wv;
+  wv.load(q + ((int64_t)b * Tq + row0 + R.wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + R.wrow0) * H_I, R.wrows);
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
+  // the lane's rows: last causal key (-1 for rows past the chunk) and threshold
+  int lim[W::ROWS / W::QPT][W::QPL];
+  float th[W::ROWS / W::QPT][W::QPL];
+#pragma unroll
+  for (int t = 0; t < ROWS / W::QPT; ++t) {
+#pragma unroll
+    for (int qq = 0; qq < W::QPL; ++qq) {
+      const int r = wv.row_of(t, qq);
+      lim[t][qq] = r < R.wrows ? (int)(R.p_first + r) : -1;
+      th[t][qq] = r < R.wrows ? thr[rbase + r] : 0.f;
+    }
+  }
+  uint32_t fill[ROWS];  // candidates of each row so far (wave-uniform)
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) fill[r] = 0;
+  // entries [start, start + HALF) of row r, all in the ring, go to the list
+  auto flush = [&](int r, uint32_t start) {
+    const uint32_t pos = start + lane;
+    if (lane < HALF && pos < (uint32_t)FZ_CAP) list[(rbase + r) * FZ_CAP + pos] = ring[r * RING + (pos & (RING - 1))];
+  };
+  auto account = [&](int r, uint32_t add) {
+    const uint32_t f0 = fill[r], f1 = f0 + add;
+    if ((f0 ^ f1) & ~(uint32_t)(HALF - 1)) flush(r, (f1 & ~(uint32_t)(HALF - 1)) - HALF);
+    fill[r] = f1;
+  };
+  const int col = wv.col, g = wv.g;
+  wv.run(k_rs, wks[wave_id()], (int)((R.p_last + 32) / 32), [](int j) { return 32 * j; },
+         [&](int, int s0, int t, int qq, float tot) {
+           const int skey = s0 + col;
+           const bool c = skey <= lim[t][qq] && tot >= th[t][qq];
+           const uint64_t bal = __ballot(c);
+           const uint32_t n0 = __popc((uint32_t)bal), n1 = __popc((uint32_t)(bal >> 32));
+           const int rA = t * W::QPT + qq, rB = rA + W::QPL;  // the rows of lane groups 0 and 1
+           const uint32_t base = g ? fill[rB] - n0 : fill[rA];
+           if (c) ring[(g ? rB : rA) * RING + ((base + mbcnt64(bal)) & (RING - 1))] =
+               make_uint2(__float_as_uint(tot), (uint32_t)skey);
+           account(rA, n0);
+           account(rB, n1);
+         });
+  // the last partial block of each row, and its count (all candidates, also past the cap)
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    if (r >= R.wrows) break;
+    const uint32_t f = fill[r], start = f & ~(uint32_t)(HALF - 1);
+    const uint32_t pos = start + lane;
+    if (pos < f && pos < (uint32_t)FZ_CAP) list[(rbase + r) * FZ_CAP + pos] = ring[r * RING + (pos & (RING - 1))];
+    if (lane == 0) cnt[rbase + r] = f;
+  }
+}
+
+__device__ __forceinline__ bool fz_row_failed(uint32_t c, int topk) { return c < (uint32_t)topk || c > (uint32_t)FZ_CAP; }
+
+// ---- 4. exact top-k of each row's candidate list
+__global__ __launch_bounds__(FZ_NT) void fz_select_kernel(const uint32_t* __restrict__ cnt,
+                                                          const uint2* __restrict__ list,
+                                                          const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0,
+                                                          int nrows, int topk, int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t red[2 * FZ_NW];
+  __shared__ uint32_t state[2];
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
+  int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * topk;
+  if (p + 1 <= topk) {  // every causal key (or none), then padding
+    for (int j = tid; j < topk; j += FZ_NT) out[j] = (j <= p) ? j : -1;
+    return;
+  }
+  const int64_t rowi = (int64_t)b * nrows + r;
+  const uint32_t c = cnt[rowi];
+  if (fz_row_failed(c, topk)) return;  // the exact pass redoes this row
+  // thread t holds list entries [t*EPT, t*EPT + EPT): list order is key order
+  uint32_t key[FZ_EPT], pos[FZ_EPT];
+  const uint2* lrow = list + rowi * FZ_CAP + tid * FZ_EPT;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < FZ_EPT; i += 2) {
+    const u32x4 v = ld16(lrow + i);
+    const bool v0 = (uint32_t)(tid * FZ_EPT + i) < c, v1 = (uint32_t)(tid * FZ_EPT + i + 1) < c;
+    key[i] = v0 ? sel_key(__uint_as_float(v[0])) : 0u;
+    pos[i] = v[1];
+    key[i + 1] = v1 ? sel_key(__uint_as_float(v[2])) : 0u;
+    pos[i + 1] = v[3];
+  }
+#pragma unroll
+  for (int i = 0; i < FZ_EPT; ++i)
+    if (key[i]) {
+      mn = min(mn, key[i]);
+      mx = max(mx, key[i]);
+    }
+  fz_minmax(mn, mx, red);
+  // radix select of the k-th largest key K* over the list (exact: the last pass has one key
+  // per bin), and `need` = ties at K* to keep
+  uint32_t need = (uint32_t)topk, lo = mn, hi = mx;
+  int sh = sel_shift(lo, hi);
+  for (;;) {
+    for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FZ_EPT; ++i)
+      if (key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> sh], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t bin, above;
+      wave_find_bin_from_top(hist, need, bin, above);
+      if (lane == 0) {
+        state[0] = bin;
+        state[1] = above;
+      }
+    }
+    __syncthreads();
+    need -= state[1];
+    lo += state[0] << sh;
+    if (sh == 0) break;
+    hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
+    sh = sel_shift(lo, hi);
+    __syncthreads();  // state read by every thread before wave 0 rewrites it
+  }
+  const uint32_t kstar = lo;
+  uint32_t na = 0, nt = 0;
+#pragma unroll
+  for (int i = 0; i < FZ_EPT; ++i) {
+    na += key[i] > kstar;
+    nt += key[i] == kstar;
+  }
+  uint32_t tot;
+  const uint32_t pre = fz_excl_scan((na << 16) | nt, red, tot);  // both counts < 2^16
+  uint32_t A = pre >> 16, E = pre & 0xFFFFu;
+#pragma unroll
+  for (int i = 0; i < FZ_EPT; ++i) {
+    // slots stay below k by construction (k - need keys above K*); the guards keep a
+    // violated invariant inside the row
+    if (key[i] > kstar) {
+      const uint32_t slot = A + min(E, need);
+      if (slot < (uint32_t)topk) out[slot] = (int32_t)pos[i];
+      ++A;
+    } else if (key[i] == kstar) {
+      if (E < need && A + E < (uint32_t)topk) out[A + E] = (int32_t)pos[i];
+      ++E;
+    }
+  }
+}
+
+// ---- 5. rows whose list failed: exact top-k from recomputed scores
+template <int H_I, int D_I>
+__global__ __launch_bounds__(FZ_NT) void fz_exact_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ w,
+                                                         const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0,
+                                                         int nrows, int topk, const uint32_t* __restrict__ cnt,
+                                                         int32_t* __restrict__ idx) {
+  using W = IdxWave<H_I, D_I, 1>;  // one query tile: the row and its tile neighbours
+  __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t wc[2][FZ_NW];
+  __shared__ uint32_t state[2];
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int64_t n = seq_len(kv_len, b, Tk) - Tq + row0 + r + 1;
+  if (n <= topk) return;
+  const int64_t rowi = (int64_t)b * nrows + r;
+  if (!fz_row_failed(cnt[rowi], topk)) return;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int t0 = r - r % W::QPT;  // first chunk row of the query tile holding row r
+  const int gsel = (r - t0) / W::QPL, qsel = (r - t0) % W::QPL;
+  W wv;
+  wv.load(q + ((int64_t)b * Tq + row0 + t0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + t0) * H_I, min(W::QPT, nrows - t0));
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
+  const int ntiles = (int)((n + 31) / 32), per = (ntiles + FZ_NW - 1) / FZ_NW;
+  const int j0 = wave * per, nt = max(0, min(per, ntiles - j0));
+  const bool mine = wv.g == gsel;
+  // on_key(valid, key index, order key) for every key of this wave's tiles (uniform calls)
+  auto pass = [&](auto&& on_key) {
+    if (nt > 0)
+      wv.run(k_rs, wks[wave], nt, [&](int j) { return 32 * (j0 + j); },
+             [&](int, int s0, int, int qq, float tot) {
+               const int skey = s0 + wv.col;
+               on_key(mine && qq == qsel && skey < n, skey, sel_key(tot));
+             });
+  };
+  // three radix passes of 11, 11 and 10 bits from the top of the key
+  uint32_t lo = 1u, hi = 0xFFFFFFFFu, need = (uint32_t)topk;
+  int sh = 32 - kSelBinBits;
+  for (;;) {
+    for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
+    __syncthreads();
+    pass([&](bool v, int, uint32_t key) {
+      if (v && key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sh], 1u);
+    });
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t bin, above;
+      wave_find_bin_from_top(hist, need, bin, above);
+      if (lane == 0) {
+        state[0] = bin;
+        state[1] = above;
+      }
+    }
+    __syncthreads();
+    need -= state[1];
+    lo += state[0] << sh;
+    if (sh == 0) break;
+    hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
+    sh = max(0, sh - kSelBinBits);
+    __syncthreads();
+  }
+  const uint32_t kstar = lo;
+  // keys above K* and ties at K* in each wave's key range, then emission in key order
+  uint32_t na = 0, nq = 0;
+  pass([&](bool v, int, uint32_t key) {
+    na += __popcll(__ballot(v && key > kstar));
+    nq += __popcll(__ballot(v && key == kstar));
+  });
+  if (lane == 0) {
+    wc[0][wave] = na;
+    wc[1][wave] = nq;
+  }
+  __syncthreads();
+  uint32_t A = 0, E = 0;
+  for (int i = 0; i < wave; ++i) {
+    A += wc[0][i];
+    E += wc[1][i];
+  }
+  int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * topk;
+  pass([&](bool v, int skey, uint32_t key) {
+    const bool above = v && key > kstar, tie = v && key == kstar;
+    const uint64_t ba = __ballot(above), bt = __ballot(tie);
+    const uint32_t ia = mbcnt64(ba), it = E + mbcnt64(bt);
+    const uint32_t slot = A + ia + min(it, need);  // below k by construction
+    if (above && slot < (uint32_t)topk) out[slot] = skey;
+    if (tie && it < need && slot < (uint32_t)topk) out[slot] = skey;
+    A += __popcll(ba);
+    E += __popcll(bt);
+  });
+}
+
+template <int H_I, int D_I>
+hipError_t launch_fz(const IndexTopkArgs& A, const FusedLayout& Lw, hipStream_t st) {
+  using W = FzWave<H_I, D_I>;
+  const int nblocks = (A.nrows + 4 * W::ROWS - 1) / (4 * W::ROWS);
+  const float alpha = A.oversample > 0.f ? A.oversample : fused_default_alpha(A.k_top);
+  char* ws = reinterpret_cast<char*>(A.ws);
+  uint32_t* smp = reinterpret_cast<uint32_t*>(ws + Lw.smp);
+  int32_t* ns = reinterpret_cast<int32_t*>(ws + Lw.ns);
+  float* thr = reinterpret_cast<float*>(ws + Lw.thr);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + Lw.cnt);
+  uint2* list = reinterpret_cast<uint2*>(ws + Lw.list);
+  const dim3 wgrid(nblocks, 1, A.B), rgrid(A.nrows, A.B);
+  hipLaunchKernelGGL((fz_sample_kernel<H_I, D_I>), wgrid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
+                     A.row0, A.nrows, nblocks, smp, Lw.smax, ns);
+  hipLaunchKernelGGL(fz_threshold_kernel, rgrid, dim3(FZ_NT), 0, st, smp, Lw.smax, ns, A.kv_len, A.Tq, A.Tk, A.row0,
+                     A.nrows, A.k_top, alpha, thr);
+  hipLaunchKernelGGL((fz_filter_kernel<H_I, D_I>), wgrid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
+                     A.row0, A.nrows, nblocks, A.k_top, thr, cnt, list);
+  hipLaunchKernelGGL(fz_select_kernel, rgrid, dim3(FZ_NT), 0, st, cnt, list, A.kv_len, A.Tq, A.Tk, A.row0, A.nrows,
+                     A.k_top, A.idx);
+  hipLaunchKernelGGL((fz_exact_kernel<H_I, D_I>), rgrid, dim3(FZ_NT), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
+                     A.row0, A.nrows, A.k_top, cnt, A.idx);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+FusedLayout fused_layout(int B, int nrows, int Tk) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  FusedLayout L;
+  const size_t R = (size_t)std::max(0, B) * (size_t)std::max(0, nrows);
+  L.smax = 32 * fz_sample_tiles(std::max(Tk, 1));
+  L.smp = 0;
+  L.ns = up(R * L.smax * 4);
+  L.thr = L.ns + up(R * 4);
+  L.cnt = L.thr + up(R * 4);
+  L.list = L.cnt + up(R * 4);
+  L.bytes = L.list + up(R * (size_t)kFusedCap * 8);
+  return L;
+}
+
+bool index_topk_fused_supported(int H_I, int d_I, int k) {
+  return (H_I == 8 || H_I == 16) && (d_I == 16 || d_I == 32 || d_I == 64 || d_I == 128) && k >= 1 &&
+         k <= kFusedMaxK;
+}
+
+hipError_t launch_index_topk(const IndexTopkArgs& A, hipStream_t st) {
+  if (A.nrows <= 0 || A.B <= 0) return hipSuccess;
+  const FusedLayout L = fused_layout(A.B, A.nrows, A.Tk);
+#define DSA_FZ_CASE(h, d) \
+  if (A.H_I == h && A.d_I == d) return launch_fz<h, d>(A, L, st);
+  DSA_FZ_CASE(8, 16) DSA_FZ_CASE(8, 32) DSA_FZ_CASE(8, 64) DSA_FZ_CASE(8, 128)
+  DSA_FZ_CASE(16, 16) DSA_FZ_CASE(16, 32) DSA_FZ_CASE(16, 64) DSA_FZ_CASE(16, 128)
+#undef DSA_FZ_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

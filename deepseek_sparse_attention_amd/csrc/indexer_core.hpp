@@ -1,0 +1,170 @@
+// Per-wave core of the lightning-indexer kernels:
+//   I[t,s] = sum_j w[t,j] * max(0, sum_d q[t,j,d] * k[s,d])
+// (DSA ablation model card, model list: ReLU indexer with a few small heads; one key per
+// token shared by the heads, as its parameter count fixes).
+//
+// One 32x32x16 bf16 MFMA tile covers 32 (query, head) rows against 32 keys.  The rows are
+// ordered so that the 16 accumulator values of a lane are all H_I heads of 16/H_I queries
+// for one key: the ReLU and the head-weighted sum then run inside the lane, with no
+// cross-lane traffic, and each lane ends with finished scores.  A wave keeps kQP query
+// tiles of Q in registers and streams 32-key tiles; what happens to each finished score is
+// the caller's epilogue (store it, sample it, filter it, histogram it).  Every kernel that
+// scores a (query, key) pair goes through this code, so all of them produce the same fp32
+// value for it: the MFMA k-steps, the head order of the sum and the rounding are fixed here.
+#pragma once
+
+#include "common.hpp"
+
+namespace dsa {
+
+// Query tiles per wave: as many (up to four) as fit the register file without spilling,
+// next to the weights and the key pipeline (two tiles of rows, two of operands).
+template <int H_I, int D_I>
+constexpr int idx_query_tiles() {
+  if (D_I <= 32 || (D_I == 64 && H_I >= 8)) return 4;
+  return (D_I == 64 && H_I >= 2) || H_I >= 8 ? 2 : 1;
+}
+
+template <int H_I, int D_I, int kQP>
+struct IdxWave {
+  static constexpr int QPT = 32 / H_I;   // queries per MFMA tile
+  static constexpr int QPL = 16 / H_I;   // queries per lane (per tile)
+  static constexpr int KS = D_I / 16;    // MFMA k-steps over the indexer width
+  static constexpr int ROWS = kQP * QPT; // query rows of the wave
+  static constexpr int CPK = D_I / 8;    // 16-byte chunks per key row
+  static constexpr int KPI = 64 / CPK;   // keys per load instruction
+  static constexpr int NLD = 32 / KPI;   // load instructions per tile
+  static constexpr uint32_t kTileBytes = 32 * D_I * 2;
+  static constexpr uint32_t kLdsBytes = 2 * kTileBytes;  // the wave's private key buffers
+
+  bf16x8 a[kQP][KS];
+  float wt[kQP][16];
+  int g, col;  // lane group (query half of a tile) and key column
+
+  // Wave-local row of (tile t, lane query qq): t*QPT + g*QPL + qq.
+  __device__ __forceinline__ int row_of(int t, int qq) const { return t * QPT + g * QPL + qq; }
+
+  // Q and head weights of rows [0, wrows) at q (bf16 [rows][H_I][D_I]) and w (bf16
+  // [rows][H_I]); rows past wrows read as zero.
+  __device__ __forceinline__ void load(const uint16_t* q, const uint16_t* w, int wrows) {
+    const int lane = threadIdx.x & 63;
+    g = lane >> 5;
+    col = lane & 31;
+    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q, (uint32_t)max(wrows, 0) * H_I * D_I * 2);
+    // A operand: lane row m = lane%32 <-> (query, head) such that D lane group g holds all
+    // heads of queries g*QPL .. g*QPL+QPL-1 of the tile.
+    const int m = lane & 31;
+    const int mi = (m >> 3) * 4 + (m & 3);          // accumulator slot of row m
+    const int mq = ((m >> 2) & 1) * QPL + mi / H_I;  // query within tile
+    const int mh = mi % H_I;                         // head
+    const int kh = (lane >> 5) * 8;                  // k offset of this lane within a k-step
+#pragma unroll
+    for (int t = 0; t < kQP; ++t) {
+      const uint32_t off = (uint32_t)(((t * QPT + mq) * H_I + mh) * D_I + kh) * 2;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[t][s] = as_bf16x8(buf_load_16(q_rs, off + s * 32, 0));
+    }
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(w, (uint32_t)max(wrows, 0) * H_I * 2);
+#pragma unroll
+    for (int t = 0; t < kQP; ++t) {
+#pragma unroll
+      for (int qq = 0; qq < QPL; ++qq) {
+        const int r = row_of(t, qq);
+        if constexpr (H_I == 1) {  // a lone bf16 weight: 2-byte aligned only
+          const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b16(w_rs, r * 2, 0, 0);
+          wt[t][qq] = __uint_as_float(bits << 16);
+        } else {  // head pairs: 4-byte aligned
+#pragma unroll
+          for (int h = 0; h < H_I; h += 2) {
+            const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(w_rs, (r * H_I + h) * 2, 0, 0);
+            wt[t][qq * H_I + h] = __uint_as_float(bits << 16);
+            wt[t][qq * H_I + h + 1] = __uint_as_float(bits & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+  }
+
+  // Scores the wave's rows against key tiles j = 0 .. ntiles-1 (ntiles >= 1); tile j holds
+  // keys start(j) .. start(j)+31 (wave-uniform; keys past the range of k_rs read as zero).
+  // epi(j, s0, t, qq, score) runs on every lane for each tile j (s0 = start(j)), query tile
+  // t and lane query qq, in a fixed order; the lane's key is s0 + col, its row row_of(t, qq).
+  //
+  // Key tiles pass through the wave's private LDS buffer `lds` (kLdsBytes): global loads
+  // read whole key rows (KPI keys of D_I*2 bytes per instruction) rather than 32 keys x 16
+  // bytes in the MFMA operand layout, and the operand comes back with one ds_read_b128 per
+  // k-step.  Only this wave touches the buffer and one wave's LDS operations complete in
+  // order, so no barrier is needed.  Rows of the next two tiles are in flight in registers
+  // and the next tile's operand is read while the current tile computes.
+  template <class Start, class Epi>
+  __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi) {
+    const int lane = threadIdx.x & 63;
+    uint8_t* const wk0 = lds;
+    uint8_t* const wk1 = lds + kTileBytes;
+    // chunk c of key j sits at chunk position c ^ ((j/2) mod 8): the row-wise writes and
+    // the operand reads (32 keys, one chunk each) both spread over all banks
+    auto kl_off = [](int key, int chunk) {
+      return key * (D_I * 2) + ((chunk ^ ((key >> 1) & (CPK < 8 ? CPK - 1 : 7))) << 4);
+    };
+    const int lk = lane / CPK, lc = lane % CPK;
+    const uint32_t lane_koff = (uint32_t)(lk * D_I + lc * 8) * 2;
+    // Tiles are loaded strictly in order (0, 1, 2, ...): one running offset, advanced by the
+    // distance to the next tile's start.  The chain also keeps each tile's loads where the
+    // pipeline puts them (independent offsets let the scheduler bunch two tiles together
+    // and wait for both).
+    uint32_t gkoff = lane_koff + (uint32_t)start(0) * (D_I * 2);
+    int jn = 0;
+    auto gload = [&](u32x4 (&gr)[NLD]) {
+      asm volatile("" : "+v"(gkoff));
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) gr[i] = buf_load_16(k_rs, gkoff + i * KPI * D_I * 2, 0);
+      gkoff += (uint32_t)(start(jn + 1) - start(jn)) * (D_I * 2);
+      ++jn;
+    };
+    auto lstore = [&](uint8_t* wk, const u32x4 (&gr)[NLD]) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(wk + kl_off(i * KPI + lk, lc)) = gr[i];
+    };
+    auto lread = [&](const uint8_t* wk, bf16x8 (&bk)[KS]) {  // B operand: key col, dims 16s + 8g
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        bk[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(wk + kl_off(col, 2 * s + g)));
+    };
+    auto tile = [&](int j, const bf16x8 (&bk)[KS]) {
+      const int s0 = start(j);
+#pragma unroll
+      for (int t = 0; t < kQP; ++t) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma32(a[t][s], bk[s], acc);
+#pragma unroll
+        for (int qq = 0; qq < QPL; ++qq) {
+          float tot = wt[t][qq * H_I] * relu(acc[qq * H_I]);
+#pragma unroll
+          for (int h = 1; h < H_I; ++h) tot = fmaf(wt[t][qq * H_I + h], relu(acc[qq * H_I + h]), tot);
+          epi(j, s0, t, qq, tot);
+        }
+      }
+    };
+    u32x4 G0[NLD], G1[NLD];
+    bf16x8 B0[KS], B1[KS];
+    gload(G0);  // tile 0
+    gload(G1);  // tile 1
+    lstore(wk0, G0);
+    gload(G0);  // tile 2
+    lread(wk0, B0);
+    for (int j = 0; j < ntiles; j += 2) {
+      lstore(wk1, G1);  // tile j+1
+      gload(G1);        // tile j+3
+      tile(j, B0);
+      lread(wk1, B1);
+      if (j + 1 >= ntiles) break;
+      lstore(wk0, G0);  // tile j+2
+      gload(G0);        // tile j+4
+      tile(j + 1, B1);
+      lread(wk0, B0);
+    }
+  }
+};
+
+}  // namespace dsa

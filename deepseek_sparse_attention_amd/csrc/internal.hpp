@@ -39,6 +39,40 @@ constexpr int kTopkMaxK = 4096;
 constexpr int64_t kTopkMaxTk = int64_t(1) << 24;
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
+// Fused indexer -> top-k for rows [row0, row0 + nrows): the indices of index_scores + topk
+// without the score rows.  Workspace: fused_layout(B, nrows, Tk).bytes.
+constexpr int kFusedCap = 6144;             // candidate entries per row
+constexpr int kFusedMaxSampleTiles = 128;   // sampled 32-key tiles per row, at most
+constexpr int kFusedMaxK = 4096;
+// Sampled tiles for a row that sees `span` keys: about one key in 16.
+__host__ __device__ inline int fz_sample_tiles(int64_t span) {
+  const int64_t t = span / 512;
+  return (int)(t < 1 ? 1 : (t > kFusedMaxSampleTiles ? kFusedMaxSampleTiles : t));
+}
+// Expected candidates per row as a multiple of k: ~3400 of the 6144 slots at k = 2048.
+__host__ __device__ inline float fused_default_alpha(int k) {
+  const float a = 0.55f * (float)kFusedCap / (float)(k < 1 ? 1 : k);
+  return a < 1.25f ? 1.25f : (a > 4.f ? 4.f : a);
+}
+struct IndexTopkArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* w;
+  const int32_t* kv_len;
+  int B, Tq, Tk, H_I, d_I, k_top;
+  int row0, nrows;
+  float oversample;  // expected candidates per row / k; <= 0: fused_default_alpha
+  int32_t* idx;      // [B][Tq][k_top]
+  void* ws;
+};
+struct FusedLayout {
+  size_t smp, ns, thr, cnt, list, bytes;  // byte offsets in the workspace, total
+  int smax;                               // sample slots per row
+};
+FusedLayout fused_layout(int B, int nrows, int Tk);
+bool index_topk_fused_supported(int H_I, int d_I, int k);
+hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t st);
+
 struct AttnArgs {
   const uint16_t* q;
   const void* kv;

@@ -15,6 +15,7 @@
 // emitted in index order from a block-wide prefix count of each thread's bit span.
 #include "common.hpp"
 #include "internal.hpp"
+#include "selection.hpp"
 
 namespace dsa {
 
@@ -24,8 +25,8 @@ constexpr int NT = 1024;
 constexpr int NWAVES = NT / 64;
 constexpr int ITEMS = 64;               // keys per thread per segment
 constexpr int SEG = NT * ITEMS;         // 65536 positions per segment
-constexpr int NBINS = 2048;
-constexpr int BIN_BITS = 11;
+constexpr int NBINS = kSelBins;
+constexpr int BIN_BITS = kSelBinBits;
 constexpr int SEG_WORDS = SEG / 32;     // bitmap words per segment
 
 // -0.0 and +0.0 share a key; larger floats get larger keys; 0 marks "no candidate".
@@ -256,36 +257,6 @@ __global__ __launch_bounds__(NT, 1) void topk_kernel(const float* __restrict__ s
 // 4. The bitmaps are emitted in position order from a block-wide prefix count.
 constexpr int kCandCap = 8192;
 constexpr int kSamples = 8;  // per thread
-
-// Top-down search of hist[0..NBINS) by one wave: the bin holding the `need`-th largest
-// count, and the count strictly above it (both wave-uniform).
-__device__ __forceinline__ void wave_find_bin_from_top(const uint32_t* hist, uint32_t need, uint32_t& bin,
-                                                       uint32_t& above) {
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = NBINS / 64;  // 32 bins per lane, lane 0 holds the top ones
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) sum += hist[NBINS - 1 - (lane * PER + i)];
-  uint32_t total;
-  const uint32_t incl = wave_incl_scan_u32(sum, &total);
-  // the lane whose 32 bins hold the need-th count (exactly one: counts are cumulative)
-  const uint64_t hit = __ballot(incl - sum < need && need <= incl);
-  const int L = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : 0);
-  const uint32_t preL = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
-  // spread that lane's bins over lanes 0..31 and scan them
-  const uint32_t c = lane < PER ? hist[NBINS - 1 - (L * PER + lane)] : 0u;
-  uint32_t t2;
-  const uint32_t incl2 = preL + wave_incl_scan_u32(c, &t2);
-  const uint64_t hit2 = __ballot(lane < PER && incl2 - c < need && need <= incl2);
-  const int i2 = hit2 ? (int)__builtin_ctzll(hit2) : 0;
-  uint32_t my_bin = 0xFFFFFFFFu, my_above = 0;
-  if (lane == i2) {
-    my_bin = NBINS - 1 - (L * PER + i2);
-    my_above = incl2 - c;
-  }
-  bin = wave_min_u32(my_bin);  // exactly one lane found it
-  above = wave_min_u32(my_bin == bin ? my_above : 0xFFFFFFFFu);
-}
 
 __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restrict__ scores, int64_t ld,
                                                           int64_t score_bstride, const int32_t* __restrict__ kv_len,
@@ -673,11 +644,7 @@ __device__ __forceinline__ void st_minmax(uint32_t& mn, uint32_t& mx, uint32_t* 
   __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t st_key(float f) {
-  // order-preserving map; adding +0 first turns -0 into +0, so the two tie
-  const uint32_t u = __float_as_uint(f + 0.0f);
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
+__device__ __forceinline__ uint32_t st_key(float f) { return sel_key(f); }
 
 __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __restrict__ scores, int64_t ld,
                                                               int64_t score_bstride, const int32_t* __restrict__ kv_len,

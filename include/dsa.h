@@ -67,10 +67,19 @@ typedef enum {
 
 typedef enum { DSA_KV_BF16 = 0, DSA_KV_FP8_E4M3 = 1 } dsa_kv_dtype;
 
-typedef enum { DSA_OP_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_ATTN = 2, DSA_OP_STACK = 3 } dsa_op;
+typedef enum {
+  DSA_OP_SCORES = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_ATTN = 2,
+  DSA_OP_STACK = 3,
+  DSA_OP_INDEX_TOPK = 4
+} dsa_op;
 
 /* flags of dsa_layer_stack */
 #define DSA_CACHE_PREFILLED 1u /* index_cache already holds indices: a leading 'S' may reuse them */
+#define DSA_STACK_UNFUSED 2u   /* 'F' layers run dsa_index_scores + dsa_topk over score chunks
+                                  even where the fused path of dsa_index_topk applies (same
+                                  indices; for comparison) */
 
 int dsa_abi_version(void);
 const char* dsa_last_error(void);
@@ -101,6 +110,32 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_
  */
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk,
                     int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Indexer scores and top-k in one call (steps 1 and 2 together).  idx is, bit for bit, what
+ * dsa_index_scores followed by dsa_topk on its scores gives (same layouts and rules as
+ * there), but where the fused path applies no score row is written: each wave scores a
+ * sample of ~1/16 of its rows' keys, derives a per-row threshold expected to pass about
+ * oversample*k keys, rescores every key and keeps only those at or above the threshold in a
+ * per-row candidate list, from which an exact selection takes the top k.  A row whose list
+ * ends up shorter than k or longer than its capacity (6144) is recomputed exactly, so the
+ * result does not depend on the sample.
+ *   oversample  expected candidates per row as a multiple of k (<= 0: the library default,
+ *               min(4, max(1.25, 3379/k))); any value gives the same idx, only the speed
+ *               differs.
+ *   idx         int32 [B][Tq][k]
+ *   ws          at least dsa_workspace_size(shape, DSA_OP_INDEX_TOPK) bytes (shape fields
+ *               used: B, Tq, Tk, H_I, d_I, k): sample keys, thresholds and candidate lists
+ *               (about 64 KB per query row at Tk = 65536), or, where the fused path does not
+ *               apply, one chunk of score rows.
+ * Supported: the shapes of dsa_index_scores with 1 <= k <= 4096.  The fused path runs for
+ * H_I in {8, 16} with at least 1024 query rows in all (B*Tq); other shapes run the two steps
+ * over chunks of score rows in the workspace.
+ */
+dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,
+                          const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I, int k,
+                          float oversample, int32_t* idx, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Attention restricted to the selected keys (step 3).
@@ -155,8 +190,9 @@ typedef struct {
  *   index_cache int32 [B][Tq][k] device buffer handed down the stack: an 'F' layer overwrites
  *            it with its own top-k indices, every layer then attends with it as it stands.
  *            A leading 'S' is rejected unless flags has DSA_CACHE_PREFILLED.
- *   ws       at least dsa_workspace_size(shape, DSA_OP_STACK) bytes: one chunk of score rows
- *            (the full Tq x Tk score matrix is never held) plus the attention workspace.
+ *   ws       at least dsa_workspace_size(shape, DSA_OP_STACK) bytes: what the 'F' layers'
+ *            dsa_index_topk needs (or one chunk of score rows, whichever is larger: the full
+ *            Tq x Tk score matrix is never held) plus the attention workspace.
  */
 dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers,
                            const dsa_shape* shape, int32_t* index_cache, unsigned flags, void* ws,

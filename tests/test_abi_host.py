@@ -145,3 +145,43 @@ def test_stack_chunk_rows_bound_the_score_chunk(L):
         rows = L.dsa_stack_chunk_rows(ctypes.byref(shp))
         assert 1 <= rows <= max(1, shp.Tq)
         assert B * rows * ((T + 63) // 64 * 64) * 4 <= max(1 << 30, B * ((T + 63) // 64 * 64) * 4)
+
+
+def test_index_topk_argument_checks(L):
+    P = ctypes.c_void_p(16)
+    f = ctypes.c_float
+    args = lambda **kw: dict(dict(q=P, k=P, w=P, B=1, Tq=4, Tk=4, H_I=16, d_I=64, topk=2, os=f(0.0), idx=P,
+                                  ws=P, nb=1 << 20), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.dsa_index_topk(a["q"], a["k"], a["w"], None, a["B"], a["Tq"], a["Tk"], a["H_I"], a["d_I"], a["topk"],
+                                a["os"], a["idx"], a["ws"], a["nb"], None)
+
+    assert call(q=None) == 1                          # NULL q_idx
+    assert call(idx=None) == 1                        # NULL idx
+    assert call(topk=0) == 2                          # k = 0
+    assert call(topk=4097) == 3                       # k too large
+    assert call(H_I=3) == 3                           # H_I
+    assert call(B=-1) == 2                            # negative B
+    assert call(os=f(float("nan"))) == 2              # oversample
+    assert call(ws=None, nb=0) == 5                   # no workspace
+    assert call(q=None, k=None, w=None, idx=None, B=0) == 0  # empty batch
+    assert call(ws=ctypes.c_void_p(24)) == 3          # unaligned workspace
+
+
+def test_index_topk_workspace_follows_the_route(L):
+    def size(B, Tq, Tk, H_I, k, op):
+        shp = dsa.Shape(B, Tq, Tk, H_I, 64, 16, 1, 576, 512, k, 0.04, 0, None)
+        return L.dsa_workspace_size(ctypes.byref(shp), op)
+
+    # fused (16 heads, many rows): sample keys (Tk/16 per row), thresholds, counts and 6144
+    # candidate slots of 8 bytes per row; nothing of size Tq x Tk
+    fused = size(1, 65536, 65536, 16, 2048, dsa.OP_INDEX_TOPK)
+    assert 65536 * (4096 * 4 + 6144 * 8) <= fused <= 65536 * (4096 * 4 + 6144 * 8 + 64) + 4096
+    # few rows (decode) or 2 indexer heads: score chunks (at most 1 GiB here)
+    assert size(64, 1, 65536, 16, 2048, dsa.OP_INDEX_TOPK) == 64 * 65536 * 4
+    assert size(1, 3072, 3072, 2, 512, dsa.OP_INDEX_TOPK) == 3072 * 3072 * 4
+    # the stack holds either route plus attention
+    st = size(1, 65536, 65536, 16, 2048, dsa.OP_STACK)
+    assert st >= fused and st >= 4096 * 65536 * 4

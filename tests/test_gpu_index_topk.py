@@ -1,0 +1,99 @@
+"""GPU parity of the fused indexer -> top-k (dsa_index_topk) through the C ABI.
+
+Its indices must equal, bit for bit, the oracle's top-k run on the score rows the GPU
+indexer produces (the same rule the unfused top-k is held to), for rows of every kind:
+shorter than k, short enough to keep every key, and long rows that go through the sampled
+threshold; and also where the candidate lists fail on purpose (an oversample factor far too
+small or too large, or massive score ties) and the exact recomputation takes over.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+dsa = pytest.importorskip("deepseek_sparse_attention_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host(x):
+    return x.detach().cpu()
+
+
+def _fused_route(B, Tq, Tk, H_I, d_I, k):
+    # the fused route's workspace holds candidate lists (6144 x 8 bytes per row), the score
+    # route's one chunk of Tk-wide fp32 rows; the two sizes tell the routes apart here
+    shp = dsa.Shape(B, Tq, Tk, H_I, d_I, 16, 1, 576, 512, k, 0.04, 0, None)
+    return dsa.workspace_size(shp, dsa.OP_INDEX_TOPK) >= B * Tq * 6144 * 8
+
+
+def _check(d, k, kv_len=None, oversample=0.0):
+    q, kk, w = (d[x].to(DEV) for x in ("q_idx", "k_idx", "w_idx"))
+    B, Tq, H_I, d_I = q.shape
+    Tk = kk.shape[1]
+    assert _fused_route(B, Tq, Tk, H_I, d_I, k)
+    kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device=DEV)
+    got = _host(dsa.index_topk(q, kk, w, k, kv_len=kl, oversample=oversample)).numpy()
+    s = dsa.index_scores(q, kk, w, kv_len=kl)
+    ref = oracle.topk(_host(s).numpy(), k, kv_len=kv_len, Tk=Tk)
+    assert np.array_equal(got, ref)
+    # and the unfused GPU route agrees
+    assert np.array_equal(got, _host(dsa.topk(s, k, kv_len=kl)).numpy())
+    return got
+
+
+@pytest.mark.parametrize("key,T,k,H_I,d_I", [
+    ("D", 7000, 2048, 16, 64),   # rows < k, rows kept whole (<= 6144 keys), sampled rows
+    ("B", 8192, 1024, 16, 128),  # the widest indexer keys
+    ("B", 4000, 512, 8, 64),     # 8 indexer heads: 16 rows per wave
+    ("B", 1100, 64, 16, 32),     # small k: oversample capped at 4
+])
+def test_index_topk_matches_scores_then_topk(key, T, k, H_I, d_I):
+    print(f"index_topk workload {key} T={T} k={k} H_I={H_I} d_I={d_I}", flush=True)
+    w = synth.workload(key, T=T, k=k, H_I=H_I, d_I=d_I)
+    _check(synth.layer_inputs(w, indexer=True), k)
+
+
+def test_index_topk_batch_with_ragged_kv_len():
+    # two sequences; the second's rows start before position 0 (p < 0: all padding)
+    print("index_topk B=2 ragged kv_len", flush=True)
+    w = synth.workload("B", B=2, T=3000, k=512)
+    got = _check(synth.layer_inputs(w, indexer=True), 512, kv_len=[3000, 1200])
+    assert np.all(got[1, :1800] == -1)
+
+
+@pytest.mark.parametrize("oversample", [0.05, 40.0])
+def test_index_topk_failed_lists_are_recomputed_exactly(oversample):
+    # 0.05: every sampled row's list ends shorter than k; 40: every sampled row's list
+    # overflows its 6144 slots.  Either way the exact pass must produce the same indices.
+    print(f"index_topk forced fallback oversample={oversample}", flush=True)
+    w = synth.workload("D", T=9000)
+    _check(synth.layer_inputs(w, indexer=True), 2048, oversample=oversample)
+
+
+def test_index_topk_integer_scores_with_massive_ties():
+    # small-integer scores: thousands of keys share the threshold value, lists overflow and
+    # ties at the k-th value are resolved by position in the exact pass
+    print("index_topk integer scores", flush=True)
+    d = synth.integer_indexer_inputs(1, 8000, 16, 64, seed=8101, qk_max=1, w_max=2)
+    _check(d, 2048)
+
+
+def test_layer_stack_fused_and_unfused_agree():
+    # 2500 query rows: the stack's 'F' layers take the fused route unless told not to
+    print("layer stack fused vs unfused FSF", flush=True)
+    w = synth.workload("C", T=2500, k=512, pattern="FSF")
+    layers = []
+    for l in range(3):
+        layers.append({k: (v.to(DEV) if v is not None else None) for k, v in synth.layer_inputs(w, l).items()})
+    a = dsa.layer_stack(w.pattern, layers, w.k, w.scale(), Dv=512)
+    b = dsa.layer_stack(w.pattern, layers, w.k, w.scale(), Dv=512, unfused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[2], b[2])
+    for x, y in zip(a[0], b[0]):
+        assert torch.equal(x, y)
+    s2 = dsa.index_scores(layers[2]["q_idx"], layers[2]["k_idx"], layers[2]["w_idx"])
+    assert np.array_equal(_host(a[2]).numpy(), oracle.topk(_host(s2).numpy(), w.k))
