@@ -13,8 +13,9 @@
 //               ~1.65 at k = 2048): the m-th largest sample, m = alpha*k*samples/n;
 // 3. filter:    each wave scores its rows against all their keys and appends every score at
 //               or above its row's threshold, with its key index, to the row's candidate
-//               list (through a small LDS ring, flushed in 32- or 64-entry blocks).  A wave
-//               owns whole rows, so a list needs no atomics and comes out in key order;
+//               list: one range-checked 8-byte store per score epilogue, dropped for lanes
+//               without a candidate.  A wave owns whole rows, so a list needs no atomics
+//               and comes out in key order;
 // 4. select:    per row, if the list holds at least k and at most kFusedCap entries it holds
 //               the whole top-k (every key at or above the k-th largest score passed the
 //               threshold test, which is monotone in the score); a radix select over the
@@ -230,23 +231,20 @@ __global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __res
                                                            uint2* __restrict__ list) {
   using W = FzWave<H_I, D_I>;
   constexpr int ROWS = W::ROWS;
-  constexpr int RING = ROWS <= 8 ? 128 : 64;  // ring entries per row (8 KB per wave)
-  constexpr int HALF = RING / 2;              // flush block; a tile adds <= 32 per row
-  static_assert(HALF >= 32 && ROWS * RING <= 1024, "ring size");
   __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
-  __shared__ uint2 rings[4][ROWS * RING];
   FzRows R;
   if (!fz_rows<ROWS>(kv_len, Tq, Tk, row0, nrows, nblocks, R)) return;
   if (R.p_last + 1 <= topk) return;  // every row keeps all its keys: nothing to select
   const int b = blockIdx.z, lane = threadIdx.x & 63;
   const int64_t rbase = (int64_t)b * nrows + R.wrow0;
-  uint2* const ring = rings[wave_id()];
   W wv;
   wv.load(q + ((int64_t)b * Tq + row0 + R.wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + R.wrow0) * H_I, R.wrows);
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
+  // the wave's lists (rows past the chunk would fall outside; they never pass anyway)
+  const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(list + rbase * FZ_CAP, (uint32_t)(R.wrows * FZ_CAP * 8));
   // the lane's rows: last causal key (-1 for rows past the chunk) and threshold
-  int lim[W::ROWS / W::QPT][W::QPL];
-  float th[W::ROWS / W::QPT][W::QPL];
+  int lim[ROWS / W::QPT][W::QPL];
+  float th[ROWS / W::QPT][W::QPL];
 #pragma unroll
   for (int t = 0; t < ROWS / W::QPT; ++t) {
 #pragma unroll
@@ -259,39 +257,32 @@ __global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __res
   uint32_t fill[ROWS];  // candidates of each row so far (wave-uniform)
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) fill[r] = 0;
-  // entries [start, start + HALF) of row r, all in the ring, go to the list
-  auto flush = [&](int r, uint32_t start) {
-    const uint32_t pos = start + lane;
-    if (lane < HALF && pos < (uint32_t)FZ_CAP) list[(rbase + r) * FZ_CAP + pos] = ring[r * RING + (pos & (RING - 1))];
-  };
-  auto account = [&](int r, uint32_t add) {
-    const uint32_t f0 = fill[r], f1 = f0 + add;
-    if ((f0 ^ f1) & ~(uint32_t)(HALF - 1)) flush(r, (f1 & ~(uint32_t)(HALF - 1)) - HALF);
-    fill[r] = f1;
-  };
   const int col = wv.col, g = wv.g;
+  const uint32_t lane_list = (uint32_t)(g * W::QPL * FZ_CAP) * 8u;  // list of row rA + g*QPL
   wv.run(k_rs, wks[wave_id()], (int)((R.p_last + 32) / 32), [](int j) { return 32 * j; },
          [&](int, int s0, int t, int qq, float tot) {
            const int skey = s0 + col;
            const bool c = skey <= lim[t][qq] && tot >= th[t][qq];
-           const uint64_t bal = __ballot(c);
+           const uint64_t bal = __ballot(skey <= lim[t][qq]) & __ballot(tot >= th[t][qq]);
            const uint32_t n0 = __popc((uint32_t)bal), n1 = __popc((uint32_t)(bal >> 32));
            const int rA = t * W::QPT + qq, rB = rA + W::QPL;  // the rows of lane groups 0 and 1
-           const uint32_t base = g ? fill[rB] - n0 : fill[rA];
-           if (c) ring[(g ? rB : rA) * RING + ((base + mbcnt64(bal)) & (RING - 1))] =
-               make_uint2(__float_as_uint(tot), (uint32_t)skey);
-           account(rA, n0);
-           account(rB, n1);
+           // slot in the lane's row: its row's count so far plus the row's passing lanes
+           // below it; entries past the capacity all land on the last slot (such a row
+           // fails its count check and is recomputed)
+           const uint32_t slot = min((g ? fill[rB] - n0 : fill[rA]) + mbcnt64(bal), (uint32_t)FZ_CAP - 1u);
+           uint32_t addr = lane_list + (uint32_t)(rA * FZ_CAP) * 8u + slot * 8u;
+           asm volatile("" : "+v"(addr));  // computed on every lane: the select stays a select
+           const uint32_t at = c ? addr : kOffNone;
+           typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+           __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(tot), (uint32_t)skey}, l_rs, (int)at, 0, 0);
+           fill[rA] += n0;
+           fill[rB] += n1;
          });
-  // the last partial block of each row, and its count (all candidates, also past the cap)
+  // each row's count: all candidates, also past the capacity
+  uint32_t mine = 0;
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    if (r >= R.wrows) break;
-    const uint32_t f = fill[r], start = f & ~(uint32_t)(HALF - 1);
-    const uint32_t pos = start + lane;
-    if (pos < f && pos < (uint32_t)FZ_CAP) list[(rbase + r) * FZ_CAP + pos] = ring[r * RING + (pos & (RING - 1))];
-    if (lane == 0) cnt[rbase + r] = f;
-  }
+  for (int r = 0; r < ROWS; ++r) mine = lane == r ? fill[r] : mine;
+  if (lane < R.wrows) cnt[rbase + lane] = mine;
 }
 
 __device__ __forceinline__ bool fz_row_failed(uint32_t c, int topk) { return c < (uint32_t)topk || c > (uint32_t)FZ_CAP; }

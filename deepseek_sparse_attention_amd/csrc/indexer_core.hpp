@@ -85,10 +85,17 @@ struct IdxWave {
     }
   }
 
+  template <class Start, class Epi>
+  __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi) {
+    run(k_rs, lds, ntiles, start, epi, [](int) {});
+  }
+
   // Scores the wave's rows against key tiles j = 0 .. ntiles-1 (ntiles >= 1); tile j holds
   // keys start(j) .. start(j)+31 (wave-uniform; keys past the range of k_rs read as zero).
   // epi(j, s0, t, qq, score) runs on every lane for each tile j (s0 = start(j)), query tile
   // t and lane query qq, in a fixed order; the lane's key is s0 + col, its row row_of(t, qq).
+  // post(j) runs after the last epilogue of tile j: work that branches belongs there, so
+  // the MFMAs of one query tile can overlap the epilogue of the previous one.
   //
   // Key tiles pass through the wave's private LDS buffer `lds` (kLdsBytes): global loads
   // read whole key rows (KPI keys of D_I*2 bytes per instruction) rather than 32 keys x 16
@@ -96,8 +103,9 @@ struct IdxWave {
   // k-step.  Only this wave touches the buffer and one wave's LDS operations complete in
   // order, so no barrier is needed.  Rows of the next two tiles are in flight in registers
   // and the next tile's operand is read while the current tile computes.
-  template <class Start, class Epi>
-  __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi) {
+  template <class Start, class Epi, class Post>
+  __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi,
+                                      Post post) {
     const int lane = threadIdx.x & 63;
     uint8_t* const wk0 = lds;
     uint8_t* const wk1 = lds + kTileBytes;
@@ -145,6 +153,7 @@ struct IdxWave {
           epi(j, s0, t, qq, tot);
         }
       }
+      post(j);
     };
     u32x4 G0[NLD], G1[NLD];
     bf16x8 B0[KS], B1[KS];
