@@ -36,9 +36,8 @@ namespace {
 constexpr int FZ_CAP = kFusedCap;      // candidate entries per row
 constexpr int FZ_NT = 256;
 constexpr int FZ_NW = FZ_NT / 64;
-constexpr int FZ_EPT = FZ_CAP / FZ_NT;  // list entries per thread in the select kernel
 constexpr int FZ_KEEP = FZ_CAP;         // rows of up to this many keys keep every key
-static_assert(FZ_CAP % FZ_NT == 0 && FZ_CAP % 64 == 0, "list blocks");
+static_assert(FZ_CAP % 64 == 0, "list rounds");
 
 // Threshold score of a key from the order-preserving map (keys from finite scores map back
 // to finite floats).
@@ -287,93 +286,142 @@ __global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __res
 
 __device__ __forceinline__ bool fz_row_failed(uint32_t c, int topk) { return c < (uint32_t)topk || c > (uint32_t)FZ_CAP; }
 
-// ---- 4. exact top-k of each row's candidate list
+// ---- 4. exact top-k of each row's candidate list: one wave per row (four rows per
+// workgroup, no barriers).  The wave keeps the list's keys in registers (entry e = 64*i +
+// lane in round i: coalesced loads, list order = (round, lane) order), narrows the bin of
+// the k-th largest key with LDS histogram passes until it holds at most 64 entries or one
+// key value, ranks such a bin's entries exactly, and writes the kept entries' key indices
+// in list order (= ascending key index).
+constexpr int FZ_EPL = FZ_CAP / 64;  // list entries per lane, at most
+
 __global__ __launch_bounds__(FZ_NT) void fz_select_kernel(const uint32_t* __restrict__ cnt,
                                                           const uint2* __restrict__ list,
                                                           const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0,
                                                           int nrows, int topk, int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[kSelBins];
-  __shared__ uint32_t red[2 * FZ_NW];
-  __shared__ uint32_t state[2];
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-  const int r = blockIdx.x, b = blockIdx.y;
+  __shared__ uint32_t hists[FZ_NW][kSelBins];
+  __shared__ uint32_t mems[FZ_NW][64];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int r = blockIdx.x * FZ_NW + wave, b = blockIdx.y;
+  if (r >= nrows) return;
   const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
   int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * topk;
   if (p + 1 <= topk) {  // every causal key (or none), then padding
-    for (int j = tid; j < topk; j += FZ_NT) out[j] = (j <= p) ? j : -1;
+    for (int j = lane; j < topk; j += 64) out[j] = (j <= p) ? j : -1;
     return;
   }
   const int64_t rowi = (int64_t)b * nrows + r;
   const uint32_t c = cnt[rowi];
   if (fz_row_failed(c, topk)) return;  // the exact pass redoes this row
-  // thread t holds list entries [t*EPT, t*EPT + EPT): list order is key order
-  uint32_t key[FZ_EPT], pos[FZ_EPT];
-  const uint2* lrow = list + rowi * FZ_CAP + tid * FZ_EPT;
+  const int nr = (int)((c + 63) / 64);
+  const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(list + rowi * FZ_CAP, c * 8u);
+  uint32_t key[FZ_EPL];
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  // (loads past the list fall outside the buffer range: they read zero and move no data;
+  // the round's base goes in the scalar offset)
 #pragma unroll
-  for (int i = 0; i < FZ_EPT; i += 2) {
-    const u32x4 v = ld16(lrow + i);
-    const bool v0 = (uint32_t)(tid * FZ_EPT + i) < c, v1 = (uint32_t)(tid * FZ_EPT + i + 1) < c;
-    key[i] = v0 ? sel_key(__uint_as_float(v[0])) : 0u;
-    pos[i] = v[1];
-    key[i + 1] = v1 ? sel_key(__uint_as_float(v[2])) : 0u;
-    pos[i + 1] = v[3];
-  }
+  for (int i0 = 0; i0 < FZ_EPL; i0 += 8) {
 #pragma unroll
-  for (int i = 0; i < FZ_EPT; ++i)
-    if (key[i]) {
-      mn = min(mn, key[i]);
+    for (int i = i0; i < i0 + 8; ++i) key[i] = 0u;  // 0: no entry (every real key is >= 1)
+    if (i0 >= nr) continue;
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) {
+      const uint32_t e = (uint32_t)(64 * i + lane);
+      const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(l_rs, lane * 8, 512 * i, 0));
+      key[i] = e < c ? sel_key(sc) : 0u;
+      mn = min(mn, e < c ? key[i] : 0xFFFFFFFFu);
       mx = max(mx, key[i]);
     }
-  fz_minmax(mn, mx, red);
-  // radix select of the k-th largest key K* over the list (exact: the last pass has one key
-  // per bin), and `need` = ties at K* to keep
-  uint32_t need = (uint32_t)topk, lo = mn, hi = mx;
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  uint32_t* const hist = hists[wave];
+  // radix passes narrow [lo, hi] to the bin holding the k-th largest key; `need` = entries
+  // of that bin to keep.  One wave's LDS operations complete in order.
+  uint32_t need = (uint32_t)topk, lo = mn, hi = mx, m;
   int sh = sel_shift(lo, hi);
   for (;;) {
-    for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
-    __syncthreads();
+    for (int j = lane; j < kSelBins; j += 64) hist[j] = 0;
+    // (rounds in groups of eight: entries past the list hold key 0 and never count; one
+    // guard per group keeps the per-round conditions from piling up in scalar registers)
 #pragma unroll
-    for (int i = 0; i < FZ_EPT; ++i)
-      if (key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> sh], 1u);
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t bin, above;
-      wave_find_bin_from_top(hist, need, bin, above);
-      if (lane == 0) {
-        state[0] = bin;
-        state[1] = above;
+    for (int i0 = 0; i0 < FZ_EPL; i0 += 8) {
+      if (i0 >= nr) continue;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i)
+        if (key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> sh], 1u);
+    }
+    uint32_t bin, above;
+    wave_find_bin_from_top(hist, need, bin, above);
+    m = __builtin_amdgcn_readfirstlane(hist[bin]);
+    need -= above;
+    lo += bin << sh;
+    hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
+    if (sh == 0 || m <= 64) break;
+    sh = sel_shift(lo, hi);
+  }
+  // a bin of m <= 64 entries over several key values: rank them exactly (score, then list
+  // position); keptm bit j = the j-th of them in list order is kept
+  uint64_t keptm = 0;
+  if (sh > 0) {
+    uint32_t* const mem = mems[wave];
+    uint32_t cm = 0;
+#pragma unroll
+    for (int i0 = 0; i0 < FZ_EPL; i0 += 8) {
+      if (i0 >= nr) continue;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) {
+        const bool inb = key[i] >= lo && key[i] <= hi;
+        const uint64_t bl = __ballot(inb);
+        if (inb) mem[cm + mbcnt64(bl)] = key[i];
+        cm += (uint32_t)__popcll(bl);
       }
     }
-    __syncthreads();
-    need -= state[1];
-    lo += state[0] << sh;
-    if (sh == 0) break;
-    hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
-    sh = sel_shift(lo, hi);
-    __syncthreads();  // state read by every thread before wave 0 rewrites it
+    const uint32_t mk = lane < (int)m ? mem[lane] : 0u;
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < m; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
+      rank += (kj > mk) || (kj == mk && (int)j < lane);
+    }
+    keptm = __ballot(lane < (int)m && rank < need);
   }
-  const uint32_t kstar = lo;
-  uint32_t na = 0, nt = 0;
+  // emission in list order, eight rounds at a time; the key indices of the next eight rounds
+  // are loaded while this one is written (issued before its stores, and the compiler
+  // barrier keeps later loads from moving further ahead).
+  // Slots stay below k by construction (k - need keys above the bin); the guard keeps a
+  // violated invariant inside the row.
+  uint32_t acc = 0, before = 0;
+  uint32_t kidx[2][8];
 #pragma unroll
-  for (int i = 0; i < FZ_EPT; ++i) {
-    na += key[i] > kstar;
-    nt += key[i] == kstar;
-  }
-  uint32_t tot;
-  const uint32_t pre = fz_excl_scan((na << 16) | nt, red, tot);  // both counts < 2^16
-  uint32_t A = pre >> 16, E = pre & 0xFFFFu;
+  for (int u = 0; u < 8; ++u) kidx[0][u] = __builtin_amdgcn_raw_buffer_load_b32(l_rs, lane * 8 + 4, 512 * u, 0);
 #pragma unroll
-  for (int i = 0; i < FZ_EPT; ++i) {
-    // slots stay below k by construction (k - need keys above K*); the guards keep a
-    // violated invariant inside the row
-    if (key[i] > kstar) {
-      const uint32_t slot = A + min(E, need);
-      if (slot < (uint32_t)topk) out[slot] = (int32_t)pos[i];
-      ++A;
-    } else if (key[i] == kstar) {
-      if (E < need && A + E < (uint32_t)topk) out[A + E] = (int32_t)pos[i];
-      ++E;
+  for (int i0 = 0; i0 < FZ_EPL; i0 += 8) {
+    const int cur = (i0 / 8) & 1;
+    if (i0 >= nr) continue;  // (uniform; a break would keep the loop from unrolling)
+    if (i0 + 8 < nr) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        kidx[cur ^ 1][u] = __builtin_amdgcn_raw_buffer_load_b32(l_rs, lane * 8 + 4, 512 * (i0 + 8 + u), 0);
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t k = key[i0 + u];  // 0 past the list: never kept
+      bool kp;
+      if (sh > 0) {
+        const bool inb = k >= lo && k <= hi;
+        const uint64_t bl = __ballot(inb);
+        kp = k > hi || (inb && ((keptm >> (before + mbcnt64(bl))) & 1u));
+        before += (uint32_t)__popcll(bl);
+      } else {  // one key value K* = lo: ties kept lowest position first
+        const bool tie = k == lo;
+        const uint64_t bl = __ballot(tie);
+        kp = k > lo || (tie && before + mbcnt64(bl) < need);
+        before += (uint32_t)__popcll(bl);
+      }
+      const uint64_t bk = __ballot(kp);
+      const uint32_t slot = acc + mbcnt64(bk);
+      acc += (uint32_t)__popcll(bk);
+      if (kp && slot < (uint32_t)topk) out[slot] = (int32_t)kidx[cur][u];
     }
   }
 }
@@ -487,8 +535,8 @@ hipError_t launch_fz(const IndexTopkArgs& A, const FusedLayout& Lw, hipStream_t 
                      A.nrows, A.k_top, alpha, thr);
   hipLaunchKernelGGL((fz_filter_kernel<H_I, D_I>), wgrid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
                      A.row0, A.nrows, nblocks, A.k_top, thr, cnt, list);
-  hipLaunchKernelGGL(fz_select_kernel, rgrid, dim3(FZ_NT), 0, st, cnt, list, A.kv_len, A.Tq, A.Tk, A.row0, A.nrows,
-                     A.k_top, A.idx);
+  hipLaunchKernelGGL(fz_select_kernel, dim3((A.nrows + FZ_NW - 1) / FZ_NW, A.B), dim3(FZ_NT), 0, st, cnt, list,
+                     A.kv_len, A.Tq, A.Tk, A.row0, A.nrows, A.k_top, A.idx);
   hipLaunchKernelGGL((fz_exact_kernel<H_I, D_I>), rgrid, dim3(FZ_NT), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
                      A.row0, A.nrows, A.k_top, cnt, A.idx);
   return hipGetLastError();
