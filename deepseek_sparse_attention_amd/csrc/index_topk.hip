@@ -147,76 +147,71 @@ __global__ __launch_bounds__(256, 2) void fz_sample_kernel(const uint16_t* __res
 }
 
 // ---- 2. per-row threshold: the m-th largest sample (to within a fine histogram bin below
-// it), m = alpha*k*samples/n; rows that keep every key get -inf
+// it), m = alpha*k*samples/n; rows that keep every key get -inf.  One wave per row (four
+// rows per workgroup, no barriers): the samples sit in registers (sample 64*i + lane in
+// round i), two passes over a per-wave LDS histogram.
+constexpr int FZ_SPL = 32 * kFusedMaxSampleTiles / 64;  // samples per lane, at most
+
 __global__ __launch_bounds__(FZ_NT) void fz_threshold_kernel(const uint32_t* __restrict__ smp, int smax,
                                                              const int32_t* __restrict__ ns,
                                                              const int32_t* __restrict__ kv_len, int Tq, int Tk,
                                                              int row0, int nrows, int topk, float alpha,
                                                              float* __restrict__ thr) {
-  __shared__ uint32_t hist[kSelBins];
-  __shared__ uint32_t red[2 * FZ_NW];
-  __shared__ uint32_t state[2];
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-  const int r = blockIdx.x, b = blockIdx.y;
+  __shared__ uint32_t hists[FZ_NW][kSelBins];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int r = blockIdx.x * FZ_NW + wave, b = blockIdx.y;
+  if (r >= nrows) return;
   const int64_t n = seq_len(kv_len, b, Tk) - Tq + row0 + r + 1;
   const int64_t rowi = (int64_t)b * nrows + r;
   if (n <= FZ_KEEP) {
-    if (tid == 0) thr[rowi] = -__builtin_inff();
+    if (lane == 0) thr[rowi] = -__builtin_inff();
     return;
   }
-  const int nsr = ns[rowi];  // <= 32 * kFusedMaxSampleTiles = 16 per thread
+  const int nsr = ns[rowi];  // a multiple of 32, at most 64 * FZ_SPL
   const uint32_t m = (uint32_t)fminf((float)nsr, fmaxf(1.f, ceilf(alpha * (float)topk * (float)nsr / (float)n)));
-  constexpr int PER = 32 * kFusedMaxSampleTiles / FZ_NT;
-  uint32_t key[PER];
+  const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(smp + rowi * smax, (uint32_t)nsr * 4u);
+  uint32_t key[FZ_SPL];
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  const uint32_t* srow = smp + rowi * smax;
+  const int nrd = (nsr + 63) / 64;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = tid + FZ_NT * i;
-    key[i] = e < nsr ? srow[e] : 0u;  // 0: no sample (every real key is >= 1)
-    if (key[i]) {
-      mn = min(mn, key[i]);
+  for (int i0 = 0; i0 < FZ_SPL; i0 += 8) {
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) key[i] = 0u;  // 0: no sample (every real key is >= 1)
+    if (i0 >= nrd) continue;
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) {
+      key[i] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, lane * 4, 256 * i, 0);  // past nsr: 0
+      mn = min(mn, key[i] ? key[i] : 0xFFFFFFFFu);
       mx = max(mx, key[i]);
     }
   }
-  for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
-  fz_minmax(mn, mx, red);  // (its barriers also order the clear)
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  uint32_t* const hist = hists[wave];
+  auto pass = [&](uint32_t lo, uint32_t hi, int sh, uint32_t need, uint32_t& bin, uint32_t& above) {
+    for (int j = lane; j < kSelBins; j += 64) hist[j] = 0;
+#pragma unroll
+    for (int i0 = 0; i0 < FZ_SPL; i0 += 8) {
+      if (i0 >= nrd) continue;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i)
+        if (key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> sh], 1u);
+    }
+    wave_find_bin_from_top(hist, need, bin, above);
+  };
   const int sh = sel_shift(mn, mx);
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (key[i]) atomicAdd(&hist[(key[i] - mn) >> sh], 1u);
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t bin, above;
-    wave_find_bin_from_top(hist, m, bin, above);
-    if (lane == 0) {
-      state[0] = bin;
-      state[1] = above;
-    }
-  }
-  __syncthreads();
-  const uint32_t blo = mn + (state[0] << sh);
-  const uint32_t bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)mx);
-  const uint32_t m2 = m - state[1];
-  uint32_t th = blo;
+  uint32_t bin, above;
+  pass(mn, mx, sh, m, bin, above);
+  uint32_t th = mn + (bin << sh);
   if (sh > 0) {  // refine inside the bin: a bin edge alone could pass many more keys
-    for (int i = tid; i < kSelBins; i += FZ_NT) hist[i] = 0;
-    __syncthreads();
-    const int sh2 = sel_shift(blo, bhi);
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (key[i] >= blo && key[i] <= bhi) atomicAdd(&hist[(key[i] - blo) >> sh2], 1u);
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t bin, above;
-      wave_find_bin_from_top(hist, m2, bin, above);
-      if (lane == 0) state[0] = blo + (bin << sh2);
-    }
-    __syncthreads();
-    th = state[0];
+    const uint32_t bhi = (uint32_t)min((uint64_t)th + ((1u << sh) - 1u), (uint64_t)mx);
+    const int sh2 = sel_shift(th, bhi);
+    uint32_t bin2, above2;
+    pass(th, bhi, sh2, m - above, bin2, above2);
+    th += bin2 << sh2;
   }
   // at least m samples have keys >= th, so the filter's count is near alpha*k
-  if (tid == 0) thr[rowi] = key_to_float(th);
+  if (lane == 0) thr[rowi] = key_to_float(th);
 }
 
 // ---- 3. scores of every causal key, filtered into per-row candidate lists
@@ -426,23 +421,14 @@ __global__ __launch_bounds__(FZ_NT) void fz_select_kernel(const uint32_t* __rest
   }
 }
 
-// ---- 5. rows whose list failed: exact top-k from recomputed scores
+// Exact top-k of row r (n > k keys) from recomputed scores, by the whole workgroup.
 template <int H_I, int D_I>
-__global__ __launch_bounds__(FZ_NT) void fz_exact_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ w,
-                                                         const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0,
-                                                         int nrows, int topk, const uint32_t* __restrict__ cnt,
-                                                         int32_t* __restrict__ idx) {
-  using W = IdxWave<H_I, D_I, 1>;  // one query tile: the row and its tile neighbours
-  __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
-  __shared__ uint32_t hist[kSelBins];
-  __shared__ uint32_t wc[2][FZ_NW];
-  __shared__ uint32_t state[2];
-  const int r = blockIdx.x, b = blockIdx.y;
-  const int64_t n = seq_len(kv_len, b, Tk) - Tq + row0 + r + 1;
-  if (n <= topk) return;
-  const int64_t rowi = (int64_t)b * nrows + r;
-  if (!fz_row_failed(cnt[rowi], topk)) return;
+__device__ __forceinline__ void fz_exact_row(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                             const uint16_t* __restrict__ w, int Tq, int Tk, int row0, int nrows,
+                                             int topk, int b, int r, int64_t n, int32_t* __restrict__ idx,
+                                             uint8_t (*wks)[IdxWave<H_I, D_I, 1>::kLdsBytes], uint32_t* hist,
+                                             uint32_t (*wc)[FZ_NW], uint32_t* state) {
+  using W = IdxWave<H_I, D_I, 1>;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int t0 = r - r % W::QPT;  // first chunk row of the query tile holding row r
   const int gsel = (r - t0) / W::QPL, qsel = (r - t0) % W::QPL;
@@ -515,6 +501,30 @@ __global__ __launch_bounds__(FZ_NT) void fz_exact_kernel(const uint16_t* __restr
     A += __popcll(ba);
     E += __popcll(bt);
   });
+  __syncthreads();  // the workgroup may take another row with the same LDS
+}
+
+// ---- 5. rows whose list failed: exact top-k from recomputed scores
+template <int H_I, int D_I>
+__global__ __launch_bounds__(FZ_NT) void fz_exact_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ w,
+                                                         const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0,
+                                                         int nrows, int topk, const uint32_t* __restrict__ cnt,
+                                                         int32_t* __restrict__ idx) {
+  using W = IdxWave<H_I, D_I, 1>;  // one query tile: the row and its tile neighbours
+  __shared__ __attribute__((aligned(16))) uint8_t wks[FZ_NW][W::kLdsBytes];
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t wc[2][FZ_NW];
+  __shared__ uint32_t state[2];
+  // each workgroup checks four rows and recomputes those whose list failed (rare)
+  const int b = blockIdx.y;
+  for (int rr = 0; rr < FZ_NW; ++rr) {
+    const int r = blockIdx.x * FZ_NW + rr;
+    if (r >= nrows) return;
+    const int64_t n = seq_len(kv_len, b, Tk) - Tq + row0 + r + 1;
+    if (n > topk && fz_row_failed(cnt[(int64_t)b * nrows + r], topk))
+      fz_exact_row<H_I, D_I>(q, k, w, Tq, Tk, row0, nrows, topk, b, r, n, idx, wks, hist, wc, state);
+  }
 }
 
 template <int H_I, int D_I>
@@ -528,16 +538,17 @@ hipError_t launch_fz(const IndexTopkArgs& A, const FusedLayout& Lw, hipStream_t 
   float* thr = reinterpret_cast<float*>(ws + Lw.thr);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + Lw.cnt);
   uint2* list = reinterpret_cast<uint2*>(ws + Lw.list);
-  const dim3 wgrid(nblocks, 1, A.B), rgrid(A.nrows, A.B);
+  const dim3 wgrid(nblocks, 1, A.B);
   hipLaunchKernelGGL((fz_sample_kernel<H_I, D_I>), wgrid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
                      A.row0, A.nrows, nblocks, smp, Lw.smax, ns);
-  hipLaunchKernelGGL(fz_threshold_kernel, rgrid, dim3(FZ_NT), 0, st, smp, Lw.smax, ns, A.kv_len, A.Tq, A.Tk, A.row0,
+  hipLaunchKernelGGL(fz_threshold_kernel, dim3((A.nrows + FZ_NW - 1) / FZ_NW, A.B), dim3(FZ_NT), 0, st, smp, Lw.smax,
+                     ns, A.kv_len, A.Tq, A.Tk, A.row0,
                      A.nrows, A.k_top, alpha, thr);
   hipLaunchKernelGGL((fz_filter_kernel<H_I, D_I>), wgrid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
                      A.row0, A.nrows, nblocks, A.k_top, thr, cnt, list);
   hipLaunchKernelGGL(fz_select_kernel, dim3((A.nrows + FZ_NW - 1) / FZ_NW, A.B), dim3(FZ_NT), 0, st, cnt, list,
                      A.kv_len, A.Tq, A.Tk, A.row0, A.nrows, A.k_top, A.idx);
-  hipLaunchKernelGGL((fz_exact_kernel<H_I, D_I>), rgrid, dim3(FZ_NT), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
+  hipLaunchKernelGGL((fz_exact_kernel<H_I, D_I>), dim3((A.nrows + FZ_NW - 1) / FZ_NW, A.B), dim3(FZ_NT), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, A.Tk,
                      A.row0, A.nrows, A.k_top, cnt, A.idx);
   return hipGetLastError();
 }
