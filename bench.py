@@ -94,8 +94,10 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_D -o trace -- "
         "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
         "#   python3 bench.py --summarize-stats gpurun_out/trace_D/trace_kernel_stats.csv",
-        "# calls: 1 warmup + 3 timed layer_stack steps + 3 event-timed launches of each kernel group",
-        "# (the indexer and top-k run once per query chunk), then the decode steps.",
+        "# calls: 1 warmup + 3 timed layer_stack steps (fused index/top-k: fz_sample, fz_threshold,",
+        "# fz_filter, fz_select, fz_exact once each, then attention), 3 event-timed launches of each",
+        "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
+        "# unfused step), then the decode steps.",
         "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel",
         "",
     ]
@@ -303,6 +305,14 @@ def main():
 
     indexer_ms = timed(indexer_all)
     topk_ms = timed(topk_all)  # (on the last chunk's scores: same row lengths per chunk)
+    # the fused route the step takes (dsa_index_topk over all rows: sample, threshold, filter,
+    # select, exact recompute of failed rows), and the step over score chunks for comparison
+    fz_ws = torch.empty(max(1, dsa.workspace_size(shp, dsa.OP_INDEX_TOPK)), dtype=torch.uint8, device=dev)
+    fused_ms = timed(lambda: dsa.index_topk(layer["q_idx"], layer["k_idx"], layer["w_idx"], k, idx=idx_cache,
+                                            ws=fz_ws))
+    del fz_ws
+    unfused_step_ms = timed(lambda: dsa.layer_stack("F", [layer], k, w.scale(), Dv=w.Dv, index_cache=idx_cache,
+                                                    ws=ws, unfused=True))
 
     # ---- roofline of the dominant kernel (sparse MLA attention)
     sel = k * T - k * (k - 1) // 2 if T >= k else T * (T + 1) // 2
@@ -317,6 +327,9 @@ def main():
     kernels = {
         "indexer": {"ms": round(indexer_ms, 3), "tflops": round(idx_flops / (indexer_ms * 1e-3) / 1e12, 1),
                     "frac_mfma_bf16": round(idx_flops / (indexer_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "index_topk_fused": {"ms": round(fused_ms, 3),
+                             "tflops": round(idx_flops / (fused_ms * 1e-3) / 1e12, 1)},
+        "step_unfused": {"ms": round(unfused_step_ms, 3)},
         "topk": {"ms": round(topk_ms, 3),
                  "gbs": round((pairs * 4 + T * k * 4) / (topk_ms * 1e-3) / 1e9, 1)},
         "sparse_attn": {"ms": round(attn_ms, 3), "gbs_logical": round(achieved, 1)},

@@ -45,7 +45,8 @@ int chunk_rows(const dsa_shape& s) {
 // Route of dsa_index_topk: the fused kernels over chunks of `rows` query rows (candidate
 // lists instead of score rows), or the score kernel + top-k over score chunks.  The fused
 // kernels give every wave whole rows, so a launch needs many rows to balance (rows of all
-// lengths at once): the whole Tq in one chunk up to kFusedBytes of workspace.
+// lengths at once): the whole Tq in one chunk up to kFusedBytes of workspace.  The fused
+// route runs where it pays: many rows, and keys beyond the keep-everything length.
 constexpr size_t kFusedBytes = size_t(8) << 30;
 constexpr int64_t kFusedMinRows = 1024;
 
@@ -57,8 +58,10 @@ struct IndexTopkPlan {
 
 IndexTopkPlan plan_index_topk(const dsa_shape& s, bool force_unfused) {
   IndexTopkPlan P;
+  // (up to kFusedCap keys every row keeps all its keys, and score rows are the cheaper
+  // hand-over: measured even at 6144 keys, 20-30% in favour of fusion from 12288 on)
   P.fused = !force_unfused && dsa::index_topk_fused_supported(s.H_I, s.d_I, s.k) &&
-            (int64_t)std::max(0, s.B) * std::max(0, s.Tq) >= kFusedMinRows;
+            (int64_t)std::max(0, s.B) * std::max(0, s.Tq) >= kFusedMinRows && s.Tk > dsa::kFusedCap;
   if (P.fused) {
     const size_t per_row = std::max<size_t>(1, dsa::fused_layout(s.B, 1, s.Tk).bytes);
     int64_t rows = std::max<int64_t>(1, (int64_t)(kFusedBytes / per_row));

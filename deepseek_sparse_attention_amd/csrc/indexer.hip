@@ -62,9 +62,12 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   const int64_t maxkeys = std::min<int64_t>(A.Tk, (int64_t)A.Tk - A.Tq + A.row0 + A.nrows);
   if (qblocks == 0 || maxkeys <= 0) return hipSuccess;
   const int64_t tiles = (maxkeys + 31) / 32;
-  // Aim at ~2048 workgroups per launch: twice what the chip holds at once, with segments
-  // short enough that the causal tail of a launch stays small.
-  int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, 2048 / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
+  // Aim at ~2048 workgroups per launch when query blocks are full (prefill chunks): twice
+  // what the chip holds at once, with segments short enough that the causal tail of a launch
+  // stays small.  Few-row launches (decode: one busy wave per workgroup) keep ~1024, which
+  // streams the key cache faster there.
+  const int64_t target = A.nrows >= 8 * QB ? 2048 : 1024;
+  int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, target / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
   int64_t seg_tiles = (tiles + segs - 1) / segs;
   segs = (tiles + seg_tiles - 1) / seg_tiles;
   dim3 grid(qblocks, (unsigned)segs, A.B);

@@ -129,7 +129,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int 
  *               (about 64 KB per query row at Tk = 65536), or, where the fused path does not
  *               apply, one chunk of score rows.
  * Supported: the shapes of dsa_index_scores with 1 <= k <= 4096.  The fused path runs for
- * H_I in {8, 16} with at least 1024 query rows in all (B*Tq); other shapes run the two steps
+ * H_I in {8, 16} with at least 1024 query rows in all (B*Tq) and Tk > 6144 (shorter rows keep
+ * every key, and score rows are then the cheaper hand-over); other shapes run the two steps
  * over chunks of score rows in the workspace.
  */
 dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_idx,

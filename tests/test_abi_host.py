@@ -182,6 +182,9 @@ def test_index_topk_workspace_follows_the_route(L):
     # few rows (decode) or 2 indexer heads: score chunks (at most 1 GiB here)
     assert size(64, 1, 65536, 16, 2048, dsa.OP_INDEX_TOPK) == 64 * 65536 * 4
     assert size(1, 3072, 3072, 2, 512, dsa.OP_INDEX_TOPK) == 3072 * 3072 * 4
+    # up to 6144 keys (every row keeps all its keys): score rows too
+    assert size(1, 6144, 6144, 16, 2048, dsa.OP_INDEX_TOPK) == 6144 * 6144 * 4
+    assert size(1, 6200, 6200, 16, 2048, dsa.OP_INDEX_TOPK) >= 6200 * 6144 * 8
     # the stack holds either route plus attention
     st = size(1, 65536, 65536, 16, 2048, dsa.OP_STACK)
     assert st >= fused and st >= 4096 * 65536 * 4

@@ -48,8 +48,8 @@ def _check(d, k, kv_len=None, oversample=0.0):
 @pytest.mark.parametrize("key,T,k,H_I,d_I", [
     ("D", 7000, 2048, 16, 64),   # rows < k, rows kept whole (<= 6144 keys), sampled rows
     ("B", 8192, 1024, 16, 128),  # the widest indexer keys
-    ("B", 4000, 512, 8, 64),     # 8 indexer heads: 16 rows per wave
-    ("B", 1100, 64, 16, 32),     # small k: oversample capped at 4
+    ("B", 7000, 512, 8, 64),     # 8 indexer heads: 16 rows per wave
+    ("B", 6500, 64, 16, 32),     # small k: oversample capped at 4
 ])
 def test_index_topk_matches_scores_then_topk(key, T, k, H_I, d_I):
     print(f"index_topk workload {key} T={T} k={k} H_I={H_I} d_I={d_I}", flush=True)
@@ -60,9 +60,21 @@ def test_index_topk_matches_scores_then_topk(key, T, k, H_I, d_I):
 def test_index_topk_batch_with_ragged_kv_len():
     # two sequences; the second's rows start before position 0 (p < 0: all padding)
     print("index_topk B=2 ragged kv_len", flush=True)
-    w = synth.workload("B", B=2, T=3000, k=512)
-    got = _check(synth.layer_inputs(w, indexer=True), 512, kv_len=[3000, 1200])
-    assert np.all(got[1, :1800] == -1)
+    w = synth.workload("B", B=2, T=7000, k=512)
+    got = _check(synth.layer_inputs(w, indexer=True), 512, kv_len=[7000, 1200])
+    assert np.all(got[1, :5800] == -1)
+
+
+def test_index_topk_short_keys_take_the_score_route():
+    # up to 6144 keys every row keeps all its keys: the call runs the score kernel + top-k
+    print("index_topk short rows", flush=True)
+    w = synth.workload("B", T=3000, k=512)
+    d = synth.layer_inputs(w, indexer=True)
+    assert not _fused_route(1, 3000, 3000, 16, 64, 512)
+    q, kk, wi = (d[x].to(DEV) for x in ("q_idx", "k_idx", "w_idx"))
+    got = _host(dsa.index_topk(q, kk, wi, 512)).numpy()
+    ref = oracle.topk(_host(dsa.index_scores(q, kk, wi)).numpy(), 512)
+    assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("oversample", [0.05, 40.0])
@@ -83,9 +95,9 @@ def test_index_topk_integer_scores_with_massive_ties():
 
 
 def test_layer_stack_fused_and_unfused_agree():
-    # 2500 query rows: the stack's 'F' layers take the fused route unless told not to
+    # 6600 query rows: the stack's 'F' layers take the fused route unless told not to
     print("layer stack fused vs unfused FSF", flush=True)
-    w = synth.workload("C", T=2500, k=512, pattern="FSF")
+    w = synth.workload("C", T=6600, k=512, pattern="FSF")
     layers = []
     for l in range(3):
         layers.append({k: (v.to(DEV) if v is not None else None) for k, v in synth.layer_inputs(w, l).items()})
