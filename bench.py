@@ -391,7 +391,47 @@ def main():
                             "ms_per_step": round(ddt * 1e3, 4), "steps": dsteps, "pattern": e.pattern,
                             "algorithmic_bytes": dbytes, "gbs": round(dbytes / ddt / 1e9, 1)}
         log(f"decode: {ddt * 1e3:.3f} ms/step, {e.B / ddt:.0f} tok/s")
-        del kc, dl
+
+        # the same step over paged caches: the same rows in shuffled 64-token pages of shared
+        # pools (one block table for every layer); must give the dense step's results
+        page = 64
+        nblk = e.T // page
+        g = torch.Generator().manual_seed(4242)
+        table = torch.randperm(e.B * nblk, generator=g).to(torch.int32).view(e.B, nblk).to(dev)
+
+        def paged(dense):  # dense [B, T, ...] -> pool [B*T, ...] laid out by the table
+            pool = torch.empty((e.B * nblk, page) + tuple(dense.shape[2:]), dtype=dense.dtype, device=dev)
+            pool[table.flatten().long()] = dense.reshape((e.B * nblk, page) + tuple(dense.shape[2:]))
+            return pool.reshape((e.B * nblk * page,) + tuple(dense.shape[2:]))
+
+        pg = dsa.paged_kv(table, page, e.B * nblk)
+        pl = []
+        for L in dl:
+            P = {"q": L["q"], "kv": paged(L["kv"][:, :, 0]), "kv_scale": paged(L["kv_scale"]),
+                 "out": torch.empty_like(L["out"]), "lse": torch.empty_like(L["lse"])}
+            if "q_idx" in L:
+                P.update(q_idx=L["q_idx"], w_idx=L["w_idx"], k_idx=paged(kc))
+            pl.append(P)
+        pcache = torch.empty_like(dcache)
+        pws = torch.empty(max(1, dsa.workspace_size(dshp, dsa.OP_STACK_PAGED)), dtype=torch.uint8, device=dev)
+
+        def pstep():
+            dsa.layer_stack(e.pattern, pl, e.k, e.scale(), Dv=e.Dv, kv_len=klen, index_cache=pcache, ws=pws,
+                            pages=pg, Tk=e.T, H_I=e.H_I, d_I=e.d_I)
+
+        for _ in range(max(1, args.warmup)):
+            pstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(dsteps):
+            pstep()
+        torch.cuda.synchronize()
+        pdt = (time.perf_counter() - t0) / dsteps
+        same = bool(torch.equal(pcache, dcache) and all(torch.equal(a["out"], b["out"]) for a, b in zip(pl, dl)))
+        result["decode"]["paged"] = {"page_size": page, "ms_per_step": round(pdt * 1e3, 4),
+                                     "value": round(e.B / pdt, 1), "matches_dense": same}
+        log(f"decode, paged caches: {pdt * 1e3:.3f} ms/step, {e.B / pdt:.0f} tok/s, matches dense: {same}")
+        del kc, dl, pl, pws
 
     # ---- CPU oracle on a bounded, evenly spread sample of the same prefill rows
     if not args.no_cpu_baseline:

@@ -15,6 +15,7 @@ import torch
 
 __all__ = [
     "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "layer_stack",
+    "index_scores_paged", "sparse_attn_paged", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
     "KV_BF16", "KV_FP8_E4M3", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
     "OP_STACK", "OP_INDEX_TOPK",
@@ -24,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 KV_BF16, KV_FP8_E4M3 = 0, 1
-OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK, OP_INDEX_TOPK = 0, 1, 2, 3, 4
+OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK, OP_INDEX_TOPK, OP_ATTN_PAGED, OP_STACK_PAGED = 0, 1, 2, 3, 4, 5, 6
 CACHE_PREFILLED, STACK_UNFUSED = 1, 2
 _STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_PATTERN",
            "DSA_ERR_WORKSPACE", "DSA_ERR_LAUNCH", "DSA_ERR_DEVICE"]
@@ -51,6 +52,22 @@ class LayerIO(ctypes.Structure):
                 ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
+class PagedKV(ctypes.Structure):
+    """dsa_paged_kv: token s of sequence b is pool row block_table[b][s // page_size] * page_size
+    + s % page_size."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int), ("page_size", ctypes.c_int),
+                ("num_pages", ctypes.c_int)]
+
+
+def paged_kv(block_table, page_size, num_pages):
+    """A PagedKV over a device int32 [B, max_blocks] block table.  The descriptor holds a
+    reference to the table tensor, so its memory stays allocated while the descriptor lives
+    (a raw pointer alone would let torch's allocator hand the memory to the next tensor)."""
+    pg = PagedKV(_ptr(block_table), block_table.shape[1], page_size, num_pages)
+    pg._table = block_table
+    return pg
+
+
 _lib = None
 
 
@@ -70,6 +87,11 @@ def lib():
         L.dsa_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P, I64, P]
         L.dsa_topk.argtypes = [P, I64, P, I, I, I, I, P, P, SZ, P]
         L.dsa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, P, SZ, P]
+        L.dsa_index_scores_paged.argtypes = [P, P, P, ctypes.POINTER(PagedKV), P, I, I, I, I, I, P, I64, P]
+        L.dsa_sparse_attn_paged.argtypes = [P, P, P, I, ctypes.POINTER(PagedKV), P, P, I, I, I, I, I, I, I, F, P, P,
+                                            P, SZ, P]
+        L.dsa_layer_stack_paged.argtypes = [ctypes.c_char_p, I, P, ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), P,
+                                            U, P, SZ, P]
         L.dsa_sparse_attn.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, F, P, P, P, SZ, P]
         L.dsa_layer_stack.argtypes = [ctypes.c_char_p, I, P, ctypes.POINTER(Shape), P, U, P, SZ, P]
         L.dsa_workspace_size.argtypes = [ctypes.POINTER(Shape), I]
@@ -78,8 +100,9 @@ def lib():
         L.dsa_stack_chunk_rows.restype = I
         L.dsa_check_pattern.argtypes = [ctypes.c_char_p, I, U]
         L.dsa_pattern_from_freq.argtypes = [I, I, ctypes.c_char_p]
-        for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_layer_stack", "dsa_check_pattern",
-                  "dsa_pattern_from_freq"):
+        for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_layer_stack",
+                  "dsa_check_pattern", "dsa_pattern_from_freq", "dsa_index_scores_paged", "dsa_sparse_attn_paged",
+                  "dsa_layer_stack_paged"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -140,6 +163,37 @@ def index_topk(q_idx, k_idx, w_idx, k, kv_len=None, oversample=0.0, idx=None, ws
     return idx
 
 
+def index_scores_paged(q_idx, k_pool, w_idx, pages, Tk, kv_len=None, scores=None, ld=None, stream=None):
+    """dsa_index_scores_paged: k_pool bf16 [num_pages * page_size, d_I]; pages a PagedKV."""
+    B, Tq, H_I, d_I = q_idx.shape
+    ld = Tk if ld is None else ld
+    if scores is None:
+        scores = torch.full((B, Tq, ld), float("-inf"), dtype=torch.float32, device=q_idx.device)
+    _check(lib().dsa_index_scores_paged(_ptr(q_idx), _ptr(k_pool), _ptr(w_idx), ctypes.byref(pages), _ptr(kv_len),
+                                        B, Tq, Tk, H_I, d_I, _ptr(scores), ld, _stream(stream)))
+    return scores
+
+
+def sparse_attn_paged(q, kv_pool, idx, sm_scale, pages, Tk, kv_len=None, kv_scale_pool=None, Dv=512, out=None,
+                      lse=None, want_lse=True, ws=None, stream=None):
+    """dsa_sparse_attn_paged (MLA form): kv_pool [num_pages * page_size, 576] bf16 or uint8 (e4m3)."""
+    B, Tq, H, Dqk = q.shape
+    fp8 = kv_pool.dtype == torch.uint8
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, Tq, H, Dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
+    kvd = KV_FP8_E4M3 if fp8 else KV_BF16
+    shp = _shape(B, Tq, Tk, H, 1, Dqk, Dv, k, sm_scale, kvd)
+    nbytes = workspace_size(shp, OP_ATTN_PAGED)
+    ws = _workspace(nbytes, q.device, ws)
+    _check(lib().dsa_sparse_attn_paged(_ptr(q), _ptr(kv_pool), _ptr(kv_scale_pool), kvd, ctypes.byref(pages), _ptr(idx),
+                                       _ptr(kv_len), B, Tq, Tk, H, Dqk, Dv, k, sm_scale, _ptr(out), _ptr(lse),
+                                       _ptr(ws), nbytes, _stream(stream)))
+    return out, lse
+
+
 def _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, H_I=16, d_I=64, kv_len=None):
     return Shape(B, Tq, Tk, H_I, d_I, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, _ptr(kv_len))
 
@@ -185,16 +239,20 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, 
 
 
 def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=None, prefilled=False,
-                H_I=None, d_I=None, ws=None, want_lse=True, unfused=False, stream=None):
+                H_I=None, d_I=None, ws=None, want_lse=True, unfused=False, pages=None, Tk=None, stream=None):
     """dsa_layer_stack over `layers` (dicts with q/kv[/v/kv_scale] and, on F layers, q_idx/k_idx/w_idx).
 
     Returns (outs, lses, index_cache).  Output tensors are allocated unless a layer dict
     carries "out"/"lse".  unfused: 'F' layers take the score-chunk route (STACK_UNFUSED).
+    pages (a PagedKV) with Tk: k_idx, kv and kv_scale are pools (dsa_layer_stack_paged).
     """
     n = len(layers)
     L0 = layers[0]
     B, Tq, H, Dqk = L0["q"].shape
-    Tk, Hkv = L0["kv"].shape[1], L0["kv"].shape[2]
+    if pages is None:
+        Tk, Hkv = L0["kv"].shape[1], L0["kv"].shape[2]
+    else:
+        Hkv = 1
     fp8 = L0["kv"].dtype == torch.uint8
     if L0.get("v") is not None:
         Dv = L0["v"].shape[3]
@@ -222,11 +280,15 @@ def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=
         lses.append(ls)
         ios[i] = LayerIO(_ptr(L.get("q_idx")), _ptr(L.get("k_idx")), _ptr(L.get("w_idx")), _ptr(L["q"]),
                          _ptr(L["kv"]), _ptr(L.get("kv_scale")), _ptr(L.get("v")), _ptr(o), _ptr(ls))
-    nbytes = workspace_size(shp, OP_STACK)
+    nbytes = workspace_size(shp, OP_STACK if pages is None else OP_STACK_PAGED)
     ws = _workspace(nbytes, dev, ws)
-    _check(lib().dsa_layer_stack(pattern.encode(), n, ios, ctypes.byref(shp), _ptr(index_cache),
-                                 (CACHE_PREFILLED if prefilled else 0) | (STACK_UNFUSED if unfused else 0),
-                                 _ptr(ws), nbytes, _stream(stream)))
+    flags = (CACHE_PREFILLED if prefilled else 0) | (STACK_UNFUSED if unfused else 0)
+    if pages is None:
+        _check(lib().dsa_layer_stack(pattern.encode(), n, ios, ctypes.byref(shp), _ptr(index_cache), flags,
+                                     _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check(lib().dsa_layer_stack_paged(pattern.encode(), n, ios, ctypes.byref(shp), ctypes.byref(pages),
+                                           _ptr(index_cache), flags, _ptr(ws), nbytes, _stream(stream)))
     return outs, lses, index_cache
 
 

@@ -78,7 +78,7 @@ IndexTopkPlan plan_index_topk(const dsa_shape& s, bool force_unfused) {
 // Indices of rows [0, Tq) of every sequence by the planned route.
 dsa_status run_index_topk(const IndexTopkPlan& P, const void* q_idx, const void* k_idx, const void* w_idx,
                           const dsa_shape& s, float oversample, int32_t* idx, void* ws, hipStream_t strm,
-                          const char* who) {
+                          const char* who, const dsa_paged_kv* pages = nullptr) {
   for (int r0 = 0; r0 < s.Tq; r0 += P.rows) {
     const int n = std::min(P.rows, s.Tq - r0);
     if (P.fused) {
@@ -92,6 +92,12 @@ dsa_status run_index_topk(const IndexTopkPlan& P, const void* q_idx, const void*
       if (s.Tk > 0) {
         dsa::IndexerArgs ia{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, s.kv_len,
                             s.B, s.Tq, s.Tk, s.H_I, s.d_I, r0, n, scores, ld, (int64_t)P.rows * ld};
+        if (pages) {  // k_idx is a key pool (the fused route is never planned for pools)
+          ia.block_table = pages->block_table;
+          ia.max_blocks = pages->max_blocks;
+          ia.page_shift = __builtin_ctz((unsigned)pages->page_size);
+          ia.pool_tokens = (int64_t)pages->num_pages * pages->page_size;
+        }
         dsa_status st = launch_status(dsa::launch_index_scores(ia, strm), who);
         if (st != DSA_OK) return st;
       }
@@ -184,6 +190,30 @@ dsa::AttnArgs attn_args(const void* q, const void* kv, const float* kv_scale, co
 
 bool valid_kv_dtype(dsa_kv_dtype d) { return d == DSA_KV_BF16 || d == DSA_KV_FP8_E4M3; }
 
+// A paged layout for sequences of up to Tk keys over pools of row_bytes-wide rows.
+dsa_status check_pages(const dsa_paged_kv* pg, int Tk, int64_t row_bytes, int64_t max_rows, const char* pool) {
+  if (!pg || !pg->block_table) return fail(DSA_ERR_NULL, "pages and its block_table are required");
+  if (pg->page_size < 32 || pg->page_size > 65536 || (pg->page_size & (pg->page_size - 1)))
+    return fail(DSA_ERR_UNSUPPORTED, "page_size must be a power of two in [32, 65536]");
+  if (pg->max_blocks < 1 || pg->num_pages < 1) return fail(DSA_ERR_SHAPE, "max_blocks and num_pages must be >= 1");
+  if ((int64_t)pg->max_blocks * pg->page_size < Tk)
+    return fail(DSA_ERR_SHAPE, "max_blocks * page_size must cover Tk");
+  const int64_t rows = (int64_t)pg->num_pages * pg->page_size;
+  if (rows > max_rows || rows * row_bytes >= (int64_t(1) << 32))
+    return fail(DSA_ERR_UNSUPPORTED, std::string(pool) + " pool too large for the kernels' 32-bit row offsets");
+  if (!aligned(pg->block_table, 4)) return fail(DSA_ERR_UNSUPPORTED, "block_table must be 4-byte aligned");
+  return DSA_OK;
+}
+
+int page_shift(int page_size) { return __builtin_ctz((unsigned)page_size); }
+int64_t pool_rows(const dsa_paged_kv& pg) { return (int64_t)pg.num_pages * pg.page_size; }
+
+// Pool rows of the attention gather: the kernel scales row indices with a 24-bit multiply.
+constexpr int64_t kMaxAttnPoolRows = int64_t(1) << 24;
+int64_t latent_row_bytes(dsa_kv_dtype d) { return d == DSA_KV_FP8_E4M3 ? 576 : 1152; }
+
+size_t paged_idx_bytes(const dsa_shape& s) { return align_up((size_t)std::max(0, s.B) * std::max(0, s.Tq) * s.k * 4); }
+
 }  // namespace
 
 extern "C" {
@@ -251,6 +281,59 @@ dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_id
   return run_index_topk(P, q_idx, k_idx, w_idx, s, oversample, idx, ws, as_stream(stream), "dsa_index_topk");
 }
 
+dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w_idx, const dsa_paged_kv* pages,
+                                  const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I, float* scores,
+                                  int64_t ld, void* stream) {
+  dsa_status st = check_indexer(q_idx, k_pool, w_idx, B, Tq, Tk, H_I, d_I, scores, ld);
+  if (st != DSA_OK) return st;
+  st = check_pages(pages, Tk, (int64_t)d_I * 2, INT64_MAX, "key");
+  if (st != DSA_OK || (int64_t)B * Tq == 0 || Tk == 0) return st;
+  dsa::IndexerArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_pool, (const uint16_t*)w_idx, kv_len, B, Tq, Tk,
+                     H_I, d_I, 0, Tq, scores, ld, (int64_t)Tq * ld};
+  a.block_table = pages->block_table;
+  a.max_blocks = pages->max_blocks;
+  a.page_shift = page_shift(pages->page_size);
+  a.pool_tokens = pool_rows(*pages);
+  return launch_status(dsa::launch_index_scores(a, as_stream(stream)), "dsa_index_scores_paged");
+}
+
+dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float* kv_scale_pool, dsa_kv_dtype kv_dtype,
+                                 const dsa_paged_kv* pages, const int32_t* idx, const int32_t* kv_len, int B, int Tq,
+                                 int Tk, int H, int Dqk, int Dv, int k, float sm_scale, void* out, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!valid_kv_dtype(kv_dtype)) return fail(DSA_ERR_SHAPE, "unknown kv dtype");
+  dsa::AttnArgs a = attn_args(q, kv_pool, kv_scale_pool, nullptr, kv_dtype, idx, B, Tq, Tk, H, 1, Dqk, Dv, k, sm_scale,
+                              out, lse, ws);
+  dsa_status st = check_attn(a, (size_t)-1);
+  if (st != DSA_OK) return st;
+  if (!dsa::attn_mla_supported(a)) return fail(DSA_ERR_UNSUPPORTED, "paged attention supports the MLA form only");
+  st = check_pages(pages, Tk, latent_row_bytes(kv_dtype), kMaxAttnPoolRows, "latent");
+  if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
+  dsa_shape s{};
+  s.B = B;
+  s.Tq = Tq;
+  s.Tk = Tk;
+  s.H = H;
+  s.Hkv = 1;
+  s.Dqk = Dqk;
+  s.Dv = Dv;
+  s.k = k;
+  const size_t need = dsa_workspace_size(&s, DSA_OP_ATTN_PAGED);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "paged attention workspace too small: need " + std::to_string(need) + " bytes");
+  hipStream_t strm = as_stream(stream);
+  int32_t* phys = reinterpret_cast<int32_t*>(ws);
+  st = launch_status(dsa::launch_page_translate(idx, phys, B, Tq, k, kv_len, Tk, pages->block_table, pages->max_blocks,
+                                                page_shift(pages->page_size), pool_rows(*pages), strm),
+                     "dsa_sparse_attn_paged: translate");
+  if (st != DSA_OK) return st;
+  a.idx = phys;
+  a.Tk = (int)pool_rows(*pages);
+  a.kv_bstride = 0;
+  a.ws = reinterpret_cast<char*>(ws) + paged_idx_bytes(s);
+  return launch_status(dsa::launch_sparse_attn(a, strm), "dsa_sparse_attn_paged");
+}
+
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
                            dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv, int Dqk,
                            int Dv, int k, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
@@ -293,6 +376,10 @@ size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
     case DSA_OP_TOPK: return 0;
     case DSA_OP_ATTN: return dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
     case DSA_OP_INDEX_TOPK: return plan_index_topk(*s, false).ws;
+    case DSA_OP_ATTN_PAGED: return paged_idx_bytes(*s) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);
+    case DSA_OP_STACK_PAGED:  // score chunks (paged keys take the score route) + pool rows + attention
+      return align_up(plan_index_topk(*s, true).ws) + paged_idx_bytes(*s) +
+             dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);
     case DSA_OP_STACK: {
       // either route of the 'F' layers fits (DSA_STACK_UNFUSED picks the score chunks)
       const size_t sel = std::max(plan_index_topk(*s, false).ws, plan_index_topk(*s, true).ws);
@@ -302,14 +389,25 @@ size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
   return 0;
 }
 
-dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers, const dsa_shape* shape,
-                           int32_t* index_cache, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// dsa_layer_stack, over dense caches (pages == nullptr) or paged pools.
+dsa_status stack_impl(const char* pattern, int n_layers, const dsa_layer_io* layers, const dsa_shape* shape,
+                      const dsa_paged_kv* pages, int32_t* index_cache, unsigned flags, void* ws, size_t ws_bytes,
+                      void* stream) {
   if (!shape) return fail(DSA_ERR_NULL, "shape is required");
   dsa_status st = dsa_check_pattern(pattern, n_layers, flags);
   if (st != DSA_OK) return st;
   if (n_layers > 0 && !layers) return fail(DSA_ERR_NULL, "layers is required");
   const dsa_shape& s = *shape;
   if (!valid_kv_dtype(s.kv_dtype)) return fail(DSA_ERR_SHAPE, "unknown kv dtype");
+  if (pages) {
+    st = check_pages(pages, s.Tk, (int64_t)s.d_I * 2, INT64_MAX, "key");
+    if (st == DSA_OK) st = check_pages(pages, s.Tk, latent_row_bytes(s.kv_dtype), kMaxAttnPoolRows, "latent");
+    if (st != DSA_OK) return st;
+  }
   // validate every layer before enqueueing anything
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer_io& L = layers[l];
@@ -326,29 +424,66 @@ dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io
                                 s.Dqk, s.Dv, s.k, s.sm_scale, L.out, L.lse, ws);
     st = check_attn(a, (size_t)-1);
     if (st != DSA_OK) return fail(st, g_last_error + at);
+    if (pages && !dsa::attn_mla_supported(a)) return fail(DSA_ERR_UNSUPPORTED, "paged caches: MLA form only" + at);
   }
   if ((int64_t)s.B * s.Tq == 0 || n_layers == 0) return DSA_OK;
   if (!index_cache) return fail(DSA_ERR_NULL, "index_cache is required");
-  const size_t need = dsa_workspace_size(shape, DSA_OP_STACK);
+  const size_t need = dsa_workspace_size(shape, pages ? DSA_OP_STACK_PAGED : DSA_OP_STACK);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "stack workspace too small: need " + std::to_string(need) + " bytes");
 
-  const IndexTopkPlan P = plan_index_topk(s, (flags & DSA_STACK_UNFUSED) != 0);
-  const size_t sel = std::max(plan_index_topk(s, false).ws, plan_index_topk(s, true).ws);
-  void* attn_ws = reinterpret_cast<char*>(ws) + align_up(sel);
+  // workspace: selection (score chunks or fused lists) | [pool rows of the cache] | attention
+  const IndexTopkPlan P = plan_index_topk(s, pages != nullptr || (flags & DSA_STACK_UNFUSED) != 0);
+  const size_t sel = pages ? P.ws : std::max(plan_index_topk(s, false).ws, plan_index_topk(s, true).ws);
+  char* const wsb = reinterpret_cast<char*>(ws);
+  int32_t* const phys = pages ? reinterpret_cast<int32_t*>(wsb + align_up(sel)) : nullptr;
+  void* attn_ws = wsb + align_up(sel) + (pages ? paged_idx_bytes(s) : 0);
   hipStream_t strm = as_stream(stream);
+  auto translate = [&]() {
+    return launch_status(dsa::launch_page_translate(index_cache, phys, s.B, s.Tq, s.k, s.kv_len, s.Tk,
+                                                    pages->block_table, pages->max_blocks,
+                                                    page_shift(pages->page_size), pool_rows(*pages), strm),
+                         "dsa_layer_stack_paged: translate");
+  };
+  if (pages && pattern[0] == 'S') {  // a prefilled cache
+    st = translate();
+    if (st != DSA_OK) return st;
+  }
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer_io& L = layers[l];
     if (pattern[l] == 'F') {
-      st = run_index_topk(P, L.q_idx, L.k_idx, L.w_idx, s, 0.f, index_cache, ws, strm, "dsa_layer_stack: index/top-k");
+      st = run_index_topk(P, L.q_idx, L.k_idx, L.w_idx, s, 0.f, index_cache, ws, strm, "dsa_layer_stack: index/top-k",
+                          pages);
+      if (st == DSA_OK && pages) st = translate();
       if (st != DSA_OK) return st;
     }
     dsa::AttnArgs a = attn_args(L.q, L.kv, L.kv_scale, L.v, s.kv_dtype, index_cache, s.B, s.Tq, s.Tk, s.H, s.Hkv,
                                 s.Dqk, s.Dv, s.k, s.sm_scale, L.out, L.lse, attn_ws);
+    if (pages) {
+      a.idx = phys;
+      a.Tk = (int)pool_rows(*pages);
+      a.kv_bstride = 0;
+    }
     st = launch_status(dsa::launch_sparse_attn(a, strm), "dsa_layer_stack: attention");
     if (st != DSA_OK) return st;
   }
   return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers, const dsa_shape* shape,
+                           int32_t* index_cache, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  return stack_impl(pattern, n_layers, layers, shape, nullptr, index_cache, flags, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_layer_stack_paged(const char* pattern, int n_layers, const dsa_layer_io* layers, const dsa_shape* shape,
+                                 const dsa_paged_kv* pages, int32_t* index_cache, unsigned flags, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!pages) return fail(DSA_ERR_NULL, "pages is required");
+  return stack_impl(pattern, n_layers, layers, shape, pages, index_cache, flags, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -114,8 +114,9 @@ struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
 template <bool FP8>
 __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                                                           const float* __restrict__ kv_scale,
-                                                          const int32_t* __restrict__ idx, int Tq, int Tk, int H, int k,
-                                                          float scale_log2, int tiles_per_split,
+                                                          const int32_t* __restrict__ idx, int Tq, int Tk,
+                                                          int64_t kv_bstride, int H, int k, float scale_log2,
+                                                          int tiles_per_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kTile * kRowB];
@@ -133,7 +134,8 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int32_t* ix = idx + row * k;
   constexpr uint32_t kRowBytes = TileStage<FP8>::kRowBytes;
-  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + (int64_t)b * Tk * kRowBytes, (uint32_t)Tk * kRowBytes);
+  // sequence b's rows start kv_bstride rows after sequence b-1's (0: one shared pool)
+  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + b * kv_bstride * kRowBytes, (uint32_t)Tk * kRowBytes);
 
   // This split's tiles.  Index entries are validated against its nominal range; the scan
   // below only trims trailing tiles that hold no valid entry, so it can run while the first
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   // validated only when the row gather is issued: waiting on a load retires every older
   // load too, so an index consumed right after its load would drain the row prefetch.
   const __amdgpu_buffer_rsrc_t ix_rs = make_rsrc(ix, (uint32_t)k * 4);
-  const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(FP8 ? kv_scale + (int64_t)b * Tk : nullptr, FP8 ? (uint32_t)Tk * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(FP8 ? kv_scale + b * kv_bstride : nullptr, FP8 ? (uint32_t)Tk * 4 : 0u);
   auto raw_entry = [&](int t) -> int {
     const int j = t * kTile + gk;
     return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, t < t_lim ? j * 4 : (int)kOffNone, 0, 0);
@@ -440,6 +442,27 @@ __global__ __launch_bounds__(256) void mha_attn_kernel(const uint16_t* __restric
   }
 }
 
+// Paged latent cache: selected key s of sequence b (an index row of Tq*k entries per
+// sequence) becomes pool row block_table[b][s >> shift] << shift | (s & (page - 1)); entries
+// outside [0, L_b), and rows a table entry places outside the pool, become -1 (skipped).
+__global__ __launch_bounds__(256) void page_translate_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ phys,
+                                                             int64_t n, int64_t per_seq, const int32_t* __restrict__ kv_len,
+                                                             int Tk, const int32_t* __restrict__ bt, int max_blocks,
+                                                             int page_shift, int64_t pool_tokens) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int b = (int)(e / per_seq);
+  const int64_t L = seq_len(kv_len, b, Tk);
+  const int s = idx[e];
+  int r = -1;
+  if (s >= 0 && s < L) {
+    const int64_t pr = ((int64_t)bt[(int64_t)b * max_blocks + (s >> page_shift)] << page_shift) +
+                       (s & ((1 << page_shift) - 1));
+    r = pr >= 0 && pr < pool_tokens ? (int)pr : -1;
+  }
+  phys[e] = r;
+}
+
 }  // namespace
 
 bool attn_mla_supported(const AttnArgs& a) {
@@ -474,6 +497,16 @@ size_t attn_workspace_bytes(int B, int Tq, int H, int Dv, int k, bool mla) {
   return (size_t)s * nrowh * ((size_t)Dv + 2) * sizeof(float);
 }
 
+hipError_t launch_page_translate(const int32_t* idx, int32_t* phys, int B, int Tq, int k, const int32_t* kv_len,
+                                 int Tk, const int32_t* block_table, int max_blocks, int page_shift,
+                                 int64_t pool_tokens, hipStream_t st) {
+  const int64_t n = (int64_t)B * Tq * k;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(page_translate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, phys, n,
+                     (int64_t)Tq * k, kv_len, Tk, block_table, max_blocks, page_shift, pool_tokens);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Tq;
   if (rows == 0) return hipSuccess;
@@ -490,12 +523,13 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
       part_ml = part_o + (size_t)nsplit * nrowh * kDv;
     }
     dim3 grid((unsigned)(rows * (a.H / 16)), nsplit);
+    const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
     if (a.fp8)
       hipLaunchKernelGGL(mla_attn_kernel<true>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale, a.idx,
-                         a.Tq, a.Tk, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+                         a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     else
       hipLaunchKernelGGL(mla_attn_kernel<false>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr, a.idx,
-                         a.Tq, a.Tk, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+                         a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((nrowh + 3) / 4)), dim3(256), 0, st, part_o, part_ml, nsplit,

@@ -9,11 +9,14 @@ namespace dsa {
 
 namespace {
 
-template <int H_I, int D_I>
+// PAGED: key s of sequence b sits in row bt[b*max_blocks + s/P]*P + s%P of a shared pool of
+// pool_tokens rows (P = 1 << page_shift, a multiple of 32, so no 32-key tile crosses a page).
+template <int H_I, int D_I, bool PAGED>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0, int nrows, float* __restrict__ scores,
-    int64_t ld, int64_t score_bstride, int key_seg) {
+    int64_t ld, int64_t score_bstride, int key_seg, const int32_t* __restrict__ bt, int max_blocks, int page_shift,
+    int64_t pool_tokens) {
   using W = IdxWave<H_I, D_I, idx_query_tiles<H_I, D_I>()>;
   constexpr int QB = 4 * W::ROWS;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
@@ -31,9 +34,10 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
 
   W wv;
   wv.load(q + ((int64_t)b * Tq + row0 + wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + wrow0) * H_I, wrows);
-  // Range-checked views: keys past Tk read as zero, and score stores outside this wave's
-  // rows are dropped.
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
+  // Range-checked views: keys past Tk (or past the pool) read as zero, and score stores
+  // outside this wave's rows are dropped.
+  const __amdgpu_buffer_rsrc_t k_rs = PAGED ? make_rsrc(k, (uint32_t)(pool_tokens * D_I * 2))
+                                            : make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
   float* sw = scores + (int64_t)b * score_bstride + (int64_t)wrow0 * ld;
   const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(sw, (uint32_t)(wrows * ld * 4));
   // Row r = t*QPT + g*QPL + qq of the wave sits at position pos0 + r and score offset
@@ -45,17 +49,31 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   const uint32_t row_bytes = (uint32_t)ld * 4u;
   const int col = wv.col;
   const int s_first = (int)seg0;
-  wv.run(k_rs, wks[wave], (int)((seg_end - seg0 + 31) / 32), [&](int j) { return s_first + 32 * j; },
-         [&](int, int s0, int t, int qq, float tot) {
-           // tiles never cross a segment edge, so the causal bound is the only mask
-           const int skey = s0 + col;
-           const int rr = t * W::QPT + qq;  // row offset from the lane's first row (a constant)
-           buf_store_f32(tot, s_rs, skey - rr <= pos0 ? off0 + (uint32_t)rr * row_bytes + (uint32_t)skey * 4u : kOffNone, 0);
-         });
+  auto start = [&](int j) { return s_first + 32 * j; };
+  auto epi = [&](int, int s0, int t, int qq, float tot) {
+    // tiles never cross a segment edge, so the causal bound is the only mask
+    const int skey = s0 + col;
+    const int rr = t * W::QPT + qq;  // row offset from the lane's first row (a constant)
+    buf_store_f32(tot, s_rs, skey - rr <= pos0 ? off0 + (uint32_t)rr * row_bytes + (uint32_t)skey * 4u : kOffNone, 0);
+  };
+  const int ntiles = (int)((seg_end - seg0 + 31) / 32);
+  if constexpr (PAGED) {
+    // tiles past the sequence (prefetch) clamp to its last table entry; a page id outside
+    // the pool reads zeros through the range check
+    const int32_t* btb = bt + (int64_t)b * max_blocks;
+    const int pmask = (1 << page_shift) - 1;
+    wv.run(k_rs, wks[wave], ntiles, start, epi, [](int) {}, [&](int j) {
+      const int s0 = start(j);
+      return (btb[min(s0 >> page_shift, max_blocks - 1)] << page_shift) + (s0 & pmask);
+    });
+  } else {
+    wv.run(k_rs, wks[wave], ntiles, start, epi);
+  }
 }
 
 template <int H_I, int D_I>
 hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
+  const bool paged = A.block_table != nullptr;
   constexpr int QB = 4 * idx_query_tiles<H_I, D_I>() * (32 / H_I);
   const int qblocks = (A.nrows + QB - 1) / QB;
   // keys any row of the chunk can see (kv_len <= Tk)
@@ -71,8 +89,14 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   int64_t seg_tiles = (tiles + segs - 1) / segs;
   segs = (tiles + seg_tiles - 1) / seg_tiles;
   dim3 grid(qblocks, (unsigned)segs, A.B);
-  hipLaunchKernelGGL((index_scores_kernel<H_I, D_I>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
-                     A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32));
+  if (paged)
+    hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, true>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
+                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), A.block_table,
+                       A.max_blocks, A.page_shift, A.pool_tokens);
+  else
+    hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, false>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
+                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), nullptr, 0, 0,
+                       (int64_t)0);
   return hipGetLastError();
 }
 

@@ -87,7 +87,12 @@ struct IdxWave {
 
   template <class Start, class Epi>
   __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi) {
-    run(k_rs, lds, ntiles, start, epi, [](int) {});
+    run(k_rs, lds, ntiles, start, epi, [](int) {}, start);
+  }
+  template <class Start, class Epi, class Post>
+  __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi,
+                                      Post post) {
+    run(k_rs, lds, ntiles, start, epi, post, start);
   }
 
   // Scores the wave's rows against key tiles j = 0 .. ntiles-1 (ntiles >= 1); tile j holds
@@ -95,7 +100,9 @@ struct IdxWave {
   // epi(j, s0, t, qq, score) runs on every lane for each tile j (s0 = start(j)), query tile
   // t and lane query qq, in a fixed order; the lane's key is s0 + col, its row row_of(t, qq).
   // post(j) runs after the last epilogue of tile j: work that branches belongs there, so
-  // the MFMAs of one query tile can overlap the epilogue of the previous one.
+  // the MFMAs of one query tile can overlap the epilogue of the previous one.  phys(j) is
+  // where tile j's 32 key rows sit in k_rs (start(j) for a dense key array; a page of a
+  // paged cache otherwise): keys are loaded from there, masks and outputs use start(j).
   //
   // Key tiles pass through the wave's private LDS buffer `lds` (kLdsBytes): global loads
   // read whole key rows (KPI keys of D_I*2 bytes per instruction) rather than 32 keys x 16
@@ -103,9 +110,9 @@ struct IdxWave {
   // k-step.  Only this wave touches the buffer and one wave's LDS operations complete in
   // order, so no barrier is needed.  Rows of the next two tiles are in flight in registers
   // and the next tile's operand is read while the current tile computes.
-  template <class Start, class Epi, class Post>
+  template <class Start, class Epi, class Post, class Phys>
   __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi,
-                                      Post post) {
+                                      Post post, Phys phys) {
     const int lane = threadIdx.x & 63;
     uint8_t* const wk0 = lds;
     uint8_t* const wk1 = lds + kTileBytes;
@@ -120,13 +127,13 @@ struct IdxWave {
     // distance to the next tile's start.  The chain also keeps each tile's loads where the
     // pipeline puts them (independent offsets let the scheduler bunch two tiles together
     // and wait for both).
-    uint32_t gkoff = lane_koff + (uint32_t)start(0) * (D_I * 2);
+    uint32_t gkoff = lane_koff + (uint32_t)phys(0) * (D_I * 2);
     int jn = 0;
     auto gload = [&](u32x4 (&gr)[NLD]) {
       asm volatile("" : "+v"(gkoff));
 #pragma unroll
       for (int i = 0; i < NLD; ++i) gr[i] = buf_load_16(k_rs, gkoff + i * KPI * D_I * 2, 0);
-      gkoff += (uint32_t)(start(jn + 1) - start(jn)) * (D_I * 2);
+      gkoff += (uint32_t)(phys(jn + 1) - phys(jn)) * (D_I * 2);
       ++jn;
     };
     auto lstore = [&](uint8_t* wk, const u32x4 (&gr)[NLD]) {

@@ -19,6 +19,11 @@ struct IndexerArgs {
   int row0, nrows;
   float* scores;
   int64_t ld, score_bstride;
+  // paged keys (block_table != nullptr): key s of sequence b is row
+  // block_table[b*max_blocks + s >> page_shift] << page_shift | (s & (page - 1)) of the pool k
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, page_shift = 0;
+  int64_t pool_tokens = 0;
 };
 constexpr int64_t kIndexerMaxLd = int64_t(1) << 22;
 bool indexer_supported(int H_I, int d_I, int64_t ld);
@@ -85,6 +90,9 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   void* ws;
+  // rows between two sequences' first rows: -1 for Tk (dense [B][Tk] caches), 0 for one
+  // pool shared by all sequences (paged caches: idx then holds pool rows, Tk the pool size)
+  int64_t kv_bstride = -1;
 };
 // MLA form: Hkv = 1, Dqk = 576, Dv = 512, V shared with K, H % 16 == 0.
 bool attn_mla_supported(const AttnArgs& a);
@@ -94,5 +102,10 @@ bool attn_mha_supported(const AttnArgs& a);
 int attn_mla_splits(int B, int Tq, int H, int k);
 size_t attn_workspace_bytes(int B, int Tq, int H, int Dv, int k, bool mla);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+// Selected keys of sequence b (rows of k entries, Tq rows per sequence) to rows of a paged
+// pool; -1 for entries outside [0, kv_len[b]) or table entries outside the pool.
+hipError_t launch_page_translate(const int32_t* idx, int32_t* phys, int B, int Tq, int k, const int32_t* kv_len,
+                                 int Tk, const int32_t* block_table, int max_blocks, int page_shift,
+                                 int64_t pool_tokens, hipStream_t st);
 
 }  // namespace dsa

@@ -72,7 +72,9 @@ typedef enum {
   DSA_OP_TOPK = 1,
   DSA_OP_ATTN = 2,
   DSA_OP_STACK = 3,
-  DSA_OP_INDEX_TOPK = 4
+  DSA_OP_INDEX_TOPK = 4,
+  DSA_OP_ATTN_PAGED = 5,
+  DSA_OP_STACK_PAGED = 6
 } dsa_op;
 
 /* flags of dsa_layer_stack */
@@ -159,6 +161,50 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale,
                            int Hkv, int Dqk, int Dv, int k, float sm_scale, void* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Paged caches, for serving batches (the pages serve many sequences at once through vLLM
+ * with an fp8 KV cache, "DeepSeek-V2-Lite-Chat SIQ K4/K3" card, "How to run"; they do not
+ * describe a page layout, so this one is the library's): token s of sequence b is row
+ *     block_table[b][s / page_size] * page_size + s % page_size
+ * of a pool shared by all sequences, each row laid out as in the dense calls.  Table entries
+ * past a sequence's length are never used for its keys (they may hold anything); a row the
+ * table places outside the pool is treated as absent.
+ */
+typedef struct {
+  const int32_t* block_table; /* device int32 [B][max_blocks] */
+  int max_blocks;             /* table entries per sequence; max_blocks * page_size >= Tk */
+  int page_size;              /* tokens per page: a power of two, 32 .. 65536 */
+  int num_pages;              /* pages in each pool */
+} dsa_paged_kv;
+
+/*
+ * dsa_index_scores with the indexer keys in a paged pool:
+ *   k_pool bf16 [num_pages * page_size][d_I]; other arguments and results as there (Tk = the
+ *   longest sequence; kv_len gives each sequence's length).  Same scores, bit for bit.
+ * Supported: as dsa_index_scores, and num_pages * page_size * d_I * 2 < 2^32 bytes.
+ */
+dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w_idx,
+                                  const dsa_paged_kv* pages, const int32_t* kv_len, int B, int Tq,
+                                  int Tk, int H_I, int d_I, float* scores, int64_t ld, void* stream);
+
+/*
+ * dsa_sparse_attn (MLA form) with the latent rows in a paged pool:
+ *   kv_pool        [num_pages * page_size][576], bf16 or e4m3 bytes
+ *   kv_scale_pool  fp32 [num_pages * page_size] for fp8 (NULL for bf16)
+ *   idx            int32 [B][Tq][k] key positions (as from dsa_topk); entries outside
+ *                  [0, kv_len[b]) are skipped
+ *   ws             at least dsa_workspace_size(shape, DSA_OP_ATTN_PAGED) bytes: the pool rows
+ *                  of the selected keys plus the attention workspace
+ * Same outputs, bit for bit, as dsa_sparse_attn on the dense cache holding the same rows.
+ * Supported: MLA (H a multiple of 16, Dqk = 576, Dv = 512); pools of fewer than 2^24 rows and
+ * 2^32 bytes.
+ */
+dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float* kv_scale_pool,
+                                 dsa_kv_dtype kv_dtype, const dsa_paged_kv* pages,
+                                 const int32_t* idx, const int32_t* kv_len, int B, int Tq, int Tk,
+                                 int H, int Dqk, int Dv, int k, float sm_scale, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Shape of one layer of a stack (all layers share it). */
 typedef struct {
   int B, Tq, Tk;        /* sequences, query rows per sequence, keys per sequence */
@@ -198,6 +244,20 @@ typedef struct {
 dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers,
                            const dsa_shape* shape, int32_t* index_cache, unsigned flags, void* ws,
                            size_t ws_bytes, void* stream);
+
+/*
+ * dsa_layer_stack over paged caches: each layer's k_idx is a key pool and kv / kv_scale a
+ * latent pool (MLA form), all laid out by `pages` (one block table for every layer, as a
+ * serving cache shares it across layers).  'F' layers score over the key pool and select as
+ * dsa_topk does (score chunks); every layer attends through the pool rows of the cached
+ * indices.  index_cache holds key positions, as in dsa_layer_stack, and the outputs equal
+ * that call's on dense caches holding the same rows, bit for bit.
+ *   ws  at least dsa_workspace_size(shape, DSA_OP_STACK_PAGED) bytes.
+ */
+dsa_status dsa_layer_stack_paged(const char* pattern, int n_layers, const dsa_layer_io* layers,
+                                 const dsa_shape* shape, const dsa_paged_kv* pages,
+                                 int32_t* index_cache, unsigned flags, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Workspace bytes an operation needs for `shape` (0 if none); 0 also for an invalid shape. */
 size_t dsa_workspace_size(const dsa_shape* shape, dsa_op op);

@@ -188,3 +188,31 @@ def test_index_topk_workspace_follows_the_route(L):
     # the stack holds either route plus attention
     st = size(1, 65536, 65536, 16, 2048, dsa.OP_STACK)
     assert st >= fused and st >= 4096 * 65536 * 4
+
+
+def test_paged_argument_checks(L):
+    P = ctypes.c_void_p(16)
+    f = ctypes.c_float
+    good = dsa.PagedKV(16, 47, 64, 100)      # 47 * 64 >= 3000 keys
+    bad_page = dsa.PagedKV(16, 47, 48, 100)  # not a power of two
+    short = dsa.PagedKV(16, 10, 64, 100)     # 640 < Tk
+    no_table = dsa.PagedKV(None, 47, 64, 100)
+    huge = dsa.PagedKV(16, 47, 65536, 1 << 16)  # 2^32 rows: past the 32-bit offsets
+    idx_call = lambda pg: L.dsa_index_scores_paged(P, P, P, ctypes.byref(pg), None, 1, 4, 3000, 16, 64, P, 3000, None)
+    assert idx_call(bad_page) == 3
+    assert idx_call(short) == 2
+    assert idx_call(no_table) == 1
+    assert idx_call(huge) == 3
+    assert L.dsa_index_scores_paged(P, P, P, None, None, 1, 4, 3000, 16, 64, P, 3000, None) == 1
+    attn = lambda pg, ws, nb: L.dsa_sparse_attn_paged(P, P, P, 1, ctypes.byref(pg), P, None, 4, 1, 3000, 16, 576, 512,
+                                                       2048, f(0.04), P, None, ws, nb, None)
+    assert attn(bad_page, P, 1 << 30) == 3
+    assert attn(good, None, 0) == 5          # workspace: the selected keys' pool rows
+    assert L.dsa_sparse_attn_paged(P, P, None, 1, ctypes.byref(good), P, None, 4, 1, 3000, 16, 576, 512, 2048,
+                                   f(0.04), P, None, P, 1 << 30, None) == 1  # fp8 pool without scales
+    assert L.dsa_sparse_attn_paged(P, P, None, 0, ctypes.byref(good), P, None, 4, 1, 3000, 4, 32, 32, 64,
+                                   f(0.1), P, None, P, 1 << 30, None) in (2, 3)  # multi-head form: not paged
+    shp = dsa.Shape(4, 1, 3000, 16, 64, 16, 1, 576, 512, 2048, 0.04, 1, None)
+    need = L.dsa_workspace_size(ctypes.byref(shp), dsa.OP_ATTN_PAGED)
+    assert need >= 4 * 2048 * 4
+    assert L.dsa_workspace_size(ctypes.byref(shp), dsa.OP_STACK_PAGED) >= need
