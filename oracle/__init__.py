@@ -42,6 +42,14 @@ def lib():
         L.oracle_bf16_to_double.restype = D
         L.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_to_double.restype = D
+        L.oracle_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_to_double.restype = D
+        L.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_to_double.restype = D
+        L.oracle_mxfp4_row_bytes.argtypes = [I]
+        L.oracle_mxfp4_row_bytes.restype = I64
+        L.oracle_mxfp4_value.argtypes = [P, I, I]
+        L.oracle_mxfp4_value.restype = D
         L.oracle_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P, I64, I]
         L.oracle_topk.argtypes = [P, I64, P, I, I, I, I, P, I]
         L.oracle_sparse_attn.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, D, P, P, I]
@@ -88,6 +96,38 @@ def e4m3_to_double(code: int) -> float:
     return lib().oracle_e4m3_to_double(code)
 
 
+def e2m1_to_double(code: int) -> float:
+    return lib().oracle_e2m1_to_double(code)
+
+
+def e8m0_to_double(code: int) -> float:
+    return lib().oracle_e8m0_to_double(code)
+
+
+def mxfp4_row_bytes(D: int) -> int:
+    return lib().oracle_mxfp4_row_bytes(D)
+
+
+def mxfp4_decode_row(row, D: int) -> np.ndarray:
+    """The D values of one MXFP4 row (uint8 [D/2 + 32]) as float64."""
+    r = np.ascontiguousarray(np.asarray(row, dtype=np.uint8))
+    assert r.shape == (mxfp4_row_bytes(D),)
+    return np.array([lib().oracle_mxfp4_value(_ptr(r), D, d) for d in range(D)])
+
+
+def _kv_format(kvn, Dqk, kv_scale):
+    """0 bf16, 1 fp8 e4m3 (+ per-token scale), 2 MXFP4 rows (no scale)."""
+    if kvn.dtype != np.uint8:
+        return 0
+    if kv_scale is not None:
+        if kvn.shape[-1] != Dqk:
+            raise ValueError("fp8 rows must be Dqk bytes wide")
+        return 1
+    if kvn.shape[-1] != Dqk // 2 + 32 or Dqk % 32:
+        raise ValueError("MXFP4 rows must be Dqk/2 + 32 bytes wide (fp8 rows need kv_scale)")
+    return 2
+
+
 def index_scores(q_idx, k_idx, w_idx, kv_len=None, nthreads=None, ld=None) -> np.ndarray:
     """Indexer scores float32 [B, Tq, ld]; entries after the causal bound are -inf."""
     q, k, w = _np(q_idx, np.uint16), _np(k_idx, np.uint16), _np(w_idx, np.uint16)
@@ -119,13 +159,14 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, nthreads=N
 
     With v None, V is kv[..., :Dv] (Dv must then be given)."""
     qn = _np(q, np.uint16)
-    fp8 = isinstance(kv, torch.Tensor) and kv.dtype == torch.uint8 or (isinstance(kv, np.ndarray) and kv.dtype == np.uint8)
-    kvn = _np(kv, np.uint8 if fp8 else np.uint16)
+    u8 = isinstance(kv, torch.Tensor) and kv.dtype == torch.uint8 or (isinstance(kv, np.ndarray) and kv.dtype == np.uint8)
+    kvn = _np(kv, np.uint8 if u8 else np.uint16)
     vn = None if v is None else _np(v, np.uint16)
     sc = None if kv_scale is None else _np(kv_scale, np.float32)
     ix = _np(idx, np.int32)
     B, Tq, H, Dqk = qn.shape
     Tk, Hkv = kvn.shape[1], kvn.shape[2]
+    fmt = _kv_format(kvn, Dqk, kv_scale)
     if vn is not None:
         Dv = vn.shape[3]
     elif Dv is None:
@@ -133,7 +174,7 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, nthreads=N
     k = ix.shape[2]
     out = np.zeros((B, Tq, H, Dv), np.float64)
     lse = np.zeros((B, Tq, H), np.float64)
-    rc = lib().oracle_sparse_attn(_ptr(qn), _ptr(kvn), _ptr(sc), _ptr(vn), int(fp8), _ptr(ix), B, Tq, Tk, H,
+    rc = lib().oracle_sparse_attn(_ptr(qn), _ptr(kvn), _ptr(sc), _ptr(vn), fmt, _ptr(ix), B, Tq, Tk, H,
                                   Hkv, Dqk, Dv, k, float(sm_scale), _ptr(out), _ptr(lse),
                                   nthreads or default_threads())
     assert rc == 0, rc
@@ -143,16 +184,17 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, nthreads=N
 def dsa_rows(q_idx, k_idx, w_idx, q, kv, rows, k, sm_scale, Dv=512, kv_scale=None, nthreads=None):
     """Streamed scores -> top-k -> MLA attention for chosen rows of one prefill sequence."""
     qi, ki, wi, qn = (_np(x, np.uint16) for x in (q_idx, k_idx, w_idx, q))
-    fp8 = kv_scale is not None
-    kvn = _np(kv, np.uint8 if fp8 else np.uint16)
+    u8 = isinstance(kv, torch.Tensor) and kv.dtype == torch.uint8 or (isinstance(kv, np.ndarray) and kv.dtype == np.uint8)
+    kvn = _np(kv, np.uint8 if u8 else np.uint16)
     sc = None if kv_scale is None else _np(kv_scale, np.float32)
     rows = np.ascontiguousarray(np.asarray(rows, np.int32))
     H_I, d_I = qi.shape[-2], qi.shape[-1]
     Tk = ki.shape[-2]
     H, Dqk = qn.shape[-2], qn.shape[-1]
+    fmt = _kv_format(kvn, Dqk, kv_scale)
     idx = np.empty((len(rows), k), np.int32)
     out = np.empty((len(rows), H, Dv), np.float64)
-    rc = lib().oracle_dsa_rows(_ptr(qi), _ptr(ki), _ptr(wi), _ptr(qn), _ptr(kvn), _ptr(sc), int(fp8),
+    rc = lib().oracle_dsa_rows(_ptr(qi), _ptr(ki), _ptr(wi), _ptr(qn), _ptr(kvn), _ptr(sc), fmt,
                                _ptr(rows), len(rows), Tk, H_I, d_I, H, Dqk, Dv, k, float(sm_scale),
                                _ptr(idx), _ptr(out), nthreads or default_threads())
     assert rc == 0, rc

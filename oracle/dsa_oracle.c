@@ -22,9 +22,12 @@
  *   - "IndexCache" (vLLM feature doc), "How It Works": F layers compute and store top-k
  *     indices, S layers receive the cached indices of the previous layer.
  *   - "DeepSeek-V2-Lite-Chat SIQ K4/K3" card, "Measured": MLA latent of 576 values per
- *     token (kv_lora_rank 512 plus 64 rotary), cached as fp8.
+ *     token (kv_lora_rank 512 plus 64 rotary), cached as fp8; same section: an nvfp4
+ *     latent-cache backend exists only for sparse MLA on sparse-indexer models, a cache
+ *     this oracle reads in the OCP Microscaling FP4 format (MXFP4, oracle_mxfp4_value).
  * Readings where the pages are silent (index score formula, tie rule, output order,
- * fp8 variant and scaling, softmax scale argument) are stated at each function.
+ * fp8 variant and scaling, fp4 row layout, softmax scale argument) are stated at each
+ * function.
  */
 #include <math.h>
 #include <pthread.h>
@@ -56,6 +59,35 @@ double oracle_e4m3_to_double(uint8_t b) {
   else
     v = ldexp(1.0 + (double)m / 8.0, e - 7);
   return s ? -v : v;
+}
+
+/* OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element (low 4 bits of `c`): 1 sign,
+ * 2 exponent bits (bias 1), 1 mantissa bit, no infinities or NaN.
+ * Value = (-1)^S * 2^(E-1) * (1 + M/2) for E > 0, (-1)^S * (M/2) for E = 0. */
+double oracle_e2m1_to_double(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? (double)m / 2.0 : ldexp(1.0 + (double)m / 2.0, e - 1);
+  return s ? -v : v;
+}
+
+/* Same spec, E8M0 shared scale: 2^(E-127), and NaN for E = 255. */
+double oracle_e8m0_to_double(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* MXFP4 latent row of D values (D a multiple of 32, at most 1024): D/32 blocks of 32
+ * values share one E8M0 scale; value d = e2m1 element * scale of block d/32.  Layout (a
+ * reading: the pages name the cache, not its bytes), D/2 + 32 bytes:
+ *   bytes [16j, 16j+16): the 32 elements of block j, element 2i in the low nibble of
+ *     byte 16j + i and element 2i+1 in its high nibble;
+ *   bytes [D/2, D/2 + 32): the scales, block j's at byte D/2 + 4*(j mod 8) + j/8;
+ *     bytes no block names are ignored. */
+int64_t oracle_mxfp4_row_bytes(int D) { return (int64_t)D / 2 + 32; }
+
+double oracle_mxfp4_value(const uint8_t* row, int D, int d) {
+  int j = d / 32, i = d % 32;
+  uint8_t byte = row[16 * j + i / 2];
+  uint8_t code = (i % 2 == 0) ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4);
+  uint8_t e = row[D / 2 + 4 * (j % 8) + j / 8];
+  return oracle_e2m1_to_double(code) * oracle_e8m0_to_double(e);
 }
 
 /* ---------- row-parallel driver ---------- */
@@ -217,7 +249,8 @@ int oracle_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, i
  *   z_s = sm_scale * sum_d q[h,d] * K[s,g,d]
  *   out[h,:] = sum_s exp(z_s - m) V[s,g,:] / sum_s exp(z_s - m),  m = max_s z_s
  *   lse[h]   = m + log(sum_s exp(z_s - m))
- * K is the bf16 key row, or the fp8 e4m3 row times its per-token scale.  When v is
+ * K is the bf16 key row, the fp8 e4m3 row times its per-token scale (kv_fmt 1), or the
+ * decoded MXFP4 row (kv_fmt 2: rows of oracle_mxfp4_row_bytes(Dqk) bytes).  When v is
  * NULL, V is the first Dv columns of the same row (MLA: one shared latent row per token
  * whose first 512 values are the compressed KV and last 64 the rotary part).
  * A row with no valid entry yields out = 0 and lse = -inf. */
@@ -225,7 +258,7 @@ int oracle_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, i
 typedef struct {
   const void *q, *kv, *v;
   const float* kv_scale;
-  int kv_fp8;
+  int kv_fmt;
   const int32_t* idx;
   int B, Tq, Tk, H, Hkv, Dqk, Dv, k;
   double sm_scale;
@@ -233,8 +266,11 @@ typedef struct {
 } attn_ctx;
 
 static double kv_value(const attn_ctx* c, int b, int64_t s, int g, int d) {
-  int64_t off = (((int64_t)b * c->Tk + s) * c->Hkv + g) * c->Dqk + d;
-  if (c->kv_fp8)
+  int64_t r = ((int64_t)b * c->Tk + s) * c->Hkv + g;
+  if (c->kv_fmt == 2)
+    return oracle_mxfp4_value((const uint8_t*)c->kv + r * oracle_mxfp4_row_bytes(c->Dqk), c->Dqk, d);
+  int64_t off = r * c->Dqk + d;
+  if (c->kv_fmt == 1)
     return oracle_e4m3_to_double(((const uint8_t*)c->kv)[off]) *
            (double)c->kv_scale[(int64_t)b * c->Tk + s];
   return oracle_bf16_to_double(((const uint16_t*)c->kv)[off]);
@@ -283,17 +319,18 @@ static void attn_row(void* c_, int64_t row) {
 }
 
 int oracle_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
-                       int kv_fp8, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv,
+                       int kv_fmt, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv,
                        int Dqk, int Dv, int k, double sm_scale, double* out, double* lse,
                        int nthreads) {
   if (!q || !kv || !idx || !out || B < 0 || Tq < 0 || Tk < 0 || H < 1 || Hkv < 1 || H % Hkv ||
-      Dqk < 1 || Dv < 1 || k < 1)
+      Dqk < 1 || Dv < 1 || k < 1 || kv_fmt < 0 || kv_fmt > 2)
     return 1;
-  if (kv_fp8 && (!kv_scale || v)) return 1;
+  if (kv_fmt == 1 && (!kv_scale || v)) return 1;
+  if (kv_fmt == 2 && (kv_scale || v || Dqk % 32 || Dqk > 1024)) return 1;
   if (!v && Dv > Dqk) return 1;
   for (int64_t r = 0; r < (int64_t)B * Tq * k; ++r)
     if (idx[r] >= Tk) return 2;
-  attn_ctx c = {q, kv, v, kv_scale, kv_fp8, idx, B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, out, lse};
+  attn_ctx c = {q, kv, v, kv_scale, kv_fmt, idx, B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, out, lse};
   for_rows((int64_t)B * Tq, nthreads, attn_row, &c);
   return 0;
 }
@@ -305,7 +342,7 @@ int oracle_sparse_attn(const void* q, const void* kv, const float* kv_scale, con
 typedef struct {
   const uint16_t *q_idx, *k_idx, *w_idx, *q, *kv;
   const float* kv_scale;
-  int kv_fp8;
+  int kv_fmt;
   const int32_t* rows;
   int Tk, H_I, d_I, H, Dqk, Dv, k;
   double sm_scale;
@@ -323,7 +360,7 @@ static void stream_row(void* c_, int64_t r) {
   idx_row(&ic, 0);
   topk_ctx tc = {sc, c->Tk, &kv_len, 1, 1, c->Tk, c->k, c->idx_out + r * c->k};
   topk_row(&tc, 0);
-  attn_ctx ac = {c->q + (int64_t)t * c->H * c->Dqk, c->kv, NULL, c->kv_scale, c->kv_fp8,
+  attn_ctx ac = {c->q + (int64_t)t * c->H * c->Dqk, c->kv, NULL, c->kv_scale, c->kv_fmt,
                  c->idx_out + r * c->k, 1, 1, c->Tk, c->H, 1, c->Dqk, c->Dv, c->k,
                  c->sm_scale, c->out + r * c->H * c->Dv, NULL};
   attn_row(&ac, 0);
@@ -331,14 +368,15 @@ static void stream_row(void* c_, int64_t r) {
 }
 
 int oracle_dsa_rows(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w_idx,
-                    const uint16_t* q, const void* kv, const float* kv_scale, int kv_fp8,
+                    const uint16_t* q, const void* kv, const float* kv_scale, int kv_fmt,
                     const int32_t* rows, int nrows, int Tk, int H_I, int d_I, int H, int Dqk,
                     int Dv, int k, double sm_scale, int32_t* idx_out, double* out, int nthreads) {
-  if (!q_idx || !k_idx || !w_idx || !q || !kv || !rows || !idx_out || !out || nrows < 0 || k < 1)
+  if (!q_idx || !k_idx || !w_idx || !q || !kv || !rows || !idx_out || !out || nrows < 0 || k < 1 ||
+      kv_fmt < 0 || kv_fmt > 2)
     return 1;
   for (int r = 0; r < nrows; ++r)
     if (rows[r] < 0 || rows[r] >= Tk) return 2;
-  stream_ctx c = {q_idx, k_idx, w_idx, q, (const uint16_t*)kv, kv_scale, kv_fp8, rows, Tk, H_I,
+  stream_ctx c = {q_idx, k_idx, w_idx, q, (const uint16_t*)kv, kv_scale, kv_fmt, rows, Tk, H_I,
                   d_I, H, Dqk, Dv, k, sm_scale, idx_out, out};
   for_rows(nrows, nthreads, stream_row, &c);
   return 0;

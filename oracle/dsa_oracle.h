@@ -10,6 +10,10 @@ extern "C" {
 #endif
 double oracle_bf16_to_double(uint16_t h);
 double oracle_e4m3_to_double(uint8_t b);
+double oracle_e2m1_to_double(uint8_t c);
+double oracle_e8m0_to_double(uint8_t e);
+int64_t oracle_mxfp4_row_bytes(int D);
+double oracle_mxfp4_value(const uint8_t* row, int D, int d);
 /* q [B][Tq][H][D], k [B][Tk][D], w [B][Tq][H] -> scores float [B][Tq][ld] */
 int oracle_index_scores(const uint16_t* q, const uint16_t* k, const uint16_t* w,
                         const int32_t* kv_len, int B, int Tq, int Tk, int H, int D,
@@ -17,17 +21,18 @@ int oracle_index_scores(const uint16_t* q, const uint16_t* k, const uint16_t* w,
 /* scores [B][Tq][ld] -> idx int32 [B][Tq][k] (ascending, -1 padded) */
 int oracle_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk,
                 int k, int32_t* idx, int nthreads);
-/* q bf16 [B][Tq][H][Dqk]; kv bf16 or e4m3 [B][Tk][Hkv][Dqk]; kv_scale [B][Tk] (fp8 only);
+/* q bf16 [B][Tq][H][Dqk]; kv (kv_fmt 0) bf16 [B][Tk][Hkv][Dqk], (1) e4m3 [B][Tk][Hkv][Dqk]
+ * with kv_scale [B][Tk], (2) MXFP4 rows [B][Tk][Hkv][Dqk/2 + 32] bytes (kv_scale NULL);
  * v bf16 [B][Tk][Hkv][Dv] or NULL (V = kv[..., :Dv]); idx [B][Tq][k]
  * -> out double [B][Tq][H][Dv], lse double [B][Tq][H] (may be NULL) */
 int oracle_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
-                       int kv_fp8, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv,
+                       int kv_fmt, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv,
                        int Dqk, int Dv, int k, double sm_scale, double* out, double* lse,
                        int nthreads);
 /* Rows `rows[0..nrows)` of one prefill sequence (query t sees keys 0..t), streamed row by
  * row through scores, top-k and MLA attention (Hkv = 1, V = kv[..., :Dv]). */
 int oracle_dsa_rows(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w_idx,
-                    const uint16_t* q, const void* kv, const float* kv_scale, int kv_fp8,
+                    const uint16_t* q, const void* kv, const float* kv_scale, int kv_fmt,
                     const int32_t* rows, int nrows, int Tk, int H_I, int d_I, int H, int Dqk,
                     int Dv, int k, double sm_scale, int32_t* idx_out, double* out, int nthreads);
 #ifdef __cplusplus

@@ -9,7 +9,11 @@ Storage formats produced here:
   * bf16: torch's float32 -> bfloat16 conversion (round to nearest even);
   * fp8: OCP e4m3 ("e4m3fn") bytes with one float32 scale per token,
     scale = amax(row)/448 (1 when the row is all zero), values clamped to +-448
-    before torch's round-to-nearest-even conversion.
+    before torch's round-to-nearest-even conversion;
+  * MXFP4 (OCP Microscaling Formats v1.0): blocks of 32 values share an E8M0 scale
+    2^(floor(log2 amax) - 2) (2 = the largest e2m1 exponent), each value divided by it,
+    rounded to the nearest e2m1 value (ties to an even code) and clamped to +-6; rows
+    of D/2 + 32 bytes laid out as mxfp4_rows states.
 
 Workloads (sizes from the task's workload list; page facts cited per field):
   A  one DSA layer, multi-head attention, T=3072, k=512, indexer 2 heads x 16
@@ -30,7 +34,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "Workload", "WORKLOADS", "workload", "tensor_seed", "normal", "bf16", "fp8_e4m3_rows",
+    "Workload", "WORKLOADS", "workload", "tensor_seed", "normal", "bf16", "fp8_e4m3_rows", "mxfp4_rows",
     "rope_half_split", "layer_inputs", "integer_indexer_inputs", "sharp_attention_inputs",
     "decode_layer_inputs", "decode_indexer_cache",
 ]
@@ -105,6 +109,35 @@ def fp8_e4m3_rows(x: torch.Tensor):
     y = (x / scale.unsqueeze(-1)).clamp_(-448.0, 448.0)
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, scale.to(torch.float32)
+
+
+# e2m1 magnitudes by 3-bit code, and the midpoints between neighbours
+_E2M1_MID = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def mxfp4_rows(x: torch.Tensor) -> torch.Tensor:
+    """float32 [..., D] (D a multiple of 32, at most 1024) -> uint8 MXFP4 rows [..., D/2 + 32].
+
+    Block j (values 32j..32j+31): its elements in bytes 16j..16j+15, element 2i in the low
+    nibble of byte 16j+i and 2i+1 in the high one (code = sign bit 3, magnitude code
+    bits 0..2); its E8M0 scale byte at D/2 + 4*(j % 8) + j // 8; other bytes zero."""
+    *lead, D = x.shape
+    assert D % 32 == 0 and D <= 1024
+    nb = D // 32
+    xb = x.reshape(-1, nb, 32).to(torch.float32)
+    _, ex = torch.frexp(xb.abs().amax(-1))  # amax = m * 2^ex, m in [0.5, 1): floor(log2) = ex - 1
+    e = (ex - 3).clamp(-127, 127)
+    y = torch.ldexp(xb, -e.unsqueeze(-1).to(torch.float32))
+    mag = y.abs().clamp(max=6.0)
+    mid = _E2M1_MID.to(x.device)
+    lo, hi = torch.bucketize(mag, mid, right=False), torch.bucketize(mag, mid, right=True)
+    m = torch.where(lo % 2 == 0, lo, hi)  # the two differ only on a midpoint: keep the even code
+    code = (m | ((y < 0) & (m > 0)).to(m.dtype) << 3).to(torch.uint8)
+    out = torch.zeros((xb.shape[0], D // 2 + 32), dtype=torch.uint8, device=x.device)
+    out[:, :D // 2] = (code[..., 0::2] | (code[..., 1::2] << 4)).reshape(-1, D // 2)
+    j = torch.arange(nb, device=x.device)
+    out[:, D // 2 + 4 * (j % 8) + j // 8] = (e + 127).to(torch.uint8)
+    return out.reshape(*lead, D // 2 + 32)
 
 
 def rope_half_split(x: torch.Tensor, pos0: int = 0, base: float = 10000.0) -> torch.Tensor:
@@ -203,25 +236,31 @@ def decode_indexer_cache(w: Workload, device="cpu", seqs=None):
     return torch.stack(rows)
 
 
-def decode_layer_inputs(w: Workload, layer: int, device="cpu", seqs=None):
-    """One decode layer: q bf16 [B,1,H,Dqk], fp8 latent cache uint8 [B,L,1,Dqk] + scale [B,L],
-    and, on 'F' layers, q_idx bf16 [B,1,H_I,d_I] and w_idx bf16 [B,1,H_I]."""
+def decode_layer_inputs(w: Workload, layer: int, device="cpu", seqs=None, kv_format: str = "fp8"):
+    """One decode layer: q bf16 [B,1,H,Dqk], the latent cache as fp8 uint8 [B,L,1,Dqk] + scale
+    [B,L] (kv_format "fp8") or MXFP4 rows uint8 [B,L,1,Dqk/2+32] ("mxfp4", drawn from the
+    same values), and, on 'F' layers, q_idx bf16 [B,1,H_I,d_I] and w_idx bf16 [B,1,H_I]."""
     assert w.decode
     seqs = list(range(w.B)) if seqs is None else list(seqs)
     sd = 1.0 / math.sqrt(w.Dqk)
+    assert kv_format in ("fp8", "mxfp4")
     codes, scales = [], []
     for b in seqs:
         x = normal((w.T, w.Dqk), sd, tensor_seed(w, layer, _T_KV, b), device)
-        c, s = fp8_e4m3_rows(x)
+        if kv_format == "fp8":
+            c, s = fp8_e4m3_rows(x)
+            scales.append(s)
+        else:
+            c = mxfp4_rows(x)
         codes.append(c)
-        scales.append(s)
         del x
     out = {
         "kv": torch.stack(codes).unsqueeze(2),
-        "kv_scale": torch.stack(scales),
         "q": torch.stack([bf16(normal((1, w.H, w.Dqk), sd, tensor_seed(w, layer, _T_Q, b), device))
                           for b in seqs]),
     }
+    if scales:
+        out["kv_scale"] = torch.stack(scales)
     if w.pattern[layer] == "F":
         si = 1.0 / math.sqrt(w.d_I)
         out["q_idx"] = torch.stack([bf16(normal((1, w.H_I, w.d_I), si, tensor_seed(w, layer, _T_QI, b), device))

@@ -33,6 +33,12 @@ MUTATIONS = {
     "lse_without_max": ("c->lse[row * c->H + h] = m + log(denom);", "c->lse[row * c->H + h] = log(denom);"),
     "fp8_bias_8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     "fp8_scale_dropped": ("(double)c->kv_scale[(int64_t)b * c->Tk + s];", "1.0;"),
+    "e2m1_bias_0": ("ldexp(1.0 + (double)m / 2.0, e - 1);", "ldexp(1.0 + (double)m / 2.0, e);"),
+    "e2m1_subnormal_as_normal": ("double v = e == 0 ? (double)m / 2.0 :", "double v = 0 ? (double)m / 2.0 :"),
+    "mxfp4_nibbles_swapped": ("(i % 2 == 0) ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4);",
+                              "(i % 2 == 1) ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4);"),
+    "mxfp4_scale_position": ("row[D / 2 + 4 * (j % 8) + j / 8];", "row[D / 2 + j];"),
+    "mxfp4_row_stride": ("r * oracle_mxfp4_row_bytes(c->Dqk), c->Dqk, d);", "r * (c->Dqk / 2), c->Dqk, d);"),
     "value_from_key_tail": ("if (!c->v) return kv_value(c, b, s, g, d);",
                             "if (!c->v) return kv_value(c, b, s, g, d + (c->Dqk - c->Dv));"),
 }

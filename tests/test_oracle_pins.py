@@ -49,6 +49,90 @@ def test_fp8_generator_round_trip_is_within_half_ulp():
     assert np.all(err <= bound * 1.0000001)
 
 
+# OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element values by 3-bit magnitude code
+# (sign in bit 3): the spec's table of representable values.
+_E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_matches_the_spec_table():
+    got = [oracle.e2m1_to_double(c) for c in range(16)]
+    assert got[:8] == _E2M1_TABLE
+    assert got[8:] == [-v for v in _E2M1_TABLE]
+    assert math.copysign(1.0, got[8]) == -1.0  # code 8 is negative zero
+
+
+def test_e8m0_decode_is_a_power_of_two():
+    for e in (0, 1, 100, 126, 127, 128, 200, 254):
+        assert oracle.e8m0_to_double(e) == math.ldexp(1.0, e - 127)
+    assert math.isnan(oracle.e8m0_to_double(255))
+
+
+def _decode_table_rows(rows, D):
+    """Decode MXFP4 rows [N, D/2+32] with the spec's value table, vectorised."""
+    tab = np.array(_E2M1_TABLE + [-v for v in _E2M1_TABLE])
+    b = rows[:, :D // 2].astype(np.int64)
+    codes = np.stack([b & 15, b >> 4], axis=-1).reshape(rows.shape[0], D)
+    j = np.arange(D // 32)
+    e = rows[:, D // 2 + 4 * (j % 8) + j // 8].astype(np.int64)
+    return tab[codes] * np.ldexp(1.0, e - 127).repeat(32, axis=1)
+
+
+def test_mxfp4_generator_round_trip_is_nearest_e2m1_value():
+    # encoder (synth) and decoder (oracle) are separate code: a layout mistake on either
+    # side (nibble order, block or scale position) breaks the round trip.  Each decoded
+    # value must be the e2m1 grid point nearest x / X (X = the block's scale) after the
+    # clamp to +-6, with X = 2^(floor(log2 amax) - 2).
+    x = synth.normal((24, 576), 1.0 / 24, 9)
+    x[3, 40] = 0.0
+    x[5, 64:96] = 0.0  # an all-zero block
+    rows = synth.mxfp4_rows(x).numpy()
+    dec = np.stack([oracle.mxfp4_decode_row(r, 576) for r in rows])
+    xd = x.numpy().astype(np.float64)
+    blk = np.abs(xd).reshape(24, 18, 32).max(-1)
+    X = np.where(blk > 0, np.ldexp(1.0, np.floor(np.log2(np.where(blk > 0, blk, 1.0))).astype(int) - 2), 0.0)
+    X = X.repeat(32, axis=1)
+    nz = X > 0
+    v = np.clip(xd[nz] / X[nz], -6.0, 6.0)
+    grid = np.array(sorted(set(_E2M1_TABLE + [-t for t in _E2M1_TABLE])))
+    dist = np.abs(v[:, None] - grid[None, :])
+    got = dec[nz] / X[nz]
+    assert np.all(np.isin(got, grid))
+    assert np.all(np.abs(got - v) <= dist.min(1) + 1e-12)
+    assert np.all(dec[~nz] == 0.0)
+    # every block's largest magnitude lands in [4, 6]: the scale is the spec's shared exponent
+    amax_code = np.abs(dec / np.where(X > 0, X, 1.0)).reshape(24, 18, 32).max(-1)
+    assert np.all((amax_code[blk > 0] >= 4.0) & (amax_code[blk > 0] <= 6.0))
+
+
+def test_mxfp4_rounding_ties_go_to_the_even_code():
+    # values exactly between two e2m1 points (scale 1: block amax 6 -> X = 2^(2-2) = 1)
+    x = torch.zeros(1, 32)
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75]
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -1.0]
+    x[0, :len(ties)] = torch.tensor(ties)
+    x[0, 31] = 6.0
+    dec = oracle.mxfp4_decode_row(synth.mxfp4_rows(x)[0].numpy(), 32)
+    assert list(dec[:len(ties)]) == want and dec[31] == 6.0
+
+
+def test_mxfp4_rows_equal_the_decoded_bf16_rows():
+    # e2m1 values times a power-of-two scale are exact in bf16, so both paths see equal keys;
+    # bytes that no block names hold garbage and must be ignored
+    rng = np.random.default_rng(7)
+    T, D = 24, 576
+    rows = rng.integers(0, 256, size=(T, D // 2 + 32)).astype(np.uint8)
+    j = np.arange(18)
+    rows[:, D // 2 + 4 * (j % 8) + j // 8] = rng.integers(118, 130, size=(T, 18))
+    dec = _decode_table_rows(rows, D)
+    kv_bf16 = torch.from_numpy(dec).to(torch.float32).to(torch.bfloat16)
+    assert np.array_equal(kv_bf16.double().numpy(), dec)
+    q = (torch.randn(1, T, 16, D, generator=torch.Generator().manual_seed(3)) * 0.01).to(torch.bfloat16)
+    idx = oracle.topk(rng.standard_normal((1, T, T)).astype(np.float32), 8)
+    a, la = oracle.sparse_attn(q, rows.reshape(1, T, 1, -1), idx, 0.05, Dv=512)
+    b, lb = oracle.sparse_attn(q, kv_bf16.reshape(1, T, 1, D), idx, 0.05, Dv=512)
+    assert np.max(np.abs(a - b)) < 1e-12 and np.max(np.abs(la - lb)) < 1e-12
+
+
 # ---------------------------------------------------------------- indexer
 
 
