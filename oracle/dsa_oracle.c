@@ -308,11 +308,11 @@ static void attn_row(void* c_, int64_t row) {
       denom += e;
       for (int d = 0; d < c->Dv; ++d) o[d] += e * v_value(c, b, sel[j], g, d);
     }
-    if (denom > 0.0) {
+    if (denom == 0.0) {  /* no valid entry (a NaN logit makes denom NaN: NaN results) */
+      if (c->lse) c->lse[row * c->H + h] = -INFINITY;
+    } else {
       for (int d = 0; d < c->Dv; ++d) o[d] /= denom;
       if (c->lse) c->lse[row * c->H + h] = m + log(denom);
-    } else if (c->lse) {
-      c->lse[row * c->H + h] = -INFINITY;
     }
   }
   free(z);

@@ -408,6 +408,21 @@ def test_masked_dense_attention_agrees_with_gather_oracle():
         assert np.max(np.abs(out - ref)) < 1e-12 and np.max(np.abs(lse - rlse)) < 1e-12
 
 
+def test_attention_row_without_valid_entry_and_nan_key():
+    # no valid entry: out 0 and lse -inf; a selected NaN key: the sum of exponentials and
+    # everything after it is NaN (the -inf rule is for an empty selection only)
+    T, D = 6, 576
+    g = torch.Generator().manual_seed(2)
+    kv = torch.randn(1, T, 1, D, generator=g).to(torch.bfloat16)
+    kv[0, 2, 0, 7] = float("nan")
+    q = (torch.randn(1, 3, 16, D, generator=g) * 0.05).to(torch.bfloat16)
+    idx = np.array([[[-1, -1, -1], [0, 2, 4], [1, 3, -1]]], np.int32)
+    out, lse = oracle.sparse_attn(q, kv, idx, 0.04, Dv=512)
+    assert np.all(out[0, 0] == 0.0) and np.all(lse[0, 0] == -np.inf)
+    assert np.all(np.isnan(out[0, 1])) and np.all(np.isnan(lse[0, 1]))
+    assert np.all(np.isfinite(out[0, 2])) and np.all(np.isfinite(lse[0, 2]))
+
+
 def test_fp8_rows_times_scale_equal_the_decoded_bf16_rows():
     # e4m3 values times a power-of-two scale are exact in bf16, so both paths see equal keys
     rng = np.random.default_rng(5)
