@@ -17,14 +17,14 @@ __all__ = [
     "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "layer_stack",
     "index_scores_paged", "sparse_attn_paged", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
-    "KV_BF16", "KV_FP8_E4M3", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
+    "KV_BF16", "KV_FP8_E4M3", "KV_MXFP4", "mxfp4_row_bytes", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
     "OP_STACK", "OP_INDEX_TOPK",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-KV_BF16, KV_FP8_E4M3 = 0, 1
+KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
 OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK, OP_INDEX_TOPK, OP_ATTN_PAGED, OP_STACK_PAGED = 0, 1, 2, 3, 4, 5, 6
 CACHE_PREFILLED, STACK_UNFUSED = 1, 2
 _STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_PATTERN",
@@ -176,15 +176,15 @@ def index_scores_paged(q_idx, k_pool, w_idx, pages, Tk, kv_len=None, scores=None
 
 def sparse_attn_paged(q, kv_pool, idx, sm_scale, pages, Tk, kv_len=None, kv_scale_pool=None, Dv=512, out=None,
                       lse=None, want_lse=True, ws=None, stream=None):
-    """dsa_sparse_attn_paged (MLA form): kv_pool [num_pages * page_size, 576] bf16 or uint8 (e4m3)."""
+    """dsa_sparse_attn_paged (MLA form): kv_pool [num_pages * page_size, row]: bf16, e4m3 bytes
+    (with kv_scale_pool) or MXFP4 bytes (320 per row)."""
     B, Tq, H, Dqk = q.shape
-    fp8 = kv_pool.dtype == torch.uint8
+    kvd = _kv_dtype(kv_pool, Dqk, kv_scale_pool)
     k = idx.shape[2]
     if out is None:
         out = torch.empty((B, Tq, H, Dv), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
-    kvd = KV_FP8_E4M3 if fp8 else KV_BF16
     shp = _shape(B, Tq, Tk, H, 1, Dqk, Dv, k, sm_scale, kvd)
     nbytes = workspace_size(shp, OP_ATTN_PAGED)
     ws = _workspace(nbytes, q.device, ws)
@@ -192,6 +192,27 @@ def sparse_attn_paged(q, kv_pool, idx, sm_scale, pages, Tk, kv_len=None, kv_scal
                                        _ptr(kv_len), B, Tq, Tk, H, Dqk, Dv, k, sm_scale, _ptr(out), _ptr(lse),
                                        _ptr(ws), nbytes, _stream(stream)))
     return out, lse
+
+
+def mxfp4_row_bytes(Dqk: int) -> int:
+    """Bytes of one MXFP4 latent row of Dqk values (dsa_kv_dtype in include/dsa.h)."""
+    return Dqk // 2 + 32
+
+
+def _kv_dtype(kv, Dqk, kv_scale):
+    """Row format of a latent cache tensor: bf16; uint8 rows of Dqk bytes with kv_scale (e4m3);
+    uint8 rows of Dqk/2 + 32 bytes without (MXFP4)."""
+    if kv.dtype == torch.bfloat16:
+        return KV_BF16
+    if kv.dtype != torch.uint8:
+        raise ValueError(f"latent rows must be bfloat16 or uint8, got {kv.dtype}")
+    if kv_scale is not None:
+        if kv.shape[-1] != Dqk:
+            raise ValueError("fp8 rows (given with kv_scale) must be Dqk bytes wide")
+        return KV_FP8_E4M3
+    if kv.shape[-1] != mxfp4_row_bytes(Dqk):
+        raise ValueError("uint8 rows without kv_scale are MXFP4 and must be Dqk/2 + 32 bytes wide")
+    return KV_MXFP4
 
 
 def _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, H_I=16, d_I=64, kv_len=None):
@@ -219,7 +240,7 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, 
     """dsa_sparse_attn: returns (out bf16 [B,Tq,H,Dv], lse fp32 [B,Tq,H] or None)."""
     B, Tq, H, Dqk = q.shape
     Tk, Hkv = kv.shape[1], kv.shape[2]
-    fp8 = kv.dtype == torch.uint8
+    kvd = _kv_dtype(kv, Dqk, kv_scale)
     if v is not None:
         Dv = v.shape[3]
     elif Dv is None:
@@ -229,7 +250,6 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, 
         out = torch.empty((B, Tq, H, Dv), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
-    kvd = KV_FP8_E4M3 if fp8 else KV_BF16
     shp = _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kvd)
     nbytes = workspace_size(shp, OP_ATTN)
     ws = _workspace(nbytes, q.device, ws)
@@ -253,7 +273,7 @@ def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=
         Tk, Hkv = L0["kv"].shape[1], L0["kv"].shape[2]
     else:
         Hkv = 1
-    fp8 = L0["kv"].dtype == torch.uint8
+    kvd = _kv_dtype(L0["kv"], Dqk, L0.get("kv_scale"))
     if L0.get("v") is not None:
         Dv = L0["v"].shape[3]
     elif Dv is None:
@@ -263,7 +283,6 @@ def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=
         H_I, d_I = f0["q_idx"].shape[2], f0["q_idx"].shape[3]
     H_I, d_I = H_I or 16, d_I or 64
     dev = L0["q"].device
-    kvd = KV_FP8_E4M3 if fp8 else KV_BF16
     shp = _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kvd, H_I, d_I, kv_len)
     if index_cache is None:
         index_cache = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)

@@ -146,14 +146,16 @@ dsa_status check_attn(const dsa::AttnArgs& a, size_t ws_bytes) {
   if (a.H % a.Hkv) return fail(DSA_ERR_SHAPE, "H must be a multiple of Hkv");
   if (!a.v && a.Dv > a.Dqk) return fail(DSA_ERR_SHAPE, "Dv > Dqk needs a separate v");
   if (!isfinite(a.sm_scale)) return fail(DSA_ERR_SHAPE, "sm_scale must be finite");
-  if (a.fp8 && a.v) return fail(DSA_ERR_UNSUPPORTED, "fp8 rows need V taken from kv (v = NULL)");
+  if (a.kv_fmt != DSA_KV_BF16 && a.v) return fail(DSA_ERR_UNSUPPORTED, "fp8 and MXFP4 rows need V taken from kv (v = NULL)");
+  if (a.kv_fmt == DSA_KV_MXFP4 && a.kv_scale)
+    return fail(DSA_ERR_UNSUPPORTED, "MXFP4 rows carry their own block scales: kv_scale must be NULL");
   if (!dsa::attn_mla_supported(a) && !dsa::attn_mha_supported(a))
     return fail(DSA_ERR_UNSUPPORTED,
-                "supported: MLA (Hkv=1, Dqk=576, Dv=512, v=NULL, H%16==0, k<=65536, bf16/fp8) or "
+                "supported: MLA (Hkv=1, Dqk=576, Dv=512, v=NULL, H%16==0, k<=65536, bf16/fp8/MXFP4) or "
                 "multi-head (Hkv=H<=16, Dqk=Dv=32, bf16, v given, k<=4096)");
   if ((int64_t)a.B * a.Tq == 0) return DSA_OK;
   if (!a.q || !a.kv || !a.idx || !a.out) return fail(DSA_ERR_NULL, "q, kv, idx and out are required");
-  if (a.fp8 && !a.kv_scale) return fail(DSA_ERR_NULL, "kv_scale is required for fp8 rows");
+  if (a.kv_fmt == DSA_KV_FP8_E4M3 && !a.kv_scale) return fail(DSA_ERR_NULL, "kv_scale is required for fp8 rows");
   if (!aligned(a.q, 16) || !aligned(a.kv, 16) || !aligned(a.v, 16) || !aligned(a.out, 16) || !aligned(a.ws, 16) ||
       !aligned(a.idx, 4) || !aligned(a.kv_scale, 4) || !aligned(a.lse, 4))
     return fail(DSA_ERR_UNSUPPORTED, "q, kv, v, out and ws must be 16-byte aligned; idx, kv_scale and lse 4-byte");
@@ -171,7 +173,7 @@ dsa::AttnArgs attn_args(const void* q, const void* kv, const float* kv_scale, co
   a.kv = kv;
   a.kv_scale = kv_scale;
   a.v = (const uint16_t*)v;
-  a.fp8 = kv_dtype == DSA_KV_FP8_E4M3;
+  a.kv_fmt = (int)kv_dtype;
   a.idx = idx;
   a.B = B;
   a.Tq = Tq;
@@ -188,7 +190,7 @@ dsa::AttnArgs attn_args(const void* q, const void* kv, const float* kv_scale, co
   return a;
 }
 
-bool valid_kv_dtype(dsa_kv_dtype d) { return d == DSA_KV_BF16 || d == DSA_KV_FP8_E4M3; }
+bool valid_kv_dtype(dsa_kv_dtype d) { return d == DSA_KV_BF16 || d == DSA_KV_FP8_E4M3 || d == DSA_KV_MXFP4; }
 
 // A paged layout for sequences of up to Tk keys over pools of row_bytes-wide rows.
 dsa_status check_pages(const dsa_paged_kv* pg, int Tk, int64_t row_bytes, int64_t max_rows, const char* pool) {
@@ -210,7 +212,7 @@ int64_t pool_rows(const dsa_paged_kv& pg) { return (int64_t)pg.num_pages * pg.pa
 
 // Pool rows of the attention gather: the kernel scales row indices with a 24-bit multiply.
 constexpr int64_t kMaxAttnPoolRows = int64_t(1) << 24;
-int64_t latent_row_bytes(dsa_kv_dtype d) { return d == DSA_KV_FP8_E4M3 ? 576 : 1152; }
+int64_t latent_row_bytes(dsa_kv_dtype d) { return d == DSA_KV_MXFP4 ? 320 : d == DSA_KV_FP8_E4M3 ? 576 : 1152; }
 
 size_t paged_idx_bytes(const dsa_shape& s) { return align_up((size_t)std::max(0, s.B) * std::max(0, s.Tq) * s.k * 4); }
 

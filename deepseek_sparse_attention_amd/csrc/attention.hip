@@ -12,6 +12,10 @@
 // exchanged through LDS (online softmax in base 2).  The next tile's gather is issued into
 // registers before the current tile is computed.  fp8 (OCP e4m3) rows are widened to bf16
 // exactly while staged; their per-token scale multiplies the logit and the probability.
+// MXFP4 rows (OCP microscaling: 32-value blocks of e2m1 elements sharing an E8M0 scale;
+// the same card's "Measured" section names an nvfp4 latent cache for sparse MLA) are
+// decoded with their block scales while staged, also exactly: e2m1 times a power of two
+// has two significant bits.
 // Decode rows (few queries) split the key list over workgroups and merge the partial
 // results by log-sum-exp in a second kernel, in a fixed order.
 //
@@ -42,24 +46,27 @@ __device__ __forceinline__ int lds_off(int r, int chunk) { return r * kRowB + ((
 
 // Gather of one tile: wave w fetches tile keys 8w..8w+7; lane l owns key 8w + l/8 and the
 // 16-byte parts l%8, l%8+8, ... of its row, so every load instruction reads eight full
-// 128-byte lines.  Rows go through registers into LDS (bf16; fp8 widened exactly).
+// 128-byte lines.  Rows go through registers into LDS (bf16; fp8 and fp4 widened exactly).
 // Row offsets use a 24-bit multiply (rows < 2^24 here): a 64-bit multiply-add would read an
 // undefined high addend register and could force a wait on an unrelated load.  A missing
-// row (s < 0) is read at an offset past the buffer range: zeros, no memory access.  Every
-// part is loaded unconditionally, so all paths issue the same loads and the compiler's
-// load-count waits stay exact.
-template <bool FP8>
+// row (s < 0) is read at offsets from kRowNone, past every buffer range these kernels
+// accept: zeros, no memory access.  Every part is loaded unconditionally, so all paths
+// issue the same loads and the compiler's load-count waits stay exact.
+enum : int { kKvBf16 = 0, kKvFp8 = 1, kKvMxfp4 = 2 };
+constexpr uint32_t kRowNone = 0xFFFFF000u;  // + any part offset of a row stays below 2^32
+
+template <int FMT>
 struct TileStage;
 
 template <>
-struct TileStage<false> {  // bf16 row: 72 parts of 16 B, 9 per lane
+struct TileStage<kKvBf16> {  // bf16 row: 72 parts of 16 B, 9 per lane
   static constexpr int kChunks = 9;
   static constexpr uint32_t kRowBytes = kDqk * 2;
   u32x4 r[kChunks];
   int s = -1;      // key index of this lane's entry (-1: none)
   float sc = 1.f;  // its scale (fp8 only)
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int part0) {
-    const uint32_t base = s >= 0 ? __umul24((uint32_t)s, kRowBytes) + part0 * 16 : kOffNone;
+    const uint32_t base = (s >= 0 ? __umul24((uint32_t)s, kRowBytes) : kRowNone) + part0 * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) r[c] = buf_load_16(rs, base + 128 * c, 0);
   }
@@ -70,18 +77,18 @@ struct TileStage<false> {  // bf16 row: 72 parts of 16 B, 9 per lane
 };
 
 template <>
-struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
+struct TileStage<kKvFp8> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
   static constexpr int kChunks = 5;
   static constexpr uint32_t kRowBytes = kDqk;
   u32x4 r[kChunks];
   int s = -1;
   float sc = 1.f;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int part0) {
-    const uint32_t base = s >= 0 ? __umul24((uint32_t)s, kRowBytes) + part0 * 16 : kOffNone;
+    const uint32_t base = (s >= 0 ? __umul24((uint32_t)s, kRowBytes) : kRowNone) + part0 * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       // part part0 + 8c; the fifth exists for part0 < 4 only (36 parts)
-      const uint32_t off = (c < 4 || part0 < 4) ? base + 128 * c : kOffNone;
+      const uint32_t off = (c < 4 || part0 < 4) ? base + 128 * c : kRowNone;
       r[c] = buf_load_16(rs, off, 0);
     }
   }
@@ -111,7 +118,56 @@ struct TileStage<true> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
   }
 };
 
-template <bool FP8>
+// MXFP4 row, 320 B: block j's 32 e2m1 elements in bytes 16j..16j+15 (element 2i in the low
+// nibble of byte i), j < 18; then 8 scale words, word p holding the E8M0 scales of blocks
+// p, p+8 and p+16 in its bytes 0, 1 and 2.  Lane part0 = p loads blocks p, p+8 (p+16 for
+// p < 2) and word p: every 16-byte part is one block, and its scale arrives with it.
+template <>
+struct TileStage<kKvMxfp4> {
+  static constexpr int kChunks = 3;
+  static constexpr int kBlocks = kDqk / 32;
+  static constexpr uint32_t kRowBytes = kDqk / 2 + 32;
+  u32x4 r[kChunks];
+  uint32_t e = 0;  // scales of this lane's blocks
+  int s = -1;
+  float sc = 1.f;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int part0) {
+    const uint32_t row = s >= 0 ? __umul24((uint32_t)s, kRowBytes) : kRowNone;
+    const uint32_t base = row + part0 * 16;
+    r[0] = buf_load_16(rs, base, 0);
+    r[1] = buf_load_16(rs, base + 128, 0);
+    r[2] = buf_load_16(rs, part0 < kBlocks - 16 ? base + 256 : kRowNone, 0);
+    e = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(row + kDqk / 2 + 4 * part0), 0, 0);
+  }
+  // elements 2B and 2B+1 of an 8-element word, times the scale, as a bf16 pair (low first)
+  template <int B>
+  __device__ __forceinline__ static uint32_t pair(uint32_t word, float scale) {
+    const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, B);
+    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int blk = part0 + 8 * c;
+      if (blk >= kBlocks) continue;
+      // the E8M0 byte as the exponent field of an fp32: the conversion reads only that
+      // field, as an E8M0 scale (measured on gfx950: byte 0 scales by 2^-127, byte 255
+      // gives NaN, as the format defines)
+      const float scale = __uint_as_float(((e >> (8 * c)) & 0xFFu) << 23);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {  // values 32 blk + 8w .. +7 -> staged chunk 4 blk + w
+        u32x4 o;
+        o[0] = pair<0>(r[c][w], scale);
+        o[1] = pair<1>(r[c][w], scale);
+        o[2] = pair<2>(r[c][w], scale);
+        o[3] = pair<3>(r[c][w], scale);
+        *reinterpret_cast<u32x4*>(lds + lds_off(key, 4 * blk + w)) = o;
+      }
+    }
+  }
+};
+
+template <int FMT>
 __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                                                           const float* __restrict__ kv_scale,
                                                           const int32_t* __restrict__ idx, int Tq, int Tk,
@@ -133,7 +189,8 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   const int b = (int)(row / Tq);
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int32_t* ix = idx + row * k;
-  constexpr uint32_t kRowBytes = TileStage<FP8>::kRowBytes;
+  constexpr bool FP8 = FMT == kKvFp8;  // per-token scale on logits and probabilities
+  constexpr uint32_t kRowBytes = TileStage<FMT>::kRowBytes;
   // sequence b's rows start kv_bstride rows after sequence b-1's (0: one shared pool)
   const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + b * kv_bstride * kRowBytes, (uint32_t)Tk * kRowBytes);
 
@@ -171,14 +228,14 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     const int lim = (t < t_lim && t * kTile + gk < k) ? Tk : 0;  // the raw value is always read
     return (uint32_t)raw < (uint32_t)lim ? raw : -1;
   };
-  auto fetch = [&](TileStage<FP8>& st, int s_idx) {  // issue the gather of one tile
+  auto fetch = [&](TileStage<FMT>& st, int s_idx) {  // issue the gather of one tile
     st.s = s_idx;
     st.load(kv_rs, part0);
     if (FP8) st.sc = buf_load_f32(sc_rs, s_idx >= 0 ? (uint32_t)s_idx * 4 : kOffNone, 0);
   };
 
   // prologue: index entries of tiles t_begin .. t_begin+3, rows of the first two in flight
-  TileStage<FP8> st0, st1;
+  TileStage<FMT> st0, st1;
   const int e0 = raw_entry(t_begin), e1 = raw_entry(t_begin + 1);
   int nx0 = raw_entry(t_begin + 2), nx1 = raw_entry(t_begin + 3);
   fetch(st0, valid_entry(t_begin, e0));
@@ -202,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   for (int n = 0; n < 8; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto tile = [&](int t, TileStage<FP8>& st, int& nx) {  // nx: raw index entry of tile t+2
+  auto tile = [&](int t, TileStage<FMT>& st, int& nx) {  // nx: raw index entry of tile t+2
     const int buf = (t - t_begin) & 1;
     uint8_t* kvb = kvs[buf];
     st.store(kvb, gk, part0);
@@ -299,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   // ---- results: lane holds O[head hl][wave*128 + n*16 + 4gq + i]
   const int h = hg * 16 + hl;
   if (nsplit == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = l_run == 0.f ? 0.f : 1.f / l_run;  // (a NaN sum stays NaN)
     uint16_t* op = out + (row * H + h) * kDv + wave * 128 + 4 * gq;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
@@ -307,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
       const uint32_t hi = cvt_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
       *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
     }
-    if (lse && wave == 0 && gq == 0) lse[row * H + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    if (lse && wave == 0 && gq == 0) lse[row * H + h] = l_run == 0.f ? -INFINITY : (m_run + __log2f(l_run)) * kLn2;
   } else {
     const int64_t nrowh = (int64_t)gridDim.x * 16;  // (row, head) pairs over all rows
     const int64_t rh = rowh * 16 + hl;
@@ -343,7 +400,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   float l = ls * wgt;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);  // butterfly: same order in every lane
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l == 0.f ? 0.f : 1.f / l;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* po = part_o + rh * kDv + lane * 8;
   for (int sp = 0; sp < nsplit; ++sp) {
@@ -357,7 +414,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
 #pragma unroll
   for (int e = 0; e < 4; ++e) pk[e] = cvt_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
   *reinterpret_cast<uint4*>(out + rh * kDv + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-  if (lse && lane == 0) lse[rh] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  if (lse && lane == 0) lse[rh] = l == 0.f ? -INFINITY : (m + __log2f(l)) * kLn2;
 }
 
 // Multi-head form: Dqk = Dv = 32, Hkv = H, one wave per head (heads strided over 4 waves),
@@ -435,8 +492,8 @@ __global__ __launch_bounds__(256) void mha_attn_kernel(const uint16_t* __restric
         }
       }
       o += __shfl_xor(o, 32, 64);
-      if (half == 0) out[(row * H + h) * kMhaD + d] = f32_to_bf16_bits(l > 0.f ? o / l : 0.f);
-      if (lse && lane == 0) lse[row * H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      if (half == 0) out[(row * H + h) * kMhaD + d] = f32_to_bf16_bits(l == 0.f ? 0.f : o / l);
+      if (lse && lane == 0) lse[row * H + h] = l == 0.f ? -INFINITY : (m + __log2f(l)) * kLn2;
     }
     __syncthreads();  // z is reused by the next round
   }
@@ -467,13 +524,17 @@ __global__ __launch_bounds__(256) void page_translate_kernel(const int32_t* __re
 
 bool attn_mla_supported(const AttnArgs& a) {
   // the gather addresses a sequence's rows with 32-bit byte offsets
-  const int64_t seq_bytes = (int64_t)a.Tk * (a.fp8 ? kDqk : kDqk * 2);
-  return a.Hkv == 1 && a.Dqk == kDqk && a.Dv == kDv && a.v == nullptr && a.H % 16 == 0 && a.H > 0 && a.k >= 1 &&
-         a.k <= 65536 && seq_bytes < (int64_t(1) << 32);
+  // (and a missing row's offsets, from kRowNone, must stay past the range)
+  const int64_t row_bytes = a.kv_fmt == kKvMxfp4 ? TileStage<kKvMxfp4>::kRowBytes
+                            : a.kv_fmt == kKvFp8 ? TileStage<kKvFp8>::kRowBytes
+                                                 : TileStage<kKvBf16>::kRowBytes;
+  const int64_t seq_bytes = (int64_t)a.Tk * row_bytes;
+  return a.kv_fmt >= kKvBf16 && a.kv_fmt <= kKvMxfp4 && a.Hkv == 1 && a.Dqk == kDqk && a.Dv == kDv &&
+         a.v == nullptr && a.H % 16 == 0 && a.H > 0 && a.k >= 1 && a.k <= 65536 && seq_bytes <= kRowNone;
 }
 
 bool attn_mha_supported(const AttnArgs& a) {
-  return !a.fp8 && a.Hkv == a.H && a.H >= 1 && a.H <= 16 && a.Dqk == kMhaD && a.Dv == kMhaD && a.v != nullptr &&
+  return a.kv_fmt == kKvBf16 && a.Hkv == a.H && a.H >= 1 && a.H <= 16 && a.Dqk == kMhaD && a.Dv == kMhaD && a.v != nullptr &&
          a.k >= 1 && a.k <= kMhaMaxK;
 }
 
@@ -524,12 +585,15 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
     }
     dim3 grid((unsigned)(rows * (a.H / 16)), nsplit);
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
-    if (a.fp8)
-      hipLaunchKernelGGL(mla_attn_kernel<true>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale, a.idx,
-                         a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+    if (a.kv_fmt == kKvFp8)
+      hipLaunchKernelGGL(mla_attn_kernel<kKvFp8>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale,
+                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+    else if (a.kv_fmt == kKvMxfp4)
+      hipLaunchKernelGGL(mla_attn_kernel<kKvMxfp4>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
+                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     else
-      hipLaunchKernelGGL(mla_attn_kernel<false>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr, a.idx,
-                         a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+      hipLaunchKernelGGL(mla_attn_kernel<kKvBf16>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
+                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((nrowh + 3) / 4)), dim3(256), 0, st, part_o, part_ml, nsplit,

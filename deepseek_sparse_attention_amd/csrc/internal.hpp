@@ -83,7 +83,7 @@ struct AttnArgs {
   const void* kv;
   const float* kv_scale;
   const uint16_t* v;
-  bool fp8;
+  int kv_fmt;  // latent rows: 0 bf16, 1 fp8 e4m3 + per-token scale, 2 MXFP4 (320-byte rows)
   const int32_t* idx;
   int B, Tq, Tk, H, Hkv, Dqk, Dv, k;
   float sm_scale;

@@ -23,8 +23,9 @@
  *   - Tensors are dense, row-major, in device memory the caller allocated; the library
  *     never allocates, frees or synchronizes.  All work is enqueued in order on `stream`.
  *     Inputs must stay valid until that work completes.  Outputs must not alias inputs.
- *   - bf16 tensors hold IEEE bfloat16 values; fp8 tensors hold OCP e4m3 ("e4m3fn") bytes.
- *   - Alignment: bf16 and fp8 tensors and workspaces start on 16-byte boundaries, fp32 and
+ *   - bf16 tensors hold IEEE bfloat16 values; fp8 tensors hold OCP e4m3 ("e4m3fn") bytes;
+ *     fp4 latent rows are OCP MXFP4 (see dsa_kv_dtype).
+ *   - Alignment: bf16, fp8 and fp4 tensors and workspaces start on 16-byte boundaries, fp32 and
  *     int32 tensors on 4-byte ones (w_idx: 4, or 2 when H_I = 1); otherwise the call
  *     returns DSA_ERR_UNSUPPORTED.  Row pitches follow from the dense layouts.
  *   - Positions: sequence b holds L_b = kv_len[b] keys (kv_len: device int32[B], or NULL
@@ -65,7 +66,23 @@ typedef enum {
   DSA_ERR_DEVICE = 7       /* no usable gfx950 device / HIP runtime error */
 } dsa_status;
 
-typedef enum { DSA_KV_BF16 = 0, DSA_KV_FP8_E4M3 = 1 } dsa_kv_dtype;
+/*
+ * Latent row formats (MLA form; the multi-head form reads bf16 only).
+ *   DSA_KV_BF16      Dqk bf16 values.
+ *   DSA_KV_FP8_E4M3  Dqk e4m3 bytes; value = code * kv_scale[row] (one fp32 per row).
+ *   DSA_KV_MXFP4     OCP Microscaling FP4, Dqk/2 + 32 = 320 bytes per row: 18 blocks of 32
+ *                    values, each an e2m1 element times its block's E8M0 scale 2^(E-127).
+ *                    Bytes 16j..16j+15 hold block j's elements, element 2i in the low nibble
+ *                    of byte 16j+i; bytes 288 + 4p .. 288 + 4p + 2 hold the scales of blocks
+ *                    p, p + 8 and p + 16 (p < 8; the byte of a block >= 18 and every fourth
+ *                    byte are ignored).  kv_scale must be NULL.  A block with scale byte 255
+ *                    (NaN) makes the outputs of every query that selects its row NaN.
+ *                    (The "DeepSeek-V2-Lite-Chat SIQ K4/K3" card,
+ *                    "Measured", names an nvfp4 latent cache for sparse MLA on sparse-indexer
+ *                    models; MXFP4 is the block-scaled fp4 that gfx950 converts natively, and
+ *                    this byte layout is the library's.)
+ */
+typedef enum { DSA_KV_BF16 = 0, DSA_KV_FP8_E4M3 = 1, DSA_KV_MXFP4 = 2 } dsa_kv_dtype;
 
 typedef enum {
   DSA_OP_SCORES = 0,
@@ -143,7 +160,8 @@ dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_id
 /*
  * Attention restricted to the selected keys (step 3).
  *   q     bf16 [B][Tq][H][Dqk]
- *   kv    [B][Tk][Hkv][Dqk], bf16 (DSA_KV_BF16) or e4m3 bytes (DSA_KV_FP8_E4M3)
+ *   kv    [B][Tk][Hkv][row], row = Dqk bf16 (DSA_KV_BF16), Dqk e4m3 bytes (DSA_KV_FP8_E4M3)
+ *         or Dqk/2 + 32 MXFP4 bytes (DSA_KV_MXFP4), see dsa_kv_dtype
  *   kv_scale fp32 [B][Tk] for fp8 (key row value = e4m3 value * kv_scale[b][s]); else NULL
  *   v     bf16 [B][Tk][Hkv][Dv], or NULL: V is kv[..., 0:Dv] (MLA shared latent row)
  *   idx   int32 [B][Tq][k]: key indices per query row, shared by all heads; entries
@@ -153,8 +171,9 @@ dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_id
  *   lse   fp32 [B][Tq][H] natural-log sum-exp of the scaled logits (-inf if none), or NULL
  *   ws    device workspace of at least dsa_workspace_size(shape, DSA_OP_ATTN) bytes (may be
  *         NULL when that size is 0); used for split-key partial results
- * Supported: MLA (Hkv = 1, Dqk = 576, Dv = 512, v = NULL, H a multiple of 16, bf16 or fp8)
- * and multi-head (Hkv = H <= 16, Dqk = Dv = 32, bf16, v given); 1 <= k <= 65536.
+ * Supported: MLA (Hkv = 1, Dqk = 576, Dv = 512, v = NULL, H a multiple of 16, any row format,
+ * Tk * row bytes <= 2^32 - 4096) and multi-head (Hkv = H <= 16, Dqk = Dv = 32, bf16, v given);
+ * 1 <= k <= 65536.
  */
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale, const void* v,
                            dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk, int H,
@@ -189,15 +208,16 @@ dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const v
 
 /*
  * dsa_sparse_attn (MLA form) with the latent rows in a paged pool:
- *   kv_pool        [num_pages * page_size][576], bf16 or e4m3 bytes
- *   kv_scale_pool  fp32 [num_pages * page_size] for fp8 (NULL for bf16)
+ *   kv_pool        [num_pages * page_size][row], rows as in dsa_sparse_attn (bf16, e4m3 or
+ *                  MXFP4)
+ *   kv_scale_pool  fp32 [num_pages * page_size] for fp8 (NULL otherwise)
  *   idx            int32 [B][Tq][k] key positions (as from dsa_topk); entries outside
  *                  [0, kv_len[b]) are skipped
  *   ws             at least dsa_workspace_size(shape, DSA_OP_ATTN_PAGED) bytes: the pool rows
  *                  of the selected keys plus the attention workspace
  * Same outputs, bit for bit, as dsa_sparse_attn on the dense cache holding the same rows.
  * Supported: MLA (H a multiple of 16, Dqk = 576, Dv = 512); pools of fewer than 2^24 rows and
- * 2^32 bytes.
+ * at most 2^32 - 4096 bytes.
  */
 dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float* kv_scale_pool,
                                  dsa_kv_dtype kv_dtype, const dsa_paged_kv* pages,

@@ -80,6 +80,15 @@ def test_attention_argument_checks(L):
                              need - 1, None) == 5
     # unknown kv dtype
     assert L.dsa_sparse_attn(P, P, None, None, 7, P, 1, 4, 4, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0, None) == 2
+    # MXFP4 rows: no kv_scale, no separate v, MLA form only; a cache past the 32-bit row
+    # offsets (more than 2^32 - 4096 bytes: 13,421,761 rows of 320 bytes) is rejected
+    assert L.dsa_sparse_attn(P, P, P, None, 2, P, 1, 4, 4, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0, None) == 3
+    assert L.dsa_sparse_attn(P, P, None, P, 2, P, 1, 4, 4, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0, None) == 3
+    assert L.dsa_sparse_attn(P, P, None, P, 2, P, 1, 4, 4, 4, 4, 32, 32, 4, f(0.1), P, None, None, 0, None) == 3
+    assert L.dsa_sparse_attn(P, P, None, None, 2, P, 1, 4, 13421761, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0,
+                             None) == 3
+    assert L.dsa_sparse_attn(P, P, None, None, 0, P, 1, 4, 3728302, 16, 1, 576, 512, 4, f(0.04), P, None, None, 0,
+                             None) == 3  # bf16: 1152-byte rows
 
 
 def test_alignment_checks(L):
