@@ -431,7 +431,48 @@ def main():
         result["decode"]["paged"] = {"page_size": page, "ms_per_step": round(pdt * 1e3, 4),
                                      "value": round(e.B / pdt, 1), "matches_dense": same}
         log(f"decode, paged caches: {pdt * 1e3:.3f} ms/step, {e.B / pdt:.0f} tok/s, matches dense: {same}")
-        del kc, dl, pl, pws
+        del pl, pws
+
+        # the same step with MXFP4 latent caches drawn from the same values (320 bytes per key
+        # instead of 576 + a 4-byte scale), and one layer's attention alone in both formats
+        ml = []
+        for l, L in enumerate(dl):
+            mx = synth.decode_layer_inputs(e, l, device=dev, kv_format="mxfp4")
+            M = {"q": L["q"], "kv": mx["kv"], "out": torch.empty_like(L["out"]), "lse": torch.empty_like(L["lse"])}
+            if "q_idx" in L:
+                M.update(q_idx=L["q_idx"], w_idx=L["w_idx"], k_idx=kc)
+            ml.append(M)
+            del mx
+        mcache = torch.empty_like(dcache)
+        mshp = dsa._shape(e.B, 1, e.T, e.H, 1, e.Dqk, e.Dv, e.k, e.scale(), dsa.KV_MXFP4, e.H_I, e.d_I, klen)
+        mws = torch.empty(max(1, dsa.workspace_size(mshp, dsa.OP_STACK)), dtype=torch.uint8, device=dev)
+
+        def mstep():
+            dsa.layer_stack(e.pattern, ml, e.k, e.scale(), Dv=e.Dv, kv_len=klen, index_cache=mcache, ws=mws)
+
+        for _ in range(max(1, args.warmup)):
+            mstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(dsteps):
+            mstep()
+        torch.cuda.synchronize()
+        mdt = (time.perf_counter() - t0) / dsteps
+        result["decode"]["mxfp4"] = {"ms_per_step": round(mdt * 1e3, 4), "value": round(e.B / mdt, 1),
+                                     "bytes_per_key": dsa.mxfp4_row_bytes(e.Dqk),
+                                     "same_indices": bool(torch.equal(mcache, dcache))}
+        log(f"decode, MXFP4 latent caches: {mdt * 1e3:.3f} ms/step, {e.B / mdt:.0f} tok/s")
+
+        def attn_layer(L, kv_scale, row_bytes):
+            us = 1e3 * timed(lambda: dsa.sparse_attn(L["q"], L["kv"], dcache, e.scale(), kv_scale=kv_scale, Dv=e.Dv,
+                                                     out=L["out"], lse=L["lse"], ws=dws))
+            nb = (e.B * e.k * (row_bytes + 4) + e.B * e.H * (e.Dqk * 2 + e.Dv * 2 + 4))
+            return {"us": round(us, 2), "algorithmic_bytes": nb, "gbs": round(nb / (us * 1e-6) / 1e9, 1)}
+
+        result["decode"]["attn_layer"] = {"fp8": attn_layer(dl[1], dl[1]["kv_scale"], e.Dqk + 4),
+                                          "mxfp4": attn_layer(ml[1], None, dsa.mxfp4_row_bytes(e.Dqk))}
+        log(f"decode attention, one layer: {result['decode']['attn_layer']}")
+        del kc, dl, ml, mws
 
     # ---- CPU oracle on a bounded, evenly spread sample of the same prefill rows
     if not args.no_cpu_baseline:
