@@ -54,7 +54,10 @@ def lib():
         L.oracle_topk.argtypes = [P, I64, P, I, I, I, I, P, I]
         L.oracle_sparse_attn.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, D, P, P, I]
         L.oracle_dsa_rows.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, D, P, P, I]
-        for f in ("oracle_index_scores", "oracle_topk", "oracle_sparse_attn", "oracle_dsa_rows"):
+        L.oracle_indexer_kl.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, D, P, P, P, P, I]
+        L.oracle_indexer_kl_f64.argtypes = L.oracle_indexer_kl.argtypes
+        for f in ("oracle_index_scores", "oracle_topk", "oracle_sparse_attn", "oracle_dsa_rows",
+                  "oracle_indexer_kl", "oracle_indexer_kl_f64"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -199,6 +202,32 @@ def dsa_rows(q_idx, k_idx, w_idx, q, kv, rows, k, sm_scale, Dv=512, kv_scale=Non
                                _ptr(idx), _ptr(out), nthreads or default_threads())
     assert rc == 0, rc
     return idx, out
+
+
+def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, nthreads=None):
+    """Indexer KL objective (dsa_oracle.c): per-row KL(P || Q) and the gradients of their sum
+    with respect to the indexer inputs.  bf16 tensors (or float64 arrays: the _f64 form);
+    k is the main attention's keys [B, Tk, Hkv, Dqk]; idx None = every causal key (dense
+    warm-up).  Returns (loss [B,Tq], dq_idx, dw_idx, dk_idx [B,Tk,d_I]) as float64."""
+    f64 = isinstance(q_idx, np.ndarray) and q_idx.dtype == np.float64
+    cv = (lambda x: np.ascontiguousarray(x, dtype=np.float64)) if f64 else (lambda x: _np(x, np.uint16))
+    qi, ki, wi, qn, kn = (cv(x) for x in (q_idx, k_idx, w_idx, q, k))
+    B, Tq, H_I, d_I = qi.shape
+    Tk = ki.shape[1]
+    H, Dqk = qn.shape[2], qn.shape[3]
+    Hkv = kn.shape[2]
+    ix = None if idx is None else _np(idx, np.int32)
+    kk = 0 if ix is None else ix.shape[2]
+    kl = _kvlen(kv_len, B)
+    loss = np.zeros((B, Tq), np.float64)
+    dq = np.zeros((B, Tq, H_I, d_I), np.float64)
+    dw = np.zeros((B, Tq, H_I), np.float64)
+    dk = np.zeros((B, Tk, d_I), np.float64)
+    fn = lib().oracle_indexer_kl_f64 if f64 else lib().oracle_indexer_kl
+    rc = fn(_ptr(qi), _ptr(ki), _ptr(wi), _ptr(qn), _ptr(kn), _ptr(kl), _ptr(ix), B, Tq, Tk, H_I, d_I, H, Hkv,
+            Dqk, kk, float(sm_scale), _ptr(loss), _ptr(dq), _ptr(dw), _ptr(dk), nthreads or default_threads())
+    assert rc == 0, rc
+    return loss, dq, dw, dk
 
 
 # ---------- IndexCache F/S reuse ("IndexCache" vLLM feature doc, "How It Works" and

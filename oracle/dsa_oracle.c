@@ -381,3 +381,179 @@ int oracle_dsa_rows(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t
   for_rows(nrows, nthreads, stream_row, &c);
   return 0;
 }
+
+/* ---------- indexer training objective ---------- */
+/* "DSA ablation model card", model list: the indexer is trained with a KL loss against the
+ * main attention distribution, which is detached; the first tenth of the steps run dense
+ * attention (indexer warm-up).  The pages give no formula.  Reading: for query row t with
+ * key set S_t (its valid index entries; in the dense warm-up every causal key 0..p),
+ *   P_s = (1/H) sum_h softmax_{s in S_t}(sm_scale * q_h . K_{s,g(h)})      target, held fixed
+ *   Q_s = softmax_{s in S_t}(I_s),   I_s = sum_j w_j max(0, q_j . k_s)     indexer (as in 1.)
+ *   L_t = KL(P || Q) = sum_s P_s (log P_s - log Q_s)        (a term with P_s = 0 is 0)
+ * and the gradients of sum_t L_t with respect to the indexer inputs, with G_s = dL_t/dI_s =
+ * Q_s - P_s and d_js = q_j . k_s (the ReLU's derivative taken as 0 at 0):
+ *   dw_j = sum_s G_s max(0, d_js),  dq_j = sum_s G_s w_j [d_js > 0] k_s,
+ *   dk_s = sum over rows t and heads j of G_ts w_tj [d_tjs > 0] q_tj.
+ * An index entry < 0 is skipped (a duplicate counts twice, as in attention); a row with no
+ * key has L_t = 0 and no gradient.  Inputs here are doubles (the bf16 entry decodes first). */
+
+typedef struct {
+  const double *qi, *ki, *wi, *q, *k;
+  const int32_t *kv_len, *idx;
+  int B, Tq, Tk, H_I, d_I, H, Hkv, Dqk, kk, width;
+  double sm_scale;
+  double *loss, *dq, *dw;
+  int32_t* keys; /* [rows][width]: the row's key list, -1 past its end */
+  double* G;     /* [rows][width]: dL_t/dI for each listed key */
+} kl_ctx;
+
+static void kl_row(void* c_, int64_t row) {
+  kl_ctx* c = (kl_ctx*)c_;
+  int b = (int)(row / c->Tq), i = (int)(row % c->Tq);
+  int32_t* keys = c->keys + row * c->width;
+  double* G = c->G + row * c->width;
+  int n = 0;
+  if (c->idx) {
+    for (int e = 0; e < c->kk; ++e)
+      if (c->idx[row * c->kk + e] >= 0) keys[n++] = c->idx[row * c->kk + e];
+  } else {
+    int64_t p = query_pos(c->kv_len, b, c->Tq, c->Tk, i);
+    for (int64_t s = 0; s <= p && s < c->Tk; ++s) keys[n++] = (int32_t)s;
+  }
+  for (int e = n; e < c->width; ++e) keys[e] = -1;
+  const double* qi = c->qi + row * c->H_I * c->d_I;
+  const double* wi = c->wi + row * c->H_I;
+  double* dq = c->dq + row * c->H_I * c->d_I;
+  double* dw = c->dw + row * c->H_I;
+  for (int x = 0; x < c->H_I * c->d_I; ++x) dq[x] = 0.0;
+  for (int j = 0; j < c->H_I; ++j) dw[j] = 0.0;
+  c->loss[row] = 0.0;
+  if (n == 0) return;
+  double* P = (double*)calloc((size_t)n, sizeof(double));
+  double* z = (double*)malloc(sizeof(double) * (size_t)n);
+  double* I = (double*)malloc(sizeof(double) * (size_t)n);
+  /* target: the mean over heads of each head's softmax over the key set */
+  for (int h = 0; h < c->H; ++h) {
+    int g = h * c->Hkv / c->H;
+    const double* qh = c->q + (row * c->H + h) * c->Dqk;
+    double m = -INFINITY, sum = 0.0;
+    for (int e = 0; e < n; ++e) {
+      const double* kr = c->k + (((int64_t)b * c->Tk + keys[e]) * c->Hkv + g) * c->Dqk;
+      double dot = 0.0;
+      for (int d = 0; d < c->Dqk; ++d) dot += qh[d] * kr[d];
+      z[e] = c->sm_scale * dot;
+      if (z[e] > m) m = z[e];
+    }
+    for (int e = 0; e < n; ++e) sum += exp(z[e] - m);
+    for (int e = 0; e < n; ++e) P[e] += exp(z[e] - m) / sum / c->H;
+  }
+  /* indexer distribution over the same keys */
+  double mI = -INFINITY, sumI = 0.0;
+  for (int e = 0; e < n; ++e) {
+    const double* kr = c->ki + ((int64_t)b * c->Tk + keys[e]) * c->d_I;
+    double total = 0.0;
+    for (int j = 0; j < c->H_I; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < c->d_I; ++d) dot += qi[j * c->d_I + d] * kr[d];
+      total += wi[j] * (dot > 0.0 ? dot : 0.0);
+    }
+    I[e] = total;
+    if (I[e] > mI) mI = I[e];
+  }
+  for (int e = 0; e < n; ++e) sumI += exp(I[e] - mI);
+  double lse_I = mI + log(sumI);
+  double L = 0.0;
+  for (int e = 0; e < n; ++e) {
+    double logQ = I[e] - lse_I;
+    if (P[e] > 0.0) L += P[e] * (log(P[e]) - logQ);
+    G[e] = exp(logQ) - P[e];
+  }
+  c->loss[row] = L;
+  /* the row's own indexer inputs */
+  for (int e = 0; e < n; ++e) {
+    const double* kr = c->ki + ((int64_t)b * c->Tk + keys[e]) * c->d_I;
+    for (int j = 0; j < c->H_I; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < c->d_I; ++d) dot += qi[j * c->d_I + d] * kr[d];
+      if (dot > 0.0) {
+        dw[j] += G[e] * dot;
+        for (int d = 0; d < c->d_I; ++d) dq[j * c->d_I + d] += G[e] * wi[j] * kr[d];
+      }
+    }
+  }
+  free(P);
+  free(z);
+  free(I);
+}
+
+int oracle_indexer_kl_f64(const double* q_idx, const double* k_idx, const double* w_idx,
+                          const double* q, const double* k, const int32_t* kv_len,
+                          const int32_t* idx, int B, int Tq, int Tk, int H_I, int d_I, int H,
+                          int Hkv, int Dqk, int kk, double sm_scale, double* loss,
+                          double* dq_idx, double* dw_idx, double* dk_idx, int nthreads) {
+  if (!q_idx || !k_idx || !w_idx || !q || !k || !loss || !dq_idx || !dw_idx || !dk_idx || B < 0 ||
+      Tq < 0 || Tk < 0 || H_I < 1 || d_I < 1 || H < 1 || Hkv < 1 || H % Hkv || Dqk < 1 ||
+      (idx && kk < 1))
+    return 1;
+  int64_t rows = (int64_t)B * Tq;
+  if (idx)
+    for (int64_t r = 0; r < rows * kk; ++r)
+      if (idx[r] >= Tk) return 2;
+  int width = idx ? kk : (Tk > 0 ? Tk : 1);
+  kl_ctx c = {q_idx, k_idx, w_idx, q, k, kv_len, idx, B, Tq, Tk, H_I, d_I, H, Hkv, Dqk, kk, width,
+              sm_scale, loss, dq_idx, dw_idx, NULL, NULL};
+  c.keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)(rows > 0 ? rows : 1) * width);
+  c.G = (double*)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * width);
+  for_rows(rows, nthreads, kl_row, &c);
+  /* key gradients: every row's contributions, rows in order */
+  for (int64_t x = 0; x < (int64_t)B * Tk * d_I; ++x) dk_idx[x] = 0.0;
+  for (int64_t row = 0; row < rows; ++row) {
+    int b = (int)(row / Tq);
+    const double* qi = q_idx + row * H_I * d_I;
+    const double* wi = w_idx + row * H_I;
+    for (int e = 0; e < width && c.keys[row * width + e] >= 0; ++e) {
+      int64_t s = c.keys[row * width + e];
+      const double* kr = k_idx + ((int64_t)b * Tk + s) * d_I;
+      double* dk = dk_idx + ((int64_t)b * Tk + s) * d_I;
+      for (int j = 0; j < H_I; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < d_I; ++d) dot += qi[j * d_I + d] * kr[d];
+        if (dot > 0.0)
+          for (int d = 0; d < d_I; ++d) dk[d] += c.G[row * width + e] * wi[j] * qi[j * d_I + d];
+      }
+    }
+  }
+  free(c.keys);
+  free(c.G);
+  return 0;
+}
+
+static double* decode_bf16_array(const uint16_t* x, int64_t n) {
+  double* y = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int64_t i = 0; i < n; ++i) y[i] = oracle_bf16_to_double(x[i]);
+  return y;
+}
+
+int oracle_indexer_kl(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w_idx,
+                      const uint16_t* q, const uint16_t* k, const int32_t* kv_len,
+                      const int32_t* idx, int B, int Tq, int Tk, int H_I, int d_I, int H, int Hkv,
+                      int Dqk, int kk, double sm_scale, double* loss, double* dq_idx,
+                      double* dw_idx, double* dk_idx, int nthreads) {
+  if (!q_idx || !k_idx || !w_idx || !q || !k || B < 0 || Tq < 0 || Tk < 0 || H_I < 1 || d_I < 1 ||
+      H < 1 || Hkv < 1 || Dqk < 1)
+    return 1;
+  int64_t rows = (int64_t)B * Tq;
+  double* a = decode_bf16_array(q_idx, rows * H_I * d_I);
+  double* bk = decode_bf16_array(k_idx, (int64_t)B * Tk * d_I);
+  double* w = decode_bf16_array(w_idx, rows * H_I);
+  double* qq = decode_bf16_array(q, rows * H * Dqk);
+  double* kk2 = decode_bf16_array(k, (int64_t)B * Tk * Hkv * Dqk);
+  int rc = oracle_indexer_kl_f64(a, bk, w, qq, kk2, kv_len, idx, B, Tq, Tk, H_I, d_I, H, Hkv, Dqk,
+                                 kk, sm_scale, loss, dq_idx, dw_idx, dk_idx, nthreads);
+  free(a);
+  free(bk);
+  free(w);
+  free(qq);
+  free(kk2);
+  return rc;
+}

@@ -35,6 +35,20 @@ int oracle_dsa_rows(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t
                     const uint16_t* q, const void* kv, const float* kv_scale, int kv_fmt,
                     const int32_t* rows, int nrows, int Tk, int H_I, int d_I, int H, int Dqk,
                     int Dv, int k, double sm_scale, int32_t* idx_out, double* out, int nthreads);
+/* Indexer KL objective (see dsa_oracle.c): q_idx [B][Tq][H_I][d_I], k_idx [B][Tk][d_I],
+ * w_idx [B][Tq][H_I], q [B][Tq][H][Dqk], k [B][Tk][Hkv][Dqk] (main attention keys), idx
+ * [B][Tq][kk] or NULL (every causal key) -> loss [B][Tq], dq_idx, dw_idx (shapes of the
+ * inputs) and dk_idx [B][Tk][d_I], all double.  The _f64 form takes doubles. */
+int oracle_indexer_kl_f64(const double* q_idx, const double* k_idx, const double* w_idx,
+                          const double* q, const double* k, const int32_t* kv_len,
+                          const int32_t* idx, int B, int Tq, int Tk, int H_I, int d_I, int H,
+                          int Hkv, int Dqk, int kk, double sm_scale, double* loss,
+                          double* dq_idx, double* dw_idx, double* dk_idx, int nthreads);
+int oracle_indexer_kl(const uint16_t* q_idx, const uint16_t* k_idx, const uint16_t* w_idx,
+                      const uint16_t* q, const uint16_t* k, const int32_t* kv_len,
+                      const int32_t* idx, int B, int Tq, int Tk, int H_I, int d_I, int H, int Hkv,
+                      int Dqk, int kk, double sm_scale, double* loss, double* dq_idx,
+                      double* dw_idx, double* dk_idx, int nthreads);
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,15 @@ MUTATIONS = {
                               "(i % 2 == 1) ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4);"),
     "mxfp4_scale_position": ("row[D / 2 + 4 * (j % 8) + j / 8];", "row[D / 2 + j];"),
     "mxfp4_row_stride": ("r * oracle_mxfp4_row_bytes(c->Dqk), c->Dqk, d);", "r * (c->Dqk / 2), c->Dqk, d);"),
+    "kl_gradient_sign": ("G[e] = exp(logQ) - P[e];", "G[e] = P[e] - exp(logQ);"),
+    "kl_target_head_sum": ("P[e] += exp(z[e] - m) / sum / c->H;", "P[e] += exp(z[e] - m) / sum;"),
+    "kl_relu_dropped": ("total += wi[j] * (dot > 0.0 ? dot : 0.0);", "total += wi[j] * dot;"),
+    "kl_dq_without_weight": ("dq[j * c->d_I + d] += G[e] * wi[j] * kr[d];", "dq[j * c->d_I + d] += G[e] * kr[d];"),
+    "kl_dk_from_key": ("dk[d] += c.G[row * width + e] * wi[j] * qi[j * d_I + d];",
+                       "dk[d] += c.G[row * width + e] * wi[j] * kr[d];"),
+    "kl_scale_dropped": ("z[e] = c->sm_scale * dot;", "z[e] = dot;"),
+    "kl_reverse_direction": ("if (P[e] > 0.0) L += P[e] * (log(P[e]) - logQ);",
+                             "L += exp(logQ) * (logQ - log(P[e]));"),
     "value_from_key_tail": ("if (!c->v) return kv_value(c, b, s, g, d);",
                             "if (!c->v) return kv_value(c, b, s, g, d + (c->Dqk - c->Dv));"),
 }

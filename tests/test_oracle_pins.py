@@ -514,3 +514,117 @@ def test_all_full_stack_equals_independent_layers():
         assert np.array_equal(ix, sets[l])
         o, _ = oracle.sparse_attn(layers[l]["q"], layers[l]["kv"], ix, w_.scale(), Dv=512)
         assert np.array_equal(o, outs[l])
+
+
+# ---------------------------------------------------------------- indexer KL objective
+
+
+def _kl_inputs(seed, B=2, Tq=3, Tk=9, H_I=2, d_I=4, H=2, Dqk=8, kk=5, margin=0.05):
+    """float64 inputs whose indexer dot products all stay at least `margin` away from the
+    ReLU's kink (so central differences are smooth)."""
+    rng = np.random.default_rng(seed)
+    while True:
+        qi = rng.standard_normal((B, Tq, H_I, d_I))
+        ki = rng.standard_normal((B, Tk, d_I))
+        if np.min(np.abs(np.einsum("btjd,bsd->btjs", qi, ki))) > margin:
+            break
+    wi = rng.standard_normal((B, Tq, H_I))
+    q = rng.standard_normal((B, Tq, H, Dqk))
+    k = rng.standard_normal((B, Tk, H, Dqk))
+    idx = np.full((B, Tq, kk), -1, np.int32)
+    for b in range(B):
+        for t in range(Tq):
+            n = int(rng.integers(1, kk + 1))
+            idx[b, t, :n] = rng.choice(Tk, size=n, replace=False)
+    return qi, ki, wi, q, k, idx
+
+
+def test_kl_is_zero_when_the_indexer_reproduces_the_target():
+    # one main head, indexer = one head with w = 1, k_I = K and q_I = sm_scale * q, all
+    # entries positive (the ReLU passes everything): I_s = z_s, so Q = P, the KL is 0 and so
+    # is every gradient
+    rng = np.random.default_rng(11)
+    B, Tq, Tk, D, scale = 1, 4, 10, 6, 0.3
+    q = rng.uniform(0.1, 1.0, (B, Tq, 1, D))
+    k = rng.uniform(0.1, 1.0, (B, Tk, 1, D))
+    idx = np.array([[[0, 3, 5, 9], [1, 2, -1, -1], [4, -1, 8, 7], [6, 0, 1, 2]]], np.int32)
+    loss, dq, dw, dk = oracle.indexer_kl(scale * q, k[:, :, 0], np.ones((B, Tq, 1)), q, k, scale, idx=idx)
+    assert np.max(np.abs(loss)) < 1e-14
+    assert max(np.max(np.abs(x)) for x in (dq, dw, dk)) < 1e-14
+    # and a different indexer gives a positive loss
+    loss2, *_ = oracle.indexer_kl(2 * scale * q, k[:, :, 0], np.ones((B, Tq, 1)), q, k, scale, idx=idx)
+    assert np.all(loss2[:, [0, 2, 3]] > 1e-6)
+
+
+def test_kl_two_keys_matches_the_bernoulli_closed_form():
+    # two keys, two main heads: P(key 0) = (sigmoid(a0) + sigmoid(a1)) / 2 with a_h the
+    # logit difference of head h; Q(key 0) = sigmoid(I_0 - I_1);
+    # KL = p log(p/r) + (1-p) log((1-p)/(1-r))
+    scale = 0.5
+    q = np.zeros((1, 1, 2, 2))
+    q[0, 0, 0] = [1.0, 0.0]
+    q[0, 0, 1] = [0.0, -2.0]
+    k = np.zeros((1, 2, 2, 2))
+    k[0, 0, :, :] = [[3.0, 1.0], [3.0, 1.0]]
+    k[0, 1, :, :] = [[1.0, 2.0], [1.0, 2.0]]
+    qi = np.array([[[[1.0, 0.5]]]])
+    ki = np.array([[[2.0, 1.0], [0.5, 3.0]]])
+    wi = np.array([[[0.7]]])
+    idx = np.array([[[1, 0]]], np.int32)
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    a0 = scale * (3.0 - 1.0)  # head 0: q . K0 - q . K1
+    a1 = scale * (-2.0 - (-4.0))
+    p = (sig(a0) + sig(a1)) / 2
+    r = sig(0.7 * (2.5 - 2.0))
+    want = p * math.log(p / r) + (1 - p) * math.log((1 - p) / (1 - r))
+    loss, dq, dw, dk = oracle.indexer_kl(qi, ki, wi, q, k, scale, idx=idx)
+    assert abs(loss[0, 0] - want) < 1e-14
+    # dL/dI_0 = r - p, so dw = (r - p) * (2.5 - 2.0)
+    assert abs(dw[0, 0, 0] - (r - p) * 0.5) < 1e-14
+
+
+def test_kl_gradients_match_central_differences():
+    qi, ki, wi, q, k, idx = _kl_inputs(3)
+    kv_len = np.array([9, 6], np.int32)
+    scale = 0.4
+    loss, dq, dw, dk = oracle.indexer_kl(qi, ki, wi, q, k, scale, idx=idx, kv_len=kv_len)
+    total = lambda a, b_, c: oracle.indexer_kl(a, b_, c, q, k, scale, idx=idx, kv_len=kv_len)[0].sum()
+    h = 1e-6
+    for name, x, g in (("q_idx", qi, dq), ("k_idx", ki, dk), ("w_idx", wi, dw)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args = {"q_idx": (xp, ki, wi), "k_idx": (qi, xp, wi), "w_idx": (qi, ki, xp)}[name]
+            argm = {"q_idx": (xm, ki, wi), "k_idx": (qi, xm, wi), "w_idx": (qi, ki, xm)}[name]
+            num[pos] = (total(*args) - total(*argm)) / (2 * h)
+        assert np.max(np.abs(num - g)) < 1e-7 * max(1.0, np.max(np.abs(g))), name
+    assert np.any(dk != 0) and np.all(loss >= 0)
+
+
+def test_kl_dense_warmup_equals_every_causal_key_selected():
+    qi, ki, wi, q, k, _ = _kl_inputs(4, B=2, Tq=4, Tk=7)
+    kv_len = np.array([7, 5], np.int32)
+    idx = np.full((2, 4, 7), -1, np.int32)
+    for b, L in enumerate(kv_len):
+        for t in range(4):
+            p = L - 4 + t
+            idx[b, t, :p + 1] = np.arange(p + 1)[::-1]  # any order
+    a = oracle.indexer_kl(qi, ki, wi, q, k, 0.3, idx=None, kv_len=kv_len)
+    b_ = oracle.indexer_kl(qi, ki, wi, q, k, 0.3, idx=idx, kv_len=kv_len)
+    for x, y in zip(a, b_):
+        assert np.max(np.abs(x - y)) < 1e-13
+
+
+def test_kl_row_without_keys_and_bf16_entry():
+    # a row that selects nothing contributes nothing; the bf16 entry equals the float64 one
+    # on the decoded values
+    qi, ki, wi, q, k, idx = _kl_inputs(5)
+    idx[1, 2, :] = -1
+    bf = [torch.from_numpy(x).to(torch.bfloat16) for x in (qi, ki, wi, q, k)]
+    a = oracle.indexer_kl(*bf, 0.25, idx=idx)
+    b_ = oracle.indexer_kl(*[x.double().numpy() for x in bf], 0.25, idx=idx)
+    for x, y in zip(a, b_):
+        assert np.array_equal(x, y)
+    assert a[0][1, 2] == 0.0 and np.all(a[1][1, 2] == 0.0) and np.all(a[2][1, 2] == 0.0)
