@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "layer_stack",
-    "index_scores_paged", "sparse_attn_paged", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
+    "index_scores_paged", "sparse_attn_paged", "indexer_kl", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
     "KV_BF16", "KV_FP8_E4M3", "KV_MXFP4", "mxfp4_row_bytes", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
     "OP_STACK", "OP_INDEX_TOPK",
@@ -100,9 +100,10 @@ def lib():
         L.dsa_stack_chunk_rows.restype = I
         L.dsa_check_pattern.argtypes = [ctypes.c_char_p, I, U]
         L.dsa_pattern_from_freq.argtypes = [I, I, ctypes.c_char_p]
+        L.dsa_indexer_kl.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, P]
         for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_layer_stack",
                   "dsa_check_pattern", "dsa_pattern_from_freq", "dsa_index_scores_paged", "dsa_sparse_attn_paged",
-                  "dsa_layer_stack_paged"):
+                  "dsa_layer_stack_paged", "dsa_indexer_kl"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -213,6 +214,27 @@ def _kv_dtype(kv, Dqk, kv_scale):
     if kv.shape[-1] != mxfp4_row_bytes(Dqk):
         raise ValueError("uint8 rows without kv_scale are MXFP4 and must be Dqk/2 + 32 bytes wide")
     return KV_MXFP4
+
+
+def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, grads=True, stream=None):
+    """dsa_indexer_kl: per-row KL(main attention || indexer) and, with grads, the gradients of
+    its sum for q_idx, w_idx and k_idx.  idx None: every causal key (dense warm-up).
+    Returns (loss fp32 [B,Tq], dq_idx, dw_idx, dk_idx) (gradients None without grads)."""
+    B, Tq, H_I, d_I = q_idx.shape
+    Tk = k_idx.shape[1]
+    H, Dqk = q.shape[2], q.shape[3]
+    kk = 0 if idx is None else idx.shape[2]
+    dev = q_idx.device
+    loss = torch.empty((B, Tq), dtype=torch.float32, device=dev)
+    dq = dw = dk = None
+    if grads:
+        dq = torch.empty((B, Tq, H_I, d_I), dtype=torch.float32, device=dev)
+        dw = torch.empty((B, Tq, H_I), dtype=torch.float32, device=dev)
+        dk = torch.empty((B, Tk, d_I), dtype=torch.float32, device=dev)
+    _check(lib().dsa_indexer_kl(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(idx), _ptr(kv_len),
+                                B, Tq, Tk, H_I, d_I, H, Dqk, kk, ctypes.c_float(sm_scale), _ptr(loss), _ptr(dq),
+                                _ptr(dw), _ptr(dk), _stream(stream)))
+    return loss, dq, dw, dk
 
 
 def _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, H_I=16, d_I=64, kv_len=None):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "index_topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "index_topk.hip", "attention.hip", "indexer_kl.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

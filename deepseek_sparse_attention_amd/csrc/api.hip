@@ -283,6 +283,30 @@ dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_id
   return run_index_topk(P, q_idx, k_idx, w_idx, s, oversample, idx, ws, as_stream(stream), "dsa_index_topk");
 }
 
+dsa_status dsa_indexer_kl(const void* q_idx, const void* k_idx, const void* w_idx, const void* q, const void* k,
+                          const int32_t* idx, const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I, int H,
+                          int Dqk, int kk, float sm_scale, float* loss, float* dq_idx, float* dw_idx, float* dk_idx,
+                          void* stream) {
+  if (B < 0 || Tq < 0 || Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
+  if (H_I < 1 || d_I < 1 || H < 1 || Dqk < 1) return fail(DSA_ERR_SHAPE, "H_I, d_I, H and Dqk must be >= 1");
+  if (idx && kk < 1) return fail(DSA_ERR_SHAPE, "kk must be >= 1 when idx is given");
+  if (!isfinite(sm_scale)) return fail(DSA_ERR_SHAPE, "sm_scale must be finite");
+  if (!dsa::indexer_kl_supported(H_I, d_I, H, H, Dqk))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer KL supports H_I <= 16, d_I in {16,32,64,128}, H <= 16, Dqk = 32");
+  if (idx ? kk > dsa::kKlMaxKeys : Tk > dsa::kKlMaxKeys)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer KL takes at most 4096 keys per row (kk, or Tk without idx)");
+  if ((int64_t)B * Tq == 0 && !(dk_idx && (int64_t)B * Tk > 0)) return DSA_OK;
+  if (!q_idx || !k_idx || !w_idx || !q || !k || !loss)
+    return fail(DSA_ERR_NULL, "q_idx, k_idx, w_idx, q, k and loss are required");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(w_idx, 2) ||
+      !aligned(idx, 4) || !aligned(loss, 4) || !aligned(dq_idx, 4) || !aligned(dw_idx, 4) || !aligned(dk_idx, 4))
+    return fail(DSA_ERR_UNSUPPORTED, "q_idx, k_idx, q and k must be 16-byte aligned; w_idx 2-byte; idx and outputs 4");
+  dsa::IndexerKlArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, (const uint16_t*)q,
+                       (const uint16_t*)k, idx, kv_len, B, Tq, Tk, H_I, d_I, H, idx ? kk : 0, sm_scale, loss,
+                       dq_idx, dw_idx, dk_idx};
+  return launch_status(dsa::launch_indexer_kl(a, as_stream(stream)), "dsa_indexer_kl");
+}
+
 dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w_idx, const dsa_paged_kv* pages,
                                   const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I, float* scores,
                                   int64_t ld, void* stream) {

@@ -78,6 +78,20 @@ FusedLayout fused_layout(int B, int nrows, int Tk);
 bool index_topk_fused_supported(int H_I, int d_I, int k);
 hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t st);
 
+// Indexer KL objective (multi-head main attention): one row of the loss and the gradients
+// of the indexer inputs.  idx == nullptr: every causal key (dense warm-up).  dq, dw, dk
+// may each be null (not computed); dk is cleared and then accumulated.
+struct IndexerKlArgs {
+  const uint16_t *q_idx, *k_idx, *w_idx, *q, *k;
+  const int32_t *idx, *kv_len;
+  int B, Tq, Tk, H_I, d_I, H, kk;
+  float sm_scale;
+  float *loss, *dq, *dw, *dk;
+};
+constexpr int kKlMaxKeys = 4096;  // key entries per row
+bool indexer_kl_supported(int H_I, int d_I, int H, int Hkv, int Dqk);
+hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st);
+
 struct AttnArgs {
   const uint16_t* q;
   const void* kv;

@@ -181,6 +181,33 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Indexer training objective: the indexer is trained with a KL loss against the detached
+ * main attention distribution, dense attention first ("DSA ablation model card", model list).
+ * The card gives no formula; per query row t (position p) with key set S (the valid entries
+ * of idx[b][t]; every key 0..p when idx is NULL, the dense warm-up):
+ *   P_s = (1/H) sum_h softmax_{s in S}(sm_scale * q[h] . k[s][h])     target, held fixed
+ *   Q_s = softmax_{s in S}(I_s), I_s the indexer score of dsa_index_scores
+ *   loss[b][t] = sum_s P_s (ln P_s - ln Q_s)
+ * and the gradients of sum(loss) with respect to the indexer inputs (ReLU'(0) = 0).
+ *   q_idx, k_idx, w_idx  bf16, as in dsa_index_scores
+ *   q     bf16 [B][Tq][H][Dqk], k bf16 [B][Tk][H][Dqk]: the main attention's queries and
+ *         keys (multi-head form, Dqk = 32)
+ *   idx   int32 [B][Tq][kk] (entries outside [0, Tk) skipped; a duplicate counts twice), or
+ *         NULL (kk ignored)
+ *   loss  fp32 [B][Tq] (0 for a row with no key)
+ *   dq_idx fp32 [B][Tq][H_I][d_I], dw_idx fp32 [B][Tq][H_I], dk_idx fp32 [B][Tk][d_I]: each
+ *         may be NULL (not computed).  dk_idx is overwritten: cleared, then accumulated with
+ *         fp32 atomics, so rows that share a key add in no fixed order and dk_idx can differ
+ *         between runs in the last bits; loss, dq_idx and dw_idx are deterministic.
+ * Supported: 1 <= H_I <= 16, d_I in {16, 32, 64, 128}, 1 <= H <= 16, Dqk = 32; at most 4096
+ * keys per row (kk <= 4096, or Tk <= 4096 without idx).
+ */
+dsa_status dsa_indexer_kl(const void* q_idx, const void* k_idx, const void* w_idx, const void* q,
+                          const void* k, const int32_t* idx, const int32_t* kv_len, int B, int Tq,
+                          int Tk, int H_I, int d_I, int H, int Dqk, int kk, float sm_scale,
+                          float* loss, float* dq_idx, float* dw_idx, float* dk_idx, void* stream);
+
+/*
  * Paged caches, for serving batches (the pages serve many sequences at once through vLLM
  * with an fp8 KV cache, "DeepSeek-V2-Lite-Chat SIQ K4/K3" card, "How to run"; they do not
  * describe a page layout, so this one is the library's): token s of sequence b is row

@@ -199,6 +199,27 @@ def test_index_topk_workspace_follows_the_route(L):
     assert st >= fused and st >= 4096 * 65536 * 4
 
 
+def test_indexer_kl_argument_checks(L):
+    P = ctypes.c_void_p(16)
+    f = ctypes.c_float
+    kl = lambda *a: L.dsa_indexer_kl(*a)
+    # MLA-width main attention: unsupported
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 16, 576, 4, f(0.04), P, None, None, None, None) == 3
+    # indexer width outside {16,32,64,128}
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 24, 4, 32, 4, f(0.1), P, None, None, None, None) == 3
+    # too many keys per row: kk > 4096, or the dense warm-up with Tk > 4096
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 4097, f(0.1), P, None, None, None, None) == 3
+    assert kl(P, P, P, P, P, None, None, 1, 4, 5000, 2, 16, 4, 32, 0, f(0.1), P, None, None, None, None) == 3
+    # missing loss / inputs; kk < 1 with idx
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 4, f(0.1), None, None, None, None, None) == 1
+    assert kl(None, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 4, f(0.1), P, None, None, None, None) == 1
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 0, f(0.1), P, None, None, None, None) == 2
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 4, f(float("nan")), P, None, None, None, None) == 2
+    # empty batch without key gradients: nothing to do
+    assert kl(None, None, None, None, None, None, None, 0, 4, 8, 2, 16, 4, 32, 4, f(0.1), None, None, None, None,
+              None) == 0
+
+
 def test_paged_argument_checks(L):
     P = ctypes.c_void_p(16)
     f = ctypes.c_float
