@@ -24,6 +24,7 @@ import time
 METRIC = "query tokens/sec through indexer+top-k+sparse attn, T=65536 k=2048; decode tok/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3  # published fp32 vector peak (packed FMA)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -196,6 +197,7 @@ def parse():
     ap.add_argument("--T", type=int, default=65536, help="prefill length (default: the named workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-kl", action="store_true", help="skip the indexer KL objective timings")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference dispatch for HBM counters)")
@@ -473,6 +475,32 @@ def main():
                                           "mxfp4": attn_layer(ml[1], None, dsa.mxfp4_row_bytes(e.Dqk))}
         log(f"decode attention, one layer: {result['decode']['attn_layer']}")
         del kc, dl, ml, mws
+
+    # ---- indexer KL objective on the ablation card's shape (indexer 2x16, four 32-wide
+    # heads, T=3072): top-512 sparse rows and the dense warm-up over every causal key
+    if not args.no_kl:
+        a = synth.workload("A")
+        la = synth.layer_inputs(a, indexer=True, device=dev)
+        sa = dsa.index_scores(la["q_idx"], la["k_idx"], la["w_idx"])
+        ia = dsa.topk(sa, a.k)
+        del sa
+        kin = [la[x] for x in ("q_idx", "k_idx", "w_idx", "q", "kv")]
+        sparse_ms = timed(lambda: dsa.indexer_kl(*kin, a.scale(), idx=ia))
+        dense_ms = timed(lambda: dsa.indexer_kl(*kin, a.scale()))
+        pairs_sparse = sum(min(t + 1, a.k) for t in range(a.T))
+        pairs_dense = a.T * (a.T + 1) // 2
+        # fp32 flops per (row, key) pair: main logits twice (2 * H * 32 * 2), indexer dots
+        # twice (2 * H_I * d_I * 2), then the dq and dk products (2 * H_I * d_I * 2)
+        per_pair = 2 * a.H * a.Dqk * 2 + 4 * a.H_I * a.d_I * 2
+        def kl_entry(ms, pairs):
+            tf = per_pair * pairs / (ms * 1e-3) / 1e12
+            return {"ms": round(ms, 4), "pairs": pairs, "gpairs_per_s": round(pairs / (ms * 1e-3) / 1e9, 2),
+                    "tflops_fp32": round(tf, 2), "frac_fp32_valu": round(tf / FP32_VALU_PEAK_TFLOPS, 4)}
+        result["indexer_kl"] = {"workload": a.name, "flops_per_pair": per_pair,
+                                "sparse_top512": kl_entry(sparse_ms, pairs_sparse),
+                                "dense_warmup": kl_entry(dense_ms, pairs_dense)}
+        log(f"indexer KL: {result['indexer_kl']}")
+        del la, ia, kin
 
     # ---- CPU oracle on a bounded, evenly spread sample of the same prefill rows
     if not args.no_cpu_baseline:

@@ -14,10 +14,10 @@
 // for the indexer, each thread folds entries e, e+256, ... into an online (max, sum) in
 // base 2 and the workgroup merges them.  Pass 2: recompute the logits, form P, Q, the loss and G, with G kept in
 // LDS.  Pass 3, per chunk of 256 entries: a thread per entry stages its indexer key row in
-// LDS, forms c_js = G_s w_j [d_js > 0], adds its dw share and its dk row (fp32 atomics:
-// rows that share a key add in no fixed order), then threads own (head, dim) pairs of dq
-// and sum c_js k_s over the chunk from LDS (dw likewise, one thread per head, in entry
-// order: loss, dq and dw are deterministic).  Main-attention keys are re-read in pass 2
+// LDS and forms c_js = G_s w_j [d_js > 0] and G_s ReLU(d_js); then threads own (head, dim)
+// pairs of dq and sum c_js k_s over the chunk from LDS (dw likewise, one thread per head,
+// in entry order: loss, dq and dw are deterministic), and (entry, dim) pairs add the dk
+// rows with fp32 atomics (rows that share a key add in no fixed order).  Main-attention keys are re-read in pass 2
 // rather than kept: at 32 values per head they come back from L2.
 #include "common.hpp"
 #include "internal.hpp"
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t kchunk[kKlThreads][D_I];  // indexer key rows of a chunk
   __shared__ float cbuf[kKlHeads][kKlThreads];   // G w_j [d_j > 0] of a chunk's entries
   __shared__ float rbuf[kKlHeads][kKlThreads];   // G ReLU(d_j) of a chunk's entries
+  __shared__ int ckey[kKlThreads];               // a chunk entry's key, -1 if it adds nothing to dk
   __shared__ float red[4][kKlHeads + 1][2];      // cross-wave (m, l) / sums
   __shared__ float lse2[kKlHeads + 1];           // base-2 log-sum-exp per head; [H]: indexer
 
@@ -214,15 +215,9 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
         rbuf[j][tid] = r;
         any |= c != 0.f;
       }
-      if (dk && any) {
-        float* dkr = dk + ((int64_t)b * Tk + s) * D_I;
-        for (int d = 0; d < D_I; ++d) {
-          float acc = 0.f;
-          for (int j = 0; j < H_I; ++j) acc = fmaf(cbuf[j][tid], qif[j][d], acc);
-          unsafeAtomicAdd(dkr + d, acc);
-        }
-      }
+      ckey[tid] = any ? s : -1;
     } else {
+      ckey[tid] = -1;
       for (int j = 0; j < kKlHeads; ++j) cbuf[j][tid] = 0.f, rbuf[j][tid] = 0.f;
 #pragma unroll
       for (int c = 0; c < D_I / 8; ++c) *reinterpret_cast<u32x4*>(&kchunk[tid][c * 8]) = u32x4{0u, 0u, 0u, 0u};
@@ -243,6 +238,18 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
     }
     if (dw && tid < H_I)
       for (int t = 0; t < cn; ++t) dw_acc += rbuf[tid][t];
+    if (dk) {
+      // (entry, dim) pairs: consecutive lanes add consecutive dims of one key row, so an
+      // atomic instruction covers 64 / D_I rows instead of 64
+      for (int x = tid; x < cn * D_I; x += kKlThreads) {
+        const int t = x / D_I, d = x % D_I;
+        const int key = ckey[t];
+        if (key < 0) continue;
+        float acc = 0.f;
+        for (int j = 0; j < H_I; ++j) acc = fmaf(cbuf[j][t], qif[j][d], acc);
+        unsafeAtomicAdd(dk + ((int64_t)b * Tk + key) * D_I + d, acc);
+      }
+    }
     __syncthreads();  // the chunk buffers are refilled
   }
   if (dq) {
