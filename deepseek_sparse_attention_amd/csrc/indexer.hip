@@ -11,12 +11,15 @@ namespace {
 
 // PAGED: key s of sequence b sits in row bt[b*max_blocks + s/P]*P + s%P of a shared pool of
 // pool_tokens rows (P = 1 << page_shift, a multiple of 32, so no 32-key tile crosses a page).
+// wave_keys > 0 (launches with no more rows than one wave holds, e.g. decode): the four
+// waves share the same rows and split the workgroup's key segment, wave w taking keys
+// [w * wave_keys, (w + 1) * wave_keys) of it, so every wave streams keys.
 template <int H_I, int D_I, bool PAGED>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0, int nrows, float* __restrict__ scores,
-    int64_t ld, int64_t score_bstride, int key_seg, const int32_t* __restrict__ bt, int max_blocks, int page_shift,
-    int64_t pool_tokens) {
+    int64_t ld, int64_t score_bstride, int key_seg, int wave_keys, const int32_t* __restrict__ bt, int max_blocks,
+    int page_shift, int64_t pool_tokens) {
   using W = IdxWave<H_I, D_I, idx_query_tiles<H_I, D_I>()>;
   constexpr int QB = 4 * W::ROWS;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
@@ -24,13 +27,14 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   const int b = blockIdx.z;
   const int64_t L = seq_len(kv_len, b, Tk);
   const int64_t pos_base = L - Tq + row0;  // position of chunk row r is pos_base + r
-  const int wrow0 = blockIdx.x * QB + wave * W::ROWS;
+  const bool wsplit = wave_keys > 0;
+  const int wrow0 = wsplit ? blockIdx.x * W::ROWS : blockIdx.x * QB + wave * W::ROWS;
   if (wrow0 >= nrows) return;
   const int wrows = min(W::ROWS, nrows - wrow0);
   const int64_t pmax = pos_base + wrow0 + wrows - 1;  // last position of this wave
-  const int64_t seg0 = (int64_t)blockIdx.y * key_seg;
+  const int64_t seg0 = (int64_t)blockIdx.y * key_seg + (wsplit ? (int64_t)wave * wave_keys : 0);
   if (pmax < 0 || seg0 > pmax) return;
-  const int64_t seg_end = min((int64_t)min((int64_t)Tk, seg0 + key_seg), pmax + 1);
+  const int64_t seg_end = min((int64_t)min((int64_t)Tk, seg0 + (wsplit ? wave_keys : key_seg)), pmax + 1);
 
   W wv;
   wv.load(q + ((int64_t)b * Tq + row0 + wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + wrow0) * H_I, wrows);
@@ -74,29 +78,33 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
 template <int H_I, int D_I>
 hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   const bool paged = A.block_table != nullptr;
-  constexpr int QB = 4 * idx_query_tiles<H_I, D_I>() * (32 / H_I);
-  const int qblocks = (A.nrows + QB - 1) / QB;
+  constexpr int ROWS = idx_query_tiles<H_I, D_I>() * (32 / H_I);  // query rows per wave
+  constexpr int QB = 4 * ROWS;
+  const bool wsplit = A.nrows <= ROWS;  // one wave's rows: the waves split keys instead
+  const int qblocks = wsplit ? 1 : (A.nrows + QB - 1) / QB;
   // keys any row of the chunk can see (kv_len <= Tk)
   const int64_t maxkeys = std::min<int64_t>(A.Tk, (int64_t)A.Tk - A.Tq + A.row0 + A.nrows);
   if (qblocks == 0 || maxkeys <= 0) return hipSuccess;
   const int64_t tiles = (maxkeys + 31) / 32;
   // Aim at ~2048 workgroups per launch when query blocks are full (prefill chunks): twice
   // what the chip holds at once, with segments short enough that the causal tail of a launch
-  // stays small.  Few-row launches (decode: one busy wave per workgroup) keep ~1024, which
-  // streams the key cache faster there.
+  // stays small.  Few-row launches keep ~1024 workgroups; with the waves splitting keys
+  // (one wave's rows) a segment is a multiple of four tiles.
   const int64_t target = A.nrows >= 8 * QB ? 2048 : 1024;
   int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, target / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
   int64_t seg_tiles = (tiles + segs - 1) / segs;
+  if (wsplit) seg_tiles = (seg_tiles + 3) / 4 * 4;
   segs = (tiles + seg_tiles - 1) / seg_tiles;
+  const int wave_keys = wsplit ? (int)(seg_tiles / 4 * 32) : 0;
   dim3 grid(qblocks, (unsigned)segs, A.B);
   if (paged)
     hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, true>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
-                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), A.block_table,
-                       A.max_blocks, A.page_shift, A.pool_tokens);
+                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys,
+                       A.block_table, A.max_blocks, A.page_shift, A.pool_tokens);
   else
     hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, false>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
-                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), nullptr, 0, 0,
-                       (int64_t)0);
+                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys,
+                       nullptr, 0, 0, (int64_t)0);
   return hipGetLastError();
 }
 
