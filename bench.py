@@ -40,7 +40,7 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        attn = [float(r["Counter_Value"]) for r in rows if "mla_attn_kernel<false>" in r["Kernel_Name"]]
+        attn = [float(r["Counter_Value"]) for r in rows if "mla_attn_kernel<0>" in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
                 or "copy_kernel" in r["Kernel_Name"]]
         return attn, copy
@@ -56,9 +56,9 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
         "# HBM traffic of mla_attn_kernel<bf16> (T=65536, k=2048, 16 heads, 576/512) per launch",
         "# made by:",
         "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch_D -o fetch -- "
-        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --copy-calibration",
+        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write_D -o write -- "
-        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --copy-calibration",
+        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl --copy-calibration",
         "#   python3 bench.py --summarize-traffic <fetch csv> <write csv>",
         f"attn_dispatches: {len(fa)}",
         f"fetch_kib_per_launch: {sum(fa) / len(fa):.1f}",
@@ -89,8 +89,9 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
     ours = [r for r in rows if "dsa::" in r["Name"]]
     ours.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = [
-        "# rocprofv3 kernel-trace summary: one T=65536, k=2048 DSA layer (workload mla_t65536_k2048_sink)",
-        "# plus the 64 x 65536 fp8 decode step (FSS over 3 layers), on one MI355X",
+        "# rocprofv3 kernel-trace summary: one T=65536, k=2048 DSA layer (workload mla_t65536_k2048_sink),",
+        "# the 64 x 65536 decode step (FSS over 3 layers; fp8, paged fp8 and MXFP4 latent caches) and",
+        "# the indexer KL objective on the ablation shape (T=3072, top-512 and dense), on one MI355X",
         "# command (from the repository root):",
         "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_D -o trace -- "
         "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
@@ -98,7 +99,8 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# calls: 1 warmup + 3 timed layer_stack steps (fused index/top-k: fz_sample, fz_threshold,",
         "# fz_filter, fz_select, fz_exact once each, then attention), 3 event-timed launches of each",
         "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
-        "# unfused step), then the decode steps.",
+        "# unfused step), then the decode steps and their per-layer attention launches, then the KL",
+        "# objective (sparse and dense, with gradients).  mla_attn_kernel<0|1|2>: bf16 | fp8 | MXFP4 rows.",
         "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel",
         "",
     ]
