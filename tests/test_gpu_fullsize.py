@@ -1,0 +1,82 @@
+"""GPU parity at the full workload sizes, in the configuration the bench times.
+
+The prefill layer (T=65536, k=2048, indexer 16x64, 16 MLA heads, sink keys) runs through
+dsa_layer_stack("F") exactly as the bench's step (the fused indexer -> top-k route), and
+the 64 x 65536 decode step (FSS over 3 layers, fp8 or MXFP4 latent caches) as the bench's
+decode step.  The oracle cannot redo a whole layer in seconds, so outputs are checked on
+sampled rows it computes one by one:
+  * indices: the oracle's top-k over the GPU's own scores of the sampled rows, bit for bit
+    (scores from dsa_index_scores with each sampled row as its own sequence of length t+1);
+  * attention: the oracle's attention over those indices, within 2e-2 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+dsa = pytest.importorskip("deepseek_sparse_attention_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host(x):
+    return x.detach().cpu()
+
+
+def test_prefill_t65536_sampled_rows():
+    print("full-size prefill T=65536 (fused route), sampled rows", flush=True)
+    w = synth.workload("D")
+    T, k = w.T, w.k
+    layer = synth.layer_inputs(w, 0, device=DEV)
+    idx_cache = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    outs, _, cache = dsa.layer_stack("F", [layer], k, w.scale(), Dv=w.Dv, index_cache=idx_cache)
+    torch.cuda.synchronize()
+    rows = np.array([0, 63, 64, 1000, 2046, 2047, 2048, 2049, 4095, 9001, 20000, 33333, 47000, 60001, 65534, 65535])
+    n = len(rows)
+    # the GPU's scores of the sampled rows: each row its own sequence of length t+1
+    q_i = layer["q_idx"][0, rows].unsqueeze(1).contiguous()
+    w_i = layer["w_idx"][0, rows].unsqueeze(1).contiguous()
+    k_i = layer["k_idx"].expand(n, T, w.d_I).contiguous()
+    kl = torch.tensor(rows + 1, dtype=torch.int32, device=DEV)
+    s = dsa.index_scores(q_i, k_i, w_i, kv_len=kl)
+    ref_idx = oracle.topk(_host(s).numpy(), k, kv_len=rows + 1, Tk=T)[:, 0]
+    got_idx = _host(cache[0, rows]).numpy()
+    assert np.array_equal(got_idx, ref_idx)
+    # attention of the sampled rows over those indices
+    q = _host(layer["q"][0, rows]).unsqueeze(1)                     # [n, 1, H, 576]
+    kv = _host(layer["kv"])                                         # [1, T, 1, 576]
+    ref, _ = oracle.sparse_attn(q.reshape(1, n, w.H, w.Dqk), kv, ref_idx.reshape(1, n, k), w.scale(), Dv=w.Dv)
+    got = _host(outs[0][0, rows]).double().numpy()
+    assert np.max(np.abs(got - ref[0])) <= 2e-2
+
+
+@pytest.mark.parametrize("kv_format", ["fp8", "mxfp4"])
+def test_decode_b64_l65536_fss(kv_format):
+    print(f"full-size decode 64 x 65536 FSS ({kv_format})", flush=True)
+    e = synth.workload("E")
+    kc = synth.decode_indexer_cache(e, device=DEV)
+    layers = []
+    for l in range(3):
+        d = synth.decode_layer_inputs(e, l, device=DEV, kv_format=kv_format)
+        if "q_idx" in d:
+            d["k_idx"] = kc
+        layers.append(d)
+    klen = torch.full((e.B,), e.T, dtype=torch.int32, device=DEV)
+    outs, _, cache = dsa.layer_stack(e.pattern, layers, e.k, e.scale(), Dv=e.Dv, kv_len=klen)
+    torch.cuda.synchronize()
+    # indices of every sequence: the oracle's top-k over the GPU's scores of the F layer
+    s = dsa.index_scores(layers[0]["q_idx"], kc, layers[0]["w_idx"], kv_len=klen)
+    ref_idx = oracle.topk(_host(s).numpy(), e.k, kv_len=[e.T] * e.B, Tk=e.T)
+    assert np.array_equal(_host(cache).numpy(), ref_idx)
+    # attention of sampled sequences in every layer (S layers reuse the F layer's indices)
+    for b in (0, 17, 63):
+        for l in range(3):
+            L = layers[l]
+            sc = None if "kv_scale" not in L else _host(L["kv_scale"][b:b + 1])
+            ref, _ = oracle.sparse_attn(_host(L["q"][b:b + 1]), _host(L["kv"][b:b + 1]), ref_idx[b:b + 1], e.scale(),
+                                        kv_scale=sc, Dv=e.Dv)
+            got = _host(outs[l][b:b + 1]).double().numpy()
+            assert np.max(np.abs(got - ref)) <= 2e-2, (b, l)
