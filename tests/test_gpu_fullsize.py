@@ -3,7 +3,8 @@
 The prefill layer (T=65536, k=2048, indexer 16x64, 16 MLA heads, sink keys) runs through
 dsa_layer_stack("F") exactly as the bench's step (the fused indexer -> top-k route), and
 the 64 x 65536 decode step (FSS over 3 layers, fp8 or MXFP4 latent caches) as the bench's
-decode step.  The oracle cannot redo a whole layer in seconds, so outputs are checked on
+decode step; the other workloads (the T=3072 multi-head ablation layer, the T=2057 MLA
+layer, the 27-layer FSS x 9 stack at T=16384) at their full sizes too.  The oracle cannot redo a whole layer in seconds, so outputs are checked on
 sampled rows it computes one by one:
   * indices: the oracle's top-k over the GPU's own scores of the sampled rows, bit for bit
     (scores from dsa_index_scores with each sampled row as its own sequence of length t+1);
@@ -80,3 +81,64 @@ def test_decode_b64_l65536_fss(kv_format):
                                         kv_scale=sc, Dv=e.Dv)
             got = _host(outs[l][b:b + 1]).double().numpy()
             assert np.max(np.abs(got - ref)) <= 2e-2, (b, l)
+
+
+def test_ablation_t3072_every_row():
+    # the multi-head ablation layer (indexer 2x16, four 32-wide heads, top-512 of 3072):
+    # small enough for the oracle to check every row
+    print("full-size ablation layer T=3072 (every row)", flush=True)
+    w = synth.workload("A")
+    layer = synth.layer_inputs(w, 0, device=DEV)
+    outs, _, cache = dsa.layer_stack("F", [layer], w.k, w.scale())
+    torch.cuda.synchronize()
+    s = dsa.index_scores(layer["q_idx"], layer["k_idx"], layer["w_idx"])
+    ref_idx = oracle.topk(_host(s).numpy(), w.k, Tk=w.T)
+    assert np.array_equal(_host(cache).numpy(), ref_idx)
+    ref, _ = oracle.sparse_attn(_host(layer["q"]), _host(layer["kv"]), ref_idx, w.scale(), v=_host(layer["v"]))
+    assert np.max(np.abs(_host(outs[0]).double().numpy() - ref)) <= 2e-2
+
+
+def _sampled_layer_check(layer, outs_l, idx_rows, rows, w):
+    q = _host(layer["q"][0, rows]).reshape(1, len(rows), w.H, w.Dqk)
+    ref, _ = oracle.sparse_attn(q, _host(layer["kv"]), idx_rows.reshape(1, len(rows), w.k), w.scale(), Dv=w.Dv)
+    got = _host(outs_l[0, rows]).double().numpy()
+    assert np.max(np.abs(got - ref[0])) <= 2e-2
+
+
+def _gpu_topk_rows(layer, rows, w):
+    n = len(rows)
+    q_i = layer["q_idx"][0, rows].unsqueeze(1).contiguous()
+    w_i = layer["w_idx"][0, rows].unsqueeze(1).contiguous()
+    k_i = layer["k_idx"].expand(n, w.T, w.d_I).contiguous()
+    s = dsa.index_scores(q_i, k_i, w_i, kv_len=torch.tensor(rows + 1, dtype=torch.int32, device=DEV))
+    return oracle.topk(_host(s).numpy(), w.k, kv_len=rows + 1, Tk=w.T)[:, 0]
+
+
+def test_mla_t2057_sampled_rows():
+    # T just past k: only rows t >= 2048 are truly sparse
+    print("full-size MLA layer T=2057, sampled rows", flush=True)
+    w = synth.workload("B")
+    layer = synth.layer_inputs(w, 0, device=DEV)
+    outs, _, cache = dsa.layer_stack("F", [layer], w.k, w.scale(), Dv=w.Dv)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 511, 1500, 2046, 2047, 2048, 2050, 2055, 2056])
+    ref_idx = _gpu_topk_rows(layer, rows, w)
+    assert np.array_equal(_host(cache[0, rows]).numpy(), ref_idx)
+    _sampled_layer_check(layer, outs[0], ref_idx, rows, w)
+
+
+def test_stack27_fss_t16384_sampled_rows():
+    # 27 layers, FSS x 9: every F layer's indices on sampled rows, and every layer's outputs
+    # there with the indices of the F layer it follows
+    print("full-size 27-layer FSS stack T=16384, sampled rows", flush=True)
+    w = synth.workload("C")
+    layers = [synth.layer_inputs(w, l, device=DEV) for l in range(len(w.pattern))]
+    outs, _, cache = dsa.layer_stack(w.pattern, layers, w.k, w.scale(), Dv=w.Dv)
+    torch.cuda.synchronize()
+    rows = np.array([5, 2047, 2048, 8191, 12345, 16383])
+    idx = None
+    for l, c in enumerate(w.pattern):
+        if c == "F":
+            idx = _gpu_topk_rows(layers[l], rows, w)
+        _sampled_layer_check(layers[l], outs[l], idx, rows, w)
+    assert np.array_equal(_host(cache[0, rows]).numpy(), idx)  # the last F layer's
