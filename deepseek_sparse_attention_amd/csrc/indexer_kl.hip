@@ -14,10 +14,10 @@
 // for the indexer, each thread folds entries e, e+256, ... into an online (max, sum) in
 // base 2 and the workgroup merges them.  Pass 2: recompute the logits, form P, Q, the loss and G, with G kept in
 // LDS.  Pass 3, per chunk of 256 entries: a thread per entry stages its indexer key row in
-// LDS and forms c_js = G_s w_j [d_js > 0] and G_s ReLU(d_js); then threads own (head, dim)
-// pairs of dq and sum c_js k_s over the chunk from LDS (dw likewise, one thread per head,
-// in entry order: loss, dq and dw are deterministic), and (entry, dim) pairs add the dk
-// rows with fp32 atomics (rows that share a key add in no fixed order).  Main-attention keys are re-read in pass 2
+// LDS, forms c_js = G_s w_j [d_js > 0] and keeps its share of dw; then threads own (head,
+// dim) pairs of dq (or slices of them) and sum c_js k_s over the chunk from LDS, and
+// (entry, dim) pairs add the dk rows with fp32 atomics (rows that share a key add in no
+// fixed order; every other sum runs in a fixed order: loss, dq and dw are deterministic).  Main-attention keys are re-read in pass 2
 // rather than kept: at 32 values per head they come back from L2.
 #include "common.hpp"
 #include "internal.hpp"
@@ -54,22 +54,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int D_I>
+// NH: heads (main and indexer) the instance holds, MAXK: key entries per row; LDS is sized
+// by both, so small shapes (the ablation: 4 + 2 heads, 512 keys) fit several workgroups
+// per CU.
+template <int D_I, int NH, int MAXK>
 __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w_idx,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int H_I, int H, int kk, float scale_log2,
     float* __restrict__ loss, float* __restrict__ dq, float* __restrict__ dw, float* __restrict__ dk) {
-  __shared__ float qf[kKlHeads][kKlD];           // main query, per head
-  __shared__ float qif[kKlHeads][D_I];           // indexer query, per head
-  __shared__ float wf[kKlHeads];
-  __shared__ float gbuf[kKlMaxKeys];             // I, then G, per entry
+  __shared__ float qf[NH][kKlD];           // main query, per head
+  __shared__ float qif[NH][D_I];           // indexer query, per head
+  __shared__ float wf[NH];
+  __shared__ float gbuf[MAXK];             // I, then G, per entry
   __shared__ __attribute__((aligned(16))) uint16_t kchunk[kKlThreads][D_I];  // indexer key rows of a chunk
-  __shared__ float cbuf[kKlHeads][kKlThreads];   // G w_j [d_j > 0] of a chunk's entries
-  __shared__ float rbuf[kKlHeads][kKlThreads];   // G ReLU(d_j) of a chunk's entries
+  __shared__ float cbuf[NH][kKlThreads];   // G w_j [d_j > 0] of a chunk's entries
   __shared__ int ckey[kKlThreads];               // a chunk entry's key, -1 if it adds nothing to dk
-  __shared__ float red[4][kKlHeads + 1][2];      // cross-wave (m, l) / sums
-  __shared__ float lse2[kKlHeads + 1];           // base-2 log-sum-exp per head; [H]: indexer
+  __shared__ float red[4][NH + 1][2];      // cross-wave (m, l) / sums
+  __shared__ float lse2[NH + 1];           // base-2 log-sum-exp per head; [H]: indexer
+  // small instances keep pass 1's logits for pass 2 instead of re-reading the keys
+  constexpr bool kKeepZ = NH * MAXK <= 4096;
+  __shared__ float zbuf[kKeepZ ? NH : 1][kKeepZ ? MAXK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int64_t row = blockIdx.x;
@@ -79,15 +84,15 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
   const bool dense = idx == nullptr;
   const int n = dense ? (int)max<int64_t>(0, min<int64_t>(p + 1, Tk)) : kk;
 
-  for (int x = tid; x < kKlHeads * kKlD; x += kKlThreads) {
+  for (int x = tid; x < NH * kKlD; x += kKlThreads) {
     const int h = x / kKlD, d = x % kKlD;
     qf[h][d] = h < H ? bf16_bits_to_f32(q[(row * H + h) * kKlD + d]) : 0.f;
   }
-  for (int x = tid; x < kKlHeads * D_I; x += kKlThreads) {
+  for (int x = tid; x < NH * D_I; x += kKlThreads) {
     const int j = x / D_I, d = x % D_I;
     qif[j][d] = j < H_I ? bf16_bits_to_f32(q_idx[(row * H_I + j) * D_I + d]) : 0.f;
   }
-  if (tid < kKlHeads) wf[tid] = tid < H_I ? bf16_bits_to_f32(w_idx[row * H_I + tid]) : 0.f;
+  if (tid < NH) wf[tid] = tid < H_I ? bf16_bits_to_f32(w_idx[row * H_I + tid]) : 0.f;
   __syncthreads();
 
   auto key_of = [&](int e) -> int {  // key of entry e, or -1
@@ -136,7 +141,11 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
     float mh = -INFINITY, lh = 0.f;
     for (int e = tid; e < n; e += kKlThreads) {
       const int s = key_of(e);
-      if (s >= 0) ml_merge(mh, lh, logit(s, h), 1.f);
+      if (s >= 0) {
+        const float z = logit(s, h);
+        if constexpr (kKeepZ) zbuf[h][e] = z;
+        ml_merge(mh, lh, z, 1.f);
+      }
     }
     wave_ml(mh, lh);
     if (lane == 0) red[wave][h][0] = mh, red[wave][h][1] = lh;
@@ -156,10 +165,10 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
       gbuf[e] = iv;
     }
     wave_ml(mi, li);
-    if (lane == 0) red[wave][kKlHeads][0] = mi, red[wave][kKlHeads][1] = li;
+    if (lane == 0) red[wave][NH][0] = mi, red[wave][NH][1] = li;
   }
   __syncthreads();
-  if (tid < H || tid == kKlHeads) {
+  if (tid < H || tid == NH) {
     float mm = red[0][tid][0], ll = red[0][tid][1];
     for (int w = 1; w < 4; ++w) ml_merge(mm, ll, red[w][tid][0], red[w][tid][1]);
     lse2[tid] = ll > 0.f ? mm + __log2f(ll) : -INFINITY;
@@ -174,9 +183,16 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
     float g = 0.f;
     if (s >= 0) {
       float pe = 0.f;
-      for (int h = 0; h < H; ++h) pe += fast_exp2(logit(s, h) - lse2[h]);
+      for (int h = 0; h < H; ++h) {
+        float z;
+        if constexpr (kKeepZ)
+          z = zbuf[h][e];  // written by this thread in pass 1
+        else
+          z = logit(s, h);
+        pe += fast_exp2(z - lse2[h]);
+      }
       pe *= inv_h;
-      const float lq2 = gbuf[e] * kLog2eKl - lse2[kKlHeads];  // log2 Q_s
+      const float lq2 = gbuf[e] * kLog2eKl - lse2[NH];  // log2 Q_s
       if (pe > 0.f) part += pe * (__log2f(pe) - lq2);
       g = fast_exp2(lq2) - pe;
     }
@@ -190,13 +206,19 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
   if (!dq && !dw && !dk) return;
 
   // ---- pass 3: gradients of the indexer inputs, 256 entries per chunk.  Entry thread:
-  // cbuf[j] = G w_j [d_j > 0], rbuf[j] = G ReLU(d_j), its dk row; then (head, dim) threads
-  // sum dq over the chunk and head threads sum dw.
-  constexpr int kPairs = (kKlHeads * D_I + kKlThreads - 1) / kKlThreads;
+  // cbuf[j] = G w_j [d_j > 0] and its own share of dw (G ReLU(d_j)); then the dq pairs
+  // (head, dim) sum c_j k over the chunk from LDS, split into S entry slices per pair when
+  // the pairs are fewer than the threads (slices combined at the end in slice order), and
+  // (entry, dim) pairs add the dk rows with fp32 atomics.
+  constexpr int kPairs = (NH * D_I + kKlThreads - 1) / kKlThreads;
+  const int P = H_I * D_I;
+  const int S = P <= kKlThreads ? kKlThreads / P : 0;  // entry slices per dq pair
   float dq_acc[kPairs];
 #pragma unroll
   for (int r = 0; r < kPairs; ++r) dq_acc[r] = 0.f;
-  float dw_acc = 0.f;
+  float dw_part[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) dw_part[j] = 0.f;
   for (int c0 = 0; c0 < n; c0 += kKlThreads) {
     const int e = c0 + tid;
     const int s = e < n ? key_of(e) : -1;
@@ -204,40 +226,49 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
       stage_key(s);
       const float g = gbuf[e];
       bool any = false;
-      for (int j = 0; j < kKlHeads; ++j) {
-        float c = 0.f, r = 0.f;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        float c = 0.f;
         if (j < H_I) {
           const float d = index_dot(j);
           c = d > 0.f ? g * wf[j] : 0.f;
-          r = g * relu(d);
+          dw_part[j] = fmaf(g, relu(d), dw_part[j]);
         }
         cbuf[j][tid] = c;
-        rbuf[j][tid] = r;
         any |= c != 0.f;
       }
       ckey[tid] = any ? s : -1;
     } else {
       ckey[tid] = -1;
-      for (int j = 0; j < kKlHeads; ++j) cbuf[j][tid] = 0.f, rbuf[j][tid] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) cbuf[j][tid] = 0.f;
 #pragma unroll
       for (int c = 0; c < D_I / 8; ++c) *reinterpret_cast<u32x4*>(&kchunk[tid][c * 8]) = u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
     const int cn = min(kKlThreads, n - c0);
     if (dq) {
+      if (S > 0) {
+        if (tid < P * S) {
+          const int pr = tid % P, sl = tid / P;
+          const int j = pr / D_I, d = pr % D_I;
+          float acc = dq_acc[0];
+          for (int t = sl; t < cn; t += S) acc = fmaf(cbuf[j][t], bf16_bits_to_f32(kchunk[t][d]), acc);
+          dq_acc[0] = acc;
+        }
+      } else {
 #pragma unroll
-      for (int r = 0; r < kPairs; ++r) {
-        const int x = tid + r * kKlThreads;
-        const int j = x / D_I, d = x % D_I;
-        if (j < H_I) {
-          float acc = dq_acc[r];
-          for (int t = 0; t < cn; ++t) acc = fmaf(cbuf[j][t], bf16_bits_to_f32(kchunk[t][d]), acc);
-          dq_acc[r] = acc;
+        for (int r = 0; r < kPairs; ++r) {
+          const int x = tid + r * kKlThreads;
+          const int j = x / D_I, d = x % D_I;
+          if (j < H_I) {
+            float acc = dq_acc[r];
+            for (int t = 0; t < cn; ++t) acc = fmaf(cbuf[j][t], bf16_bits_to_f32(kchunk[t][d]), acc);
+            dq_acc[r] = acc;
+          }
         }
       }
     }
-    if (dw && tid < H_I)
-      for (int t = 0; t < cn; ++t) dw_acc += rbuf[tid][t];
     if (dk) {
       // (entry, dim) pairs: consecutive lanes add consecutive dims of one key row, so an
       // atomic instruction covers 64 / D_I rows instead of 64
@@ -253,13 +284,33 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(
     __syncthreads();  // the chunk buffers are refilled
   }
   if (dq) {
+    if (S > 0) {
+      float* part = &cbuf[0][0];  // free now: the slices' partial sums, slice-major
+      part[tid] = tid < P * S ? dq_acc[0] : 0.f;
+      __syncthreads();
+      if (tid < P) {
+        float v = part[tid];
+        for (int sl = 1; sl < S; ++sl) v += part[sl * P + tid];
+        dq[row * P + tid] = v;
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < kPairs; ++r) {
-      const int x = tid + r * kKlThreads;
-      if (x / D_I < H_I) dq[row * H_I * D_I + x] = dq_acc[r];
+      for (int r = 0; r < kPairs; ++r) {
+        const int x = tid + r * kKlThreads;
+        if (x / D_I < H_I) dq[row * P + x] = dq_acc[r];
+      }
     }
   }
-  if (dw && tid < H_I) dw[row * H_I + tid] = dw_acc;
+  if (dw) {
+    __syncthreads();  // red held the loss partials (and no chunk ran for an empty row)
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const float v = wave_sum(dw_part[j]);
+      if (lane == 0) red[wave][j][0] = v;
+    }
+    __syncthreads();
+    if (tid < H_I) dw[row * H_I + tid] = (red[0][tid][0] + red[1][tid][0]) + (red[2][tid][0] + red[3][tid][0]);
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ x, int64_t n) {
@@ -284,16 +335,25 @@ hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st) {
   }
   if (rows == 0) return hipSuccess;
   const float sl2 = a.sm_scale * kLog2eKl;
-#define DSA_KL_LAUNCH(DI)                                                                                         \
-  hipLaunchKernelGGL(indexer_kl_kernel<DI>, dim3((unsigned)rows), dim3(kKlThreads), 0, st, a.q_idx, a.k_idx, a.w_idx, \
-                     a.q, a.k, a.idx, a.kv_len, a.Tq, a.Tk, a.H_I, a.H, a.kk, sl2, a.loss, a.dq, a.dw, a.dk)
+  const bool few_heads = a.H <= 4 && a.H_I <= 4;
+  const bool few_keys = (a.idx ? a.kk : a.Tk) <= 1024;
+#define DSA_KL_LAUNCH(DI, NH, MK)                                                                                \
+  hipLaunchKernelGGL((indexer_kl_kernel<DI, NH, MK>), dim3((unsigned)rows), dim3(kKlThreads), 0, st, a.q_idx,     \
+                     a.k_idx, a.w_idx, a.q, a.k, a.idx, a.kv_len, a.Tq, a.Tk, a.H_I, a.H, a.kk, sl2, a.loss, a.dq, \
+                     a.dw, a.dk)
+#define DSA_KL_SIZES(DI)                                  \
+  if (few_heads && few_keys) DSA_KL_LAUNCH(DI, 4, 1024);  \
+  else if (few_heads) DSA_KL_LAUNCH(DI, 4, kKlMaxKeys);   \
+  else if (few_keys) DSA_KL_LAUNCH(DI, kKlHeads, 1024);   \
+  else DSA_KL_LAUNCH(DI, kKlHeads, kKlMaxKeys);
   switch (a.d_I) {
-    case 16: DSA_KL_LAUNCH(16); break;
-    case 32: DSA_KL_LAUNCH(32); break;
-    case 64: DSA_KL_LAUNCH(64); break;
-    case 128: DSA_KL_LAUNCH(128); break;
+    case 16: DSA_KL_SIZES(16); break;
+    case 32: DSA_KL_SIZES(32); break;
+    case 64: DSA_KL_SIZES(64); break;
+    case 128: DSA_KL_SIZES(128); break;
     default: return hipErrorInvalidValue;
   }
+#undef DSA_KL_SIZES
 #undef DSA_KL_LAUNCH
   return hipGetLastError();
 }
