@@ -487,8 +487,15 @@ def main():
         ia = dsa.topk(sa, a.k)
         del sa
         kin = [la[x] for x in ("q_idx", "k_idx", "w_idx", "q", "kv")]
-        sparse_ms = timed(lambda: dsa.indexer_kl(*kin, a.scale(), idx=ia))
-        dense_ms = timed(lambda: dsa.indexer_kl(*kin, a.scale()))
+        kout = dsa.indexer_kl(*kin, a.scale(), idx=ia)  # outputs reused by the timed calls
+        nrep = 20
+
+        def kl_batch(ix):  # back-to-back launches, so host work overlaps the kernels
+            for _ in range(nrep):
+                dsa.indexer_kl(*kin, a.scale(), idx=ix, out=kout)
+
+        sparse_ms = timed(lambda: kl_batch(ia)) / nrep
+        dense_ms = timed(lambda: kl_batch(None)) / nrep
         pairs_sparse = sum(min(t + 1, a.k) for t in range(a.T))
         pairs_dense = a.T * (a.T + 1) // 2
         # fp32 flops per (row, key) pair: main logits twice (2 * H * 32 * 2), indexer dots

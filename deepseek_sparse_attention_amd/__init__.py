@@ -216,21 +216,25 @@ def _kv_dtype(kv, Dqk, kv_scale):
     return KV_MXFP4
 
 
-def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, grads=True, stream=None):
+def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, grads=True, out=None, stream=None):
     """dsa_indexer_kl: per-row KL(main attention || indexer) and, with grads, the gradients of
     its sum for q_idx, w_idx and k_idx.  idx None: every causal key (dense warm-up).
-    Returns (loss fp32 [B,Tq], dq_idx, dw_idx, dk_idx) (gradients None without grads)."""
+    Returns (loss fp32 [B,Tq], dq_idx, dw_idx, dk_idx) (gradients None without grads);
+    `out` may hold those four tensors, preallocated."""
     B, Tq, H_I, d_I = q_idx.shape
     Tk = k_idx.shape[1]
     H, Dqk = q.shape[2], q.shape[3]
     kk = 0 if idx is None else idx.shape[2]
     dev = q_idx.device
-    loss = torch.empty((B, Tq), dtype=torch.float32, device=dev)
-    dq = dw = dk = None
-    if grads:
-        dq = torch.empty((B, Tq, H_I, d_I), dtype=torch.float32, device=dev)
-        dw = torch.empty((B, Tq, H_I), dtype=torch.float32, device=dev)
-        dk = torch.empty((B, Tk, d_I), dtype=torch.float32, device=dev)
+    if out is not None:
+        loss, dq, dw, dk = out
+    else:
+        loss = torch.empty((B, Tq), dtype=torch.float32, device=dev)
+        dq = dw = dk = None
+        if grads:
+            dq = torch.empty((B, Tq, H_I, d_I), dtype=torch.float32, device=dev)
+            dw = torch.empty((B, Tq, H_I), dtype=torch.float32, device=dev)
+            dk = torch.empty((B, Tk, d_I), dtype=torch.float32, device=dev)
     _check(lib().dsa_indexer_kl(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(idx), _ptr(kv_len),
                                 B, Tq, Tk, H_I, d_I, H, Dqk, kk, ctypes.c_float(sm_scale), _ptr(loss), _ptr(dq),
                                 _ptr(dw), _ptr(dk), _stream(stream)))
