@@ -468,8 +468,11 @@ def main():
         log(f"decode, MXFP4 latent caches: {mdt * 1e3:.3f} ms/step, {e.B / mdt:.0f} tok/s")
 
         def attn_layer(L, kv_scale, row_bytes):
-            us = 1e3 * timed(lambda: dsa.sparse_attn(L["q"], L["kv"], dcache, e.scale(), kv_scale=kv_scale, Dv=e.Dv,
-                                                     out=L["out"], lse=L["lse"], ws=dws))
+            def batch():  # back-to-back launches, so host work overlaps the kernels
+                for _ in range(20):
+                    dsa.sparse_attn(L["q"], L["kv"], dcache, e.scale(), kv_scale=kv_scale, Dv=e.Dv, out=L["out"],
+                                    lse=L["lse"], ws=dws)
+            us = 1e3 * timed(batch) / 20
             nb = (e.B * e.k * (row_bytes + 4) + e.B * e.H * (e.Dqk * 2 + e.Dv * 2 + 4))
             return {"us": round(us, 2), "algorithmic_bytes": nb, "gbs": round(nb / (us * 1e-6) / 1e9, 1)}
 
