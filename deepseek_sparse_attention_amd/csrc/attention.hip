@@ -19,8 +19,9 @@
 // Decode rows (few queries) split the key list over workgroups and merge the partial
 // results by log-sum-exp in a second kernel, in a fixed order.
 //
-// Multi-head form (DSA ablation card: 4 heads of width 32, RoPE'd inputs): one wave per
-// head, logits in LDS, three fixed-order passes.
+// Multi-head form (DSA ablation card: 4 heads of width 32, RoPE'd inputs): a workgroup per
+// query row, key rows read as 16-byte chunks spread over the lanes, logits in LDS, three
+// fixed-order passes.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -417,86 +418,126 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   if (lse && lane == 0) lse[rh] = l == 0.f ? -INFINITY : (m + __log2f(l)) * kLn2;
 }
 
-// Multi-head form: Dqk = Dv = 32, Hkv = H, one wave per head (heads strided over 4 waves),
-// logits of up to kMhaMaxK selected keys kept in LDS.
+// Multi-head form (Dqk = Dv = 32, Hkv = H <= 16): one workgroup per query row, heads taken
+// in groups of G (a power of two: all H, padded, when G x k logits fit the LDS area).  A
+// key's rows of a group, K[s][h0 .. h0+G-1][32] and likewise V, are G*64 contiguous bytes:
+// C = 4G lanes read them as 16-byte chunks (chunk c: head c/4, dims 8(c%4) .. +7), so a
+// wave reads 64/C keys per step with every load 16 contiguous bytes.  Pass 1 forms the
+// logits (partial dot per lane, two shuffles over a head's four chunk lanes) into LDS;
+// pass 2 turns each head's logits into probabilities (a wave per head: max, exp2, sum);
+// pass 3 accumulates P V per lane for its (head, 8 dims) over its keys, then lanes with the
+// same chunk and the four waves are summed in a fixed order.
 constexpr int kMhaD = 32;
 constexpr int kMhaMaxK = 4096;
 
+template <int G, int ZCAP>  // heads per round, logits per round held in LDS
 __global__ __launch_bounds__(256) void mha_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kk,
                                                        const uint16_t* __restrict__ vv, const int32_t* __restrict__ idx,
                                                        int Tq, int Tk, int H, int k, float scale_log2,
                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float zb[4][kMhaMaxK];
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  constexpr int C = 4 * G;      // lanes per key (one 16-byte chunk each)
+  constexpr int KW = 64 / C;    // keys per wave step
+  constexpr int KB = 4 * KW;    // keys per workgroup step
+  __shared__ float zs[ZCAP];                    // [G][k] logits, then probabilities
+  __shared__ float qs[G][kMhaD];                // the group's queries, times sm_scale * log2(e)
+  __shared__ float stat[G][2];                  // per head: max, sum
+  __shared__ __attribute__((aligned(16))) float ored[4][G * kMhaD];  // P V per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int64_t row = blockIdx.x;
   const int b = (int)(row / Tq);
   const int32_t* ix = idx + row * k;
-  float* z = zb[wave];
-  // every wave runs the same number of rounds, so the barriers below are uniform
-  for (int h0 = 0; h0 < H; h0 += 4) {
-    const int h = h0 + wave;
-    const bool active = h < H;
-    float m = -INFINITY, l = 0.f;
-    if (active) {
-      float qf[kMhaD];
-      const uint16_t* qp = q + (row * H + h) * kMhaD;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 w4 = ld16(qp + c * 8);
+  const int kl = lane / C, c = lane % C;
+  const int hh = c >> 2, dc = c & 3;  // this lane's head within the group, dim chunk
+  for (int h0 = 0; h0 < H; h0 += G) {  // uniform rounds
+    for (int x = tid; x < G * kMhaD; x += 256) {
+      const int h = h0 + x / kMhaD;
+      qs[x / kMhaD][x % kMhaD] = h < H ? bf16_bits_to_f32(q[(row * H + h) * kMhaD + x % kMhaD]) * scale_log2 : 0.f;
+    }
+    __syncthreads();
+    const bool hv = h0 + hh < H;
+    // ---- pass 1: base-2 logits
+#pragma unroll 4
+    for (int j = wave * KW + kl; j < k; j += KB) {
+      const int s = ix[j];
+      const bool ok = hv && s >= 0 && s < Tk;
+      float part = 0.f;
+      if (ok) {
+        const u32x4 w4 = ld16(kk + (((int64_t)b * Tk + s) * H + h0 + hh) * kMhaD + dc * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[c * 8 + 2 * e] = __uint_as_float(w4[e] << 16);
-          qf[c * 8 + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+          part = fmaf(qs[hh][dc * 8 + 2 * e], __uint_as_float(w4[e] << 16), part);
+          part = fmaf(qs[hh][dc * 8 + 2 * e + 1], __uint_as_float(w4[e] & 0xFFFF0000u), part);
         }
       }
-      for (int j = lane; j < k; j += 64) {
-        const int s = ix[j];
-        float zz = -INFINITY;
-        if (s >= 0 && s < Tk) {
-          const uint16_t* kp = kk + (((int64_t)b * Tk + s) * H + h) * kMhaD;
-          float dot = 0.f;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4 w4 = ld16(kp + c * 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              dot = fmaf(qf[c * 8 + 2 * e], __uint_as_float(w4[e] << 16), dot);
-              dot = fmaf(qf[c * 8 + 2 * e + 1], __uint_as_float(w4[e] & 0xFFFF0000u), dot);
-            }
-          }
-          zz = dot * scale_log2;
-        }
-        z[j] = zz;
-        m = fmaxf(m, zz);
-      }
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      if (dc == 0) zs[hh * k + j] = ok ? part : -INFINITY;
+    }
+    __syncthreads();
+    // ---- pass 2: probabilities, a wave per head
+    for (int g = wave; g < G; g += 4) {
+      float m = -INFINITY;
+      for (int j = lane; j < k; j += 64) m = fmaxf(m, zs[g * k + j]);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float l = 0.f;
       for (int j = lane; j < k; j += 64) {
-        const float p = (z[j] == -INFINITY) ? 0.f : fast_exp2(z[j] - m);
-        z[j] = p;
-        l += p;
+        const float z = zs[g * k + j];
+        const float pj = z == -INFINITY ? 0.f : fast_exp2(z - m);
+        zs[g * k + j] = pj;
+        l += pj;
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+      if (lane == 0) stat[g][0] = m, stat[g][1] = l;
     }
-    __syncthreads();  // probabilities written by other lanes are read below
-    if (active) {
-      // P V: lane -> (column d = lane % 32, half = lane / 32), keys of that parity
-      const int d = lane & 31, half = lane >> 5;
-      float o = 0.f;
-      for (int j = half; j < k; j += 2) {
-        const float p = z[j];
-        if (p != 0.f) {
-          const int s = ix[j];
-          o = fmaf(p, bf16_bits_to_f32(vv[(((int64_t)b * Tk + s) * H + h) * kMhaD + d]), o);
+    __syncthreads();
+    // ---- pass 3: P V for this lane's head and 8 dims over its keys
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int j = wave * KW + kl; j < k; j += KB) {
+      const float pj = hv ? zs[hh * k + j] : 0.f;
+      if (pj != 0.f) {  // (a masked or missing key has probability 0)
+        const int s = ix[j];
+        const u32x4 w4 = ld16(vv + (((int64_t)b * Tk + s) * H + h0 + hh) * kMhaD + dc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(pj, __uint_as_float(w4[e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(pj, __uint_as_float(w4[e] & 0xFFFF0000u), acc[2 * e + 1]);
         }
       }
-      o += __shfl_xor(o, 32, 64);
-      if (half == 0) out[(row * H + h) * kMhaD + d] = f32_to_bf16_bits(l == 0.f ? 0.f : o / l);
-      if (lse && lane == 0) lse[row * H + h] = l == 0.f ? -INFINITY : (m + __log2f(l)) * kLn2;
     }
-    __syncthreads();  // z is reused by the next round
+#pragma unroll
+    for (int o = C; o < 64; o <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    }
+    if (kl == 0) {
+      *reinterpret_cast<float4*>(&ored[wave][hh * kMhaD + dc * 8]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(&ored[wave][hh * kMhaD + dc * 8 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    for (int x = tid; x < G * kMhaD; x += 256) {
+      const int g = x / kMhaD, h = h0 + g;
+      if (h < H) {
+        const float l = stat[g][1];
+        const float o = (ored[0][x] + ored[1][x]) + (ored[2][x] + ored[3][x]);
+        out[(row * H + h) * kMhaD + x % kMhaD] = f32_to_bf16_bits(l == 0.f ? 0.f : o / l);
+        if (lse && x % kMhaD == 0) lse[row * H + h] = l == 0.f ? -INFINITY : (stat[g][0] + __log2f(l)) * kLn2;
+      }
+    }
+    __syncthreads();  // the LDS areas are reused by the next round
   }
+}
+
+// heads per round and LDS capacity of the multi-head kernel: all heads (padded to a power
+// of two) when they fit, else as many as 16384 logits allow (k <= 4096: at least four)
+int mha_group(int H, int k) {
+  int hp = 1;
+  while (hp < H) hp <<= 1;
+  int g = hp;
+  while (g > 1 && (int64_t)g * k > 16384) g >>= 1;
+  return g;
 }
 
 // Paged latent cache: selected key s of sequence b (an index row of Tq*k entries per
@@ -601,8 +642,23 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   if (attn_mha_supported(a)) {
-    hipLaunchKernelGGL(mha_attn_kernel, dim3((unsigned)rows), dim3(256), 0, st, a.q, (const uint16_t*)a.kv, a.v,
-                       a.idx, a.Tq, a.Tk, a.H, a.k, a.sm_scale * kLog2e, a.out, a.lse);
+    const int g = mha_group(a.H, a.k);
+    const bool small = (int64_t)g * a.k <= 2048;
+    const float sl2 = a.sm_scale * kLog2e;
+#define DSA_MHA_LAUNCH(G, Z)                                                                                      \
+  hipLaunchKernelGGL((mha_attn_kernel<G, Z>), dim3((unsigned)rows), dim3(256), 0, st, a.q, (const uint16_t*)a.kv, \
+                     a.v, a.idx, a.Tq, a.Tk, a.H, a.k, sl2, a.out, a.lse)
+#define DSA_MHA_CAP(G) \
+  if (small) DSA_MHA_LAUNCH(G, 2048); else DSA_MHA_LAUNCH(G, 16384);
+    switch (g) {
+      case 1: DSA_MHA_CAP(1); break;
+      case 2: DSA_MHA_CAP(2); break;
+      case 4: DSA_MHA_CAP(4); break;
+      case 8: DSA_MHA_CAP(8); break;
+      default: DSA_MHA_CAP(16); break;
+    }
+#undef DSA_MHA_CAP
+#undef DSA_MHA_LAUNCH
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
