@@ -6,7 +6,8 @@
 // equal scores resolved toward the lower key index, -0.0 == +0.0.  Output ascending,
 // -1 padded.
 //
-// One 1024-thread workgroup per row.  Scores become order-preserving uint32 keys.  A radix
+// Rows of up to 6144 keys: one wave per row (topk_short_kernel, below).  Longer rows:
+// one 1024-thread workgroup per row.  Scores become order-preserving uint32 keys.  A radix
 // select over LDS histograms finds the k-th largest key K*: the first pass bins the
 // row's actual [min, max] key range into 2048 bins (so the populated bins spread out and
 // LDS atomics rarely collide), later passes refine inside the threshold bin only, at
@@ -1009,15 +1010,148 @@ __global__ __launch_bounds__(ST_NT, 4) void topk_stream_kernel(const float* __re
   }
 }
 
+// Rows of at most 64*EPL keys (up to 6144): one wave per row, the row's scores in
+// registers (the lane's item i is position 64 i + lane), and the same wave-local radix
+// select as the fused route's list select: histogram passes over [lo, hi] narrow to the bin
+// holding the k-th largest key, a final bin of at most 64 keys is ranked exactly (score,
+// then position), a bin of one key value keeps its lowest positions; kept positions are
+// written in increasing order.  Four rows per workgroup, 32 KB of LDS.
+constexpr int SH_NW = 4;
+
+__device__ __forceinline__ uint32_t sh_mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+template <int EPL>
+__global__ __launch_bounds__(64 * SH_NW) void topk_short_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                int64_t score_bstride,
+                                                                const int32_t* __restrict__ kv_len, int Tq, int Tk,
+                                                                int k, int row0, int nrows,
+                                                                int32_t* __restrict__ idx) {
+  __shared__ uint32_t hists[SH_NW][kSelBins];
+  __shared__ uint32_t mems[SH_NW][64];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int r = blockIdx.x * SH_NW + wave, b = blockIdx.y;
+  if (r >= nrows) return;
+  const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
+  int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * k;
+  if (p + 1 <= k) {  // every causal key (or none), then padding
+    for (int j = lane; j < k; j += 64) out[j] = (j <= p) ? j : -1;
+    return;
+  }
+  const int n = (int)min<int64_t>(p + 1, Tk);
+  const int nr = (n + 63) / 64;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(scores + (int64_t)b * score_bstride + (int64_t)r * ld, (uint32_t)n * 4u);
+  uint32_t key[EPL];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int i0 = 0; i0 < EPL; i0 += 8) {
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) key[i] = 0u;  // 0: no entry (every real key is >= 1)
+    if (i0 >= nr) continue;
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) {
+      const int e = 64 * i + lane;
+      const float sc = buf_load_f32(rs, (uint32_t)lane * 4u, (uint32_t)(256 * i));
+      key[i] = e < n ? sel_key(sc) : 0u;
+      mn = min(mn, e < n ? key[i] : 0xFFFFFFFFu);
+      mx = max(mx, key[i]);
+    }
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  uint32_t* const hist = hists[wave];
+  uint32_t need = (uint32_t)k, lo = mn, hi = mx, m;
+  int sh = sel_shift(lo, hi);
+  for (;;) {
+    for (int j = lane; j < kSelBins; j += 64) hist[j] = 0;
+#pragma unroll
+    for (int i0 = 0; i0 < EPL; i0 += 8) {
+      if (i0 >= nr) continue;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i)
+        if (key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> sh], 1u);
+    }
+    uint32_t bin, above;
+    wave_find_bin_from_top(hist, need, bin, above);
+    m = __builtin_amdgcn_readfirstlane(hist[bin]);
+    need -= above;
+    lo += bin << sh;
+    hi = (uint32_t)min((uint64_t)lo + ((1u << sh) - 1u), (uint64_t)hi);
+    if (sh == 0 || m <= 64) break;
+    sh = sel_shift(lo, hi);
+  }
+  // a final bin of m <= 64 keys over several values: rank them exactly (score, then
+  // position); bit j of keptm = the j-th of them in position order is kept
+  uint64_t keptm = 0;
+  if (sh > 0) {
+    uint32_t* const mem = mems[wave];
+    uint32_t cm = 0;
+#pragma unroll
+    for (int i0 = 0; i0 < EPL; i0 += 8) {
+      if (i0 >= nr) continue;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) {
+        const bool inb = key[i] >= lo && key[i] <= hi;
+        const uint64_t bl = __ballot(inb);
+        if (inb) mem[cm + sh_mbcnt(bl)] = key[i];
+        cm += (uint32_t)__popcll(bl);
+      }
+    }
+    const uint32_t mk = lane < (int)m ? mem[lane] : 0u;
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < m; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
+      rank += (kj > mk) || (kj == mk && (int)j < lane);
+    }
+    keptm = __ballot(lane < (int)m && rank < need);
+  }
+  // emission in position order (item i of every lane before item i+1)
+  uint32_t acc = 0, before = 0;
+#pragma unroll
+  for (int i0 = 0; i0 < EPL; i0 += 8) {
+    if (i0 >= nr) continue;
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) {
+      const uint32_t kv = key[i];  // 0 past the row: never kept
+      bool kp;
+      if (sh > 0) {
+        const bool inb = kv >= lo && kv <= hi;
+        const uint64_t bl = __ballot(inb);
+        kp = kv > hi || (inb && ((keptm >> (before + sh_mbcnt(bl))) & 1u));
+        before += (uint32_t)__popcll(bl);
+      } else {  // one key value K* = lo: ties kept lowest position first
+        const bool tie = kv == lo;
+        const uint64_t bl = __ballot(tie);
+        kp = kv > lo || (tie && before + sh_mbcnt(bl) < need);
+        before += (uint32_t)__popcll(bl);
+      }
+      const uint64_t bk = __ballot(kp);
+      const uint32_t slot = acc + sh_mbcnt(bk);
+      acc += (uint32_t)__popcll(bk);
+      if (kp && slot < (uint32_t)k) out[slot] = 64 * i + lane;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.nrows <= 0 || A.B <= 0) return hipSuccess;
   dim3 grid(A.nrows, A.B);
-  // rows see at most Tk keys: up to one segment they are kept in registers
-  // Many rows: the streaming kernel (256 threads, two rows per CU); few rows (decode):
-  // 1024 threads per row keep the chip busy.
-  if (A.Tk <= SEG && (int64_t)A.nrows * A.B >= 1024)
+  // rows see at most Tk keys.  Up to 6144: a wave per row.  Up to one segment (65536) they
+  // stay in registers: many rows take the streaming kernel (256 threads, four rows per CU),
+  // few rows (decode) 1024 threads per row, which keeps the chip busy.
+  if (A.Tk <= 64 * 96) {
+    dim3 g2((unsigned)((A.nrows + SH_NW - 1) / SH_NW), A.B);
+    if (A.Tk <= 64 * 48)
+      hipLaunchKernelGGL(topk_short_kernel<48>, g2, dim3(64 * SH_NW), 0, st, A.scores, A.ld, A.score_bstride,
+                         A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, A.idx);
+    else
+      hipLaunchKernelGGL(topk_short_kernel<96>, g2, dim3(64 * SH_NW), 0, st, A.scores, A.ld, A.score_bstride,
+                         A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, A.idx);
+  } else if (A.Tk <= SEG && (int64_t)A.nrows * A.B >= 1024)
     hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(ST_NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len,
                        A.Tq, A.Tk, A.k, A.row0, A.idx);
   else if (A.Tk <= SEG)

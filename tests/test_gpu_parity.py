@@ -127,6 +127,23 @@ def test_topk_ties_signed_zeros_and_short_rows():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("T,k,ties", [(6144, 2048, False), (6144, 4096, False), (5000, 2048, True),
+                                      (3073, 3000, True), (4000, 1, False)])
+def test_topk_wave_per_row_up_to_6144_keys(T, k, ties):
+    # rows of 3073..6144 keys take the wave-per-row kernel's wide instance; ragged lengths,
+    # heavy ties (single-value threshold bins far above 64 members) and signed zeros
+    print(f"topk wave per row T={T} k={k} ties={ties}", flush=True)
+    rng = np.random.default_rng(T + k)
+    if ties:
+        s = rng.integers(0, 4, size=(2, 60, T)).astype(np.float32)
+        z = s == 0
+        s[z] = np.where(rng.random(np.count_nonzero(z)) < 0.5, -0.0, 0.0).astype(np.float32)
+    else:
+        s = rng.standard_normal((2, 60, T)).astype(np.float32)
+    got, ref = _topk_case(s, k, kv_len=[T, T - 777])
+    assert np.array_equal(got, ref)
+
+
 def test_topk_threshold_bin_larger_than_candidate_list():
     # >4096 equal scores straddle the threshold: the register fallback path
     rng = np.random.default_rng(8)
