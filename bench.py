@@ -40,7 +40,7 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        attn = [float(r["Counter_Value"]) for r in rows if "mla_attn_kernel<0>" in r["Kernel_Name"]]
+        attn = [float(r["Counter_Value"]) for r in rows if "mla_attn_kernel<0, 0>" in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
                 or "copy_kernel" in r["Kernel_Name"]]
         return attn, copy
@@ -100,7 +100,7 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# fz_filter, fz_select, fz_exact once each, then attention), 3 event-timed launches of each",
         "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
         "# unfused step), then the decode steps and their per-layer attention launches, then the KL",
-        "# objective (sparse and dense, with gradients).  mla_attn_kernel<0|1|2>: bf16 | fp8 | MXFP4 rows.",
+        "# objective (sparse and dense, with gradients).  mla_attn_kernel<f, w>: rows f = 0 bf16, 1 fp8, 2 MXFP4; w = 1 the three-workgroup schedule.",
         "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel",
         "",
     ]

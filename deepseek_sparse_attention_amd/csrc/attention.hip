@@ -168,18 +168,27 @@ struct TileStage<kKvMxfp4> {
   }
 };
 
-template <int FMT>
-__global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+// Two schedules.  WIDE = 0: two row stages in registers, two LDS tile buffers, two
+// workgroups per CU.  WIDE = 1 (bf16 rows, no key split, at most kWideMaxTk keys): one
+// register stage and one LDS buffer, three workgroups per CU.  The tile body is a latency
+// chain and a third workgroup hides more of it; measured 4.7% faster at T=16384 and 1.5%
+// slower at T=32768 (the extra workgroups' rows then cost more in cache than they gain).
+constexpr int kWideMaxTk = 24576;
+
+template <int FMT, int WIDE>
+__global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                                                           const float* __restrict__ kv_scale,
                                                           const int32_t* __restrict__ idx, int Tq, int Tk,
                                                           int64_t kv_bstride, int H, int k, float scale_log2,
                                                           int tiles_per_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kTile * kRowB];
+  constexpr int NBUF = WIDE ? 1 : 2;  // LDS tile buffers
+  constexpr int NST = WIDE ? 1 : 2;   // row stages in registers (tiles in flight)
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[NBUF][kTile * kRowB];
   __shared__ __attribute__((aligned(16))) f32x4 sbuf[4][64];           // partial S^T per wave and lane
-  __shared__ __attribute__((aligned(16))) float tile_bias[2][kTile];   // 0 for a valid key, -inf otherwise
-  __shared__ __attribute__((aligned(16))) float tile_scale[2][kTile];  // fp8 row scales
+  __shared__ __attribute__((aligned(16))) float tile_bias[NBUF][kTile];   // 0 for a valid key, -inf otherwise
+  __shared__ __attribute__((aligned(16))) float tile_scale[NBUF][kTile];  // fp8 row scales
   __shared__ int jmax_red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -235,12 +244,23 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     if (FP8) st.sc = buf_load_f32(sc_rs, s_idx >= 0 ? (uint32_t)s_idx * 4 : kOffNone, 0);
   };
 
-  // prologue: index entries of tiles t_begin .. t_begin+3, rows of the first two in flight
+  // prologue: index entries of tiles t_begin .. t_begin + 2*NST - 1, rows of the first NST
+  // in flight
   TileStage<FMT> st0, st1;
-  const int e0 = raw_entry(t_begin), e1 = raw_entry(t_begin + 1);
-  int nx0 = raw_entry(t_begin + 2), nx1 = raw_entry(t_begin + 3);
-  fetch(st0, valid_entry(t_begin, e0));
-  fetch(st1, valid_entry(t_begin + 1, e1));
+  int nx0, nx1 = 0;
+  {
+    const int e0 = raw_entry(t_begin);
+    if constexpr (NST == 2) {
+      const int e1 = raw_entry(t_begin + 1);
+      nx0 = raw_entry(t_begin + 2);
+      nx1 = raw_entry(t_begin + 3);
+      fetch(st0, valid_entry(t_begin, e0));
+      fetch(st1, valid_entry(t_begin + 1, e1));
+    } else {
+      nx0 = raw_entry(t_begin + 1);
+      fetch(st0, valid_entry(t_begin, e0));
+    }
+  }
 
   // extent of this split's entries that are valid: the loop ends after its last tile
   int jm = -1;
@@ -260,19 +280,20 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
   for (int n = 0; n < 8; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto tile = [&](int t, TileStage<FMT>& st, int& nx) {  // nx: raw index entry of tile t+2
-    const int buf = (t - t_begin) & 1;
+  auto tile = [&](int t, TileStage<FMT>& st, int& nx) {  // nx: raw index entry of tile t+NST
+    const int buf = NBUF == 2 ? (t - t_begin) & 1 : 0;
     uint8_t* kvb = kvs[buf];
+    if constexpr (NBUF == 1) __syncthreads();  // every wave is done with the previous tile
     st.store(kvb, gk, part0);
     if (key_owner) {
       tile_bias[buf][gk] = st.s >= 0 ? 0.f : -INFINITY;
       if (FP8) tile_scale[buf][gk] = st.sc;
     }
     __syncthreads();  // tile t staged (the other buffer may still be read by PV of t-1)
-    // refill this stage with tile t+2; its index entry arrived with tile t's rows
+    // refill this stage with tile t+NST; its index entry arrived with tile t's rows
     {
-      const int s2 = valid_entry(t + 2, nx);
-      nx = raw_entry(t + 4);
+      const int s2 = valid_entry(t + NST, nx);
+      nx = raw_entry(t + 2 * NST);
       fetch(st, s2);
     }
 
@@ -347,12 +368,16 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(const uint16_t* __rest
     }
   };
 
-  int t = t_begin;
-  for (; t + 1 < t_end; t += 2) {
-    tile(t, st0, nx0);
-    tile(t + 1, st1, nx1);
+  if constexpr (NST == 1) {
+    for (int t = t_begin; t < t_end; ++t) tile(t, st0, nx0);
+  } else {
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+      tile(t, st0, nx0);
+      tile(t + 1, st1, nx1);
+    }
+    if (t < t_end) tile(t, st0, nx0);
   }
-  if (t < t_end) tile(t, st0, nx0);
 
   // ---- results: lane holds O[head hl][wave*128 + n*16 + 4gq + i]
   const int h = hg * 16 + hl;
@@ -626,14 +651,18 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
     }
     dim3 grid((unsigned)(rows * (a.H / 16)), nsplit);
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
+    const bool wide = a.kv_fmt == kKvBf16 && nsplit == 1 && a.Tk <= kWideMaxTk;
     if (a.kv_fmt == kKvFp8)
-      hipLaunchKernelGGL(mla_attn_kernel<kKvFp8>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale,
+      hipLaunchKernelGGL((mla_attn_kernel<kKvFp8, 0>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale,
                          a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     else if (a.kv_fmt == kKvMxfp4)
-      hipLaunchKernelGGL(mla_attn_kernel<kKvMxfp4>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
+      hipLaunchKernelGGL((mla_attn_kernel<kKvMxfp4, 0>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
+                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+    else if (wide)
+      hipLaunchKernelGGL((mla_attn_kernel<kKvBf16, 1>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
                          a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     else
-      hipLaunchKernelGGL(mla_attn_kernel<kKvBf16>, grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
+      hipLaunchKernelGGL((mla_attn_kernel<kKvBf16, 0>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
                          a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
