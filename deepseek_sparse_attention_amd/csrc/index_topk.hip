@@ -139,7 +139,8 @@ __global__ __launch_bounds__(256, 2) void fz_sample_kernel(const uint16_t* __res
   // rows past the wave's count fall outside the store range and are dropped
   const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(smp + rbase * smax, (uint32_t)(R.wrows * smax * 4));
   const int col = wv.col;
-  wv.run(k_rs, wks[wave_id()], nst, [&](int j) { return min(max(j * step + half, 0), span - 32); },
+  wv.template run<W::EPIS>(k_rs, wks[wave_id()], nst,
+                           [&](int j) { return min(max(j * step + half, 0), span - 32); },
          [&](int j, int, int t, int qq, float tot) {
            const uint32_t off = (uint32_t)(wv.row_of(t, qq) * smax + j * 32 + col) * 4u;
            __builtin_amdgcn_raw_buffer_store_b32(sel_key(tot), s_rs, (int)off, 0, 0);
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __res
   for (int r = 0; r < ROWS; ++r) fill[r] = 0;
   const int col = wv.col, g = wv.g;
   const uint32_t lane_list = (uint32_t)(g * W::QPL * FZ_CAP) * 8u;  // list of row rA + g*QPL
-  wv.run(k_rs, wks[wave_id()], (int)((R.p_last + 32) / 32), [](int j) { return 32 * j; },
+  wv.template run<W::EPIS>(k_rs, wks[wave_id()], (int)((R.p_last + 32) / 32), [](int j) { return 32 * j; },
          [&](int, int s0, int t, int qq, float tot) {
            const int skey = s0 + col;
            const bool c = skey <= lim[t][qq] && tot >= th[t][qq];

@@ -66,12 +66,12 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     // the pool reads zeros through the range check
     const int32_t* btb = bt + (int64_t)b * max_blocks;
     const int pmask = (1 << page_shift) - 1;
-    wv.run(k_rs, wks[wave], ntiles, start, epi, [](int) {}, [&](int j) {
+    wv.template run<W::EPIS>(k_rs, wks[wave], ntiles, start, epi, [](int) {}, [&](int j) {
       const int s0 = start(j);
       return (btb[min(s0 >> page_shift, max_blocks - 1)] << page_shift) + (s0 & pmask);
     });
   } else {
-    wv.run(k_rs, wks[wave], ntiles, start, epi);
+    wv.template run<W::EPIS>(k_rs, wks[wave], ntiles, start, epi);
   }
 }
 

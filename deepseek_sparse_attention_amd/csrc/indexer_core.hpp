@@ -7,8 +7,8 @@
 // ordered so that the 16 accumulator values of a lane are all H_I heads of 16/H_I queries
 // for one key: the ReLU and the head-weighted sum then run inside the lane, with no
 // cross-lane traffic, and each lane ends with finished scores.  A wave keeps kQP query
-// tiles of Q in registers and streams 32-key tiles; what happens to each finished score is
-// the caller's epilogue (store it, sample it, filter it, histogram it).  Every kernel that
+// tiles of Q in registers and streams 32-key tiles through LDS; what happens to each
+// finished score is the caller's epilogue (store it, sample it, filter it, histogram it).  Every kernel that
 // scores a (query, key) pair goes through this code, so all of them produce the same fp32
 // value for it: the MFMA k-steps, the head order of the sum and the rounding are fixed here.
 #pragma once
@@ -25,17 +25,31 @@ constexpr int idx_query_tiles() {
   return (D_I == 64 && H_I >= 2) || H_I >= 8 ? 2 : 1;
 }
 
+// Waits until at most N vector memory operations of this wave are outstanding (they
+// complete in issue order); also a compiler barrier for memory accesses.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int H_I, int D_I, int kQP>
 struct IdxWave {
   static constexpr int QPT = 32 / H_I;   // queries per MFMA tile
   static constexpr int QPL = 16 / H_I;   // queries per lane (per tile)
   static constexpr int KS = D_I / 16;    // MFMA k-steps over the indexer width
   static constexpr int ROWS = kQP * QPT; // query rows of the wave
+  static constexpr int EPIS = kQP * QPL; // epilogue calls per key tile
   static constexpr int CPK = D_I / 8;    // 16-byte chunks per key row
   static constexpr int KPI = 64 / CPK;   // keys per load instruction
   static constexpr int NLD = 32 / KPI;   // load instructions per tile
   static constexpr uint32_t kTileBytes = 32 * D_I * 2;
-  static constexpr uint32_t kLdsBytes = 2 * kTileBytes;  // the wave's private key buffers
+  // key tiles in flight, and LDS tile buffers: one more than in flight, so that a buffer is
+  // refilled only once the operand reads of its last tile have completed.  128-wide keys
+  // keep one tile in flight so that two workgroups still fit a CU.
+  static constexpr int DEPTH = D_I >= 128 ? 1 : 3;
+  static constexpr int NB = DEPTH + 1;
+  static constexpr uint32_t kLdsBytes = NB * kTileBytes;  // the wave's private key buffers
 
   bf16x8 a[kQP][KS];
   float wt[kQP][16];
@@ -85,14 +99,14 @@ struct IdxWave {
     }
   }
 
-  template <class Start, class Epi>
+  template <int EPI_VM = 0, class Start, class Epi>
   __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi) {
-    run(k_rs, lds, ntiles, start, epi, [](int) {}, start);
+    run<EPI_VM>(k_rs, lds, ntiles, start, epi, [](int) {}, start);
   }
-  template <class Start, class Epi, class Post>
+  template <int EPI_VM = 0, class Start, class Epi, class Post>
   __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi,
                                       Post post) {
-    run(k_rs, lds, ntiles, start, epi, post, start);
+    run<EPI_VM>(k_rs, lds, ntiles, start, epi, post, start);
   }
 
   // Scores the wave's rows against key tiles j = 0 .. ntiles-1 (ntiles >= 1); tile j holds
@@ -103,44 +117,48 @@ struct IdxWave {
   // the MFMAs of one query tile can overlap the epilogue of the previous one.  phys(j) is
   // where tile j's 32 key rows sit in k_rs (start(j) for a dense key array; a page of a
   // paged cache otherwise): keys are loaded from there, masks and outputs use start(j).
+  // EPI_VM is a lower bound on the vector memory operations that epi and post issue per
+  // tile; the load waits count them (0 is always safe, only slower).
   //
-  // Key tiles pass through the wave's private LDS buffer `lds` (kLdsBytes): global loads
-  // read whole key rows (KPI keys of D_I*2 bytes per instruction) rather than 32 keys x 16
-  // bytes in the MFMA operand layout, and the operand comes back with one ds_read_b128 per
-  // k-step.  Only this wave touches the buffer and one wave's LDS operations complete in
-  // order, so no barrier is needed.  Rows of the next two tiles are in flight in registers
-  // and the next tile's operand is read while the current tile computes.
-  template <class Start, class Epi, class Post, class Phys>
+  // Key tiles go from memory straight into the wave's private LDS buffers (`lds`,
+  // kLdsBytes) with buffer loads that write LDS: each load instruction reads whole key rows
+  // (KPI keys of D_I*2 bytes), so no registers hold rows in flight, and DEPTH tiles are in
+  // flight while one computes.  The next tile's MFMA operand comes back with one
+  // ds_read_b128 per k-step before the current tile computes.  Only this wave touches its
+  // buffers, so there is no barrier: the explicit waits order each tile's LDS writes before
+  // its reads, and a buffer is refilled only after the reads of its previous tile.
+  template <int EPI_VM = 0, class Start, class Epi, class Post, class Phys>
   __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t k_rs, uint8_t* lds, int ntiles, Start start, Epi epi,
                                       Post post, Phys phys) {
     const int lane = threadIdx.x & 63;
-    uint8_t* const wk0 = lds;
-    uint8_t* const wk1 = lds + kTileBytes;
-    // chunk c of key j sits at chunk position c ^ ((j/2) mod 8): the row-wise writes and
-    // the operand reads (32 keys, one chunk each) both spread over all banks
-    auto kl_off = [](int key, int chunk) {
-      return key * (D_I * 2) + ((chunk ^ ((key >> 1) & (CPK < 8 ? CPK - 1 : 7))) << 4);
-    };
-    const int lk = lane / CPK, lc = lane % CPK;
-    const uint32_t lane_koff = (uint32_t)(lk * D_I + lc * 8) * 2;
-    // Tiles are loaded strictly in order (0, 1, 2, ...): one running offset, advanced by the
-    // distance to the next tile's start.  The chain also keeps each tile's loads where the
-    // pipeline puts them (independent offsets let the scheduler bunch two tiles together
-    // and wait for both).
-    uint32_t gkoff = lane_koff + (uint32_t)phys(0) * (D_I * 2);
-    int jn = 0;
-    auto gload = [&](u32x4 (&gr)[NLD]) {
-      asm volatile("" : "+v"(gkoff));
+    constexpr int MASK = CPK < 8 ? CPK - 1 : 7;
+    // chunk c of key j sits at chunk position c ^ ((j/2) & MASK): the operand reads (32 keys,
+    // one chunk each) spread over all banks
+    auto kl_off = [](int key, int chunk) { return key * (D_I * 2) + ((chunk ^ ((key >> 1) & MASK)) << 4); };
+    // load instruction i: lane l fills LDS bytes 16*l of the instruction's KPI keys, i.e.
+    // key i*KPI + l/CPK at chunk position l%CPK, so it reads chunk (l%CPK) ^ swizzle(key)
+    uint32_t loff[NLD];
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) gr[i] = buf_load_16(k_rs, gkoff + i * KPI * D_I * 2, 0);
+    for (int i = 0; i < NLD; ++i) {
+      const int key = i * KPI + lane / CPK;
+      loff[i] = (uint32_t)(key * D_I * 2 + (((lane % CPK) ^ ((key >> 1) & MASK)) << 4));
+    }
+    // Tiles are loaded strictly in order (0, 1, 2, ...): one running offset, advanced by the
+    // distance to the next tile's start.
+    uint32_t gkoff = (uint32_t)phys(0) * (D_I * 2);
+    int jn = 0;
+    auto gload = [&](int buf) {
+      typedef __attribute__((address_space(3))) uint8_t lds_u8;
+      lds_u8* dst = (lds_u8*)(lds + buf * kTileBytes);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rs, (__attribute__((address_space(3))) void*)(dst + i * KPI * D_I * 2),
+                                                 16, gkoff + loff[i], 0, 0, 0);
       gkoff += (uint32_t)(phys(jn + 1) - phys(jn)) * (D_I * 2);
       ++jn;
     };
-    auto lstore = [&](uint8_t* wk, const u32x4 (&gr)[NLD]) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(wk + kl_off(i * KPI + lk, lc)) = gr[i];
-    };
-    auto lread = [&](const uint8_t* wk, bf16x8 (&bk)[KS]) {  // B operand: key col, dims 16s + 8g
+    auto lread = [&](int buf, bf16x8 (&bk)[KS]) {  // B operand: key col, dims 16s + 8g
+      const uint8_t* wk = lds + buf * kTileBytes;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         bk[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(wk + kl_off(col, 2 * s + g)));
@@ -162,24 +180,79 @@ struct IdxWave {
       }
       post(j);
     };
-    u32x4 G0[NLD], G1[NLD];
     bf16x8 B0[KS], B1[KS];
-    gload(G0);  // tile 0
-    gload(G1);  // tile 1
-    lstore(wk0, G0);
-    gload(G0);  // tile 2
-    lread(wk0, B0);
-    for (int j = 0; j < ntiles; j += 2) {
-      lstore(wk1, G1);  // tile j+1
-      gload(G1);        // tile j+3
-      tile(j, B0);
-      lread(wk1, B1);
-      if (j + 1 >= ntiles) break;
-      lstore(wk0, G0);  // tile j+2
-      gload(G0);        // tile j+4
-      tile(j + 1, B1);
-      lread(wk0, B0);
+    constexpr int kWE = EPI_VM < 63 ? EPI_VM : 63;
+    if constexpr (DEPTH == 1) {
+      // tile j+1 loads (into the buffer of tile j-1, read before tile j-1 computed) while
+      // tile j computes; its load is older than tile j's epilogue operations
+      gload(0);
+      vm_wait<0>();
+      lread(0, B0);
+      for (int j = 0; j < ntiles; j += 2) {
+        gload(1);
+        tile(j, B0);
+        vm_wait<kWE>();
+        lread(1, B1);
+        if (j + 1 >= ntiles) break;
+        gload(0);
+        tile(j + 1, B1);
+        vm_wait<kWE>();
+        lread(0, B0);
+      }
+    } else {
+      // Tiles 0 .. DEPTH-1 in flight, tile 0's operand in registers.  Tile j+DEPTH loads into
+      // the buffer of tile j-1 (read before tile j-1 computed); then tile j+1's operand is
+      // read.  At that point the loads of tiles j+2 .. j+DEPTH and the epilogue operations of
+      // tiles max(0, j+1-DEPTH) .. j-1 may still be in flight, and vector memory operations
+      // complete in issue order: the first DEPTH-1 tiles wait as if no epilogue operation
+      // had been issued, the rest count DEPTH-1 tiles' worth.
+      constexpr int kWHead = (DEPTH - 1) * NLD;
+      constexpr int kWFull = (DEPTH - 1) * (NLD + EPI_VM) < 63 ? (DEPTH - 1) * (NLD + EPI_VM) : 63;
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) gload(d);
+      vm_wait<kWHead>();
+      lread(0, B0);
+      int j = 0;
+#pragma unroll
+      for (; j < DEPTH - 1; ++j) {  // unrolled: B0 / B1 alternate with j
+        if (j >= ntiles) break;
+        gload((j + DEPTH) % NB);
+        vm_wait<kWHead>();
+        if (j % 2 == 0) {
+          lread((j + 1) % NB, B1);
+          tile(j, B0);
+        } else {
+          lread((j + 1) % NB, B0);
+          tile(j, B1);
+        }
+      }
+      if constexpr ((DEPTH - 1) % 2 == 0) {
+        for (; j < ntiles; j += 2) {
+          gload((j + DEPTH) % NB);
+          vm_wait<kWFull>();
+          lread((j + 1) % NB, B1);
+          tile(j, B0);
+          if (j + 1 >= ntiles) break;
+          gload((j + 1 + DEPTH) % NB);
+          vm_wait<kWFull>();
+          lread((j + 2) % NB, B0);
+          tile(j + 1, B1);
+        }
+      } else {
+        for (; j < ntiles; j += 2) {
+          gload((j + DEPTH) % NB);
+          vm_wait<kWFull>();
+          lread((j + 1) % NB, B0);
+          tile(j, B1);
+          if (j + 1 >= ntiles) break;
+          gload((j + 1 + DEPTH) % NB);
+          vm_wait<kWFull>();
+          lread((j + 2) % NB, B1);
+          tile(j + 1, B0);
+        }
+      }
     }
+    vm_wait<0>();  // no load may land in the buffers after the wave moves on
   }
 };
 
