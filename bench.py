@@ -338,6 +338,22 @@ def main():
                  "gbs": round((pairs * 4 + T * k * 4) / (topk_ms * 1e-3) / 1e9, 1)},
         "sparse_attn": {"ms": round(attn_ms, 3), "gbs_logical": round(achieved, 1)},
     }
+    # the platform's own bf16 GEMM (torch -> hipBLASLt) on random data, as context for the
+    # indexer's MFMA fraction: a large square product and the indexer's contraction shape
+    # ((query, head) rows x keys, K = d_I)
+    def gemm_tflops(M, N, K):
+        ga = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+        ga @ gb
+        ms = timed(lambda: ga @ gb)
+        return round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)
+
+    ref_sq = gemm_tflops(8192, 8192, 8192)
+    ref_idx = gemm_tflops(T * w.H_I // 4, 2048, w.d_I)
+    kernels["reference_gemm_bf16"] = {"8192x8192x8192_tflops": ref_sq,
+                                      f"{T * w.H_I // 4}x2048x{w.d_I}_tflops": ref_idx,
+                                      "frac_mfma_bf16_square": round(ref_sq / MFMA_BF16_PEAK_TFLOPS, 4)}
+    kernels["index_topk_fused"]["frac_of_square_gemm"] = round(kernels["index_topk_fused"]["tflops"] / ref_sq, 4)
     log(f"kernels: {kernels}")
 
     result = {
