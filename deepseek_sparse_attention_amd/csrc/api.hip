@@ -403,13 +403,15 @@ size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
     case DSA_OP_ATTN: return dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
     case DSA_OP_INDEX_TOPK: return plan_index_topk(*s, false).ws;
     case DSA_OP_ATTN_PAGED: return paged_idx_bytes(*s) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);
+    // stacks: the attention of up to kMaxAttnLayers layers that share an index list runs in
+    // one launch, each layer with its own split partials
     case DSA_OP_STACK_PAGED:  // score chunks (paged keys take the score route) + pool rows + attention
       return align_up(plan_index_topk(*s, true).ws) + paged_idx_bytes(*s) +
-             dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);
+             dsa::kMaxAttnLayers * dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);
     case DSA_OP_STACK: {
       // either route of the 'F' layers fits (DSA_STACK_UNFUSED picks the score chunks)
       const size_t sel = std::max(plan_index_topk(*s, false).ws, plan_index_topk(*s, true).ws);
-      return align_up(sel) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
+      return align_up(sel) + dsa::kMaxAttnLayers * dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
     }
   }
   return 0;
@@ -475,7 +477,7 @@ dsa_status stack_impl(const char* pattern, int n_layers, const dsa_layer_io* lay
     st = translate();
     if (st != DSA_OK) return st;
   }
-  for (int l = 0; l < n_layers; ++l) {
+  for (int l = 0; l < n_layers;) {
     const dsa_layer_io& L = layers[l];
     if (pattern[l] == 'F') {
       st = run_index_topk(P, L.q_idx, L.k_idx, L.w_idx, s, 0.f, index_cache, ws, strm, "dsa_layer_stack: index/top-k",
@@ -490,8 +492,19 @@ dsa_status stack_impl(const char* pattern, int n_layers, const dsa_layer_io* lay
       a.Tk = (int)pool_rows(*pages);
       a.kv_bstride = 0;
     }
-    st = launch_status(dsa::launch_sparse_attn(a, strm), "dsa_layer_stack: attention");
+    // layer l and the 'S' layers right after it read the same indices: when the MLA kernel
+    // splits keys (few query rows, each launch latency-bound) they share one launch
+    int n = 1;
+    if (dsa::attn_mla_supported(a) && dsa::attn_mla_splits(s.B, s.Tq, s.H, s.k) > 1)
+      while (n < dsa::kMaxAttnLayers && l + n < n_layers && pattern[l + n] == 'S') ++n;
+    dsa::AttnLayer group[dsa::kMaxAttnLayers];
+    for (int i = 0; i < n; ++i) {
+      const dsa_layer_io& Li = layers[l + i];
+      group[i] = {static_cast<const uint16_t*>(Li.q), Li.kv, Li.kv_scale, static_cast<uint16_t*>(Li.out), Li.lse};
+    }
+    st = launch_status(dsa::launch_sparse_attn_layers(a, group, n, strm), "dsa_layer_stack: attention");
     if (st != DSA_OK) return st;
+    l += n;
   }
   return DSA_OK;
 }

@@ -175,14 +175,32 @@ struct TileStage<kKvMxfp4> {
 // slower at T=32768 (the extra workgroups' rows then cost more in cache than they gain).
 constexpr int kWideMaxTk = 24576;
 
+// Per-layer operands of one launch: blockIdx.z picks the layer.  Layers that share one
+// index list (an 'F' layer and the 'S' layers after it) run in one launch, so a decode
+// step's short, latency-bound attention layers overlap instead of running back to back.
+struct MlaLayers {
+  const uint16_t* q[kMaxAttnLayers];
+  const uint8_t* kv[kMaxAttnLayers];
+  const float* kv_scale[kMaxAttnLayers];
+  uint16_t* out[kMaxAttnLayers];
+  float* lse[kMaxAttnLayers];
+};
+
 template <int FMT, int WIDE>
-__global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
-                                                          const float* __restrict__ kv_scale,
+__global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLayers Ls,
                                                           const int32_t* __restrict__ idx, int Tq, int Tk,
                                                           int64_t kv_bstride, int H, int k, float scale_log2,
-                                                          int tiles_per_split,
-                                                          uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                          float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                                          int tiles_per_split, float* __restrict__ part_o,
+                                                          float* __restrict__ part_ml, int64_t part_layer) {
+  // layer z's operands; its split partials sit part_layer floats after layer z-1's
+  const int z = blockIdx.z;
+  const uint16_t* __restrict__ q = Ls.q[z];
+  const uint8_t* __restrict__ kv = Ls.kv[z];
+  const float* __restrict__ kv_scale = Ls.kv_scale[z];
+  uint16_t* __restrict__ out = Ls.out[z];
+  float* __restrict__ lse = Ls.lse[z];
+  part_o += z * part_layer;
+  part_ml += z * part_layer;
   constexpr int NBUF = WIDE ? 1 : 2;  // LDS tile buffers
   constexpr int NST = WIDE ? 1 : 2;   // row stages in registers (tiles in flight)
   __shared__ __attribute__((aligned(16))) uint8_t kvs[NBUF][kTile * kRowB];
@@ -409,8 +427,13 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const uint1
 // one wave per head: lane s holds split s's (m, l) (up to 64 splits), the wave reduces
 // them, and each lane then sums 8 output dims over the splits with 16-byte loads.
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                          int nsplit, int64_t nrowh, int H, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
+                                                          int64_t part_layer, int nsplit, int64_t nrowh, int H,
+                                                          const MlaLayers Ls) {
+  const int z = blockIdx.y;  // layer
+  part_o += z * part_layer;
+  part_ml += z * part_layer;
+  uint16_t* __restrict__ out = Ls.out[z];
+  float* __restrict__ lse = Ls.lse[z];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int64_t rh = (int64_t)blockIdx.x * 4 + wave;  // (row, head)
   if (rh >= nrowh) return;
@@ -634,40 +657,51 @@ hipError_t launch_page_translate(const int32_t* idx, int32_t* phys, int B, int T
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers, int nlayers, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Tq;
-  if (rows == 0) return hipSuccess;
+  if (rows == 0 || nlayers < 1) return hipSuccess;
+  if (nlayers > kMaxAttnLayers || (nlayers > 1 && !attn_mla_supported(a))) return hipErrorInvalidValue;
   if (attn_mla_supported(a)) {
     const float sl2 = a.sm_scale * kLog2e;
     const int tiles = (a.k + kTile - 1) / kTile;
     const int nsplit = attn_mla_splits(a.B, a.Tq, a.H, a.k);
     const int per = (tiles + nsplit - 1) / nsplit;
     const int64_t nrowh = rows * a.H;
+    MlaLayers Ls = {};
+    for (int z = 0; z < nlayers; ++z) {
+      Ls.q[z] = layers[z].q;
+      Ls.kv[z] = (const uint8_t*)layers[z].kv;
+      Ls.kv_scale[z] = layers[z].kv_scale;
+      Ls.out[z] = layers[z].out;
+      Ls.lse[z] = layers[z].lse;
+    }
+    // split partials of layer z: one layer's workspace (O then (m, l)) after layer z-1's
     float* part_o = nullptr;
     float* part_ml = nullptr;
+    const int64_t part_layer = (int64_t)(attn_workspace_bytes(a.B, a.Tq, a.H, a.Dv, a.k, true) / sizeof(float));
     if (nsplit > 1) {
       part_o = reinterpret_cast<float*>(a.ws);
       part_ml = part_o + (size_t)nsplit * nrowh * kDv;
     }
-    dim3 grid((unsigned)(rows * (a.H / 16)), nsplit);
+    dim3 grid((unsigned)(rows * (a.H / 16)), nsplit, nlayers);
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
     const bool wide = a.kv_fmt == kKvBf16 && nsplit == 1 && a.Tk <= kWideMaxTk;
+#define DSA_MLA_LAUNCH(F, W)                                                                                       \
+  hipLaunchKernelGGL((mla_attn_kernel<F, W>), grid, dim3(256), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, \
+                     per, part_o, part_ml, part_layer)
     if (a.kv_fmt == kKvFp8)
-      hipLaunchKernelGGL((mla_attn_kernel<kKvFp8, 0>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, a.kv_scale,
-                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+      DSA_MLA_LAUNCH(kKvFp8, 0);
     else if (a.kv_fmt == kKvMxfp4)
-      hipLaunchKernelGGL((mla_attn_kernel<kKvMxfp4, 0>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
-                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+      DSA_MLA_LAUNCH(kKvMxfp4, 0);
     else if (wide)
-      hipLaunchKernelGGL((mla_attn_kernel<kKvBf16, 1>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
-                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+      DSA_MLA_LAUNCH(kKvBf16, 1);
     else
-      hipLaunchKernelGGL((mla_attn_kernel<kKvBf16, 0>), grid, dim3(256), 0, st, a.q, (const uint8_t*)a.kv, nullptr,
-                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, per, a.out, a.lse, part_o, part_ml);
+      DSA_MLA_LAUNCH(kKvBf16, 0);
+#undef DSA_MLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((nrowh + 3) / 4)), dim3(256), 0, st, part_o, part_ml, nsplit,
-                       nrowh, a.H, a.out, a.lse);
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((nrowh + 3) / 4), nlayers), dim3(256), 0, st, part_o,
+                       part_ml, part_layer, nsplit, nrowh, a.H, Ls);
     return hipGetLastError();
   }
   if (attn_mha_supported(a)) {
@@ -691,6 +725,11 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
+  const AttnLayer l0{a.q, a.kv, a.kv_scale, a.out, a.lse};
+  return launch_sparse_attn_layers(a, &l0, 1, st);
 }
 
 }  // namespace dsa

@@ -116,6 +116,18 @@ bool attn_mha_supported(const AttnArgs& a);
 int attn_mla_splits(int B, int Tq, int H, int k);
 size_t attn_workspace_bytes(int B, int Tq, int H, int Dv, int k, bool mla);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+// Layers that share a's index list and shape in one launch (MLA form; at most
+// kMaxAttnLayers): layer z reads layers[z]'s q / kv / kv_scale and writes its out / lse
+// (a's own pointers are not used), and takes the z-th attn_workspace_bytes slice of a.ws.
+constexpr int kMaxAttnLayers = 4;
+struct AttnLayer {
+  const uint16_t* q;
+  const void* kv;
+  const float* kv_scale;
+  uint16_t* out;
+  float* lse;
+};
+hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers, int nlayers, hipStream_t st);
 // Selected keys of sequence b (rows of k entries, Tq rows per sequence) to rows of a paged
 // pool; -1 for entries outside [0, kv_len[b]) or table entries outside the pool.
 hipError_t launch_page_translate(const int32_t* idx, int32_t* phys, int B, int Tq, int k, const int32_t* kv_len,

@@ -286,7 +286,9 @@ typedef struct {
  *            A leading 'S' is rejected unless flags has DSA_CACHE_PREFILLED.
  *   ws       at least dsa_workspace_size(shape, DSA_OP_STACK) bytes: what the 'F' layers'
  *            dsa_index_topk needs (or one chunk of score rows, whichever is larger: the full
- *            Tq x Tk score matrix is never held) plus the attention workspace.
+ *            Tq x Tk score matrix is never held) plus four layers' attention workspace (with
+ *            few query rows, up to four consecutive layers that share the index cache run
+ *            their attention in one launch).
  */
 dsa_status dsa_layer_stack(const char* pattern, int n_layers, const dsa_layer_io* layers,
                            const dsa_shape* shape, int32_t* index_cache, unsigned flags, void* ws,

@@ -52,6 +52,24 @@ def test_indexer_integer_inputs_bit_exact(H_I, d_I, T):
     assert np.all(np.isneginf(got[~c]))  # untouched (the binding pre-fills -inf)
 
 
+@pytest.mark.parametrize("d_I", [16, 32, 64, 128])
+def test_indexer_few_key_tiles_integer_inputs_bit_exact(d_I):
+    # 1 .. 5 key tiles of 32 per wave, with ragged ends: the start and the end of the key
+    # pipeline (tiles in flight, the first iterations' waits) on every key width; square
+    # causal chunks and single query rows (whose waves split the keys)
+    for T in (1, 31, 32, 33, 64, 65, 96, 97, 130, 160):
+        print(f"indexer few tiles d_I={d_I} T={T}", flush=True)
+        d = synth.integer_indexer_inputs(1, T, 16, d_I, seed=9000 + d_I + T, qk_max=1, w_max=2)
+        ref = oracle.index_scores(d["q_idx"], d["k_idx"], d["w_idx"])
+        got = _host(dsa.index_scores(*(d[x].to(DEV) for x in ("q_idx", "k_idx", "w_idx")))).numpy()
+        c = _causal(1, T, T)
+        assert np.array_equal(got[c], ref[c]), T
+        q, w = d["q_idx"][:, -1:].contiguous(), d["w_idx"][:, -1:].contiguous()
+        ref1 = oracle.index_scores(q, d["k_idx"], w)
+        got1 = _host(dsa.index_scores(q.to(DEV), d["k_idx"].to(DEV), w.to(DEV))).numpy()
+        assert np.array_equal(got1, ref1), T
+
+
 @pytest.mark.parametrize("d_I,Tq,Tk", [(64, 1, 5000), (32, 3, 777), (128, 8, 1500)])
 def test_indexer_few_rows_integer_inputs_bit_exact(d_I, Tq, Tk):
     # a few query rows per sequence (decode shapes) take the key-streaming kernel
@@ -360,6 +378,29 @@ def test_decode_step_fss_matches_prefill_row_rule():
         ref, _ = oracle.sparse_attn(_host(layers[l]["q"]), _host(layers[l]["kv"]), ref_idx, w.scale(),
                                     kv_scale=_host(layers[l]["kv_scale"]), Dv=512)
         assert np.max(np.abs(_host(outs[l]).double().numpy() - ref)) <= 2e-2
+
+
+def test_decode_stack_groups_shared_layers_bit_identical_to_single_calls():
+    # with few query rows the attention of an 'F' layer and the 'S' layers after it runs in
+    # one launch (at most four layers per launch): every layer's output and lse must equal
+    # a separate dsa_sparse_attn call on the same indices, bit for bit
+    print("decode grouped layers", flush=True)
+    pattern = "FSSSSSF"  # groups of 4 and 2 layers after the first F, then a lone F layer
+    w = synth.workload("E", B=3, T=3000, pattern=pattern)
+    kcache = synth.decode_indexer_cache(w)
+    first = synth.decode_layer_inputs(w, 0)
+    layers = []
+    for l in range(len(pattern)):
+        d = synth.decode_layer_inputs(w, l)
+        d["q_idx"], d["w_idx"], d["k_idx"] = first["q_idx"], first["w_idx"], kcache  # both F layers: same indices
+        layers.append({k: v.to(DEV) for k, v in d.items()})
+    kv_len = torch.tensor([3000, 2047, 1024], dtype=torch.int32, device=DEV)
+    outs, lses, cache = dsa.layer_stack(pattern, layers, 2048, w.scale(), Dv=512, kv_len=kv_len)
+    torch.cuda.synchronize()
+    for l in range(len(pattern)):
+        o, lse = dsa.sparse_attn(layers[l]["q"], layers[l]["kv"], cache, w.scale(), kv_scale=layers[l]["kv_scale"],
+                                 Dv=512)
+        assert torch.equal(outs[l], o) and torch.equal(lses[l], lse), l
 
 
 def test_empty_batch_and_no_keys():
