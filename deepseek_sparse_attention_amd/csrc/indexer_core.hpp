@@ -123,7 +123,9 @@ struct IdxWave {
   // Key tiles go from memory straight into the wave's private LDS buffers (`lds`,
   // kLdsBytes) with buffer loads that write LDS: each load instruction reads whole key rows
   // (KPI keys of D_I*2 bytes), so no registers hold rows in flight, and DEPTH tiles are in
-  // flight while one computes.  The next tile's MFMA operand comes back with one
+  // flight while one computes (a lane whose row is past the range of k_rs writes zeros to
+  // its LDS slot, as a register load would return them: checked on the device).  The next
+  // tile's MFMA operand comes back with one
   // ds_read_b128 per k-step before the current tile computes.  Only this wave touches its
   // buffers, so there is no barrier: the explicit waits order each tile's LDS writes before
   // its reads, and a buffer is refilled only after the reads of its previous tile.
