@@ -112,8 +112,9 @@ struct AttnArgs {
 bool attn_mla_supported(const AttnArgs& a);
 // Multi-head form: Hkv = H <= 16, Dqk = Dv = 32, separate V, bf16.
 bool attn_mha_supported(const AttnArgs& a);
-// Split-key factor the MLA kernel uses for this shape (1 = no partial results).
-int attn_mla_splits(int B, int Tq, int H, int k);
+// Split-key factor the MLA kernel uses for this shape in a launch of nlayers layers (1 = no
+// partial results); never more than for one layer, whose count sizes the workspace.
+int attn_mla_splits(int B, int Tq, int H, int k, int nlayers = 1);
 size_t attn_workspace_bytes(int B, int Tq, int H, int Dv, int k, bool mla);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 // Layers that share a's index list and shape in one launch (MLA form; at most
