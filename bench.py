@@ -75,6 +75,58 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     print("\n".join(lines))
 
 
+MFMA_FILE = os.path.join(PROFILES, "indexer_t65536_mfma_counters.txt")
+MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU GRBM_GUI_ACTIVE"
+
+
+def summarize_mfma(pmc_csv, trace_csv, out_path=MFMA_FILE):
+    """MFMA counters of the indexer kernels (the fused route's filter and the score kernel)
+    from a `rocprofv3 --pmc ... --kernel-trace` run of the prefill bench: bf16 MFMA work in
+    FLOP (MOPS_BF16 counts units of 512), per-dispatch duration from the kernel trace, and
+    the resulting rate against the 2.5 PFLOP/s peak; VALU instructions per MFMA."""
+    import collections
+    import csv
+
+    dur = {}
+    for r in csv.DictReader(open(trace_csv)):
+        dur[r["Dispatch_Id"]] = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    seen = collections.defaultdict(set)
+    for r in csv.DictReader(open(pmc_csv)):
+        name = r["Kernel_Name"]
+        key = ("fz_filter_kernel<16, 64>" if "fz_filter_kernel<16, 64>" in name else
+               "index_scores_kernel<16, 64, false>" if "index_scores_kernel<16, 64, false>" in name else None)
+        if key is None:
+            continue
+        agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        seen[key].add(r["Dispatch_Id"])
+    lines = [
+        "# bf16 MFMA counters of the indexer kernels at T=65536 (16 heads x 64, workload mla_t65536_k2048_sink)",
+        "# command (from the repository root):",
+        f"#   rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
+        "-d gpurun_out/mfma_D -o mfma -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl",
+        "#   python3 bench.py --summarize-mfma <counter_collection csv> <kernel_trace csv>",
+        "# flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; rate = flop / the dispatches' summed duration;",
+        "# algorithmic indexer work of one layer: 2 x 16 x 64 x T(T+1)/2 = 4.398e12 flop",
+    ]
+    for key in ("fz_filter_kernel<16, 64>", "index_scores_kernel<16, 64, false>"):
+        if key not in agg:
+            continue
+        c, ids = agg[key], seen[key]
+        t = sum(dur.get(i, 0.0) for i in ids)
+        flop = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        lines += [f"kernel: {key}", f"  dispatches: {len(ids)}", f"  seconds: {t:.6f}",
+                  f"  mfma_flop: {flop:.4e}",
+                  f"  tflops: {flop / t / 1e12 if t else 0:.1f}",
+                  f"  frac_of_2.5_pflops: {flop / t / 2.5e15 if t else 0:.4f}",
+                  f"  valu_insts_per_mfma: {c.get('SQ_INSTS_VALU', 0) / max(1.0, c.get('SQ_INSTS_MFMA', 0)):.2f}"]
+        for n in sorted(c):
+            lines.append(f"  {n}: {c[n]:.6g}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 STATS_FILE = os.path.join(PROFILES, "prefill_t65536_k2048_kernel_stats.txt")
 
 
@@ -207,6 +259,8 @@ def parse():
                     help="write the HBM traffic summary from two rocprofv3 --pmc counter CSVs and exit")
     ap.add_argument("--configs", action="store_true",
                     help="time one step of each workload A-E (one JSON line each) instead of the headline")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_CSV", "TRACE_CSV"),
+                    help="write the indexer MFMA counter summary under profiles/ and exit")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
                     help="write the per-kernel summary from a rocprofv3 kernel_stats.csv and exit")
     return ap.parse_args()
@@ -231,6 +285,9 @@ def main():
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
