@@ -129,12 +129,13 @@ def abi_version() -> int:
 
 
 def index_scores(q_idx, k_idx, w_idx, kv_len=None, scores=None, ld=None, stream=None):
-    """dsa_index_scores: returns the fp32 score tensor [B, Tq, ld] (entries s > p untouched)."""
+    """dsa_index_scores: returns the fp32 score tensor [B, Tq, ld] (the library writes -inf
+    into entries s > p)."""
     B, Tq, H_I, d_I = q_idx.shape
     Tk = k_idx.shape[1]
     ld = Tk if ld is None else ld
     if scores is None:
-        scores = torch.full((B, Tq, ld), float("-inf"), dtype=torch.float32, device=q_idx.device)
+        scores = torch.empty((B, Tq, ld), dtype=torch.float32, device=q_idx.device)
     _check(lib().dsa_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(kv_len), B, Tq, Tk, H_I, d_I,
                                   _ptr(scores), ld, _stream(stream)))
     return scores
@@ -169,7 +170,7 @@ def index_scores_paged(q_idx, k_pool, w_idx, pages, Tk, kv_len=None, scores=None
     B, Tq, H_I, d_I = q_idx.shape
     ld = Tk if ld is None else ld
     if scores is None:
-        scores = torch.full((B, Tq, ld), float("-inf"), dtype=torch.float32, device=q_idx.device)
+        scores = torch.empty((B, Tq, ld), dtype=torch.float32, device=q_idx.device)
     _check(lib().dsa_index_scores_paged(_ptr(q_idx), _ptr(k_pool), _ptr(w_idx), ctypes.byref(pages), _ptr(kv_len),
                                         B, Tq, Tk, H_I, d_I, _ptr(scores), ld, _stream(stream)))
     return scores

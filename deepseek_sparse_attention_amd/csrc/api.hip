@@ -241,7 +241,10 @@ const char* dsa_status_string(dsa_status s) {
 dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_idx, const int32_t* kv_len, int B,
                             int Tq, int Tk, int H_I, int d_I, float* scores, int64_t ld, void* stream) {
   dsa_status st = check_indexer(q_idx, k_idx, w_idx, B, Tq, Tk, H_I, d_I, scores, ld);
-  if (st != DSA_OK || (int64_t)B * Tq == 0 || Tk == 0) return st;
+  if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
+  st = launch_status(dsa::launch_fill_masked(scores, ld, (int64_t)Tq * ld, kv_len, B, Tq, Tk, as_stream(stream)),
+                     "dsa_index_scores: -inf fill");
+  if (st != DSA_OK || Tk == 0) return st;
   dsa::IndexerArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, kv_len, B, Tq, Tk,
                      H_I, d_I, 0, Tq, scores, ld, (int64_t)Tq * ld};
   return launch_status(dsa::launch_index_scores(a, as_stream(stream)), "dsa_index_scores");
@@ -313,7 +316,10 @@ dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const v
   dsa_status st = check_indexer(q_idx, k_pool, w_idx, B, Tq, Tk, H_I, d_I, scores, ld);
   if (st != DSA_OK) return st;
   st = check_pages(pages, Tk, (int64_t)d_I * 2, INT64_MAX, "key");
-  if (st != DSA_OK || (int64_t)B * Tq == 0 || Tk == 0) return st;
+  if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
+  st = launch_status(dsa::launch_fill_masked(scores, ld, (int64_t)Tq * ld, kv_len, B, Tq, Tk, as_stream(stream)),
+                     "dsa_index_scores_paged: -inf fill");
+  if (st != DSA_OK || Tk == 0) return st;
   dsa::IndexerArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_pool, (const uint16_t*)w_idx, kv_len, B, Tq, Tk,
                      H_I, d_I, 0, Tq, scores, ld, (int64_t)Tq * ld};
   a.block_table = pages->block_table;

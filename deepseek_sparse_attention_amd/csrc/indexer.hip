@@ -108,7 +108,38 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Entries s = p+1 .. ld-1 of every score row (keys a query cannot see, and the row's
+// padding past Tk) become -inf, so a caller's row is defined everywhere.  One workgroup
+// per row: scalar stores up to a 16-byte boundary, then 16-byte stores, then the tail.
+__global__ __launch_bounds__(256) void fill_masked_kernel(float* __restrict__ scores, int64_t ld,
+                                                          int64_t score_bstride, const int32_t* __restrict__ kv_len,
+                                                          int Tq, int Tk) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x;
+  const int64_t p = seq_len(kv_len, b, Tk) - Tq + r;  // last visible key (< 0: none)
+  const int64_t s0 = p < 0 ? 0 : p + 1;
+  if (s0 >= ld) return;
+  float* row = scores + (int64_t)b * score_bstride + (int64_t)r * ld;
+  const float ninf = -INFINITY;
+  // first 16-byte-aligned entry at or after s0
+  const int64_t mis = (int64_t)((reinterpret_cast<uintptr_t>(row + s0) >> 2) & 3);
+  const int64_t a0 = min(ld, s0 + ((4 - mis) & 3));
+  const int64_t nvec = (ld - a0) >> 2;
+  for (int64_t s = s0 + threadIdx.x; s < a0; s += 256) row[s] = ninf;
+  float4* v = reinterpret_cast<float4*>(row + a0);
+  for (int64_t i = threadIdx.x; i < nvec; i += 256) v[i] = make_float4(ninf, ninf, ninf, ninf);
+  for (int64_t s = a0 + 4 * nvec + threadIdx.x; s < ld; s += 256) row[s] = ninf;
+}
+
 }  // namespace
+
+hipError_t launch_fill_masked(float* scores, int64_t ld, int64_t score_bstride, const int32_t* kv_len, int B, int Tq,
+                              int Tk, hipStream_t st) {
+  if ((int64_t)B * Tq == 0 || ld == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_masked_kernel, dim3((unsigned)Tq, (unsigned)B), dim3(256), 0, st, scores, ld, score_bstride,
+                     kv_len, Tq, Tk);
+  return hipGetLastError();
+}
 
 bool indexer_supported(int H_I, int d_I, int64_t ld) {
   // a wave's score rows (at most 4 * 32/H_I of them) are addressed with 32-bit byte offsets

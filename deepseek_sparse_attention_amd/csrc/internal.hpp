@@ -28,6 +28,10 @@ struct IndexerArgs {
 constexpr int64_t kIndexerMaxLd = int64_t(1) << 22;
 bool indexer_supported(int H_I, int d_I, int64_t ld);
 hipError_t launch_index_scores(const IndexerArgs& a, hipStream_t st);
+// -inf into entries p+1 .. ld-1 of each score row (row r of sequence b at
+// scores + b*score_bstride + r*ld, query position p = kv_len[b] - Tq + r).
+hipError_t launch_fill_masked(float* scores, int64_t ld, int64_t score_bstride, const int32_t* kv_len, int B, int Tq,
+                              int Tk, hipStream_t st);
 
 // Top-k for rows [row0, row0 + nrows): score row r of sequence b at
 // scores + b*score_bstride + r*ld; index row (row0 + r) of sequence b at

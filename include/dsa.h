@@ -39,7 +39,10 @@
  *     the caller's next synchronization.  dsa_last_error() gives a message for the calling
  *     thread's last failure.
  *   - Determinism: identical inputs and shapes give bit-identical outputs (fixed reduction
- *     orders, no floating-point atomics), whatever chunk size the library picks.
+ *     orders), whatever chunk size the library picks.  Inside dsa_layer_stack, the attention
+ *     of an 'F' layer and the 'S' layers after it may run as one launch with fewer key splits
+ *     per layer than a lone dsa_sparse_attn call takes (few query rows), so such a layer's
+ *     outputs can differ from the lone call's in the last bits (not between runs).
  *   - Thread safety: re-entrant; concurrent calls on different streams need separate
  *     workspaces.
  */
@@ -111,7 +114,8 @@ const char* dsa_status_string(dsa_status s);
  *   w_idx  bf16 [B][Tq][H_I]       per-query head weights
  *   scores fp32 [B][Tq][ld], ld >= Tk: for every row, entries s = 0..p are written with
  *          I[t,s] (fp32 accumulation of the bf16 products, ReLU per head, then the weighted
- *          head sum in head order); entries s > p are not written.
+ *          head sum in head order) and entries s = p+1 .. ld-1 (keys the query cannot see,
+ *          then the padding past Tk) with -inf; every entry of every row is written.
  * Supported: H_I in {1,2,4,8,16}, d_I in {16,32,64,128}, ld <= 2^22.
  */
 dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_idx,
@@ -165,7 +169,8 @@ dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_id
  *   kv_scale fp32 [B][Tk] for fp8 (key row value = e4m3 value * kv_scale[b][s]); else NULL
  *   v     bf16 [B][Tk][Hkv][Dv], or NULL: V is kv[..., 0:Dv] (MLA shared latent row)
  *   idx   int32 [B][Tq][k]: key indices per query row, shared by all heads; entries
- *         outside [0, Tk) (e.g. the -1 padding) are skipped
+ *         outside [0, Tk) (e.g. the -1 padding) are skipped, and a key listed twice is two
+ *         terms of the softmax sum
  *   out   bf16 [B][Tq][H][Dv] = sum_s softmax_s(sm_scale * q[h].K[s]) V[s] over valid s
  *         (0 for a row with no valid entry); head h reads kv head h*Hkv/H
  *   lse   fp32 [B][Tq][H] natural-log sum-exp of the scaled logits (-inf if none), or NULL
@@ -226,7 +231,8 @@ typedef struct {
 /*
  * dsa_index_scores with the indexer keys in a paged pool:
  *   k_pool bf16 [num_pages * page_size][d_I]; other arguments and results as there (Tk = the
- *   longest sequence; kv_len gives each sequence's length).  Same scores, bit for bit.
+ *   longest sequence; kv_len gives each sequence's length; -inf past each row's last key).
+ *   Same scores, bit for bit.
  * Supported: as dsa_index_scores, and num_pages * page_size * d_I * 2 < 2^32 bytes.
  */
 dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w_idx,

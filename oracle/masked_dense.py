@@ -28,18 +28,29 @@ def index_scores(q_idx, k_idx, w_idx) -> np.ndarray:
     return np.where(causal[None], scores, -np.inf)
 
 
-def selection_mask(idx, Tk: int) -> np.ndarray:
-    """Boolean [B, Tq, Tk]: True where key s is in query row i's index list."""
+def selection_counts(idx, Tk: int) -> np.ndarray:
+    """Integer [B, Tq, Tk]: how many entries of query row i's index list name key s.
+
+    A key listed twice is two terms of the softmax sum, as in the gather form, which adds
+    one term per index entry."""
     ix = np.asarray(idx)
     B, Tq, k = ix.shape
-    m = np.zeros((B, Tq, Tk), bool)
+    c = np.zeros((B, Tq, Tk), np.int64)
     b, t, j = np.nonzero(ix >= 0)
-    m[b, t, ix[b, t, j]] = True
-    return m
+    np.add.at(c, (b, t, ix[b, t, j]), 1)
+    return c
+
+
+def selection_mask(idx, Tk: int) -> np.ndarray:
+    """Boolean [B, Tq, Tk]: True where key s is in query row i's index list."""
+    return selection_counts(idx, Tk) > 0
 
 
 def sparse_attn(q, kv, idx, sm_scale, v=None, Dv=None, kv_scale=None):
-    """Masked dense attention: softmax over the selected keys only, (out, lse) float64."""
+    """Masked dense attention: softmax over the selected keys only, (out, lse) float64.
+
+    Each key's exponential is weighted by the number of entries that name it, so a
+    duplicated entry counts twice, exactly as a sum over the index list would."""
     qd = _f64(q)
     if kv_scale is not None:
         raise NotImplementedError("fp8 rows: decode them first")
@@ -49,10 +60,10 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, Dv=None, kv_scale=None):
     Tk, Hkv = K.shape[1], K.shape[2]
     g = np.arange(H) * Hkv // H
     logits = sm_scale * np.einsum("bthd,bshd->bhts", qd, K[:, :, g, :])
-    mask = selection_mask(idx, Tk)[:, None, :, :]
-    logits = np.where(mask, logits, -np.inf)
+    count = selection_counts(idx, Tk)[:, None, :, :]
+    logits = np.where(count > 0, logits, -np.inf)
     m = logits.max(axis=-1, keepdims=True)
-    p = np.exp(logits - m)
+    p = count * np.exp(logits - m)
     denom = p.sum(axis=-1, keepdims=True)
     out = np.einsum("bhts,bshd->bthd", p / denom, V[:, :, g, :])
     lse = (m + np.log(denom))[..., 0].transpose(0, 2, 1)

@@ -43,10 +43,10 @@ def test_indexer_argument_checks(L):
     assert L.dsa_index_scores(None, P, P, None, 1, 4, 4, 16, 64, P, 4, None) == 1          # NULL
     assert L.dsa_index_scores(P, P, P, None, -1, 4, 4, 16, 64, P, 4, None) == 2            # negative B
     assert L.dsa_index_scores(P, P, P, None, 1, 4, 4, 16, 64, P, 3, None) == 2             # ld < Tk
+    assert b"ld must be >= Tk" in L.dsa_last_error()
     assert L.dsa_index_scores(P, P, P, None, 1, 4, 4, 3, 64, P, 4, None) == 3              # H_I
     assert L.dsa_index_scores(P, P, P, None, 1, 4, 4, 16, 48, P, 4, None) == 3             # d_I
     assert L.dsa_index_scores(None, None, None, None, 0, 4, 4, 16, 64, None, 4, None) == 0  # empty batch
-    assert b"ld" in L.dsa_last_error() or True
 
 
 def test_topk_argument_checks(L):

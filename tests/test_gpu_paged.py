@@ -68,6 +68,7 @@ def test_paged_indexer_matches_dense(page, Tq, d_I):
     L = np.array(lens)[:, None, None]
     c = np.arange(Tk)[None, None, :] <= (L - Tq + np.arange(Tq)[None, :, None])
     assert np.array_equal(paged[c], dense[c])
+    assert np.all(np.isneginf(paged[~c])) and np.all(np.isneginf(dense[~c]))  # written by the library
     # and the dense scores are the oracle's (integer inputs: exact)
     ref = oracle.index_scores(q, d["k_idx"], w, kv_len=lens)
     assert np.array_equal(dense[c], ref[c])

@@ -48,6 +48,9 @@ MUTATIONS = {
     "kl_scale_dropped": ("z[e] = c->sm_scale * dot;", "z[e] = dot;"),
     "kl_reverse_direction": ("if (P[e] > 0.0) L += P[e] * (log(P[e]) - logQ);",
                              "L += exp(logQ) * (logQ - log(P[e]));"),
+    "stream_row_excludes_own_key": ("int32_t kv_len = t + 1;", "int32_t kv_len = t;"),
+    "stream_row_query_of_previous_row": ("attn_ctx ac = {c->q + (int64_t)t * c->H * c->Dqk,",
+                                         "attn_ctx ac = {c->q + (int64_t)(t > 0 ? t - 1 : 0) * c->H * c->Dqk,"),
     "value_from_key_tail": ("if (!c->v) return kv_value(c, b, s, g, d);",
                             "if (!c->v) return kv_value(c, b, s, g, d + (c->Dqk - c->Dv));"),
 }
@@ -62,6 +65,9 @@ def _run_pins():
             if t.__name__ == "test_topk_matches_numpy_lexsort_with_heavy_ties":
                 for k in (1, 3, 8, 33):
                     t(k)
+            elif t.__name__ == "test_streamed_rows_equal_scores_topk_attention_composed":
+                for fmt in ("bf16", "fp8", "mxfp4"):
+                    t(fmt)
             else:
                 t()
         except Exception:  # noqa: BLE001 - any failure counts as caught

@@ -408,6 +408,56 @@ def test_masked_dense_attention_agrees_with_gather_oracle():
         assert np.max(np.abs(out - ref)) < 1e-12 and np.max(np.abs(lse - rlse)) < 1e-12
 
 
+def test_duplicate_entries_count_twice_in_both_forms():
+    # an index list that names a key twice puts two terms for it in the softmax sum: with
+    # q = 0 every logit is 0, so the output is the entry-weighted mean of the value rows
+    # (2 V_a + V_b) / 3 and lse = ln 3; the gather form and the masked-dense form agree
+    T, D = 8, 576
+    g = torch.Generator().manual_seed(11)
+    kv = torch.randn(1, T, 1, D, generator=g).to(torch.bfloat16)
+    q = torch.zeros(1, 2, 16, D).to(torch.bfloat16)
+    idx = np.array([[[3, 3, 5, -1], [1, 6, 6, 6]]], np.int32)
+    V = kv[0, :, 0, :512].double().numpy()
+    for out, lse in (oracle.sparse_attn(q, kv, idx, 0.05, Dv=512),
+                     masked_dense.sparse_attn(q, kv, idx, 0.05, Dv=512)):
+        assert np.allclose(out[0, 0], np.tile((2 * V[3] + V[5]) / 3, (16, 1)), rtol=0, atol=1e-13)
+        assert np.allclose(out[0, 1], np.tile((V[1] + 3 * V[6]) / 4, (16, 1)), rtol=0, atol=1e-13)
+        assert np.allclose(lse[0, 0], math.log(3), atol=1e-13) and np.allclose(lse[0, 1], math.log(4), atol=1e-13)
+    # random sharp inputs with repeated entries: the two forms agree to rounding
+    w_ = synth.workload("B", T=48, k=24)
+    d = synth.sharp_attention_inputs(w_)
+    rng = np.random.default_rng(12)
+    idx = np.stack([np.sort(rng.integers(0, t + 1, size=24)) for t in range(48)])[None].astype(np.int32)
+    idx[0, ::5, -3:] = -1
+    out, lse = oracle.sparse_attn(d["q"], d["kv"], idx, w_.scale(), Dv=512)
+    ref, rlse = masked_dense.sparse_attn(d["q"], d["kv"], idx, w_.scale(), Dv=512)
+    assert np.max(np.abs(out - ref)) < 1e-12 and np.max(np.abs(lse - rlse)) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_streamed_rows_equal_scores_topk_attention_composed(fmt):
+    # the CPU baseline's row-streaming entry runs scores -> top-k -> attention for single
+    # rows of a prefill; it must equal the three separate calls on the whole sequence, rows
+    # on both sides of k and the first and last rows included
+    T, k = 300, 64
+    w_ = synth.workload("B", T=T, k=k)
+    d = synth.layer_inputs(w_, 0, indexer=True)
+    kv, sc = d["kv"], None
+    if fmt == "fp8":
+        codes, sc = synth.fp8_e4m3_rows(d["kv"].float()[:, :, 0])
+        kv = codes.unsqueeze(2)
+    elif fmt == "mxfp4":
+        kv = synth.mxfp4_rows(d["kv"].float()[:, :, 0]).unsqueeze(2)
+    rows = np.array([0, 1, 62, 63, 64, 65, 150, 298, 299], np.int32)
+    idx_s, out_s = oracle.dsa_rows(d["q_idx"], d["k_idx"], d["w_idx"], d["q"], kv, rows, k, w_.scale(),
+                                   kv_scale=sc)
+    scores = oracle.index_scores(d["q_idx"], d["k_idx"], d["w_idx"])
+    idx = oracle.topk(scores, k)
+    ref, _ = oracle.sparse_attn(d["q"][:, rows], kv, idx[:, rows], w_.scale(), kv_scale=sc, Dv=512)
+    assert np.array_equal(idx_s, idx[0, rows])
+    assert np.max(np.abs(out_s - ref[0])) < 1e-12
+
+
 def test_attention_row_without_valid_entry_and_nan_key():
     # no valid entry: out 0 and lse -inf; a selected NaN key: the sum of exponentials and
     # everything after it is NaN (the -inf rule is for an empty selection only)
