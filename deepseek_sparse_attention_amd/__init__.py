@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = [
-    "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "layer_stack",
+    "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "sparse_attn_noalloc",
+    "noalloc_scratch_bytes", "layer_stack",
     "index_scores_paged", "sparse_attn_paged", "indexer_kl", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
     "KV_BF16", "KV_FP8_E4M3", "KV_MXFP4", "mxfp4_row_bytes", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
@@ -93,6 +94,8 @@ def lib():
         L.dsa_layer_stack_paged.argtypes = [ctypes.c_char_p, I, P, ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), P,
                                             U, P, SZ, P]
         L.dsa_sparse_attn.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, F, P, P, P, SZ, P]
+        L.dsa_sparse_attn_noalloc.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, F, P, P, P]
+        L.dsa_noalloc_scratch_bytes.restype = SZ
         L.dsa_layer_stack.argtypes = [ctypes.c_char_p, I, P, ctypes.POINTER(Shape), P, U, P, SZ, P]
         L.dsa_workspace_size.argtypes = [ctypes.POINTER(Shape), I]
         L.dsa_workspace_size.restype = SZ
@@ -101,7 +104,8 @@ def lib():
         L.dsa_check_pattern.argtypes = [ctypes.c_char_p, I, U]
         L.dsa_pattern_from_freq.argtypes = [I, I, ctypes.c_char_p]
         L.dsa_indexer_kl.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, P]
-        for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_layer_stack",
+        for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_sparse_attn_noalloc",
+                  "dsa_layer_stack",
                   "dsa_check_pattern", "dsa_pattern_from_freq", "dsa_index_scores_paged", "dsa_sparse_attn_paged",
                   "dsa_layer_stack_paged", "dsa_indexer_kl"):
             getattr(L, f).restype = I
@@ -283,6 +287,31 @@ def sparse_attn(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, 
     _check(lib().dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(v), kvd, _ptr(idx), B, Tq, Tk, H, Hkv,
                                  Dqk, Dv, k, sm_scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
     return out, lse
+
+
+def sparse_attn_noalloc(q, kv, idx, sm_scale, v=None, kv_scale=None, Dv=None, out=None, lse=None, want_lse=True,
+                        stream=None):
+    """dsa_sparse_attn_noalloc: dsa_sparse_attn with the library's built-in scratch instead of
+    a workspace (outputs are allocated here unless given)."""
+    B, Tq, H, Dqk = q.shape
+    Tk, Hkv = kv.shape[1], kv.shape[2]
+    kvd = _kv_dtype(kv, Dqk, kv_scale)
+    if v is not None:
+        Dv = v.shape[3]
+    elif Dv is None:
+        raise ValueError("Dv is required when V is taken from the kv rows")
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, Tq, H, Dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
+    _check(lib().dsa_sparse_attn_noalloc(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(v), kvd, _ptr(idx), B, Tq, Tk, H,
+                                         Hkv, Dqk, Dv, k, sm_scale, _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return lib().dsa_noalloc_scratch_bytes()
 
 
 def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=None, prefilled=False,

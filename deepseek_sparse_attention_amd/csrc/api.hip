@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "dsa.h"
@@ -375,6 +376,70 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale,
   dsa_status st = check_attn(a, ws_bytes);
   if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
   return launch_status(dsa::launch_sparse_attn(a, as_stream(stream)), "dsa_sparse_attn");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device-resident scratch of dsa_sparse_attn_noalloc: the split-key partial results of a
+// call live here instead of in a caller's workspace.  Each device holds its own copy from
+// the library's load until the process ends; host code addresses it only through the
+// pointer hipGetSymbolAddress returns for the current device (the array's name is a host
+// stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = size_t(20) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device (with it current).
+dsa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_DEVICE, std::string("dsa_sparse_attn_noalloc: no usable device: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DSA_ERR_DEVICE, std::string("dsa_sparse_attn_noalloc: scratch lookup failed: ") +
+                                      hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+dsa_status dsa_sparse_attn_noalloc(const void* q, const void* kv, const float* kv_scale, const void* v,
+                                   dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk, int H, int Hkv,
+                                   int Dqk, int Dv, int k, float sm_scale, void* out, float* lse, void* stream) {
+  if (!valid_kv_dtype(kv_dtype)) return fail(DSA_ERR_SHAPE, "unknown kv dtype");
+  dsa::AttnArgs a = attn_args(q, kv, kv_scale, v, kv_dtype, idx, B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, out, lse,
+                              nullptr);
+  // the workspace check below is the scratch limit; check_attn sees an unlimited one
+  const size_t need = dsa::attn_workspace_bytes(B, Tq, H, Dv, k, dsa::attn_mla_supported(a));
+  a.ws = reinterpret_cast<void*>(uintptr_t(256));  // alignment placeholder for the checks only
+  dsa_status st = check_attn(a, (size_t)-1);
+  if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
+  if (need > kNoAllocScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attn_noalloc: this shape needs " + std::to_string(need) +
+                                         " bytes of split-key scratch; the built-in scratch holds " +
+                                         std::to_string(kNoAllocScratchBytes) + " (use dsa_sparse_attn with a workspace)");
+  a.ws = nullptr;
+  if (need) {
+    st = scratch_for_current_device(&a.ws);
+    if (st != DSA_OK) return st;
+  }
+  return launch_status(dsa::launch_sparse_attn(a, as_stream(stream)), "dsa_sparse_attn_noalloc");
 }
 
 dsa_status dsa_check_pattern(const char* pattern, int n_layers, unsigned flags) {

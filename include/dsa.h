@@ -258,6 +258,27 @@ dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float
                                  int H, int Dqk, int Dv, int k, float sm_scale, void* out,
                                  float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * dsa_sparse_attn for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments and
+ * results without ws / ws_bytes.  The split-key partial results that few-row (decode)
+ * shapes need go to a scratch area built into the library, one per device, held from the
+ * library's load until the process ends; the call itself never allocates.  The shapes that
+ * need no workspace (dsa_workspace_size(shape, DSA_OP_ATTN) == 0) use none.
+ *   Limit: dsa_noalloc_scratch_bytes() bytes (20 MiB) of partial results, i.e. the
+ *   workspace dsa_sparse_attn would take for the shape (16.8 MB for 64 decode rows of 16
+ *   heads at k = 2048); larger shapes return DSA_ERR_UNSUPPORTED with nothing enqueued.
+ *   Every call on one device shares that device's scratch and overwrites it: calls whose
+ *   work overlaps on one device (different streams, or host threads without ordering)
+ *   race and give undefined outputs.  Calls ordered on one stream are safe.
+ * Outputs equal dsa_sparse_attn's for the same inputs, bit for bit.
+ */
+dsa_status dsa_sparse_attn_noalloc(const void* q, const void* kv, const float* kv_scale, const void* v,
+                                   dsa_kv_dtype kv_dtype, const int32_t* idx, int B, int Tq, int Tk,
+                                   int H, int Hkv, int Dqk, int Dv, int k, float sm_scale, void* out,
+                                   float* lse, void* stream);
+size_t dsa_noalloc_scratch_bytes(void);
+
 /* Shape of one layer of a stack (all layers share it). */
 typedef struct {
   int B, Tq, Tk;        /* sequences, query rows per sequence, keys per sequence */
