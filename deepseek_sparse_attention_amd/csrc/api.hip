@@ -548,9 +548,11 @@ dsa_status stack_impl(const char* pattern, int n_layers, const dsa_layer_io* lay
     st = translate();
     if (st != DSA_OK) return st;
   }
+  bool any_full = false;
   for (int l = 0; l < n_layers;) {
     const dsa_layer_io& L = layers[l];
     if (pattern[l] == 'F') {
+      any_full = true;
       st = run_index_topk(P, L.q_idx, L.k_idx, L.w_idx, s, 0.f, index_cache, ws, strm, "dsa_layer_stack: index/top-k",
                           pages);
       if (st == DSA_OK && pages) st = translate();
@@ -558,6 +560,12 @@ dsa_status stack_impl(const char* pattern, int n_layers, const dsa_layer_io* lay
     }
     dsa::AttnArgs a = attn_args(L.q, L.kv, L.kv_scale, L.v, s.kv_dtype, index_cache, s.B, s.Tq, s.Tk, s.H, s.Hkv,
                                 s.Dqk, s.Dv, s.k, s.sm_scale, L.out, L.lse, attn_ws);
+    // the cache holds this library's top-k rows (valid entries first), unless the caller
+    // prefilled it and no 'F' layer has run yet
+    if (!(flags & DSA_CACHE_PREFILLED) || any_full) {
+      a.tail_kv_len = s.kv_len;
+      a.tail_Tk = s.Tk;
+    }
     if (pages) {
       a.idx = phys;
       a.Tk = (int)pool_rows(*pages);

@@ -186,12 +186,17 @@ struct MlaLayers {
   float* lse[kMaxAttnLayers];
 };
 
+// tail_kv_len / tail_Tk (tail_Tk > 0): every row's valid entries are its first min(k, p+1),
+// p its position among sequences of tail_kv_len[b] (NULL: tail_Tk) keys, as the library's
+// own top-k writes them; the kernel then takes its tile count from p instead of scanning the
+// list for the last valid entry.
 template <int FMT, int WIDE>
 __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLayers Ls,
                                                           const int32_t* __restrict__ idx, int Tq, int Tk,
                                                           int64_t kv_bstride, int H, int k, float scale_log2,
                                                           int tiles_per_split, float* __restrict__ part_o,
-                                                          float* __restrict__ part_ml, int64_t part_layer) {
+                                                          float* __restrict__ part_ml, int64_t part_layer,
+                                                          const int32_t* __restrict__ tail_kv_len, int tail_Tk) {
   // layer z's operands; its split partials sit part_layer floats after layer z-1's
   const int z = blockIdx.z;
   const uint16_t* __restrict__ q = Ls.q[z];
@@ -202,7 +207,10 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
   part_o += z * part_layer;
   part_ml += z * part_layer;
   constexpr int NBUF = WIDE ? 1 : 2;  // LDS tile buffers
-  constexpr int NST = WIDE ? 1 : 2;   // row stages in registers (tiles in flight)
+  // row stages in registers (tiles in flight).  (Three stages for fp8 rows and four for
+  // MXFP4 rows gave the 64-row decode step no gain: its tiles wait on the tile body, not on
+  // the gather.)
+  constexpr int NST = WIDE ? 1 : 2;
   __shared__ __attribute__((aligned(16))) uint8_t kvs[NBUF][kTile * kRowB];
   __shared__ __attribute__((aligned(16))) f32x4 sbuf[4][64];           // partial S^T per wave and lane
   __shared__ __attribute__((aligned(16))) float tile_bias[NBUF][kTile];   // 0 for a valid key, -inf otherwise
@@ -264,34 +272,37 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
 
   // prologue: index entries of tiles t_begin .. t_begin + 2*NST - 1, rows of the first NST
   // in flight
-  TileStage<FMT> st0, st1;
-  int nx0, nx1 = 0;
+  TileStage<FMT> st[NST];
+  int nx[NST];
   {
-    const int e0 = raw_entry(t_begin);
-    if constexpr (NST == 2) {
-      const int e1 = raw_entry(t_begin + 1);
-      nx0 = raw_entry(t_begin + 2);
-      nx1 = raw_entry(t_begin + 3);
-      fetch(st0, valid_entry(t_begin, e0));
-      fetch(st1, valid_entry(t_begin + 1, e1));
-    } else {
-      nx0 = raw_entry(t_begin + 1);
-      fetch(st0, valid_entry(t_begin, e0));
-    }
+    int e[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) e[j] = raw_entry(t_begin + j);
+#pragma unroll
+    for (int j = 0; j < NST; ++j) nx[j] = raw_entry(t_begin + NST + j);
+#pragma unroll
+    for (int j = 0; j < NST; ++j) fetch(st[j], valid_entry(t_begin + j, e[j]));
   }
 
   // extent of this split's entries that are valid: the loop ends after its last tile
-  int jm = -1;
-  for (int j = t_begin * kTile + tid; j < min(k, t_lim * kTile); j += 256) {
-    const int sj = ix[j];
-    if (sj >= 0 && sj < Tk) jm = j;
-  }
+  int t_end;
+  if (tail_Tk > 0) {
+    const int64_t p = seq_len(tail_kv_len, b, tail_Tk) - Tq + (int)(row % Tq);
+    const int64_t nv = min((int64_t)k, p + 1);
+    t_end = min(t_lim, (int)((max(nv, (int64_t)0) + kTile - 1) / kTile));
+  } else {
+    int jm = -1;
+    for (int j = t_begin * kTile + tid; j < min(k, t_lim * kTile); j += 256) {
+      const int sj = ix[j];
+      if (sj >= 0 && sj < Tk) jm = j;
+    }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
-  if (lane == 0) jmax_red[wave] = jm;
-  __syncthreads();
-  jm = max(max(jmax_red[0], jmax_red[1]), max(jmax_red[2], jmax_red[3]));
-  const int t_end = min((jm + kTile) / kTile, t_lim);  // tiles covering entries 0..jm
+    for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
+    if (lane == 0) jmax_red[wave] = jm;
+    __syncthreads();
+    jm = max(max(jmax_red[0], jmax_red[1]), max(jmax_red[2], jmax_red[3]));
+    t_end = min((jm + kTile) / kTile, t_lim);  // tiles covering entries 0..jm
+  }
 
   f32x4 o_acc[8];  // O^T: rows = dims wave*128 + n*16 + 4gq + i, column = head hl
 #pragma unroll
@@ -386,15 +397,15 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
     }
   };
 
-  if constexpr (NST == 1) {
-    for (int t = t_begin; t < t_end; ++t) tile(t, st0, nx0);
-  } else {
+  {
     int t = t_begin;
-    for (; t + 1 < t_end; t += 2) {
-      tile(t, st0, nx0);
-      tile(t + 1, st1, nx1);
+    for (; t + NST - 1 < t_end; t += NST) {
+#pragma unroll
+      for (int j = 0; j < NST; ++j) tile(t + j, st[j], nx[j]);
     }
-    if (t < t_end) tile(t, st0, nx0);
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+      if (t + j < t_end) tile(t + j, st[j], nx[j]);
   }
 
   // ---- results: lane holds O[head hl][wave*128 + n*16 + 4gq + i]
@@ -628,16 +639,17 @@ bool attn_mha_supported(const AttnArgs& a) {
 }
 
 int attn_mla_splits(int B, int Tq, int H, int k, int nlayers) {
-  // few rows (decode): split each row's key list so ~512 workgroups (2 per CU) run; a
-  // launch of several layers aims at ~768 in all (measured on the 64-row decode step with
-  // three layers: 4 splits per layer 0.213 ms, 8 splits 0.226 ms, 16 splits 0.238 ms)
+  // few rows (decode): split each row's key list so that up to 512 workgroups (two per CU,
+  // what the chip holds at once) run in one round.  (A launch of three 64-row layers at
+  // four splits, 768 workgroups, ran in two rounds: 65 us, the second round starting after
+  // 31-39 us.)
   const int64_t wgs = (int64_t)B * Tq * (H / 16);
   const int tiles = (k + kTile - 1) / kTile;
   if (wgs >= 256) return 1;
-  const int64_t target = nlayers > 1 ? 768 / nlayers : 512;
+  const int64_t target = 512 / std::max(1, nlayers);
   // (at most 64: the merge holds one split per lane)
   int s = (int)std::min<int64_t>(std::min(tiles, 64), (target + wgs - 1) / std::max<int64_t>(1, wgs));
-  if (nlayers > 1) {  // a power of two (even splits of a power-of-two tile count); rounding down
+  if (nlayers > 1) {  // a power of two (even splits of a power-of-two tile count) within the round
     int p = 1;
     while (2 * p <= s) p *= 2;
     s = p;
@@ -697,7 +709,7 @@ hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers,
     const bool wide = a.kv_fmt == kKvBf16 && nsplit == 1 && a.Tk <= kWideMaxTk;
 #define DSA_MLA_LAUNCH(F, W)                                                                                       \
   hipLaunchKernelGGL((mla_attn_kernel<F, W>), grid, dim3(256), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, \
-                     per, part_o, part_ml, part_layer)
+                     per, part_o, part_ml, part_layer, a.tail_kv_len, a.tail_Tk)
     if (a.kv_fmt == kKvFp8)
       DSA_MLA_LAUNCH(kKvFp8, 0);
     else if (a.kv_fmt == kKvMxfp4)

@@ -14,13 +14,13 @@ namespace {
 // wave_keys > 0 (launches with no more rows than one wave holds, e.g. decode): the four
 // waves share the same rows and split the workgroup's key segment, wave w taking keys
 // [w * wave_keys, (w + 1) * wave_keys) of it, so every wave streams keys.
-template <int H_I, int D_I, bool PAGED>
+template <int H_I, int D_I, bool PAGED, int QP = idx_query_tiles<H_I, D_I>()>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0, int nrows, float* __restrict__ scores,
     int64_t ld, int64_t score_bstride, int key_seg, int wave_keys, const int32_t* __restrict__ bt, int max_blocks,
     int page_shift, int64_t pool_tokens) {
-  using W = IdxWave<H_I, D_I, idx_query_tiles<H_I, D_I>()>;
+  using W = IdxWave<H_I, D_I, QP>;
   constexpr int QB = 4 * W::ROWS;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
   const int wave = wave_id();
@@ -81,6 +81,10 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   constexpr int ROWS = idx_query_tiles<H_I, D_I>() * (32 / H_I);  // query rows per wave
   constexpr int QB = 4 * ROWS;
   const bool wsplit = A.nrows <= ROWS;  // one wave's rows: the waves split keys instead
+  // rows of one query tile (decode: one query per sequence) need no more MFMA and epilogue
+  // work than that tile: the key-streaming launch then uses one query tile per wave
+  constexpr int ROWS1 = 32 / H_I;
+  const bool one_tile = wsplit && A.nrows <= ROWS1;
   const int qblocks = wsplit ? 1 : (A.nrows + QB - 1) / QB;
   // keys any row of the chunk can see (kv_len <= Tk)
   const int64_t maxkeys = std::min<int64_t>(A.Tk, (int64_t)A.Tk - A.Tq + A.row0 + A.nrows);
@@ -88,23 +92,31 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   const int64_t tiles = (maxkeys + 31) / 32;
   // Aim at ~2048 workgroups per launch when query blocks are full (prefill chunks): twice
   // what the chip holds at once, with segments short enough that the causal tail of a launch
-  // stays small.  Few-row launches keep ~1024 workgroups; with the waves splitting keys
-  // (one wave's rows) a segment is a multiple of four tiles.
-  const int64_t target = A.nrows >= 8 * QB ? 2048 : 1024;
+  // stays small.  Few-row launches take ~1536 (measured on the 64 x 65536 decode key cache:
+  // 108 us against 112-116 us at 512-1024 and 109-113 us at 2048-4096); with the waves
+  // splitting keys (one wave's rows) a segment is a multiple of four tiles.
+  const int64_t target = A.nrows >= 8 * QB ? 2048 : 1536;
   int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, target / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
   int64_t seg_tiles = (tiles + segs - 1) / segs;
   if (wsplit) seg_tiles = (seg_tiles + 3) / 4 * 4;
   segs = (tiles + seg_tiles - 1) / seg_tiles;
   const int wave_keys = wsplit ? (int)(seg_tiles / 4 * 32) : 0;
   dim3 grid(qblocks, (unsigned)segs, A.B);
-  if (paged)
-    hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, true>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
-                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys,
-                       A.block_table, A.max_blocks, A.page_shift, A.pool_tokens);
+#define DSA_IDX_LAUNCH(PG, QP)                                                                                        \
+  hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, PG, QP>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, \
+                     A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys,      \
+                     PG ? A.block_table : nullptr, PG ? A.max_blocks : 0, PG ? A.page_shift : 0,                    \
+                     PG ? A.pool_tokens : (int64_t)0)
+  constexpr int QPF = idx_query_tiles<H_I, D_I>();
+  if (paged && one_tile)
+    DSA_IDX_LAUNCH(true, 1);
+  else if (paged)
+    DSA_IDX_LAUNCH(true, QPF);
+  else if (one_tile)
+    DSA_IDX_LAUNCH(false, 1);
   else
-    hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, false>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq,
-                       A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys,
-                       nullptr, 0, 0, (int64_t)0);
+    DSA_IDX_LAUNCH(false, QPF);
+#undef DSA_IDX_LAUNCH
   return hipGetLastError();
 }
 

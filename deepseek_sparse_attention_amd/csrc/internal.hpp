@@ -111,6 +111,10 @@ struct AttnArgs {
   // rows between two sequences' first rows: -1 for Tk (dense [B][Tk] caches), 0 for one
   // pool shared by all sequences (paged caches: idx then holds pool rows, Tk the pool size)
   int64_t kv_bstride = -1;
+  // tail_Tk > 0: idx rows are the library's own top-k output (valid entries first, then -1
+  // padding) for sequences of tail_kv_len[b] (NULL: tail_Tk) keys
+  const int32_t* tail_kv_len = nullptr;
+  int tail_Tk = 0;
 };
 // MLA form: Hkv = 1, Dqk = 576, Dv = 512, V shared with K, H % 16 == 0.
 bool attn_mla_supported(const AttnArgs& a);

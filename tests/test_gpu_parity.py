@@ -389,11 +389,12 @@ def test_decode_step_fss_matches_oracle():
         assert np.max(np.abs(_host(outs[l]).double().numpy() - ref)) <= 2e-2
 
 
-def test_decode_stack_groups_shared_layers_bit_identical_to_single_calls():
-    # with few query rows the attention of an 'F' layer and the 'S' layers after it runs in
-    # one launch (at most four layers per launch): every layer's output and lse must equal
-    # a separate dsa_sparse_attn call on the same indices, bit for bit
+def test_decode_stack_grouped_layers_match_single_calls():
     print("decode grouped layers", flush=True)
+    # with few query rows the attention of an 'F' layer and the 'S' layers after it runs in
+    # one launch (at most four layers per launch, fewer key splits per layer than a lone
+    # call): every layer's output and lse must match a separate dsa_sparse_attn call on the
+    # same indices to rounding
     pattern = "FSSSSSF"  # groups of 4 and 2 layers after the first F, then a lone F layer
     w = synth.workload("E", B=3, T=3000, pattern=pattern)
     kcache = synth.decode_indexer_cache(w)
@@ -409,7 +410,9 @@ def test_decode_stack_groups_shared_layers_bit_identical_to_single_calls():
     for l in range(len(pattern)):
         o, lse = dsa.sparse_attn(layers[l]["q"], layers[l]["kv"], cache, w.scale(), kv_scale=layers[l]["kv_scale"],
                                  Dv=512)
-        assert torch.equal(outs[l], o) and torch.equal(lses[l], lse), l
+        a, b = _host(outs[l]).double().numpy(), _host(o).double().numpy()
+        assert np.max(np.abs(a - b)) <= 2.0 ** -7 * np.max(np.abs(b)), l  # rounding: a bf16 ulp at most
+        assert np.max(np.abs(_host(lses[l]).double().numpy() - _host(lse).double().numpy())) <= 1e-5, l
 
 
 def test_empty_batch_and_no_keys():
