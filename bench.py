@@ -29,49 +29,84 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-TRAFFIC_FILE = os.path.join(PROFILES, "mla_attn_t65536_k2048_traffic.txt")
+PROBE_LIB = os.path.join(ROOT, "libdsa_probe.so")
+_probe_lib = None
+
+
+def probe():
+    """libdsa_probe.so (bench_probe.hip): the read and gather ceiling kernels."""
+    global _probe_lib
+    if _probe_lib is None:
+        import ctypes
+
+        if not os.path.exists(PROBE_LIB):
+            raise ImportError(f"{PROBE_LIB} is missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(PROBE_LIB)
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.probe_read.argtypes = [P, SZ, P, I, P]
+        L.probe_gather.argtypes = [P, I, I64, P, I64, I, I, P, P]
+        _probe_lib = L
+    return _probe_lib
+
+
+TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_t65536_and_decode.txt")
+
+
+def _short(name):
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
 
 
 def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     """Turn two rocprofv3 --pmc runs of `bench.py --copy-calibration` (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch) into the HBM bytes per launch of the sparse-attention
-    kernel, each counter scaled by what it reads for the plain 1 GiB device copy."""
+    WRITE_SIZE; KiB per dispatch) into the bytes per launch that each kernel moved between
+    L2 and memory (the last-level cache or HBM), each counter scaled by what it reads for
+    the plain 1 GiB device copy."""
+    import collections
     import csv
 
     def per_kernel(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        attn = [float(r["Counter_Value"]) for r in rows if "mla_attn_kernel<0, 0>" in r["Kernel_Name"]]
-        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
-                or "copy_kernel" in r["Kernel_Name"]]
-        return attn, copy
+        vals = collections.defaultdict(list)
+        copy = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            n = r["Kernel_Name"]
+            if "copyBuffer" in n or "copy_kernel" in n:
+                copy.append(float(r["Counter_Value"]))
+            elif "dsa::" in n or "_kernel<" in n or "gather_kernel" in n or "read_kernel" in n:
+                vals[_short(n)].append(float(r["Counter_Value"]))
+        return vals, copy
 
-    fa, fc = per_kernel(fetch_csv, "FETCH_SIZE")
-    wa, wc = per_kernel(write_csv, "WRITE_SIZE")
+    fv, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    wv, wc = per_kernel(write_csv, "WRITE_SIZE")
     copy_bytes = 1 << 30
     f_scale = copy_bytes / (max(fc) * 1024.0)  # the copy reads 1 GiB
     w_scale = copy_bytes / (max(wc) * 1024.0)  # and writes 1 GiB
-    f_bytes = sum(fa) / len(fa) * 1024.0 * f_scale
-    w_bytes = sum(wa) / len(wa) * 1024.0 * w_scale
     lines = [
-        "# HBM traffic of mla_attn_kernel<bf16> (T=65536, k=2048, 16 heads, 576/512) per launch",
-        "# made by:",
+        "# Bytes each kernel moved between L2 and memory per launch (FETCH_SIZE + WRITE_SIZE, KiB per",
+        "# dispatch, scaled by the counts of a plain 1 GiB device copy in the same run): the T=65536,",
+        "# k=2048 prefill layer, the 64 x 65536 decode step and the bench's ceiling kernels",
+        "# made by (from the repository root):",
         "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch_D -o fetch -- "
-        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl --copy-calibration",
+        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-kl --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write_D -o write -- "
-        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl --copy-calibration",
+        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-kl --copy-calibration",
         "#   python3 bench.py --summarize-traffic <fetch csv> <write csv>",
-        f"attn_dispatches: {len(fa)}",
-        f"fetch_kib_per_launch: {sum(fa) / len(fa):.1f}",
-        f"write_kib_per_launch: {sum(wa) / len(wa):.1f}",
         f"copy_fetch_kib: {max(fc):.1f}",
         f"copy_write_kib: {max(wc):.1f}",
         f"fetch_scale: {f_scale:.4f}",
         f"write_scale: {w_scale:.4f}",
-        f"hbm_bytes_per_launch: {int(f_bytes + w_bytes)}",
-        f"source_hash: {source_hash('attention.hip', 'common.hpp')}",
+        f"source_hash: {source_hash(*LIB_SOURCES)}",
+        "# kernel | dispatches | fetch bytes/launch | write bytes/launch | total bytes/launch",
     ]
-    with open(out_path, "w") as f:
-        f.write("\n".join(lines) + "\n")
+    for name in sorted(set(fv) | set(wv), key=lambda n: -(sum(fv.get(n, [0])) / max(1, len(fv.get(n, [1]))))):
+        f = fv.get(name, [0.0])
+        w = wv.get(name, [0.0])
+        fb = sum(f) / len(f) * 1024.0 * f_scale
+        wb = sum(w) / len(w) * 1024.0 * w_scale
+        lines.append(f"{name} | {len(f)} | {int(fb)} | {int(wb)} | {int(fb + wb)}")
+    with open(out_path, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -230,17 +265,18 @@ def run_configs(steps, warmup):
 
 
 def read_traffic():
-    """HBM bytes per launch from the committed summary, if the kernel source is unchanged."""
+    """Counter bytes per launch by kernel from the committed summary ({} once any library
+    source changed since the counters were taken)."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
+        return {}
+    out, ok = {}, False
     for line in open(TRAFFIC_FILE):
-        if line.strip() and not line.startswith("#") and ":" in line:
-            a, b = line.split(":", 1)
-            kv[a.strip()] = b.strip()
-    if kv.get("source_hash") != source_hash("attention.hip", "common.hpp"):
-        return None
-    return int(kv["hbm_bytes_per_launch"])
+        if line.startswith("source_hash:"):
+            ok = line.split(":", 1)[1].strip() == source_hash(*LIB_SOURCES)
+        elif not line.startswith("#") and line.count("|") == 4:
+            name, _, _, _, tot = (x.strip() for x in line.split("|"))
+            out[name] = int(tot)
+    return out if ok else {}
 
 
 def parse():
@@ -268,6 +304,10 @@ def parse():
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+LIB_SOURCES = ("api.hip", "indexer.hip", "topk.hip", "index_topk.hip", "attention.hip", "indexer_kl.hip", "common.hpp",
+               "indexer_core.hpp", "internal.hpp", "selection.hpp")
 
 
 def source_hash(*names):
@@ -375,14 +415,46 @@ def main():
     unfused_step_ms = timed(lambda: dsa.layer_stack("F", [layer], k, w.scale(), Dv=w.Dv, index_cache=idx_cache,
                                                     ws=ws, unfused=True))
 
-    # ---- roofline of the dominant kernel (sparse MLA attention)
+    # ---- roofline of the dominant kernel (sparse MLA attention).  Its contraction is MFMA
+    # work (34,816 flop per selected key: 16 heads x 2 x (576 + 512)); its gathered rows
+    # (1152 B per selected key) come mostly from L2 and the last-level cache (75.5 MB of
+    # latent rows, each gathered ~2000 times), so the logical gather rate exceeds the HBM
+    # peak and is held instead against the same gather without the arithmetic
+    # (bench_probe.hip) on the kernel's own index rows.
     sel = k * T - k * (k - 1) // 2 if T >= k else T * (T + 1) // 2
     attn_bytes = sel * w.Dqk * 2 + T * w.H * w.Dqk * 2 + T * k * 4 + T * w.H * w.Dv * 2 + T * w.H * 4
-    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = read_traffic() if T == 65536 else None
-    roofline = {"kernel": "mla_attn_kernel<bf16>", "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": attn_bytes, "ms_per_launch": round(attn_ms, 3)}
+    attn_flops = sel * w.H * 2 * (w.Dqk + w.Dv)
+    logical = attn_bytes / (attn_ms * 1e-3) / 1e9
+    traffic_all = read_traffic()
+    traffic = traffic_all.get("dsa::mla_attn_kernel<0, 0>") if T == 65536 else None
+    pl = probe()
+    psum = torch.empty(T * 4, dtype=torch.int32, device=dev)
+
+    def gather_probe():
+        rc = pl.probe_gather(layer["kv"].data_ptr(), w.Dqk * 2, T, idx_cache.data_ptr(), T, k, 1, psum.data_ptr(),
+                             stream.cuda_stream)
+        assert rc == 0, rc
+
+    probe_ms = timed(gather_probe)
+    probe_logical = attn_bytes / (probe_ms * 1e-3) / 1e9
+    rbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    rsum = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+
+    def read_probe():
+        rc = pl.probe_read(rbuf.data_ptr(), rbuf.numel() // 4, rsum.data_ptr(), 4096, stream.cuda_stream)
+        assert rc == 0, rc
+
+    read_gbs = rbuf.numel() * 4 / (timed(read_probe) * 1e-3) / 1e9
+    del rbuf, rsum, psum
+    tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    roofline = {"kernel": "mla_attn_kernel<bf16>", "bound": "mfma", "achieved": round(tflops, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "flops": attn_flops, "ms_per_launch": round(attn_ms, 3),
+                "gather": {"algorithmic_bytes": attn_bytes, "logical_gbs": round(logical, 1),
+                           "probe_ms": round(probe_ms, 3), "probe_logical_gbs": round(probe_logical, 1),
+                           "frac_of_probe": round(logical / probe_logical, 4),
+                           "l2_to_memory_gbs": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 1)},
+                "hbm_read_probe_gbs": round(read_gbs, 1)}
     pairs = T * (T + 1) // 2
     idx_flops = 2 * w.H_I * w.d_I * pairs
     kernels = {
@@ -393,7 +465,7 @@ def main():
         "step_unfused": {"ms": round(unfused_step_ms, 3)},
         "topk": {"ms": round(topk_ms, 3),
                  "gbs": round((pairs * 4 + T * k * 4) / (topk_ms * 1e-3) / 1e9, 1)},
-        "sparse_attn": {"ms": round(attn_ms, 3), "gbs_logical": round(achieved, 1)},
+        "sparse_attn": {"ms": round(attn_ms, 3), "gbs_logical": round(logical, 1)},
     }
     # the platform's own bf16 GEMM (torch -> hipBLASLt) on random data, as context for the
     # indexer's MFMA fraction: a large square product and the indexer's contraction shape
@@ -468,6 +540,71 @@ def main():
                             "ms_per_step": round(ddt * 1e3, 4), "steps": dsteps, "pattern": e.pattern,
                             "algorithmic_bytes": dbytes, "gbs": round(dbytes / ddt / 1e9, 1)}
         log(f"decode: {ddt * 1e3:.3f} ms/step, {e.B / ddt:.0f} tok/s")
+
+        # the step's parts, event-timed: selection (indexer + top-k through dsa_index_topk,
+        # scores in its workspace), top-k alone on those scores, and the three attention
+        # layers alone (an "SSS" stack over the cached indices: one grouped launch and its
+        # merge); each against the ceiling kernels of bench_probe.hip
+        nrep = 10
+        sshp = dsa._shape(e.B, 1, e.T, 1, 1, 1, 1, e.k, 1.0, dsa.KV_BF16, e.H_I, e.d_I, klen)
+        sws = torch.empty(max(1, dsa.workspace_size(sshp, dsa.OP_INDEX_TOPK)), dtype=torch.uint8, device=dev)
+        sidx = torch.empty_like(dcache)
+        L0 = dl[0]
+
+        def sel_batch():
+            for _ in range(nrep):
+                dsa.index_topk(L0["q_idx"], kc, L0["w_idx"], e.k, kv_len=klen, idx=sidx, ws=sws)
+
+        sel_us = 1e3 * timed(sel_batch) / nrep
+        dscores = dsa.index_scores(L0["q_idx"], kc, L0["w_idx"], kv_len=klen)
+
+        def topk_batch():
+            for _ in range(nrep):
+                dsa.topk(dscores, e.k, kv_len=klen, idx=sidx)
+
+        topk_us = 1e3 * timed(topk_batch) / nrep
+        same_sel = bool(torch.equal(sidx, dcache))
+        del dscores, sws
+
+        def attn3_batch():
+            for _ in range(nrep):
+                dsa.layer_stack("SSS", dl, e.k, e.scale(), Dv=e.Dv, kv_len=klen, index_cache=dcache, ws=dws,
+                                prefilled=True, topk_rows=True)
+
+        attn3_us = 1e3 * timed(attn3_batch) / nrep
+        goff = (torch.arange(e.B, device=dev, dtype=torch.int32) * e.T).view(e.B, 1, 1)
+        gidx = torch.where(dcache >= 0, dcache + goff, -1).to(torch.int32).contiguous()
+        gsplit = 8  # workgroups per decode row, as the attention splits its keys
+        gsum = torch.empty(e.B * gsplit * 4, dtype=torch.int32, device=dev)
+
+        def gather3_batch():
+            for _ in range(nrep):
+                for L in dl:
+                    rc = pl.probe_gather(L["kv"].data_ptr(), e.Dqk, e.B * e.T, gidx.data_ptr(), e.B, e.k, gsplit,
+                                         gsum.data_ptr(), stream.cuda_stream)
+                    assert rc == 0, rc
+
+        gather3_us = 1e3 * timed(gather3_batch) / nrep
+        del gidx, gsum
+        key_bytes = e.B * e.T * e.d_I * 2
+        score_bytes = e.B * e.T * 4 + e.B * e.k * 4
+        attn3_bytes = 3 * (e.B * e.k * (e.Dqk + 4) + e.B * e.H * (e.Dqk * 2 + e.Dv * 2 + 4))
+        idx_us = sel_us - topk_us
+
+        def rate(nb, us, probe_gbs=None):
+            g = nb / (us * 1e-6) / 1e9
+            d = {"us": round(us, 2), "bytes": nb, "gbs": round(g, 1), "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4),
+                 "frac_of_read_probe": round(g / read_gbs, 4)}
+            if probe_gbs:
+                d["frac_of_gather_probe"] = round(g / probe_gbs, 4)
+            return d
+
+        gather3_gbs = attn3_bytes / (gather3_us * 1e-6) / 1e9
+        decode_kernels = {"indexer": rate(key_bytes, idx_us), "topk": rate(score_bytes, topk_us),
+                          "attention_3_layers": rate(attn3_bytes, attn3_us, gather3_gbs),
+                          "gather_probe_3_layers_us": round(gather3_us, 2), "selection_matches_step": same_sel}
+        result["decode"]["kernels"] = decode_kernels
+        log(f"decode kernels: {decode_kernels}")
 
         # the same step over paged caches: the same rows in shuffled 64-token pages of shared
         # pools (one block table for every layer); must give the dense step's results
@@ -596,8 +733,9 @@ def main():
         stride = max(1, T // args.cpu_rows)
         rows = np.arange(stride // 2, T, stride, dtype=np.int32)[: args.cpu_rows]
         host = {x: layer[x].cpu() for x in ("q_idx", "k_idx", "w_idx", "q", "kv")}
-        nthreads = oracle.default_threads()
-        log(f"oracle on {len(rows)} rows with {nthreads} threads")
+        nproc = len(os.sched_getaffinity(0))  # the cores this process may run on (nproc)
+        nthreads = nproc
+        log(f"oracle on {len(rows)} rows with {nthreads} threads (nproc {nproc})")
         t0 = time.perf_counter()
         ridx, rout = oracle.dsa_rows(host["q_idx"][0], host["k_idx"][0], host["w_idx"][0], host["q"][0],
                                      host["kv"][0], rows, k, w.scale(), Dv=w.Dv, nthreads=nthreads)
@@ -608,7 +746,8 @@ def main():
         same_sets = float(np.mean([len(np.intersect1d(a[a >= 0], b[b >= 0])) / max(1, (b >= 0).sum())
                                    for a, b in zip(got_idx, ridx)]))
         result["cpu_baseline"] = {
-            "value": round(len(rows) / cdt, 3), "unit": "query tokens/s", "cores": nthreads, "kind": "oracle",
+            "value": round(len(rows) / cdt, 3), "unit": "query tokens/s", "cores": nthreads, "nproc": nproc,
+            "kind": "oracle",
             "sample": f"{len(rows)} query rows of the T={T} layer (every {stride}th position), "
                       f"scores+top-k+attention in fp64, {cdt:.1f} s wall",
             "sample_check": {"max_abs_out_diff": float(np.max(np.abs(got_out - rout))),

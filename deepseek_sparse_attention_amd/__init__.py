@@ -18,7 +18,7 @@ __all__ = [
     "noalloc_scratch_bytes", "layer_stack",
     "index_scores_paged", "sparse_attn_paged", "indexer_kl", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
-    "KV_BF16", "KV_FP8_E4M3", "KV_MXFP4", "mxfp4_row_bytes", "CACHE_PREFILLED", "STACK_UNFUSED", "OP_SCORES", "OP_TOPK", "OP_ATTN",
+    "KV_BF16", "KV_FP8_E4M3", "KV_MXFP4", "mxfp4_row_bytes", "CACHE_PREFILLED", "STACK_UNFUSED", "CACHE_TOPK_ROWS", "OP_SCORES", "OP_TOPK", "OP_ATTN",
     "OP_STACK", "OP_INDEX_TOPK",
 ]
 
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
 OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK, OP_INDEX_TOPK, OP_ATTN_PAGED, OP_STACK_PAGED = 0, 1, 2, 3, 4, 5, 6
-CACHE_PREFILLED, STACK_UNFUSED = 1, 2
+CACHE_PREFILLED, STACK_UNFUSED, CACHE_TOPK_ROWS = 1, 2, 4
 _STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_PATTERN",
            "DSA_ERR_WORKSPACE", "DSA_ERR_LAUNCH", "DSA_ERR_DEVICE"]
 
@@ -315,11 +315,13 @@ def noalloc_scratch_bytes() -> int:
 
 
 def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=None, prefilled=False,
-                H_I=None, d_I=None, ws=None, want_lse=True, unfused=False, pages=None, Tk=None, stream=None):
+                H_I=None, d_I=None, ws=None, want_lse=True, unfused=False, pages=None, Tk=None, topk_rows=False,
+                stream=None):
     """dsa_layer_stack over `layers` (dicts with q/kv[/v/kv_scale] and, on F layers, q_idx/k_idx/w_idx).
 
     Returns (outs, lses, index_cache).  Output tensors are allocated unless a layer dict
     carries "out"/"lse".  unfused: 'F' layers take the score-chunk route (STACK_UNFUSED).
+    topk_rows (with prefilled): the prefilled cache holds dsa_topk rows (CACHE_TOPK_ROWS).
     pages (a PagedKV) with Tk: k_idx, kv and kv_scale are pools (dsa_layer_stack_paged).
     """
     n = len(layers)
@@ -357,7 +359,8 @@ def layer_stack(pattern, layers, k, sm_scale, Dv=None, kv_len=None, index_cache=
                          _ptr(L["kv"]), _ptr(L.get("kv_scale")), _ptr(L.get("v")), _ptr(o), _ptr(ls))
     nbytes = workspace_size(shp, OP_STACK if pages is None else OP_STACK_PAGED)
     ws = _workspace(nbytes, dev, ws)
-    flags = (CACHE_PREFILLED if prefilled else 0) | (STACK_UNFUSED if unfused else 0)
+    flags = (CACHE_PREFILLED if prefilled else 0) | (STACK_UNFUSED if unfused else 0) | \
+        (CACHE_TOPK_ROWS if topk_rows else 0)
     if pages is None:
         _check(lib().dsa_layer_stack(pattern.encode(), n, ios, ctypes.byref(shp), _ptr(index_cache), flags,
                                      _ptr(ws), nbytes, _stream(stream)))

@@ -42,6 +42,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libdsa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the measurement kernels bench.py holds the library against (read and gather
+    ceilings; not part of the DSA path) into libdsa_probe.so next to bench.py."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *CFLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for bench_probe.hip:\n{r.stderr[-6000:]}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libdsa.so next to this file (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
@@ -60,4 +78,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
     sys.exit(0)

@@ -561,8 +561,8 @@ dsa_status stack_impl(const char* pattern, int n_layers, const dsa_layer_io* lay
     dsa::AttnArgs a = attn_args(L.q, L.kv, L.kv_scale, L.v, s.kv_dtype, index_cache, s.B, s.Tq, s.Tk, s.H, s.Hkv,
                                 s.Dqk, s.Dv, s.k, s.sm_scale, L.out, L.lse, attn_ws);
     // the cache holds this library's top-k rows (valid entries first), unless the caller
-    // prefilled it and no 'F' layer has run yet
-    if (!(flags & DSA_CACHE_PREFILLED) || any_full) {
+    // prefilled it with other rows and no 'F' layer has run yet
+    if (!(flags & DSA_CACHE_PREFILLED) || any_full || (flags & DSA_CACHE_TOPK_ROWS)) {
       a.tail_kv_len = s.kv_len;
       a.tail_Tk = s.Tk;
     }

@@ -188,8 +188,8 @@ struct MlaLayers {
 
 // tail_kv_len / tail_Tk (tail_Tk > 0): every row's valid entries are its first min(k, p+1),
 // p its position among sequences of tail_kv_len[b] (NULL: tail_Tk) keys, as the library's
-// own top-k writes them; the kernel then takes its tile count from p instead of scanning the
-// list for the last valid entry.
+// own top-k writes them; a split launch then takes its tile count from p instead of
+// scanning the list for the last valid entry.
 template <int FMT, int WIDE>
 __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLayers Ls,
                                                           const int32_t* __restrict__ idx, int Tq, int Tk,
@@ -284,9 +284,14 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
     for (int j = 0; j < NST; ++j) fetch(st[j], valid_entry(t_begin + j, e[j]));
   }
 
-  // extent of this split's entries that are valid: the loop ends after its last tile
+  // extent of this split's entries that are valid: the loop ends after its last tile.  A
+  // split launch (few rows) takes it from the row's position when the list is a top-k row
+  // (the scan is one more memory round trip in its prologue: 7 -> 3.6 us per workgroup on
+  // the 64-row decode step); a launch of whole rows scans, which also brings the row's
+  // index list into L2 ahead of the per-tile index loads (without the scan the T=65536
+  // layer took 16.1 ms against 15.5)
   int t_end;
-  if (tail_Tk > 0) {
+  if (tail_Tk > 0 && nsplit > 1) {
     const int64_t p = seq_len(tail_kv_len, b, tail_Tk) - Tq + (int)(row % Tq);
     const int64_t nv = min((int64_t)k, p + 1);
     t_end = min(t_lim, (int)((max(nv, (int64_t)0) + kTile - 1) / kTile));

@@ -102,6 +102,11 @@ typedef enum {
 #define DSA_STACK_UNFUSED 2u   /* 'F' layers run dsa_index_scores + dsa_topk over score chunks
                                   even where the fused path of dsa_index_topk applies (same
                                   indices; for comparison) */
+#define DSA_CACHE_TOPK_ROWS 4u /* with DSA_CACHE_PREFILLED: the prefilled rows are as dsa_topk
+                                  writes them (each row's min(k, p+1) valid entries first,
+                                  then -1), e.g. a previous stack's cache; attention then takes
+                                  each row's extent from its position instead of scanning the
+                                  row (any row otherwise is read entry by entry) */
 
 int dsa_abi_version(void);
 const char* dsa_last_error(void);

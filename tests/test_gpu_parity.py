@@ -415,6 +415,30 @@ def test_decode_stack_grouped_layers_match_single_calls():
         assert np.max(np.abs(_host(lses[l]).double().numpy() - _host(lse).double().numpy())) <= 1e-5, l
 
 
+def test_prefilled_cache_of_topk_rows_gives_the_same_layers():
+    # a stack that starts with 'S' layers on a cache a previous stack wrote: with
+    # DSA_CACHE_TOPK_ROWS the attention takes each row's extent from its position, without
+    # it every row is scanned; both equal the layers of one stack that computes the cache
+    print("prefilled cache of top-k rows", flush=True)
+    w = synth.workload("E", B=5, T=3000, pattern="FSS")
+    kcache = synth.decode_indexer_cache(w)
+    layers = []
+    for l in range(3):
+        d = synth.decode_layer_inputs(w, l)
+        if "q_idx" in d:
+            d["k_idx"] = kcache
+        layers.append({k: v.to(DEV) for k, v in d.items()})
+    kv_len = torch.tensor([3000, 2047, 1024, 2049, 1], dtype=torch.int32, device=DEV)
+    outs, lses, cache = dsa.layer_stack("FSS", layers, 2048, w.scale(), Dv=512, kv_len=kv_len)
+    for flag in (False, True):
+        o2, l2, c2 = dsa.layer_stack("SS", layers[1:], 2048, w.scale(), Dv=512, kv_len=kv_len,
+                                     index_cache=cache.clone(), prefilled=True, topk_rows=flag)
+        for a, b in zip(o2, outs[1:]):
+            assert torch.equal(a, b), flag
+        for a, b in zip(l2, lses[1:]):
+            assert torch.equal(a, b), flag
+
+
 def test_empty_batch_and_no_keys():
     q = torch.empty((0, 5, 16, 64), dtype=torch.bfloat16, device=DEV)
     k = torch.empty((0, 5, 64), dtype=torch.bfloat16, device=DEV)
