@@ -73,8 +73,9 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
             n = r["Kernel_Name"]
             if "copyBuffer" in n or "copy_kernel" in n:
                 copy.append(float(r["Counter_Value"]))
-            elif "dsa::" in n or "_kernel<" in n or "gather_kernel" in n or "read_kernel" in n:
-                vals[_short(n)].append(float(r["Counter_Value"]))
+            elif "at::" not in n and ("dsa::" in n or "::gather_kernel<" in n or "::read_kernel(" in n):
+                # one line per kernel and launch shape (grid size in threads)
+                vals[f"{_short(n)} grid={r['Grid_Size']}"].append(float(r["Counter_Value"]))
         return vals, copy
 
     fv, fc = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -97,7 +98,7 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
         f"fetch_scale: {f_scale:.4f}",
         f"write_scale: {w_scale:.4f}",
         f"source_hash: {source_hash(*LIB_SOURCES)}",
-        "# kernel | dispatches | fetch bytes/launch | write bytes/launch | total bytes/launch",
+        "# kernel grid=<threads> | dispatches | fetch bytes/launch | write bytes/launch | total bytes/launch",
     ]
     for name in sorted(set(fv) | set(wv), key=lambda n: -(sum(fv.get(n, [0])) / max(1, len(fv.get(n, [1]))))):
         f = fv.get(name, [0.0])
@@ -166,15 +167,21 @@ STATS_FILE = os.path.join(PROFILES, "prefill_t65536_k2048_kernel_stats.txt")
 
 
 def summarize_stats(stats_csv, out_path=STATS_FILE):
-    """Turn the kernel_stats.csv of a `rocprofv3 --kernel-trace --stats` run of the default
-    bench command into the per-kernel summary kept with the repository (the library's
-    kernels; torch's own input-generation kernels only enter the total)."""
+    """Turn a `rocprofv3 --kernel-trace --stats` run of the bench (its kernel_stats.csv, and the
+    kernel_trace.csv beside it) into the per-kernel summary kept with the repository: one
+    line per library kernel and launch shape (grid size in threads); torch's own
+    input-generation kernels only enter the total."""
+    import collections
     import csv
 
-    rows = list(csv.DictReader(open(stats_csv)))
-    total_ns = sum(float(r["TotalDurationNs"]) for r in rows)
-    ours = [r for r in rows if "dsa::" in r["Name"]]
-    ours.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total_ns = sum(float(r["TotalDurationNs"]) for r in csv.DictReader(open(stats_csv)))
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if "dsa::" not in r["Kernel_Name"]:
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups[(_short(r["Kernel_Name"]), grid)].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
     lines = [
         "# rocprofv3 kernel-trace summary: one T=65536, k=2048 DSA layer (workload mla_t65536_k2048_sink),",
         "# the 64 x 65536 decode step (FSS over 3 layers; fp8, paged fp8 and MXFP4 latent caches) and",
@@ -186,16 +193,17 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# calls: 1 warmup + 3 timed layer_stack steps (fused index/top-k: fz_sample, fz_threshold,",
         "# fz_filter, fz_select, fz_exact once each, then attention), 3 event-timed launches of each",
         "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
-        "# unfused step), then the decode steps and their per-layer attention launches, then the KL",
-        "# objective (sparse and dense, with gradients).  mla_attn_kernel<f, w>: rows f = 0 bf16, 1 fp8, 2 MXFP4; w = 1 the three-workgroup schedule.",
-        "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel",
+        "# unfused step), then the decode steps and the bench's timings of their parts, the per-layer",
+        "# attention launches, then the KL objective (sparse and dense, with gradients).",
+        "# mla_attn_kernel<f, w>: rows f = 0 bf16, 1 fp8, 2 MXFP4; w = 1 the three-workgroup schedule;",
+        "# index_scores_kernel<H_I, d_I, paged, query tiles per wave>.  grid = threads of the launch",
+        "# (the 64-row decode: grouped 3-layer attention 98304, one layer 131072; decode indexer 393216)",
+        "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel, grid",
         "",
     ]
-    for r in ours:
-        short = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} {float(r['MinNs']) / 1e3:10.1f} "
-                     f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['TotalDurationNs']) / 1e6:10.2f} "
-                     f"{100 * float(r['TotalDurationNs']) / total_ns:6.2f}%  {short}")
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{len(d):6d} {sum(d) / len(d) / 1e3:12.1f} {min(d) / 1e3:10.1f} {max(d) / 1e3:10.1f} "
+                     f"{sum(d) / 1e6:10.2f} {100 * sum(d) / total_ns:6.2f}%  {name}  grid={grid}")
     lines += ["", f"# all kernels (incl. torch's input generation): {total_ns / 1e6:.1f} ms"]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -426,7 +434,7 @@ def main():
     attn_flops = sel * w.H * 2 * (w.Dqk + w.Dv)
     logical = attn_bytes / (attn_ms * 1e-3) / 1e9
     traffic_all = read_traffic()
-    traffic = traffic_all.get("dsa::mla_attn_kernel<0, 0>") if T == 65536 else None
+    traffic = traffic_all.get(f"dsa::mla_attn_kernel<0, 0> grid={T * w.H // 16 * 256}")
     pl = probe()
     psum = torch.empty(T * 4, dtype=torch.int32, device=dev)
 
