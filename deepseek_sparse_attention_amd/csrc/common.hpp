@@ -61,6 +61,24 @@ __device__ __forceinline__ void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r,
 // A byte offset no buffer range reaches (ranges here stay below 2 GiB): the store is dropped.
 constexpr uint32_t kOffNone = 0x80000000u;
 
+// The same buffer resource as its four descriptor words (base address, stride 0, range,
+// the flags make_rsrc passes), for stores written as single instructions below.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+// Exactly one vector-memory store instruction each: written in assembly, so the compiler
+// can neither merge nor drop them.  Loops whose explicit `s_waitcnt vmcnt` waits count the
+// stores issued between loads use these (a store outside the range is dropped by the
+// hardware, like the buffer stores above).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void buf_store1_b32(uint32_t v, u32x4 rs, uint32_t voff) {
+  asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(rs) : "memory");
+}
+__device__ __forceinline__ void buf_store1_b64(u32x2 v, u32x4 rs, uint32_t voff) {
+  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(rs) : "memory");
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -137,13 +137,13 @@ __global__ __launch_bounds__(256, 2) void fz_sample_kernel(const uint16_t* __res
   wv.load(q + ((int64_t)b * Tq + row0 + R.wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + R.wrow0) * H_I, R.wrows);
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
   // rows past the wave's count fall outside the store range and are dropped
-  const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(smp + rbase * smax, (uint32_t)(R.wrows * smax * 4));
+  const u32x4 s_rs = rsrc_words(smp + rbase * smax, (uint32_t)(R.wrows * smax * 4));
   const int col = wv.col;
   wv.template run<W::EPIS>(k_rs, wks[wave_id()], nst,
                            [&](int j) { return min(max(j * step + half, 0), span - 32); },
          [&](int j, int, int t, int qq, float tot) {
            const uint32_t off = (uint32_t)(wv.row_of(t, qq) * smax + j * 32 + col) * 4u;
-           __builtin_amdgcn_raw_buffer_store_b32(sel_key(tot), s_rs, (int)off, 0, 0);
+           buf_store1_b32(sel_key(tot), s_rs, off);  // one store per call (EPIS per tile)
          });
 }
 
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __res
   wv.load(q + ((int64_t)b * Tq + row0 + R.wrow0) * H_I * D_I, w + ((int64_t)b * Tq + row0 + R.wrow0) * H_I, R.wrows);
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
   // the wave's lists (rows past the chunk would fall outside; they never pass anyway)
-  const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(list + rbase * FZ_CAP, (uint32_t)(R.wrows * FZ_CAP * 8));
+  const u32x4 l_rs = rsrc_words(list + rbase * FZ_CAP, (uint32_t)(R.wrows * FZ_CAP * 8));
   // the lane's rows: last causal key (-1 for rows past the chunk) and threshold
   int lim[ROWS / W::QPT][W::QPL];
   float th[ROWS / W::QPT][W::QPL];
@@ -268,8 +268,7 @@ __global__ __launch_bounds__(256, 2) void fz_filter_kernel(const uint16_t* __res
            uint32_t addr = lane_list + (uint32_t)(rA * FZ_CAP) * 8u + slot * 8u;
            asm volatile("" : "+v"(addr));  // computed on every lane: the select stays a select
            const uint32_t at = c ? addr : kOffNone;
-           typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-           __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(tot), (uint32_t)skey}, l_rs, (int)at, 0, 0);
+           buf_store1_b64(u32x2{__float_as_uint(tot), (uint32_t)skey}, l_rs, at);  // one store per call
            fill[rA] += n0;
            fill[rB] += n1;
          });

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   const __amdgpu_buffer_rsrc_t k_rs = PAGED ? make_rsrc(k, (uint32_t)(pool_tokens * D_I * 2))
                                             : make_rsrc(k + (int64_t)b * Tk * D_I, (uint32_t)Tk * D_I * 2);
   float* sw = scores + (int64_t)b * score_bstride + (int64_t)wrow0 * ld;
-  const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(sw, (uint32_t)(wrows * ld * 4));
+  const u32x4 s_rs = rsrc_words(sw, (uint32_t)(wrows * ld * 4));
   // Row r = t*QPT + g*QPL + qq of the wave sits at position pos0 + r and score offset
   // r*ld*4; only the lane part (g*QPL) lives in registers (positions and keys fit in 32
   // bits: Tk <= ld <= 2^22).  Rows past the chunk need no mask: their score offsets fall
@@ -58,7 +58,9 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     // tiles never cross a segment edge, so the causal bound is the only mask
     const int skey = s0 + col;
     const int rr = t * W::QPT + qq;  // row offset from the lane's first row (a constant)
-    buf_store_f32(tot, s_rs, skey - rr <= pos0 ? off0 + (uint32_t)rr * row_bytes + (uint32_t)skey * 4u : kOffNone, 0);
+    // one store instruction per call: the key pipeline's waits count EPIS per tile
+    buf_store1_b32(__float_as_uint(tot), s_rs,
+                   skey - rr <= pos0 ? off0 + (uint32_t)rr * row_bytes + (uint32_t)skey * 4u : kOffNone);
   };
   const int ntiles = (int)((seg_end - seg0 + 31) / 32);
   if constexpr (PAGED) {

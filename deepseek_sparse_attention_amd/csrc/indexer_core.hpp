@@ -118,7 +118,9 @@ struct IdxWave {
   // where tile j's 32 key rows sit in k_rs (start(j) for a dense key array; a page of a
   // paged cache otherwise): keys are loaded from there, masks and outputs use start(j).
   // EPI_VM is a lower bound on the vector memory operations that epi and post issue per
-  // tile; the load waits count them (0 is always safe, only slower).
+  // tile; the load waits count them (0 is always safe, only slower).  The kernels that pass
+  // EPIS issue exactly one store per epi call as a single assembly instruction
+  // (buf_store1_*), so the count holds whatever the compiler does around it.
   //
   // Key tiles go from memory straight into the wave's private LDS buffers (`lds`,
   // kLdsBytes) with buffer loads that write LDS: each load instruction reads whole key rows
