@@ -709,11 +709,14 @@ def main():
         del sa
         kin = [la[x] for x in ("q_idx", "k_idx", "w_idx", "q", "kv")]
         kout = dsa.indexer_kl(*kin, a.scale(), idx=ia)  # outputs reused by the timed calls
+        kws = torch.empty(max(dsa.indexer_kl_workspace_size(a.B, a.T, a.T, a.H_I, a.d_I, kk=a.k),
+                              dsa.indexer_kl_workspace_size(a.B, a.T, a.T, a.H_I, a.d_I)), dtype=torch.uint8,
+                          device=dev)
         nrep = 20
 
         def kl_batch(ix):  # back-to-back launches, so host work overlaps the kernels
             for _ in range(nrep):
-                dsa.indexer_kl(*kin, a.scale(), idx=ix, out=kout)
+                dsa.indexer_kl(*kin, a.scale(), idx=ix, out=kout, ws=kws)
 
         sparse_ms = timed(lambda: kl_batch(ia)) / nrep
         dense_ms = timed(lambda: kl_batch(None)) / nrep

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "DSAError", "lib", "abi_version", "index_scores", "topk", "index_topk", "sparse_attn", "sparse_attn_noalloc",
     "noalloc_scratch_bytes", "layer_stack",
-    "index_scores_paged", "sparse_attn_paged", "indexer_kl", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED",
+    "index_scores_paged", "sparse_attn_paged", "indexer_kl", "indexer_kl_workspace_size", "PagedKV", "paged_kv", "OP_ATTN_PAGED", "OP_STACK_PAGED", "OP_INDEXER_KL", "OP_INDEXER_KL_DENSE",
     "workspace_size", "stack_chunk_rows", "check_pattern", "pattern_from_freq", "Shape",
     "KV_BF16", "KV_FP8_E4M3", "KV_MXFP4", "mxfp4_row_bytes", "CACHE_PREFILLED", "STACK_UNFUSED", "CACHE_TOPK_ROWS", "OP_SCORES", "OP_TOPK", "OP_ATTN",
     "OP_STACK", "OP_INDEX_TOPK",
@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
 OP_SCORES, OP_TOPK, OP_ATTN, OP_STACK, OP_INDEX_TOPK, OP_ATTN_PAGED, OP_STACK_PAGED = 0, 1, 2, 3, 4, 5, 6
+OP_INDEXER_KL, OP_INDEXER_KL_DENSE = 7, 8
 CACHE_PREFILLED, STACK_UNFUSED, CACHE_TOPK_ROWS = 1, 2, 4
 _STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_PATTERN",
            "DSA_ERR_WORKSPACE", "DSA_ERR_LAUNCH", "DSA_ERR_DEVICE"]
@@ -103,7 +104,7 @@ def lib():
         L.dsa_stack_chunk_rows.restype = I
         L.dsa_check_pattern.argtypes = [ctypes.c_char_p, I, U]
         L.dsa_pattern_from_freq.argtypes = [I, I, ctypes.c_char_p]
-        L.dsa_indexer_kl.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, P]
+        L.dsa_indexer_kl.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, P, SZ, P]
         for f in ("dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_attn", "dsa_sparse_attn_noalloc",
                   "dsa_layer_stack",
                   "dsa_check_pattern", "dsa_pattern_from_freq", "dsa_index_scores_paged", "dsa_sparse_attn_paged",
@@ -221,11 +222,13 @@ def _kv_dtype(kv, Dqk, kv_scale):
     return KV_MXFP4
 
 
-def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, grads=True, out=None, stream=None):
+def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, grads=True, out=None, ws=None,
+               stream=None):
     """dsa_indexer_kl: per-row KL(main attention || indexer) and, with grads, the gradients of
     its sum for q_idx, w_idx and k_idx.  idx None: every causal key (dense warm-up).
     Returns (loss fp32 [B,Tq], dq_idx, dw_idx, dk_idx) (gradients None without grads);
-    `out` may hold those four tensors, preallocated."""
+    `out` may hold those four tensors, preallocated, and `ws` a uint8 workspace (the key
+    gradient's; allocated here when absent or too small)."""
     B, Tq, H_I, d_I = q_idx.shape
     Tk = k_idx.shape[1]
     H, Dqk = q.shape[2], q.shape[3]
@@ -240,10 +243,21 @@ def indexer_kl(q_idx, k_idx, w_idx, q, k, sm_scale, idx=None, kv_len=None, grads
             dq = torch.empty((B, Tq, H_I, d_I), dtype=torch.float32, device=dev)
             dw = torch.empty((B, Tq, H_I), dtype=torch.float32, device=dev)
             dk = torch.empty((B, Tk, d_I), dtype=torch.float32, device=dev)
+    nbytes = 0
+    if dk is not None:
+        shp = _shape(B, Tq, Tk, H, H, Dqk, Dqk, max(kk, 1), sm_scale, KV_BF16, H_I, d_I)
+        nbytes = workspace_size(shp, OP_INDEXER_KL_DENSE if idx is None else OP_INDEXER_KL)
+    ws = _workspace(nbytes, dev, ws)
     _check(lib().dsa_indexer_kl(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(idx), _ptr(kv_len),
                                 B, Tq, Tk, H_I, d_I, H, Dqk, kk, ctypes.c_float(sm_scale), _ptr(loss), _ptr(dq),
-                                _ptr(dw), _ptr(dk), _stream(stream)))
+                                _ptr(dw), _ptr(dk), _ptr(ws), nbytes, _stream(stream)))
     return loss, dq, dw, dk
+
+
+def indexer_kl_workspace_size(B, Tq, Tk, H_I, d_I, kk=0):
+    """Bytes of workspace dsa_indexer_kl needs for key gradients (kk 0: dense warm-up)."""
+    shp = _shape(B, Tq, Tk, 1, 1, 32, 32, max(kk, 1), 1.0, KV_BF16, H_I, d_I)
+    return workspace_size(shp, OP_INDEXER_KL if kk else OP_INDEXER_KL_DENSE)
 
 
 def _shape(B, Tq, Tk, H, Hkv, Dqk, Dv, k, sm_scale, kv_dtype, H_I=16, d_I=64, kv_len=None):

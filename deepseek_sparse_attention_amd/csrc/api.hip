@@ -290,7 +290,7 @@ dsa_status dsa_index_topk(const void* q_idx, const void* k_idx, const void* w_id
 dsa_status dsa_indexer_kl(const void* q_idx, const void* k_idx, const void* w_idx, const void* q, const void* k,
                           const int32_t* idx, const int32_t* kv_len, int B, int Tq, int Tk, int H_I, int d_I, int H,
                           int Dqk, int kk, float sm_scale, float* loss, float* dq_idx, float* dw_idx, float* dk_idx,
-                          void* stream) {
+                          void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || Tq < 0 || Tk < 0) return fail(DSA_ERR_SHAPE, "B, Tq and Tk must be >= 0");
   if (H_I < 1 || d_I < 1 || H < 1 || Dqk < 1) return fail(DSA_ERR_SHAPE, "H_I, d_I, H and Dqk must be >= 1");
   if (idx && kk < 1) return fail(DSA_ERR_SHAPE, "kk must be >= 1 when idx is given");
@@ -299,16 +299,24 @@ dsa_status dsa_indexer_kl(const void* q_idx, const void* k_idx, const void* w_id
     return fail(DSA_ERR_UNSUPPORTED, "indexer KL supports H_I <= 16, d_I in {16,32,64,128}, H <= 16, Dqk = 32");
   if (idx ? kk > dsa::kKlMaxKeys : Tk > dsa::kKlMaxKeys)
     return fail(DSA_ERR_UNSUPPORTED, "indexer KL takes at most 4096 keys per row (kk, or Tk without idx)");
+  if (dk_idx && ((int64_t)B * Tk >= INT32_MAX || (idx && (int64_t)B * Tq * kk >= INT32_MAX)))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer KL key gradients need B * Tk and B * Tq * kk below 2^31 - 1");
   if ((int64_t)B * Tq == 0 && !(dk_idx && (int64_t)B * Tk > 0)) return DSA_OK;
   if (!q_idx || !k_idx || !w_idx || !q || !k || !loss)
     return fail(DSA_ERR_NULL, "q_idx, k_idx, w_idx, q, k and loss are required");
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(w_idx, 2) ||
       !aligned(idx, 4) || !aligned(loss, 4) || !aligned(dq_idx, 4) || !aligned(dw_idx, 4) || !aligned(dk_idx, 4))
     return fail(DSA_ERR_UNSUPPORTED, "q_idx, k_idx, q and k must be 16-byte aligned; w_idx 2-byte; idx and outputs 4");
+  if (dk_idx) {
+    const size_t need = dsa::indexer_kl_workspace_bytes(B, Tq, Tk, H_I, kk, idx == nullptr);
+    if (need && (!ws || ws_bytes < need))
+      return fail(DSA_ERR_WORKSPACE, "indexer KL workspace too small: need " + std::to_string(need) + " bytes");
+    if (!aligned(ws, 256)) return fail(DSA_ERR_UNSUPPORTED, "ws must be 256-byte aligned");
+  }
   dsa::IndexerKlArgs a{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, (const uint16_t*)q,
                        (const uint16_t*)k, idx, kv_len, B, Tq, Tk, H_I, d_I, H, idx ? kk : 0, sm_scale, loss,
                        dq_idx, dw_idx, dk_idx};
-  return launch_status(dsa::launch_indexer_kl(a, as_stream(stream)), "dsa_indexer_kl");
+  return launch_status(dsa::launch_indexer_kl(a, ws, as_stream(stream)), "dsa_indexer_kl");
 }
 
 dsa_status dsa_index_scores_paged(const void* q_idx, const void* k_pool, const void* w_idx, const dsa_paged_kv* pages,
@@ -466,7 +474,12 @@ dsa_status dsa_pattern_from_freq(int freq, int n_layers, char* out) {
 int dsa_stack_chunk_rows(const dsa_shape* shape) { return shape ? chunk_rows(*shape) : 1; }
 
 size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
-  if (!s || s->B < 0 || s->Tq < 0 || s->Tk < 0 || s->H < 1 || s->Dv < 1 || s->k < 1) return 0;
+  if (!s || s->B < 0 || s->Tq < 0 || s->Tk < 0) return 0;
+  if (op == DSA_OP_INDEXER_KL_DENSE)
+    return s->H_I < 1 ? 0 : dsa::indexer_kl_workspace_bytes(s->B, s->Tq, s->Tk, s->H_I, 0, true);
+  if (op == DSA_OP_INDEXER_KL)
+    return s->H_I < 1 || s->k < 1 ? 0 : dsa::indexer_kl_workspace_bytes(s->B, s->Tq, s->Tk, s->H_I, s->k, false);
+  if (s->H < 1 || s->Dv < 1 || s->k < 1) return 0;
   const bool mla = s->Hkv == 1 && s->Dqk == 576 && s->Dv == 512;
   switch (op) {
     case DSA_OP_SCORES:
@@ -479,6 +492,8 @@ size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
     case DSA_OP_STACK_PAGED:  // score chunks (paged keys take the score route) + pool rows + attention
       return align_up(plan_index_topk(*s, true).ws) + paged_idx_bytes(*s) +
              dsa::kMaxAttnLayers * dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);
+    case DSA_OP_INDEXER_KL:
+    case DSA_OP_INDEXER_KL_DENSE: return 0;  // handled above
     case DSA_OP_STACK: {
       // either route of the 'F' layers fits (DSA_STACK_UNFUSED picks the score chunks)
       const size_t sel = std::max(plan_index_topk(*s, false).ws, plan_index_topk(*s, true).ws);

@@ -94,7 +94,10 @@ struct IndexerKlArgs {
 };
 constexpr int kKlMaxKeys = 4096;  // key entries per row
 bool indexer_kl_supported(int H_I, int d_I, int H, int Hkv, int Dqk);
-hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st);
+// workspace of the key-major dk pass (rows * entries coefficients, plus the key sort for
+// index lists); none is needed without dk
+size_t indexer_kl_workspace_bytes(int B, int Tq, int Tk, int H_I, int kk, bool dense);
+hipError_t launch_indexer_kl(const IndexerKlArgs& a, void* ws, hipStream_t st);
 
 struct AttnArgs {
   const uint16_t* q;

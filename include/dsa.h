@@ -94,7 +94,9 @@ typedef enum {
   DSA_OP_STACK = 3,
   DSA_OP_INDEX_TOPK = 4,
   DSA_OP_ATTN_PAGED = 5,
-  DSA_OP_STACK_PAGED = 6
+  DSA_OP_STACK_PAGED = 6,
+  DSA_OP_INDEXER_KL = 7,      /* dsa_indexer_kl with index lists of shape k entries */
+  DSA_OP_INDEXER_KL_DENSE = 8 /* dsa_indexer_kl over every causal key (idx NULL; k ignored) */
 } dsa_op;
 
 /* flags of dsa_layer_stack */
@@ -206,16 +208,23 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const float* kv_scale,
  *         NULL (kk ignored)
  *   loss  fp32 [B][Tq] (0 for a row with no key)
  *   dq_idx fp32 [B][Tq][H_I][d_I], dw_idx fp32 [B][Tq][H_I], dk_idx fp32 [B][Tk][d_I]: each
- *         may be NULL (not computed).  dk_idx is overwritten: cleared, then accumulated with
- *         fp32 atomics, so rows that share a key add in no fixed order and dk_idx can differ
- *         between runs in the last bits; loss, dq_idx and dw_idx are deterministic.
+ *         may be NULL (not computed).  dk_idx is overwritten.  Every output is deterministic,
+ *         bit for bit: dk_idx adds, for each key, the terms of the rows that list it in row
+ *         order (then list order), through the workspace.
+ *   ws    with dk_idx, at least dsa_workspace_size(shape, DSA_OP_INDEXER_KL) bytes (index
+ *         lists; shape.k = kk) or DSA_OP_INDEXER_KL_DENSE (idx NULL), 256-byte aligned; the
+ *         shape fields read are B, Tq, Tk, H_I (and k).  It holds every entry's head terms
+ *         (B Tq kk H_I floats, or B Tq Tk H_I dense) and, for index lists, the key sort
+ *         (16 bytes per entry plus per-key offsets).  Unused without dk_idx (may be NULL).
  * Supported: 1 <= H_I <= 16, d_I in {16, 32, 64, 128}, 1 <= H <= 16, Dqk = 32; at most 4096
- * keys per row (kk <= 4096, or Tk <= 4096 without idx).
+ * keys per row (kk <= 4096, or Tk <= 4096 without idx); with dk_idx, B Tk and B Tq kk below
+ * 2^31 - 1.
  */
 dsa_status dsa_indexer_kl(const void* q_idx, const void* k_idx, const void* w_idx, const void* q,
                           const void* k, const int32_t* idx, const int32_t* kv_len, int B, int Tq,
                           int Tk, int H_I, int d_I, int H, int Dqk, int kk, float sm_scale,
-                          float* loss, float* dq_idx, float* dw_idx, float* dk_idx, void* stream);
+                          float* loss, float* dq_idx, float* dw_idx, float* dk_idx, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Paged caches, for serving batches (the pages serve many sequences at once through vLLM

@@ -202,7 +202,7 @@ def test_index_topk_workspace_follows_the_route(L):
 def test_indexer_kl_argument_checks(L):
     P = ctypes.c_void_p(16)
     f = ctypes.c_float
-    kl = lambda *a: L.dsa_indexer_kl(*a)
+    kl = lambda *a: L.dsa_indexer_kl(*a[:-1], None, 0, a[-1])  # no workspace
     # MLA-width main attention: unsupported
     assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 16, 576, 4, f(0.04), P, None, None, None, None) == 3
     # indexer width outside {16,32,64,128}
@@ -218,6 +218,28 @@ def test_indexer_kl_argument_checks(L):
     # empty batch without key gradients: nothing to do
     assert kl(None, None, None, None, None, None, None, 0, 4, 8, 2, 16, 4, 32, 4, f(0.1), None, None, None, None,
               None) == 0
+    # key gradients need the workspace; 16-byte alignment is not enough
+    need = dsa.indexer_kl_workspace_size(1, 4, 8, 2, 16, kk=4)
+    assert kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 4, f(0.1), P, None, None, P, None) == 5
+    assert L.dsa_indexer_kl(P, P, P, P, P, P, None, 1, 4, 8, 2, 16, 4, 32, 4, f(0.1), P, None, None, P,
+                            ctypes.c_void_p(16), need, None) == 3
+    # key and entry counts past the 32-bit sort
+    assert kl(P, P, P, P, P, P, None, 1 << 16, 1 << 10, 1 << 15, 2, 16, 4, 32, 4, f(0.1), P, None, None, P,
+              None) == 3
+
+
+def test_indexer_kl_workspace_sizes():
+    # index lists: every entry's head terms, the two ping-pong (key, entry) arrays, the
+    # per-tile digit counts and the per-key offsets
+    B, Tq, Tk, H_I, kk = 1, 3072, 3072, 2, 512
+    E = B * Tq * kk
+    sparse = dsa.indexer_kl_workspace_size(B, Tq, Tk, H_I, 16, kk=kk)
+    assert E * H_I * 4 + 4 * E * 4 + (B * Tk + 1) * 4 <= sparse <= E * (H_I * 4 + 16) + 2 ** 20
+    # dense warm-up: the head terms of every (row, key) pair, no sort
+    dense = dsa.indexer_kl_workspace_size(B, Tq, Tk, H_I, 16)
+    assert B * Tq * Tk * H_I * 4 <= dense < B * Tq * Tk * H_I * 4 + 512
+    assert dsa.indexer_kl_workspace_size(0, 5, 5, 2, 16) == 0
+    assert dsa.indexer_kl_workspace_size(2, 0, 7, 2, 16, kk=3) > 0  # per-key offsets only
 
 
 def test_paged_argument_checks(L):

@@ -96,3 +96,64 @@ def test_indexer_kl_empty_rows_and_forward_only():
     loss2, *rest = dsa.indexer_kl(*args, w.scale(), idx=torch.from_numpy(idx).to(DEV), grads=False)
     assert all(r is None for r in rest)
     assert np.array_equal(_host(loss2).numpy(), gl.astype(np.float32))
+
+
+def test_indexer_kl_key_gradient_is_bit_identical_across_runs():
+    # many rows list the same keys (top-512 of 3072, and the dense warm-up's every causal
+    # key): dk adds their terms key by key in row order, so repeated calls agree bit for bit
+    print("indexer KL determinism", flush=True)
+    w = synth.workload("A")
+    d = _inputs(w, q_gain=6.0, qi_gain=3.0)
+    args = [d[x].to(DEV) for x in ("q_idx", "k_idx", "w_idx", "q", "kv")]
+    s = dsa.index_scores(*args[:3])
+    ix = dsa.topk(s, w.k)
+    del s
+    for idx in (ix, None):
+        runs = [dsa.indexer_kl(*args, w.scale(), idx=idx) for _ in range(3)]
+        torch.cuda.synchronize()
+        for name, pos in (("loss", 0), ("dq", 1), ("dw", 2), ("dk", 3)):
+            a = runs[0][pos].cpu()
+            for r in runs[1:]:
+                assert torch.equal(a.view(torch.int32), r[pos].cpu().view(torch.int32)), (name, idx is None)
+
+
+def test_indexer_kl_duplicates_and_two_sequences():
+    # two sequences (keys b * Tk + s in the key sort), ragged lengths, lists with repeated
+    # keys (each copy is a term of both distributions and of dk) and -1 holes
+    print("indexer KL duplicates, B=2", flush=True)
+    w = synth.workload("A", B=2, T=520, k=96)
+    d = _inputs(w, q_gain=6.0, qi_gain=3.0)
+    rng = np.random.default_rng(7)
+    kv_len = [520, 301]
+    idx = np.full((2, 520, 96), -1, np.int32)
+    for b in range(2):
+        for t in range(520):
+            p = kv_len[b] - 520 + t
+            if p < 0:
+                continue
+            n = min(p + 1, 80)
+            idx[b, t, :n] = rng.choice(p + 1, size=n, replace=False)
+            if t % 3 == 0:
+                idx[b, t, n:n + 5] = idx[b, t, :5]  # five keys listed twice
+    _compare(d, w.scale(), idx=idx, kv_len=kv_len)
+    # and again, bit for bit
+    args = [d[x].to(DEV) for x in ("q_idx", "k_idx", "w_idx", "q", "kv")]
+    ix = torch.from_numpy(idx).to(DEV)
+    kl = torch.tensor(kv_len, dtype=torch.int32, device=DEV)
+    a = dsa.indexer_kl(*args, w.scale(), idx=ix, kv_len=kl)[3].cpu()
+    b_ = dsa.indexer_kl(*args, w.scale(), idx=ix, kv_len=kl)[3].cpu()
+    assert torch.equal(a.view(torch.int32), b_.view(torch.int32))
+
+
+def test_indexer_kl_large_key_sort():
+    # 20000 rows of 2048 entries (41M pairs): the key sort takes two 8-bit passes, the
+    # first with more than 1024 scan blocks; entries drawn with repeats (early rows list
+    # most of their few keys many times)
+    print("indexer KL T=20000 k=2048 key sort", flush=True)
+    T, kk = 20000, 2048
+    w = synth.workload("A", T=T, k=kk, H_I=1, d_I=16, H=1, Hkv=1)
+    d = _inputs(w, q_gain=6.0, qi_gain=3.0)
+    rng = np.random.default_rng(11)
+    u = rng.random((1, T, kk))
+    idx = np.floor(u * (np.arange(T)[None, :, None] + 1)).astype(np.int32)
+    _compare(d, w.scale(), idx=idx)
