@@ -195,6 +195,7 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
         "# unfused step), then the decode steps and the bench's timings of their parts, the per-layer",
         "# attention launches, then the KL objective (sparse and dense, with gradients).",
+        "# mla_attn_wk_kernel: bf16 rows, whole-row launches over more than 24576 keys (the prefill layer);",
         "# mla_attn_kernel<f, w>: rows f = 0 bf16, 1 fp8, 2 MXFP4; w = 1 the three-workgroup schedule;",
         "# index_scores_kernel<H_I, d_I, paged, query tiles per wave>.  grid = threads of the launch",
         "# (the 64-row decode: grouped 3-layer attention 98304, one layer 131072; decode indexer 393216)",
@@ -434,7 +435,7 @@ def main():
     attn_flops = sel * w.H * 2 * (w.Dqk + w.Dv)
     logical = attn_bytes / (attn_ms * 1e-3) / 1e9
     traffic_all = read_traffic()
-    traffic = traffic_all.get(f"dsa::mla_attn_kernel<0, 0> grid={T * w.H // 16 * 256}")
+    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel grid={T * w.H // 16 * 128}")
     pl = probe()
     psum = torch.empty(T * 4, dtype=torch.int32, device=dev)
 
@@ -455,7 +456,7 @@ def main():
     read_gbs = rbuf.numel() * 4 / (timed(read_probe) * 1e-3) / 1e9
     del rbuf, rsum, psum
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
-    roofline = {"kernel": "mla_attn_kernel<bf16>", "bound": "mfma", "achieved": round(tflops, 1),
+    roofline = {"kernel": "mla_attn_wk_kernel (bf16 rows)", "bound": "mfma", "achieved": round(tflops, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "flops": attn_flops, "ms_per_launch": round(attn_ms, 3),
                 "gather": {"algorithmic_bytes": attn_bytes, "logical_gbs": round(logical, 1),

@@ -4,10 +4,10 @@
 //
 // MLA form (DeepSeek-V2-Lite-Chat SIQ card, "Measured": one 576-wide latent row per token,
 // 512 compressed-KV values then 64 rotary values; V = the first 512 values of the same
-// row).  A workgroup serves one query row and 16 heads.  Per tile of 64 selected keys the
+// row).  A workgroup serves one query row and 16 heads.  Per tile of 32 selected keys the
 // gathered rows are staged once in LDS and used twice: as K (all 576 columns) for
-// S = Q K^T with the 16 heads as the MFMA M dimension, and as V (columns 0..511) for
-// O += P V, read transposed straight from LDS with ds_read_b64_tr_b16.  The 4 waves split
+// S^T = K Q^T with the keys as the MFMA M dimension, and as V (columns 0..511) for
+// O^T += V^T P^T, read transposed straight from LDS with ds_read_b64_tr_b16.  The 4 waves split
 // the keys of a tile for Q K^T and the 512 value columns for P V; softmax statistics are
 // exchanged through LDS (online softmax in base 2).  The next tile's gather is issued into
 // registers before the current tile is computed.  fp8 (OCP e4m3) rows are widened to bf16
@@ -16,12 +16,16 @@
 // the same card's "Measured" section names an nvfp4 latent cache for sparse MLA) are
 // decoded with their block scales while staged, also exactly: e2m1 times a power of two
 // has two significant bits.
+// Launches of whole rows over long bf16 caches run mla_attn_wk_kernel instead: a wave per
+// 16-key step with its own softmax state and O, merged once per row (below).
 // Decode rows (few queries) split the key list over workgroups and merge the partial
 // results by log-sum-exp in a second kernel, in a fixed order.
 //
 // Multi-head form (DSA ablation card: 4 heads of width 32, RoPE'd inputs): a workgroup per
 // query row, key rows read as 16-byte chunks spread over the lanes, logits in LDS, three
 // fixed-order passes.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -439,6 +443,280 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
   }
 }
 
+// ---- one wave per key step: bf16 rows, launches of whole rows ---------------------------
+// A workgroup of two waves serves one query row and 16 heads.  Wave w takes the 16-key
+// steps w, w + 2, w + 4, ... of the row's index list (entries 16 (2i + w) .. +15) and keeps
+// its own online-softmax state and O for all 16 heads and 512 dims, so the key loop has no
+// barrier: each wave stages its rows in two LDS slots of its own (the swizzle above).
+// Per step:
+//   S^T (16 keys x 16 heads) = K Q^T in 18 MFMA k-steps, the keys as M (K rows from LDS,
+//   Q^T in registers); the softmax leaves each lane the probabilities of its 4 keys for its
+//   head, which is exactly the B operand of O^T += V^T P^T over those 16 keys (16x16x16
+//   MFMAs, V read transposed from LDS).
+// The two waves' (m, l, O) are merged once per row, in a fixed order.  Rows are gathered
+// into registers and written to the free slot one step before they are used.
+// O is never rescaled inside the loop: each head's reference is the max of its first tile
+// with a valid key, and later probabilities exp2(s - ref) may reach 2^kWkSlack, which fp32
+// sums and bf16 probabilities hold.  A tile that exceeds its head's reference by more than
+// that flags the row, which is then computed again from the head's exact max (a pass of
+// Q K^T alone first); ordinary rows never take that path, and the loop keeps O in the
+// accumulator registers (a rescale inside it made the compiler move O to vector registers
+// and spill).
+constexpr int kWkKeys = 16;               // keys per wave step
+constexpr int kWkSlot = kWkKeys * kRowB;  // 18 KB
+constexpr float kWkSlack = 64.f;
+
+__device__ __forceinline__ f32x4 mfma16k16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(128, 2) void mla_attn_wk_kernel(const MlaLayers Ls, const int32_t* __restrict__ idx,
+                                                             int Tq, int Tk, int64_t kv_bstride, int H, int k,
+                                                             float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][2][kWkSlot];  // [wave][slot]
+  __shared__ float ml_red[2][16][2];
+  __shared__ int jmax_red[2];
+
+  const int z = blockIdx.z;
+  const uint16_t* __restrict__ q = Ls.q[z];
+  const uint8_t* __restrict__ kv = Ls.kv[z];
+  uint16_t* __restrict__ out = Ls.out[z];
+  float* __restrict__ lse = Ls.lse[z];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int HG = H >> 4;
+  const int64_t rowh = blockIdx.x;
+  const int64_t row = rowh / HG;
+  const int hg = (int)(rowh % HG);
+  const int b = (int)(row / Tq);
+  const int32_t* ix = idx + row * k;
+  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + b * kv_bstride * kRowB, (uint32_t)Tk * kRowB);
+  const __amdgpu_buffer_rsrc_t ix_rs = make_rsrc(ix, (uint32_t)k * 4);
+
+  // lane roles: hl = head (S^T and O^T column), gq = which 4 keys of a step (rows 4gq..)
+  const int hl = lane & 15, gq = lane >> 4;
+  bf16x8 qb[18];  // Q^T as the B operand: column = head hl, dims 32s + 8gq .. +7
+  {
+    const uint16_t* qp = q + (row * H + hg * 16 + hl) * kDqk + gq * 8;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qb[s] = as_bf16x8(ld16(qp + s * 32));
+    // Q^T lives in accumulator registers (an MFMA reads its B operand from there too),
+    // leaving the vector registers to the row stage and the LDS operands read ahead
+#pragma unroll
+    for (int s = 0; s < 18; ++s) asm volatile("" : "+a"(qb[s]));
+  }
+
+  // last valid entry of the row: steps past it are skipped
+  int jm = -1;
+  for (int j = tid; j < k; j += 128) {
+    const int sj = ix[j];
+    if (sj >= 0 && sj < Tk) jm = j;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
+  if (lane == 0) jmax_red[wave] = jm;
+  __syncthreads();
+  jm = max(jmax_red[0], jmax_red[1]);
+  const int nblk = (jm + kWkKeys) / kWkKeys;  // 16-entry blocks covering entries 0..jm
+  const int nsteps = (nblk - wave + 1) / 2;   // this wave's blocks: wave, wave + 2, ... < nblk
+
+  // gather roles: lane l loads the rows of keys l/8 and 8 + l/8 of a step, 16-byte parts
+  // l%8 + 8c (eight lanes per row: every load instruction reads eight full 128-byte lines)
+  const int gkey = lane >> 3, part0 = lane & 7;
+  auto entry_off = [&](int i, int g) -> int { return (2 * i + wave) * kWkKeys + gkey + 8 * g; };
+  auto raw_entry = [&](int i, int g) -> int {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, i < nsteps ? entry_off(i, g) * 4 : (int)kOffNone, 0, 0);
+  };
+  auto valid_entry = [&](int i, int g, int raw) -> int {
+    const int lim = (i < nsteps && entry_off(i, g) < k) ? Tk : 0;
+    return (uint32_t)raw < (uint32_t)lim ? raw : -1;
+  };
+  u32x4 rr[1][2][9];  // the register stage: [row role][part]
+  uint32_t rmask[1];   // its valid keys (bit r: key r of the step)
+  auto gather = [&](u32x4 (&r)[2][9], uint32_t& msk, int i, int e0, int e1) __attribute__((always_inline)) {
+    const int s0 = valid_entry(i, 0, e0), s1 = valid_entry(i, 1, e1);
+    const uint32_t b0 = (s0 >= 0 ? __umul24((uint32_t)s0, (uint32_t)kRowB) : kRowNone) + part0 * 16;
+    const uint32_t b1 = (s1 >= 0 ? __umul24((uint32_t)s1, (uint32_t)kRowB) : kRowNone) + part0 * 16;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      r[0][c] = buf_load_16(kv_rs, b0 + 128 * c, 0);
+      r[1][c] = buf_load_16(kv_rs, b1 + 128 * c, 0);
+    }
+    // lanes 8r hold keys r and 8 + r
+    const uint64_t v0 = __ballot(s0 >= 0), v1 = __ballot(s1 >= 0);
+    uint32_t m = 0;
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2)
+      m |= (uint32_t)((v0 >> (8 * r2)) & 1u) << r2 | (uint32_t)((v1 >> (8 * r2)) & 1u) << (8 + r2);
+    msk = m;
+  };
+  auto stage = [&](const u32x4 (&r)[2][9], uint8_t* slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int c = 0; c < 9; ++c) *reinterpret_cast<u32x4*>(slot + lds_off(gkey + 8 * g, part0 + 8 * c)) = r[g][c];
+  };
+
+  f32x4 o_acc[32];  // O^T: rows = dims 16n + 4gq + i, column = head hl
+#pragma unroll
+  for (int n = 0; n < 32; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // base-2 logits of the lane's 4 keys for head hl (-inf for a missing key)
+  auto qk = [&](const uint8_t* sl, uint32_t msk, float (&sv)[4]) __attribute__((always_inline)) {
+    // two accumulation chains (even and odd k-steps), added at the end
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    u32x4 kr[18];  // every K operand read first, so the reads overlap
+#pragma unroll
+    for (int s = 0; s < 18; ++s) kr[s] = *reinterpret_cast<const u32x4*>(sl + lds_off(hl, 4 * s + gq));
+#pragma unroll
+    for (int s = 0; s < 18; s += 2) {
+      a0 = mfma16(as_bf16x8(kr[s]), qb[s], a0);
+      a1 = mfma16(as_bf16x8(kr[s + 1]), qb[s + 1], a1);
+    }
+    // six reads ahead, then one MFMA per read (the scheduler otherwise waits on each read
+    // right before its MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int g = 0; g < 12; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = ((msk >> (4 * gq + e)) & 1u) ? (a0[e] + a1[e]) * scale_log2 : -INFINITY;
+  };
+  bool redo = false;
+  // online softmax of one step's logits: P^T as the B operand of P V
+  auto softmax = [&](const float (&sv)[4]) __attribute__((always_inline)) -> i16x4 {
+    const float tm = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    if (m_run == -INFINITY)
+      m_run = tm;  // the head's first valid keys (O and l are still 0); stays -inf otherwise
+    else if (tm > m_run + kWkSlack)
+      redo = true;
+    const float mref = m_run == -INFINITY ? 0.f : m_run;  // (then every sv is -inf)
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sv[e] - mref);
+    l_run += rows_sum((p[0] + p[1]) + (p[2] + p[3]));
+    return __builtin_bit_cast(i16x4, make_uint2(cvt_bf16x2(p[0], p[1]), cvt_bf16x2(p[2], p[3])));
+  };
+  // O^T += V^T P^T: lane (gq, hl) reads keys 4gq .. 4gq+3 at dim 16n + hl (transposed)
+  auto pv = [&](const uint8_t* sl, i16x4 pb) __attribute__((always_inline)) {
+    const int r0 = 4 * gq + (hl >> 2);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {  // sixteen operand reads, then their MFMAs
+      i16x4 v[16];
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int dim = (16 * h2 + n) * 16 + 4 * (hl & 3);
+        v[n] = lds_read_tr16(sl + lds_off(r0, dim >> 3) + (dim & 7) * 2);
+      }
+#pragma unroll
+      for (int n = 0; n < 16; ++n) o_acc[16 * h2 + n] = mfma16k16(v[n], pb, o_acc[16 * h2 + n]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int g = 0; g < 10; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    }
+  };
+  auto compute = [&](const uint8_t* sl, uint32_t msk) __attribute__((always_inline)) {
+    float sv[4];
+    qk(sl, msk, sv);
+    pv(sl, softmax(sv));
+  };
+
+  for (int attempt = 0;; ++attempt) {
+    if (attempt == 1) {
+      // a tile outgrew its head's reference: the exact max of every head first (Q K^T
+      // alone, one step at a time), then the row again from it
+      float mt = -INFINITY;
+      for (int i = 0; i < nsteps; ++i) {
+        gather(rr[0], rmask[0], i, raw_entry(i, 0), raw_entry(i, 1));
+        stage(rr[0], kvs[wave][0]);
+        float sv[4];
+        qk(kvs[wave][0], rmask[0], sv);
+        mt = fmaxf(mt, rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
+      }
+      m_run = mt;
+      l_run = 0.f;
+#pragma unroll
+      for (int n = 0; n < 32; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    redo = false;
+    // one register stage.  Iteration i (parity P) finds step i in slot P and step i+1 in the
+    // register stage; it stages step i+1 into slot 1-P, gathers step i+2 and computes step i.
+    uint32_t mask_slot[2];
+    int en0, en1;
+    {
+      const int e00 = raw_entry(0, 0), e01 = raw_entry(0, 1);
+      const int e10 = raw_entry(1, 0), e11 = raw_entry(1, 1);
+      en0 = raw_entry(2, 0);
+      en1 = raw_entry(2, 1);
+      gather(rr[0], rmask[0], 0, e00, e01);
+      stage(rr[0], kvs[wave][0]);
+      mask_slot[0] = rmask[0];
+      gather(rr[0], rmask[0], 1, e10, e11);
+    }
+    auto iter = [&](auto par_c, int i) __attribute__((always_inline)) {
+      constexpr int P = decltype(par_c)::value;
+      stage(rr[0], kvs[wave][1 - P]);
+      mask_slot[1 - P] = rmask[0];
+      __builtin_amdgcn_sched_barrier(0);  // the stage's registers are free before the next gather
+      gather(rr[0], rmask[0], i + 2, en0, en1);
+      en0 = raw_entry(i + 3, 0);
+      en1 = raw_entry(i + 3, 1);
+      compute(kvs[wave][P], mask_slot[P]);
+    };
+    {
+      int i = 0;
+      for (; i + 1 < nsteps; i += 2) {
+        iter(std::integral_constant<int, 0>{}, i);
+        iter(std::integral_constant<int, 1>{}, i + 1);
+      }
+      if (i < nsteps) iter(std::integral_constant<int, 0>{}, i);
+    }
+    if (!__syncthreads_or(redo) || attempt == 1) break;  // (the second pass never flags)
+  }
+
+  // ---- merge the two waves: (m, l) per head, then O over the waves in order
+  __syncthreads();  // both waves are done with their slots
+  if (gq == 0) {
+    ml_red[wave][hl][0] = m_run;
+    ml_red[wave][hl][1] = l_run;
+  }
+  __syncthreads();
+  const float m0 = ml_red[0][hl][0], m1 = ml_red[1][hl][0];
+  const float mx = fmaxf(m0, m1);
+  const float mxr = mx == -INFINITY ? 0.f : mx;
+  const float f0 = fast_exp2(m0 - mxr), f1 = fast_exp2(m1 - mxr);
+  const float lt = ml_red[0][hl][1] * f0 + ml_red[1][hl][1] * f1;
+  {
+    const float mine = wave == 0 ? f0 : f1;
+    f32x4* ob = reinterpret_cast<f32x4*>(&kvs[wave][0][0]);  // 32 KB of this wave's region
+#pragma unroll
+    for (int n = 0; n < 32; ++n) ob[n * 64 + lane] = o_acc[n] * mine;
+  }
+  __syncthreads();
+  const float inv = lt == 0.f ? 0.f : 1.f / lt;  // (a NaN sum stays NaN)
+  const int h = hg * 16 + hl;
+  const f32x4* o0 = reinterpret_cast<const f32x4*>(&kvs[0][0][0]);
+  const f32x4* o1 = reinterpret_cast<const f32x4*>(&kvs[1][0][0]);
+  uint16_t* op = out + (row * H + h) * kDv + 4 * gq;
+#pragma unroll
+  for (int nn = 0; nn < 16; ++nn) {  // wave w writes dims 256w .. 256w + 255
+    const int n = wave * 16 + nn;
+    const f32x4 x = o0[n * 64 + lane] + o1[n * 64 + lane];
+    const uint32_t lo = cvt_bf16x2(x[0] * inv, x[1] * inv);
+    const uint32_t hi = cvt_bf16x2(x[2] * inv, x[3] * inv);
+    *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
+  }
+  if (lse && wave == 0 && gq == 0) lse[row * H + h] = lt == 0.f ? -INFINITY : (mxr + __log2f(lt)) * kLn2;
+}
+
 // Merge split-key partial results (fixed split order).  One workgroup per (row, 4 heads),
 // one wave per head: lane s holds split s's (m, l) (up to 64 splits), the wave reduces
 // them, and each lane then sums 8 output dims over the splits with 16-byte loads.
@@ -712,6 +990,11 @@ hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers,
     dim3 grid((unsigned)(rows * (a.H / 16)), nsplit, nlayers);
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
     const bool wide = a.kv_fmt == kKvBf16 && nsplit == 1 && a.Tk <= kWideMaxTk;
+    if (a.kv_fmt == kKvBf16 && nsplit == 1 && !wide) {  // long whole-row launches: one wave per key step
+      hipLaunchKernelGGL(mla_attn_wk_kernel, dim3((unsigned)(rows * (a.H / 16)), 1, nlayers), dim3(128), 0, st, Ls,
+                         a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2);
+      return hipGetLastError();
+    }
 #define DSA_MLA_LAUNCH(F, W)                                                                                       \
   hipLaunchKernelGGL((mla_attn_kernel<F, W>), grid, dim3(256), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, \
                      per, part_o, part_ml, part_layer, a.tail_kv_len, a.tail_Tk)

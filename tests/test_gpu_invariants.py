@@ -3,7 +3,8 @@
   * the score boundary: dsa_index_scores writes every entry of a caller's row (-inf past the
     causal bound and in the padding), whatever the buffer held;
   * the dominant attention instance (bf16 rows, no key split, more keys than the three-
-    workgroup schedule takes) on sharp inputs, where a wrong gather moves outputs by O(1);
+    workgroup schedule takes) on sharp inputs, where a wrong gather moves outputs by O(1),
+    and its exact-max recomputation when a late key's logit jumps far above the first ones;
   * duplicate index entries count twice, as in the oracle's gather form;
   * decode equals prefill: a one-query step over a cache of length L gives the indices of
     prefill row L-1 bit for bit, and its outputs within the attention bar ("cached versus
@@ -110,6 +111,34 @@ def test_mla_attention_bf16_unsplit_long_sharp():
     o = _host(out[:, :n]).double().numpy()
     per_row = np.max(np.abs(o - ref_bad), axis=(2, 3))[0]
     assert np.mean(per_row > 2e-2 * np.max(np.abs(ref_bad))) > 0.5
+
+
+def test_mla_attention_unsplit_logit_jump_beyond_the_first_tiles():
+    # the long whole-row kernel takes each head's reference max from its first tile with a
+    # valid key and recomputes a row from the exact max when a later key exceeds it by more
+    # than 2^64 (base 2): here one key per even row, late in the list, has a logit about
+    # 230 (base 2) above the rest for head 0, and the first 20 entries of every third row
+    # are missing (the reference then comes from a later tile)
+    print("mla attention bf16, unsplit, logit jump", flush=True)
+    Tq, Tk, k = 256, 25000, 256
+    q, kv = _sharp_qkv(Tq, Tk, seed=51)
+    idx = _random_index_rows(1, Tq, Tk, k, [Tk], seed=52)
+    idx[0, ::3, :20] = -1
+    scale = 1.0 / 24
+    for t in range(0, Tq, 2):
+        # the jump sits in the 64 rotary columns (K only), so the value rows stay unit-scale
+        key = int(idx[0, t, 200])
+        q0 = q[0, t, 0, 512:].float()
+        kv[0, key, 0, 512:] = (120.0 * q0 / q0.norm()).to(torch.bfloat16)
+    # keys may be shared between rows: the oracle sees the same rows
+    out, lse = dsa.sparse_attn(q.to(DEV), kv.to(DEV), torch.from_numpy(idx).to(DEV), scale, Dv=512)
+    ref, rlse = oracle.sparse_attn(q, kv, idx, scale, Dv=512)
+    _sharp_check(out, lse, ref, rlse, "logit jump")
+    # head 0 of the even rows is the jumping key's value row
+    o = _host(out).double().numpy()
+    for t in (0, 2, 100):
+        v = kv[0, int(idx[0, t, 200]), 0, :512].double().numpy()
+        assert np.max(np.abs(o[0, t, 0] - v)) <= 2e-2 * np.max(np.abs(v))
 
 
 @pytest.mark.parametrize("Tq,B", [(300, 1), (1, 5)])
