@@ -435,7 +435,7 @@ def main():
     attn_flops = sel * w.H * 2 * (w.Dqk + w.Dv)
     logical = attn_bytes / (attn_ms * 1e-3) / 1e9
     traffic_all = read_traffic()
-    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel grid={T * w.H // 16 * 128}")
+    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel<4> grid={T * w.H // 16 * 256}")
     pl = probe()
     psum = torch.empty(T * 4, dtype=torch.int32, device=dev)
 

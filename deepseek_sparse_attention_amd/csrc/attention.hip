@@ -444,16 +444,20 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
 }
 
 // ---- one wave per key step: bf16 rows, launches of whole rows ---------------------------
-// A workgroup of two waves serves one query row and 16 heads.  Wave w takes the 16-key
-// steps w, w + 2, w + 4, ... of the row's index list (entries 16 (2i + w) .. +15) and keeps
-// its own online-softmax state and O for all 16 heads and 512 dims, so the key loop has no
-// barrier: each wave stages its rows in two LDS slots of its own (the swizzle above).
+// A workgroup of kWkWaves waves serves one query row and 16 heads.  Wave w takes the 16-key
+// steps w, w + NW, w + 2 NW, ... of the row's index list (entries 16 (NW i + w) .. +15) and
+// keeps its own online-softmax state and O for all 16 heads and 512 dims, so the key loop has
+// no barrier: each wave stages its rows in two LDS slots of its own (the swizzle above).
+// Four waves (one workgroup per CU, 145 KB of LDS) keep 256 rows in flight; at T=65536 that
+// gathers with fewer L2 misses than two waves at two workgroups per CU (13.3 against 14.9 ms)
+// or one wave at four (16.4 ms): concurrent rows at the same list position read the same
+// key range, and fewer, faster rows keep that range narrower.
 // Per step:
 //   S^T (16 keys x 16 heads) = K Q^T in 18 MFMA k-steps, the keys as M (K rows from LDS,
 //   Q^T in registers); the softmax leaves each lane the probabilities of its 4 keys for its
 //   head, which is exactly the B operand of O^T += V^T P^T over those 16 keys (16x16x16
 //   MFMAs, V read transposed from LDS).
-// The two waves' (m, l, O) are merged once per row, in a fixed order.  Rows are gathered
+// The waves' (m, l, O) are merged once per row, in a fixed order.  Rows are gathered
 // into registers and written to the free slot one step before they are used.
 // O is never rescaled inside the loop: each head's reference is the max of its first tile
 // with a valid key, and later probabilities exp2(s - ref) may reach 2^kWkSlack, which fp32
@@ -463,6 +467,7 @@ __global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLa
 // accumulator registers (a rescale inside it made the compiler move O to vector registers
 // and spill).
 constexpr int kWkKeys = 16;               // keys per wave step
+constexpr int kWkWaves = 4;               // waves per workgroup (query row)
 constexpr int kWkSlot = kWkKeys * kRowB;  // 18 KB
 constexpr float kWkSlack = 64.f;
 
@@ -470,12 +475,13 @@ __device__ __forceinline__ f32x4 mfma16k16(i16x4 a, i16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(128, 2) void mla_attn_wk_kernel(const MlaLayers Ls, const int32_t* __restrict__ idx,
+template <int NW>  // waves per workgroup (query row)
+__global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_kernel(const MlaLayers Ls, const int32_t* __restrict__ idx,
                                                              int Tq, int Tk, int64_t kv_bstride, int H, int k,
                                                              float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][2][kWkSlot];  // [wave][slot]
-  __shared__ float ml_red[2][16][2];
-  __shared__ int jmax_red[2];
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[NW][2][kWkSlot];  // [wave][slot]
+  __shared__ float ml_red[NW][16][2];
+  __shared__ int jmax_red[NW];
 
   const int z = blockIdx.z;
   const uint16_t* __restrict__ q = Ls.q[z];
@@ -508,7 +514,7 @@ __global__ __launch_bounds__(128, 2) void mla_attn_wk_kernel(const MlaLayers Ls,
 
   // last valid entry of the row: steps past it are skipped
   int jm = -1;
-  for (int j = tid; j < k; j += 128) {
+  for (int j = tid; j < k; j += 64 * NW) {
     const int sj = ix[j];
     if (sj >= 0 && sj < Tk) jm = j;
   }
@@ -516,14 +522,16 @@ __global__ __launch_bounds__(128, 2) void mla_attn_wk_kernel(const MlaLayers Ls,
   for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
   if (lane == 0) jmax_red[wave] = jm;
   __syncthreads();
-  jm = max(jmax_red[0], jmax_red[1]);
+  jm = jmax_red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) jm = max(jm, jmax_red[w]);
   const int nblk = (jm + kWkKeys) / kWkKeys;  // 16-entry blocks covering entries 0..jm
-  const int nsteps = (nblk - wave + 1) / 2;   // this wave's blocks: wave, wave + 2, ... < nblk
+  const int nsteps = (nblk - wave + NW - 1) / NW;  // this wave's blocks: wave, wave + NW, ... < nblk
 
   // gather roles: lane l loads the rows of keys l/8 and 8 + l/8 of a step, 16-byte parts
   // l%8 + 8c (eight lanes per row: every load instruction reads eight full 128-byte lines)
   const int gkey = lane >> 3, part0 = lane & 7;
-  auto entry_off = [&](int i, int g) -> int { return (2 * i + wave) * kWkKeys + gkey + 8 * g; };
+  auto entry_off = [&](int i, int g) -> int { return (NW * i + wave) * kWkKeys + gkey + 8 * g; };
   auto raw_entry = [&](int i, int g) -> int {
     return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, i < nsteps ? entry_off(i, g) * 4 : (int)kOffNone, 0, 0);
   };
@@ -682,39 +690,57 @@ __global__ __launch_bounds__(128, 2) void mla_attn_wk_kernel(const MlaLayers Ls,
     if (!__syncthreads_or(redo) || attempt == 1) break;  // (the second pass never flags)
   }
 
-  // ---- merge the two waves: (m, l) per head, then O over the waves in order
-  __syncthreads();  // both waves are done with their slots
-  if (gq == 0) {
-    ml_red[wave][hl][0] = m_run;
-    ml_red[wave][hl][1] = l_run;
-  }
-  __syncthreads();
-  const float m0 = ml_red[0][hl][0], m1 = ml_red[1][hl][0];
-  const float mx = fmaxf(m0, m1);
-  const float mxr = mx == -INFINITY ? 0.f : mx;
-  const float f0 = fast_exp2(m0 - mxr), f1 = fast_exp2(m1 - mxr);
-  const float lt = ml_red[0][hl][1] * f0 + ml_red[1][hl][1] * f1;
-  {
-    const float mine = wave == 0 ? f0 : f1;
-    f32x4* ob = reinterpret_cast<f32x4*>(&kvs[wave][0][0]);  // 32 KB of this wave's region
-#pragma unroll
-    for (int n = 0; n < 32; ++n) ob[n * 64 + lane] = o_acc[n] * mine;
-  }
-  __syncthreads();
-  const float inv = lt == 0.f ? 0.f : 1.f / lt;  // (a NaN sum stays NaN)
   const int h = hg * 16 + hl;
-  const f32x4* o0 = reinterpret_cast<const f32x4*>(&kvs[0][0][0]);
-  const f32x4* o1 = reinterpret_cast<const f32x4*>(&kvs[1][0][0]);
   uint16_t* op = out + (row * H + h) * kDv + 4 * gq;
+  if constexpr (NW == 1) {
+    const float mxr = m_run == -INFINITY ? 0.f : m_run;
+    const float inv = l_run == 0.f ? 0.f : 1.f / l_run;  // (a NaN sum stays NaN)
 #pragma unroll
-  for (int nn = 0; nn < 16; ++nn) {  // wave w writes dims 256w .. 256w + 255
-    const int n = wave * 16 + nn;
-    const f32x4 x = o0[n * 64 + lane] + o1[n * 64 + lane];
-    const uint32_t lo = cvt_bf16x2(x[0] * inv, x[1] * inv);
-    const uint32_t hi = cvt_bf16x2(x[2] * inv, x[3] * inv);
-    *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
+    for (int n = 0; n < 32; ++n) {
+      const uint32_t lo = cvt_bf16x2(o_acc[n][0] * inv, o_acc[n][1] * inv);
+      const uint32_t hi = cvt_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
+      *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
+    }
+    if (lse && gq == 0) lse[row * H + h] = l_run == 0.f ? -INFINITY : (mxr + __log2f(l_run)) * kLn2;
+  } else {
+    // ---- merge the waves: (m, l) per head, then O over the waves in wave order
+    __syncthreads();  // every wave is done with its slots
+    if (gq == 0) {
+      ml_red[wave][hl][0] = m_run;
+      ml_red[wave][hl][1] = l_run;
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, ml_red[w][hl][0]);
+    const float mxr = mx == -INFINITY ? 0.f : mx;
+    float lt = 0.f, mine = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(ml_red[w][hl][0] - mxr);
+      lt += ml_red[w][hl][1] * f;
+      mine = w == wave ? f : mine;
+    }
+    {
+      f32x4* ob = reinterpret_cast<f32x4*>(&kvs[wave][0][0]);  // 32 KB of this wave's region
+#pragma unroll
+      for (int n = 0; n < 32; ++n) ob[n * 64 + lane] = o_acc[n] * mine;
+    }
+    __syncthreads();
+    const float inv = lt == 0.f ? 0.f : 1.f / lt;  // (a NaN sum stays NaN)
+    constexpr int NT = 32 / NW;  // dim tiles each wave writes
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+      const int n = wave * NT + nn;
+      f32x4 x = reinterpret_cast<const f32x4*>(&kvs[0][0][0])[n * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) x += reinterpret_cast<const f32x4*>(&kvs[w][0][0])[n * 64 + lane];
+      const uint32_t lo = cvt_bf16x2(x[0] * inv, x[1] * inv);
+      const uint32_t hi = cvt_bf16x2(x[2] * inv, x[3] * inv);
+      *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
+    }
+    if (lse && wave == 0 && gq == 0) lse[row * H + h] = lt == 0.f ? -INFINITY : (mxr + __log2f(lt)) * kLn2;
   }
-  if (lse && wave == 0 && gq == 0) lse[row * H + h] = lt == 0.f ? -INFINITY : (mxr + __log2f(lt)) * kLn2;
 }
 
 // Merge split-key partial results (fixed split order).  One workgroup per (row, 4 heads),
@@ -991,7 +1017,8 @@ hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers,
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
     const bool wide = a.kv_fmt == kKvBf16 && nsplit == 1 && a.Tk <= kWideMaxTk;
     if (a.kv_fmt == kKvBf16 && nsplit == 1 && !wide) {  // long whole-row launches: one wave per key step
-      hipLaunchKernelGGL(mla_attn_wk_kernel, dim3((unsigned)(rows * (a.H / 16)), 1, nlayers), dim3(128), 0, st, Ls,
+      hipLaunchKernelGGL(mla_attn_wk_kernel<kWkWaves>, dim3((unsigned)(rows * (a.H / 16)), 1, nlayers),
+                         dim3(64 * kWkWaves), 0, st, Ls,
                          a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2);
       return hipGetLastError();
     }
