@@ -195,10 +195,10 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
         "# unfused step), then the decode steps and the bench's timings of their parts, the per-layer",
         "# attention launches, then the KL objective (sparse and dense, with gradients).",
-        "# mla_attn_wk_kernel: bf16 rows, whole-row launches over more than 24576 keys (the prefill layer);",
-        "# mla_attn_kernel<f, w>: rows f = 0 bf16, 1 fp8, 2 MXFP4; w = 1 the three-workgroup schedule;",
+        "# mla_attn_wk_kernel<f, waves>: latent rows f = 0 bf16, 1 fp8, 2 MXFP4, four waves per row;",
         "# index_scores_kernel<H_I, d_I, paged, query tiles per wave>.  grid = threads of the launch",
-        "# (the 64-row decode: grouped 3-layer attention 98304, one layer 131072; decode indexer 393216)",
+        "# (the 64-row decode: grouped 3-layer attention 49152, one layer in 4 key splits 65536;",
+        "# decode indexer 393216)",
         "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel, grid",
         "",
     ]
@@ -435,7 +435,7 @@ def main():
     attn_flops = sel * w.H * 2 * (w.Dqk + w.Dv)
     logical = attn_bytes / (attn_ms * 1e-3) / 1e9
     traffic_all = read_traffic()
-    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel<4> grid={T * w.H // 16 * 256}")
+    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel<0, 4> grid={T * w.H // 16 * 256}")
     pl = probe()
     psum = torch.empty(T * 4, dtype=torch.int32, device=dev)
 

@@ -395,7 +395,9 @@ namespace {
 // the library's load until the process ends; host code addresses it only through the
 // pointer hipGetSymbolAddress returns for the current device (the array's name is a host
 // stand-in, not a device address).
-constexpr size_t kNoAllocScratchBytes = size_t(20) << 20;
+// The split planner keeps splits x workgroups within one round of 256, so the partials of
+// any shape fit: 256 x 16 (row, head) pairs x (512 + 2) floats = 8,421,376 bytes.
+constexpr size_t kNoAllocScratchBytes = size_t(256) * 16 * (512 + 2) * sizeof(float);
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 constexpr int kMaxDevices = 64;

@@ -4,22 +4,20 @@
 //
 // MLA form (DeepSeek-V2-Lite-Chat SIQ card, "Measured": one 576-wide latent row per token,
 // 512 compressed-KV values then 64 rotary values; V = the first 512 values of the same
-// row).  A workgroup serves one query row and 16 heads.  Per tile of 32 selected keys the
-// gathered rows are staged once in LDS and used twice: as K (all 576 columns) for
-// S^T = K Q^T with the keys as the MFMA M dimension, and as V (columns 0..511) for
-// O^T += V^T P^T, read transposed straight from LDS with ds_read_b64_tr_b16.  The 4 waves split
-// the keys of a tile for Q K^T and the 512 value columns for P V; softmax statistics are
-// exchanged through LDS (online softmax in base 2).  The next tile's gather is issued into
-// registers before the current tile is computed.  fp8 (OCP e4m3) rows are widened to bf16
+// row).  A workgroup of four waves serves one query row and 16 heads; each wave owns the
+// 16-key steps w, w + 4, ... of the row's index list with its own online softmax (base 2)
+// and O, and the waves' results are merged once per row.  A step's gathered rows are staged
+// in the wave's LDS and used twice: as K (all 576 columns) for S^T = K Q^T with the keys as
+// the MFMA M dimension, and as V (columns 0..511) for O^T += V^T P^T, read transposed
+// straight from LDS with ds_read_b64_tr_b16.  The next step's gather is issued into
+// registers before the current step is computed.  fp8 (OCP e4m3) rows are widened to bf16
 // exactly while staged; their per-token scale multiplies the logit and the probability.
 // MXFP4 rows (OCP microscaling: 32-value blocks of e2m1 elements sharing an E8M0 scale;
 // the same card's "Measured" section names an nvfp4 latent cache for sparse MLA) are
 // decoded with their block scales while staged, also exactly: e2m1 times a power of two
-// has two significant bits.
-// Launches of whole rows over long bf16 caches run mla_attn_wk_kernel instead: a wave per
-// 16-key step with its own softmax state and O, merged once per row (below).
-// Decode rows (few queries) split the key list over workgroups and merge the partial
-// results by log-sum-exp in a second kernel, in a fixed order.
+// has two significant bits.  Decode rows (few queries) split the key list over
+// workgroups and merge the partial results by log-sum-exp in a second kernel, in a fixed
+// order.
 //
 // Multi-head form (DSA ablation card: 4 heads of width 32, RoPE'd inputs): a workgroup per
 // query row, key rows read as 16-byte chunks spread over the lanes, logits in LDS, three
@@ -36,7 +34,6 @@ namespace {
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kTile = 32;                // selected keys per tile
 constexpr int kRowB = kDqk * 2;          // staged bf16 row: 1152 B = 72 chunks of 16 B
-constexpr int kQSteps = kDqk / 32 / 2;   // MFMA k-steps of Q K^T per wave (half of 18)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -49,9 +46,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 __device__ __forceinline__ int lds_off(int r, int chunk) { return r * kRowB + ((chunk ^ swz(r)) << 4); }
 
-// Gather of one tile: wave w fetches tile keys 8w..8w+7; lane l owns key 8w + l/8 and the
-// 16-byte parts l%8, l%8+8, ... of its row, so every load instruction reads eight full
-// 128-byte lines.  Rows go through registers into LDS (bf16; fp8 and fp4 widened exactly).
+// Gather of a key row: eight lanes per row, lane l owning the 16-byte parts l%8, l%8+8, ...,
+// so every load instruction reads eight full 128-byte lines.  Rows go through registers into LDS (bf16; fp8 and fp4 widened exactly).
 // Row offsets use a 24-bit multiply (rows < 2^24 here): a 64-bit multiply-add would read an
 // undefined high addend register and could force a wait on an unrelated load.  A missing
 // row (s < 0) is read at offsets from kRowNone, past every buffer range these kernels
@@ -172,13 +168,6 @@ struct TileStage<kKvMxfp4> {
   }
 };
 
-// Two schedules.  WIDE = 0: two row stages in registers, two LDS tile buffers, two
-// workgroups per CU.  WIDE = 1 (bf16 rows, no key split, at most kWideMaxTk keys): one
-// register stage and one LDS buffer, three workgroups per CU.  The tile body is a latency
-// chain and a third workgroup hides more of it; measured 4.7% faster at T=16384 and 1.5%
-// slower at T=32768 (the extra workgroups' rows then cost more in cache than they gain).
-constexpr int kWideMaxTk = 24576;
-
 // Per-layer operands of one launch: blockIdx.z picks the layer.  Layers that share one
 // index list (an 'F' layer and the 'S' layers after it) run in one launch, so a decode
 // step's short, latency-bound attention layers overlap instead of running back to back.
@@ -190,260 +179,8 @@ struct MlaLayers {
   float* lse[kMaxAttnLayers];
 };
 
-// tail_kv_len / tail_Tk (tail_Tk > 0): every row's valid entries are its first min(k, p+1),
-// p its position among sequences of tail_kv_len[b] (NULL: tail_Tk) keys, as the library's
-// own top-k writes them; a split launch then takes its tile count from p instead of
-// scanning the list for the last valid entry.
-template <int FMT, int WIDE>
-__global__ __launch_bounds__(256, WIDE ? 3 : 2) void mla_attn_kernel(const MlaLayers Ls,
-                                                          const int32_t* __restrict__ idx, int Tq, int Tk,
-                                                          int64_t kv_bstride, int H, int k, float scale_log2,
-                                                          int tiles_per_split, float* __restrict__ part_o,
-                                                          float* __restrict__ part_ml, int64_t part_layer,
-                                                          const int32_t* __restrict__ tail_kv_len, int tail_Tk) {
-  // layer z's operands; its split partials sit part_layer floats after layer z-1's
-  const int z = blockIdx.z;
-  const uint16_t* __restrict__ q = Ls.q[z];
-  const uint8_t* __restrict__ kv = Ls.kv[z];
-  const float* __restrict__ kv_scale = Ls.kv_scale[z];
-  uint16_t* __restrict__ out = Ls.out[z];
-  float* __restrict__ lse = Ls.lse[z];
-  part_o += z * part_layer;
-  part_ml += z * part_layer;
-  constexpr int NBUF = WIDE ? 1 : 2;  // LDS tile buffers
-  // row stages in registers (tiles in flight).  (Three stages for fp8 rows and four for
-  // MXFP4 rows gave the 64-row decode step no gain: its tiles wait on the tile body, not on
-  // the gather.)
-  constexpr int NST = WIDE ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[NBUF][kTile * kRowB];
-  __shared__ __attribute__((aligned(16))) f32x4 sbuf[4][64];           // partial S^T per wave and lane
-  __shared__ __attribute__((aligned(16))) float tile_bias[NBUF][kTile];   // 0 for a valid key, -inf otherwise
-  __shared__ __attribute__((aligned(16))) float tile_scale[NBUF][kTile];  // fp8 row scales
-  __shared__ int jmax_red[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int HG = H >> 4;
-  const int64_t rowh = blockIdx.x;  // (b*Tq + t)*HG + hg
-  const int64_t row = rowh / HG;
-  const int hg = (int)(rowh % HG);
-  const int b = (int)(row / Tq);
-  const int split = blockIdx.y, nsplit = gridDim.y;
-  const int32_t* ix = idx + row * k;
-  constexpr bool FP8 = FMT == kKvFp8;  // per-token scale on logits and probabilities
-  constexpr uint32_t kRowBytes = TileStage<FMT>::kRowBytes;
-  // sequence b's rows start kv_bstride rows after sequence b-1's (0: one shared pool)
-  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + b * kv_bstride * kRowBytes, (uint32_t)Tk * kRowBytes);
-
-  // This split's tiles.  Index entries are validated against its nominal range; the scan
-  // below only trims trailing tiles that hold no valid entry, so it can run while the first
-  // loads are in flight (it used to sit in front of them as one more memory round trip).
-  const int t_begin = split * tiles_per_split;
-  const int t_lim = min((k + kTile - 1) / kTile, t_begin + tiles_per_split);
-
-  // Lane roles.  hl = lane % 16 is this lane's head in S^T and O^T; gq = lane / 16 picks
-  // which 4 keys of each 16-key half it holds (keys 4gq..4gq+3 and 16+4gq..16+4gq+3).
-  // Wave roles in S^T = K Q^T: key half kh (tile keys 16kh..16kh+15), k-step half ksh.
-  const int hl = lane & 15, gq = lane >> 4;
-  const int kh = wave >> 1, ksh = wave & 1;
-  bf16x8 qb[kQSteps];  // Q^T as the B operand: column = head hl, 8 dims per k-step
-  {
-    const uint16_t* qp = q + (row * H + hg * 16 + hl) * kDqk + (ksh * kQSteps) * 32 + gq * 8;
-#pragma unroll
-    for (int s = 0; s < kQSteps; ++s) qb[s] = as_bf16x8(ld16(qp + s * 32));
-  }
-  // gather: this lane's key of the tile and its first 16-byte part
-  const int gk = 8 * wave + (lane >> 3), part0 = lane & 7;
-  const bool key_owner = (lane & 7) == 0;
-  // Index entries are fetched two tiles ahead of the rows they name, as unconditional
-  // buffer loads (past the list or past this split: the range check returns 0), and
-  // validated only when the row gather is issued: waiting on a load retires every older
-  // load too, so an index consumed right after its load would drain the row prefetch.
-  const __amdgpu_buffer_rsrc_t ix_rs = make_rsrc(ix, (uint32_t)k * 4);
-  const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(FP8 ? kv_scale + b * kv_bstride : nullptr, FP8 ? (uint32_t)Tk * 4 : 0u);
-  auto raw_entry = [&](int t) -> int {
-    const int j = t * kTile + gk;
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, t < t_lim ? j * 4 : (int)kOffNone, 0, 0);
-  };
-  auto valid_entry = [&](int t, int raw) -> int {  // key index of this lane's entry in tile t, or -1
-    const int lim = (t < t_lim && t * kTile + gk < k) ? Tk : 0;  // the raw value is always read
-    return (uint32_t)raw < (uint32_t)lim ? raw : -1;
-  };
-  auto fetch = [&](TileStage<FMT>& st, int s_idx) {  // issue the gather of one tile
-    st.s = s_idx;
-    st.load(kv_rs, part0);
-    if (FP8) st.sc = buf_load_f32(sc_rs, s_idx >= 0 ? (uint32_t)s_idx * 4 : kOffNone, 0);
-  };
-
-  // prologue: index entries of tiles t_begin .. t_begin + 2*NST - 1, rows of the first NST
-  // in flight
-  TileStage<FMT> st[NST];
-  int nx[NST];
-  {
-    int e[NST];
-#pragma unroll
-    for (int j = 0; j < NST; ++j) e[j] = raw_entry(t_begin + j);
-#pragma unroll
-    for (int j = 0; j < NST; ++j) nx[j] = raw_entry(t_begin + NST + j);
-#pragma unroll
-    for (int j = 0; j < NST; ++j) fetch(st[j], valid_entry(t_begin + j, e[j]));
-  }
-
-  // extent of this split's entries that are valid: the loop ends after its last tile.  A
-  // split launch (few rows) takes it from the row's position when the list is a top-k row
-  // (the scan is one more memory round trip in its prologue: 7 -> 3.6 us per workgroup on
-  // the 64-row decode step); a launch of whole rows scans, which also brings the row's
-  // index list into L2 ahead of the per-tile index loads (without the scan the T=65536
-  // layer took 16.1 ms against 15.5)
-  int t_end;
-  if (tail_Tk > 0 && nsplit > 1) {
-    const int64_t p = seq_len(tail_kv_len, b, tail_Tk) - Tq + (int)(row % Tq);
-    const int64_t nv = min((int64_t)k, p + 1);
-    t_end = min(t_lim, (int)((max(nv, (int64_t)0) + kTile - 1) / kTile));
-  } else {
-    int jm = -1;
-    for (int j = t_begin * kTile + tid; j < min(k, t_lim * kTile); j += 256) {
-      const int sj = ix[j];
-      if (sj >= 0 && sj < Tk) jm = j;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) jm = max(jm, __shfl_xor(jm, o, 64));
-    if (lane == 0) jmax_red[wave] = jm;
-    __syncthreads();
-    jm = max(max(jmax_red[0], jmax_red[1]), max(jmax_red[2], jmax_red[3]));
-    t_end = min((jm + kTile) / kTile, t_lim);  // tiles covering entries 0..jm
-  }
-
-  f32x4 o_acc[8];  // O^T: rows = dims wave*128 + n*16 + 4gq + i, column = head hl
-#pragma unroll
-  for (int n = 0; n < 8; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  auto tile = [&](int t, TileStage<FMT>& st, int& nx) {  // nx: raw index entry of tile t+NST
-    const int buf = NBUF == 2 ? (t - t_begin) & 1 : 0;
-    uint8_t* kvb = kvs[buf];
-    if constexpr (NBUF == 1) __syncthreads();  // every wave is done with the previous tile
-    st.store(kvb, gk, part0);
-    if (key_owner) {
-      tile_bias[buf][gk] = st.s >= 0 ? 0.f : -INFINITY;
-      if (FP8) tile_scale[buf][gk] = st.sc;
-    }
-    __syncthreads();  // tile t staged (the other buffer may still be read by PV of t-1)
-    // refill this stage with tile t+NST; its index entry arrived with tile t's rows
-    {
-      const int s2 = valid_entry(t + NST, nx);
-      nx = raw_entry(t + 2 * NST);
-      fetch(st, s2);
-    }
-
-    // ---- partial S^T = K Q^T over this wave's k-steps, keys 16kh .. 16kh+15
-    {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const int krow = 16 * kh + hl;
-#pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        const int chunk = (ksh * kQSteps + s) * 4 + gq;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kvb + lds_off(krow, chunk)));
-        sacc = mfma16(ka, qb[s], sacc);
-      }
-      sbuf[wave][lane] = sacc;
-    }
-    __syncthreads();  // partial sums visible
-
-    // ---- logits of the lane's 8 keys for head hl, online softmax in base 2
-    // (the lane's keys 16h+4gq .. +3 are contiguous: one 16-byte LDS read per half)
-    float sv[8], ksc[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 pa = sbuf[2 * h][lane], pb2 = sbuf[2 * h + 1][lane];
-      const f32x4 bias = *reinterpret_cast<const f32x4*>(&tile_bias[buf][16 * h + 4 * gq]);
-      f32x4 kscv = {1.f, 1.f, 1.f, 1.f};
-      if (FP8) kscv = *reinterpret_cast<const f32x4*>(&tile_scale[buf][16 * h + 4 * gq]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ksc[4 * h + i] = kscv[i];
-        const float sfull = pa[i] + pb2[i];
-        sv[4 * h + i] = __builtin_fmaf(sfull, FP8 ? kscv[i] * scale_log2 : scale_log2, bias[i]);  // -inf if masked
-      }
-    }
-    float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    tm = rows_max(tm);
-    const float mn = fmaxf(m_run, tm);
-    // exp2(-inf) = 0 covers masked keys and a first valid tile; only a head with no valid
-    // key yet (mn = -inf) needs a finite reference to avoid -inf - -inf
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m_run - mref);
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sv[e] - mref);
-    const float ts = rows_sum(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
-    l_run = l_run * alpha + ts;
-    m_run = mn;
-    // P^T as the B operand: k-slot e of group gq <-> key 4gq+e (e<4), 16+4gq+(e-4) (e>=4);
-    // probabilities carry the fp8 row scale for V
-    u32x4 pw;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      pw[e] = FP8 ? cvt_bf16x2(pv[2 * e] * ksc[2 * e], pv[2 * e + 1] * ksc[2 * e + 1]) : cvt_bf16x2(pv[2 * e], pv[2 * e + 1]);
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-    if (__ballot(alpha != 1.f)) {  // rescale only when some head's running max moved
-#pragma unroll
-      for (int n = 0; n < 8; ++n) o_acc[n] *= alpha;
-    }
-
-    // ---- O^T[dims wave*128 .. +128] += V^T P^T  (V read transposed from the staged rows)
-    {
-      const int r0 = 4 * gq + (hl >> 2);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int dim = wave * 128 + n * 16 + 4 * (hl & 3);  // 4 dims = 8 bytes
-        const int chunk = dim >> 3, half = (dim & 7) * 2;
-        const i16x4 v0 = lds_read_tr16(kvb + lds_off(r0, chunk) + half);
-        const i16x4 v1 = lds_read_tr16(kvb + lds_off(r0 + 16, chunk) + half);
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o_acc[n] = mfma16(__builtin_bit_cast(bf16x8, vv), pb, o_acc[n]);
-      }
-    }
-  };
-
-  {
-    int t = t_begin;
-    for (; t + NST - 1 < t_end; t += NST) {
-#pragma unroll
-      for (int j = 0; j < NST; ++j) tile(t + j, st[j], nx[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NST - 1; ++j)
-      if (t + j < t_end) tile(t + j, st[j], nx[j]);
-  }
-
-  // ---- results: lane holds O[head hl][wave*128 + n*16 + 4gq + i]
-  const int h = hg * 16 + hl;
-  if (nsplit == 1) {
-    const float inv = l_run == 0.f ? 0.f : 1.f / l_run;  // (a NaN sum stays NaN)
-    uint16_t* op = out + (row * H + h) * kDv + wave * 128 + 4 * gq;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint32_t lo = cvt_bf16x2(o_acc[n][0] * inv, o_acc[n][1] * inv);
-      const uint32_t hi = cvt_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
-      *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
-    }
-    if (lse && wave == 0 && gq == 0) lse[row * H + h] = l_run == 0.f ? -INFINITY : (m_run + __log2f(l_run)) * kLn2;
-  } else {
-    const int64_t nrowh = (int64_t)gridDim.x * 16;  // (row, head) pairs over all rows
-    const int64_t rh = rowh * 16 + hl;
-    float* po = part_o + ((int64_t)split * nrowh + rh) * kDv + wave * 128 + 4 * gq;
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-      *reinterpret_cast<float4*>(po + n * 16) = make_float4(o_acc[n][0], o_acc[n][1], o_acc[n][2], o_acc[n][3]);
-    if (wave == 0 && gq == 0) {
-      part_ml[((int64_t)split * nrowh + rh) * 2 + 0] = m_run;
-      part_ml[((int64_t)split * nrowh + rh) * 2 + 1] = l_run;
-    }
-  }
-}
-
-// ---- one wave per key step: bf16 rows, launches of whole rows ---------------------------
+// ---- the MLA kernel: one wave per key step ------------------------------------------------
 // A workgroup of kWkWaves waves serves one query row and 16 heads.  Wave w takes the 16-key
 // steps w, w + NW, w + 2 NW, ... of the row's index list (entries 16 (NW i + w) .. +15) and
 // keeps its own online-softmax state and O for all 16 heads and 512 dims, so the key loop has
@@ -475,19 +212,26 @@ __device__ __forceinline__ f32x4 mfma16k16(i16x4 a, i16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-template <int NW>  // waves per workgroup (query row)
-__global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_kernel(const MlaLayers Ls, const int32_t* __restrict__ idx,
-                                                             int Tq, int Tk, int64_t kv_bstride, int H, int k,
-                                                             float scale_log2, const int32_t* __restrict__ tail_kv_len,
-                                                             int tail_Tk) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[NW][2][kWkSlot];  // [wave][slot]
-  __shared__ float ml_red[NW][16][2];
+template <int FMT, int NW>  // row format; waves per workgroup (query row)
+__global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_kernel(
+    const MlaLayers Ls, const int32_t* __restrict__ idx, int Tq, int Tk, int64_t kv_bstride, int H, int k,
+    float scale_log2, int tiles_per_split, float* __restrict__ part_o, float* __restrict__ part_ml, int64_t part_layer,
+    const int32_t* __restrict__ tail_kv_len, int tail_Tk) {
+  constexpr bool FP8 = FMT == kKvFp8;  // per-token scale on logits and probabilities
+  constexpr uint32_t kRowBytes = TileStage<FMT>::kRowBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[NW][2][kWkSlot];  // [wave][slot]: bf16 rows once staged
+  __shared__ __attribute__((aligned(16))) float kscale[NW][2][kWkKeys];  // fp8 row scales of each slot
+  __shared__ float ml_red[NW][16][3];
 
+  // layer z's operands; its split partials sit part_layer floats after layer z-1's
   const int z = blockIdx.z;
   const uint16_t* __restrict__ q = Ls.q[z];
   const uint8_t* __restrict__ kv = Ls.kv[z];
+  const float* __restrict__ kv_scale = Ls.kv_scale[z];
   uint16_t* __restrict__ out = Ls.out[z];
   float* __restrict__ lse = Ls.lse[z];
+  part_o += z * part_layer;
+  part_ml += z * part_layer;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int HG = H >> 4;
@@ -495,8 +239,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
   const int64_t row = rowh / HG;
   const int hg = (int)(rowh % HG);
   const int b = (int)(row / Tq);
+  const int split = blockIdx.y, nsplit = gridDim.y;
   const int32_t* ix = idx + row * k;
-  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + b * kv_bstride * kRowB, (uint32_t)Tk * kRowB);
+  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kv + b * kv_bstride * kRowBytes, (uint32_t)Tk * kRowBytes);
+  const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(FP8 ? kv_scale + b * kv_bstride : nullptr, FP8 ? (uint32_t)Tk * 4 : 0u);
   const __amdgpu_buffer_rsrc_t ix_rs = make_rsrc(ix, (uint32_t)k * 4);
 
   // lane roles: hl = head (S^T and O^T column), gq = which 4 keys of a step (rows 4gq..)
@@ -512,63 +258,71 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
     for (int s = 0; s < 18; ++s) asm volatile("" : "+a"(qb[s]));
   }
 
-  // entries past the row's valid ones add nothing (they read no row and their logits are
-  // -inf), so the loop runs over all k entries unless the list is a top-k row, whose valid
-  // entries are its first min(k, p+1): then the extent follows from the position.  (A scan
-  // of the list for its last valid entry, with a barrier, cost 9% at T=65536: 13.5 against
-  // 12.3 ms.)
-  int nblk = (k + kWkKeys - 1) / kWkKeys;
+  // This split's entries [e_lo, e_hi).  Entries past a row's valid ones add nothing (they
+  // read no row and their logits are -inf), so the loop covers the split's whole range
+  // unless the list is a top-k row, whose valid entries are its first min(k, p+1): then the
+  // range ends there.  (A scan of the list for its last valid entry, with a barrier, cost 9%
+  // at T=65536: 13.5 against 12.3 ms.)
+  const int e_lo = split * tiles_per_split * kTile;
+  int e_hi = min(k, e_lo + tiles_per_split * kTile);
   if (tail_Tk > 0) {
     const int64_t p = seq_len(tail_kv_len, b, tail_Tk) - Tq + (int)(row % Tq);
-    const int64_t nv = min((int64_t)k, p + 1);
-    nblk = (int)((max(nv, (int64_t)0) + kWkKeys - 1) / kWkKeys);
+    e_hi = (int)min<int64_t>(e_hi, max<int64_t>(0, min<int64_t>(k, p + 1)));
   }
+  const int nblk = e_hi > e_lo ? (e_hi - e_lo + kWkKeys - 1) / kWkKeys : 0;
   const int nsteps = (nblk - wave + NW - 1) / NW;  // this wave's blocks: wave, wave + NW, ... < nblk
 
   // gather roles: lane l loads the rows of keys l/8 and 8 + l/8 of a step, 16-byte parts
   // l%8 + 8c (eight lanes per row: every load instruction reads eight full 128-byte lines)
   const int gkey = lane >> 3, part0 = lane & 7;
-  auto entry_off = [&](int i, int g) -> int { return (NW * i + wave) * kWkKeys + gkey + 8 * g; };
+  auto entry_off = [&](int i, int g) -> int { return e_lo + (NW * i + wave) * kWkKeys + gkey + 8 * g; };
   auto raw_entry = [&](int i, int g) -> int {
     return (int)__builtin_amdgcn_raw_buffer_load_b32(ix_rs, i < nsteps ? entry_off(i, g) * 4 : (int)kOffNone, 0, 0);
   };
   auto valid_entry = [&](int i, int g, int raw) -> int {
-    const int lim = (i < nsteps && entry_off(i, g) < k) ? Tk : 0;
+    const int lim = (i < nsteps && entry_off(i, g) < e_hi) ? Tk : 0;
     return (uint32_t)raw < (uint32_t)lim ? raw : -1;
   };
-  u32x4 rr[1][2][9];  // the register stage: [row role][part]
-  uint32_t rmask[1];   // its valid keys (bit r: key r of the step)
-  auto gather = [&](u32x4 (&r)[2][9], uint32_t& msk, int i, int e0, int e1) __attribute__((always_inline)) {
-    const int s0 = valid_entry(i, 0, e0), s1 = valid_entry(i, 1, e1);
-    const uint32_t b0 = (s0 >= 0 ? __umul24((uint32_t)s0, (uint32_t)kRowB) : kRowNone) + part0 * 16;
-    const uint32_t b1 = (s1 >= 0 ? __umul24((uint32_t)s1, (uint32_t)kRowB) : kRowNone) + part0 * 16;
+  TileStage<FMT> st[2];  // the register stage: rows gkey and gkey + 8 of one step
+  uint32_t rmask = 0;    // its valid keys (bit r: key r of the step)
+  auto gather = [&](int i, int e0, int e1) __attribute__((always_inline)) {
+    st[0].s = valid_entry(i, 0, e0);
+    st[1].s = valid_entry(i, 1, e1);
 #pragma unroll
-    for (int c = 0; c < 9; ++c) {
-      r[0][c] = buf_load_16(kv_rs, b0 + 128 * c, 0);
-      r[1][c] = buf_load_16(kv_rs, b1 + 128 * c, 0);
+    for (int g = 0; g < 2; ++g) {
+      st[g].load(kv_rs, part0);
+      if (FP8) st[g].sc = buf_load_f32(sc_rs, st[g].s >= 0 ? (uint32_t)st[g].s * 4 : kOffNone, 0);
     }
     // lanes 8r hold keys r and 8 + r
-    const uint64_t v0 = __ballot(s0 >= 0), v1 = __ballot(s1 >= 0);
+    const uint64_t v0 = __ballot(st[0].s >= 0), v1 = __ballot(st[1].s >= 0);
     uint32_t m = 0;
 #pragma unroll
     for (int r2 = 0; r2 < 8; ++r2)
       m |= (uint32_t)((v0 >> (8 * r2)) & 1u) << r2 | (uint32_t)((v1 >> (8 * r2)) & 1u) << (8 + r2);
-    msk = m;
+    rmask = m;
   };
-  auto stage = [&](const u32x4 (&r)[2][9], uint8_t* slot) __attribute__((always_inline)) {
+  auto stage = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int c = 0; c < 9; ++c) *reinterpret_cast<u32x4*>(slot + lds_off(gkey + 8 * g, part0 + 8 * c)) = r[g][c];
+    for (int g = 0; g < 2; ++g) st[g].store(kvs[wave][slot], gkey + 8 * g, part0);
+    if (FP8 && part0 == 0) {
+      kscale[wave][slot][gkey] = st[0].sc;
+      kscale[wave][slot][gkey + 8] = st[1].sc;
+    }
   };
 
   f32x4 o_acc[32];  // O^T: rows = dims 16n + 4gq + i, column = head hl
 #pragma unroll
   for (int n = 0; n < 32; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_run: the head's reference (uniform over its lanes); l_run and l_rnd: this lane's share
+  // of the sum of exponentials, exact and as rounded into the P V operand (bf16 and MXFP4
+  // rows normalize by the rounded sum, so the weights of O sum to one exactly; the exact
+  // sum gives lse).  Both are reduced over the head's lanes once, after the loop.
+  float m_run = -INFINITY, l_run = 0.f, l_rnd = 0.f;
 
-  // base-2 logits of the lane's 4 keys for head hl (-inf for a missing key)
-  auto qk = [&](const uint8_t* sl, uint32_t msk, float (&sv)[4]) __attribute__((always_inline)) {
+  // base-2 logits of the lane's 4 keys for head hl (-inf for a missing key); ksc: the keys'
+  // fp8 scales (1 otherwise)
+  auto qk = [&](int slot, uint32_t msk, float (&sv)[4], float (&ksc)[4]) __attribute__((always_inline)) {
+    const uint8_t* sl = kvs[wave][slot];
     // two accumulation chains (even and odd k-steps), added at the end
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     u32x4 kr[18];  // every K operand read first, so the reads overlap
@@ -588,12 +342,18 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    f32x4 kscv = {1.f, 1.f, 1.f, 1.f};
+    if (FP8) kscv = *reinterpret_cast<const f32x4*>(&kscale[wave][slot][4 * gq]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[e] = ((msk >> (4 * gq + e)) & 1u) ? (a0[e] + a1[e]) * scale_log2 : -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      ksc[e] = kscv[e];
+      sv[e] = ((msk >> (4 * gq + e)) & 1u) ? (a0[e] + a1[e]) * (FP8 ? kscv[e] * scale_log2 : scale_log2) : -INFINITY;
+    }
   };
   bool redo = false;
-  // online softmax of one step's logits: P^T as the B operand of P V
-  auto softmax = [&](const float (&sv)[4]) __attribute__((always_inline)) -> i16x4 {
+  // online softmax of one step's logits: P^T as the B operand of P V (probabilities carry
+  // the fp8 row scale for V; the sum does not)
+  auto softmax = [&](const float (&sv)[4], const float (&ksc)[4]) __attribute__((always_inline)) -> i16x4 {
     const float tm = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     if (m_run == -INFINITY)
       m_run = tm;  // the head's first valid keys (O and l are still 0); stays -inf otherwise
@@ -603,11 +363,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
     float p[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sv[e] - mref);
-    l_run += rows_sum((p[0] + p[1]) + (p[2] + p[3]));
-    return __builtin_bit_cast(i16x4, make_uint2(cvt_bf16x2(p[0], p[1]), cvt_bf16x2(p[2], p[3])));
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    if (FP8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] *= ksc[e];
+    }
+    const uint32_t w0 = cvt_bf16x2(p[0], p[1]), w1 = cvt_bf16x2(p[2], p[3]);
+    if (!FP8)
+      l_rnd += (__uint_as_float(w0 << 16) + __uint_as_float(w0 & 0xffff0000u)) +
+               (__uint_as_float(w1 << 16) + __uint_as_float(w1 & 0xffff0000u));
+    return __builtin_bit_cast(i16x4, make_uint2(w0, w1));
   };
   // O^T += V^T P^T: lane (gq, hl) reads keys 4gq .. 4gq+3 at dim 16n + hl (transposed)
-  auto pv = [&](const uint8_t* sl, i16x4 pb) __attribute__((always_inline)) {
+  auto pv = [&](int slot, i16x4 pb) __attribute__((always_inline)) {
+    const uint8_t* sl = kvs[wave][slot];
     const int r0 = 4 * gq + (hl >> 2);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {  // sixteen operand reads, then their MFMAs
@@ -628,10 +397,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
       __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     }
   };
-  auto compute = [&](const uint8_t* sl, uint32_t msk) __attribute__((always_inline)) {
-    float sv[4];
-    qk(sl, msk, sv);
-    pv(sl, softmax(sv));
+  auto compute = [&](int slot, uint32_t msk) __attribute__((always_inline)) {
+    float sv[4], ksc[4];
+    qk(slot, msk, sv, ksc);
+    pv(slot, softmax(sv, ksc));
   };
 
   for (int attempt = 0;; ++attempt) {
@@ -640,14 +409,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
       // alone, one step at a time), then the row again from it
       float mt = -INFINITY;
       for (int i = 0; i < nsteps; ++i) {
-        gather(rr[0], rmask[0], i, raw_entry(i, 0), raw_entry(i, 1));
-        stage(rr[0], kvs[wave][0]);
-        float sv[4];
-        qk(kvs[wave][0], rmask[0], sv);
+        gather(i, raw_entry(i, 0), raw_entry(i, 1));
+        stage(0);
+        float sv[4], ksc[4];
+        qk(0, rmask, sv, ksc);
         mt = fmaxf(mt, rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
       }
       m_run = mt;
       l_run = 0.f;
+      l_rnd = 0.f;
 #pragma unroll
       for (int n = 0; n < 32; ++n) o_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -661,20 +431,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
       const int e10 = raw_entry(1, 0), e11 = raw_entry(1, 1);
       en0 = raw_entry(2, 0);
       en1 = raw_entry(2, 1);
-      gather(rr[0], rmask[0], 0, e00, e01);
-      stage(rr[0], kvs[wave][0]);
-      mask_slot[0] = rmask[0];
-      gather(rr[0], rmask[0], 1, e10, e11);
+      gather(0, e00, e01);
+      stage(0);
+      mask_slot[0] = rmask;
+      gather(1, e10, e11);
     }
     auto iter = [&](auto par_c, int i) __attribute__((always_inline)) {
       constexpr int P = decltype(par_c)::value;
-      stage(rr[0], kvs[wave][1 - P]);
-      mask_slot[1 - P] = rmask[0];
+      stage(1 - P);
+      mask_slot[1 - P] = rmask;
       __builtin_amdgcn_sched_barrier(0);  // the stage's registers are free before the next gather
-      gather(rr[0], rmask[0], i + 2, en0, en1);
+      gather(i + 2, en0, en1);
       en0 = raw_entry(i + 3, 0);
       en1 = raw_entry(i + 3, 1);
-      compute(kvs[wave][P], mask_slot[P]);
+      compute(P, mask_slot[P]);
     };
     {
       int i = 0;
@@ -687,56 +457,78 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
     if (!__syncthreads_or(redo) || attempt == 1) break;  // (the second pass never flags)
   }
 
+  // ---- results: merge the waves ((m, l) per head, then O over the waves in wave order),
+  // then the normalized output, or this split's partial (O relative to m, and (m, l))
   const int h = hg * 16 + hl;
-  uint16_t* op = out + (row * H + h) * kDv + 4 * gq;
-  if constexpr (NW == 1) {
-    const float mxr = m_run == -INFINITY ? 0.f : m_run;
-    const float inv = l_run == 0.f ? 0.f : 1.f / l_run;  // (a NaN sum stays NaN)
-#pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      const uint32_t lo = cvt_bf16x2(o_acc[n][0] * inv, o_acc[n][1] * inv);
-      const uint32_t hi = cvt_bf16x2(o_acc[n][2] * inv, o_acc[n][3] * inv);
-      *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
-    }
-    if (lse && gq == 0) lse[row * H + h] = l_run == 0.f ? -INFINITY : (mxr + __log2f(l_run)) * kLn2;
-  } else {
-    // ---- merge the waves: (m, l) per head, then O over the waves in wave order
+  l_run = rows_sum(l_run);
+  l_rnd = FP8 ? l_run : rows_sum(l_rnd);
+  float mx = m_run, lt = l_run, lr = l_rnd;
+  if constexpr (NW > 1) {
     __syncthreads();  // every wave is done with its slots
     if (gq == 0) {
       ml_red[wave][hl][0] = m_run;
       ml_red[wave][hl][1] = l_run;
+      ml_red[wave][hl][2] = l_rnd;
     }
     __syncthreads();
-    float mx = -INFINITY;
+    mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, ml_red[w][hl][0]);
-    const float mxr = mx == -INFINITY ? 0.f : mx;
-    float lt = 0.f, mine = 0.f;
+    const float mxr0 = mx == -INFINITY ? 0.f : mx;
+    float mine = 0.f;
+    lt = 0.f;
+    lr = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(ml_red[w][hl][0] - mxr);
+      const float f = fast_exp2(ml_red[w][hl][0] - mxr0);
       lt += ml_red[w][hl][1] * f;
+      lr += ml_red[w][hl][2] * f;
       mine = w == wave ? f : mine;
     }
-    {
-      f32x4* ob = reinterpret_cast<f32x4*>(&kvs[wave][0][0]);  // 32 KB of this wave's region
+    f32x4* ob = reinterpret_cast<f32x4*>(&kvs[wave][0][0]);  // 32 KB of this wave's region
 #pragma unroll
-      for (int n = 0; n < 32; ++n) ob[n * 64 + lane] = o_acc[n] * mine;
-    }
+    for (int n = 0; n < 32; ++n) ob[n * 64 + lane] = o_acc[n] * mine;
     __syncthreads();
-    const float inv = lt == 0.f ? 0.f : 1.f / lt;  // (a NaN sum stays NaN)
-    constexpr int NT = 32 / NW;  // dim tiles each wave writes
-#pragma unroll
-    for (int nn = 0; nn < NT; ++nn) {
-      const int n = wave * NT + nn;
+  }
+  const float mxr = mx == -INFINITY ? 0.f : mx;
+  constexpr int NT = 32 / NW;  // dim tiles each wave writes
+  auto o_tile = [&](int n) -> f32x4 {
+    if constexpr (NW == 1) {
+      return o_acc[n];
+    } else {
       f32x4 x = reinterpret_cast<const f32x4*>(&kvs[0][0][0])[n * 64 + lane];
 #pragma unroll
       for (int w = 1; w < NW; ++w) x += reinterpret_cast<const f32x4*>(&kvs[w][0][0])[n * 64 + lane];
+      return x;
+    }
+  };
+  if (nsplit == 1) {
+    const float inv = lr == 0.f ? 0.f : 1.f / lr;  // (a NaN sum stays NaN)
+    uint16_t* op = out + (row * H + h) * kDv + 4 * gq;
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+      const int n = wave * NT + nn;
+      const f32x4 x = o_tile(n);
       const uint32_t lo = cvt_bf16x2(x[0] * inv, x[1] * inv);
       const uint32_t hi = cvt_bf16x2(x[2] * inv, x[3] * inv);
       *reinterpret_cast<uint2*>(op + n * 16) = make_uint2(lo, hi);
     }
     if (lse && wave == 0 && gq == 0) lse[row * H + h] = lt == 0.f ? -INFINITY : (mxr + __log2f(lt)) * kLn2;
+  } else {
+    const int64_t nrowh = (int64_t)gridDim.x * 16;  // (row, head) pairs over all rows
+    const int64_t rh = rowh * 16 + hl;
+    float* po = part_o + ((int64_t)split * nrowh + rh) * kDv + 4 * gq;
+    // the partial carries the exact sum: O rescaled to it from the rounded one
+    const float corr = lr == 0.f ? 1.f : lt / lr;
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+      const int n = wave * NT + nn;
+      *reinterpret_cast<f32x4*>(po + n * 16) = o_tile(n) * corr;
+    }
+    if (wave == 0 && gq == 0) {
+      part_ml[((int64_t)split * nrowh + rh) * 2 + 0] = mx;
+      part_ml[((int64_t)split * nrowh + rh) * 2 + 1] = lt;
+    }
   }
 }
 
@@ -945,21 +737,18 @@ bool attn_mha_supported(const AttnArgs& a) {
 }
 
 int attn_mla_splits(int B, int Tq, int H, int k, int nlayers) {
-  // few rows (decode): split each row's key list so that up to 512 workgroups (two per CU,
-  // what the chip holds at once) run in one round.  (A launch of three 64-row layers at
-  // four splits, 768 workgroups, ran in two rounds: 65 us, the second round starting after
-  // 31-39 us.)
-  const int64_t wgs = (int64_t)B * Tq * (H / 16);
+  // few rows (decode): split each row's key list so that one round of whole-key workgroups
+  // (one per CU) covers the launch, every layer of a grouped launch alike: a lone 64-row
+  // layer takes four splits (256 workgroups), three grouped 64-row layers none (192, and no
+  // merge).  A power of two: even splits of a power-of-two tile count.
+  const int64_t wgs = (int64_t)B * Tq * (H / 16) * std::max(1, nlayers);
   const int tiles = (k + kTile - 1) / kTile;
   if (wgs >= 256) return 1;
-  const int64_t target = 512 / std::max(1, nlayers);
   // (at most 64: the merge holds one split per lane)
-  int s = (int)std::min<int64_t>(std::min(tiles, 64), (target + wgs - 1) / std::max<int64_t>(1, wgs));
-  if (nlayers > 1) {  // a power of two (even splits of a power-of-two tile count) within the round
-    int p = 1;
-    while (2 * p <= s) p *= 2;
-    s = p;
-  }
+  int s = (int)std::min<int64_t>(std::min(tiles, 64), 256 / std::max<int64_t>(1, wgs));
+  int p = 1;
+  while (2 * p <= s) p *= 2;
+  s = p;
   if (s <= 1) return 1;
   const int per = (tiles + s - 1) / s;
   return (tiles + per - 1) / per;
@@ -1012,25 +801,18 @@ hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers,
     }
     dim3 grid((unsigned)(rows * (a.H / 16)), nsplit, nlayers);
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
-    const bool wide = a.kv_fmt == kKvBf16 && nsplit == 1 && a.Tk <= kWideMaxTk;
-    if (a.kv_fmt == kKvBf16 && nsplit == 1 && !wide) {  // long whole-row launches: one wave per key step
-      hipLaunchKernelGGL(mla_attn_wk_kernel<kWkWaves>, dim3((unsigned)(rows * (a.H / 16)), 1, nlayers),
-                         dim3(64 * kWkWaves), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2,
-                         a.tail_kv_len, a.tail_Tk);
-      return hipGetLastError();
+    {
+#define DSA_WK_LAUNCH(F)                                                                                             \
+  hipLaunchKernelGGL((mla_attn_wk_kernel<F, kWkWaves>), grid, dim3(64 * kWkWaves), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, \
+                     a.H, a.k, sl2, per, part_o, part_ml, part_layer, a.tail_kv_len, a.tail_Tk)
+      if (a.kv_fmt == kKvFp8)
+        DSA_WK_LAUNCH(kKvFp8);
+      else if (a.kv_fmt == kKvMxfp4)
+        DSA_WK_LAUNCH(kKvMxfp4);
+      else
+        DSA_WK_LAUNCH(kKvBf16);
+#undef DSA_WK_LAUNCH
     }
-#define DSA_MLA_LAUNCH(F, W)                                                                                       \
-  hipLaunchKernelGGL((mla_attn_kernel<F, W>), grid, dim3(256), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, a.H, a.k, sl2, \
-                     per, part_o, part_ml, part_layer, a.tail_kv_len, a.tail_Tk)
-    if (a.kv_fmt == kKvFp8)
-      DSA_MLA_LAUNCH(kKvFp8, 0);
-    else if (a.kv_fmt == kKvMxfp4)
-      DSA_MLA_LAUNCH(kKvMxfp4, 0);
-    else if (wide)
-      DSA_MLA_LAUNCH(kKvBf16, 1);
-    else
-      DSA_MLA_LAUNCH(kKvBf16, 0);
-#undef DSA_MLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((nrowh + 3) / 4), nlayers), dim3(256), 0, st, part_o,

@@ -279,9 +279,11 @@ dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float
  * shapes need go to a scratch area built into the library, one per device, held from the
  * library's load until the process ends; the call itself never allocates.  The shapes that
  * need no workspace (dsa_workspace_size(shape, DSA_OP_ATTN) == 0) use none.
- *   Limit: dsa_noalloc_scratch_bytes() bytes (20 MiB) of partial results, i.e. the
- *   workspace dsa_sparse_attn would take for the shape (16.8 MB for 64 decode rows of 16
- *   heads at k = 2048); larger shapes return DSA_ERR_UNSUPPORTED with nothing enqueued.
+ *   Limit: dsa_noalloc_scratch_bytes() bytes (8.4 MB) of partial results, i.e. the
+ *   workspace dsa_sparse_attn would take for the shape; the library splits keys so that
+ *   splits x (row, 16-head group) pairs stay within 256, which keeps every shape's partials
+ *   within that size (8.4 MB for 64 decode rows of 16 heads at k = 2048).  A larger need
+ *   would return DSA_ERR_UNSUPPORTED with nothing enqueued.
  *   Every call on one device shares that device's scratch and overwrites it: calls whose
  *   work overlaps on one device (different streams, or host threads without ordering)
  *   race and give undefined outputs.  Calls ordered on one stream are safe.
