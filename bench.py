@@ -566,14 +566,16 @@ def main():
 
         sel_us = 1e3 * timed(sel_batch) / nrep
         dscores = dsa.index_scores(L0["q_idx"], kc, L0["w_idx"], kv_len=klen)
+        tshp = dsa._shape(e.B, 1, e.T, 1, 1, 1, 1, e.k, 1.0, dsa.KV_BF16)
+        tws = torch.empty(max(1, dsa.workspace_size(tshp, dsa.OP_TOPK)), dtype=torch.uint8, device=dev)
 
         def topk_batch():
             for _ in range(nrep):
-                dsa.topk(dscores, e.k, kv_len=klen, idx=sidx)
+                dsa.topk(dscores, e.k, kv_len=klen, idx=sidx, ws=tws)
 
         topk_us = 1e3 * timed(topk_batch) / nrep
         same_sel = bool(torch.equal(sidx, dcache))
-        del dscores, sws
+        del dscores, sws, tws
 
         def attn3_batch():
             for _ in range(nrep):

@@ -146,13 +146,17 @@ def index_scores(q_idx, k_idx, w_idx, kv_len=None, scores=None, ld=None, stream=
     return scores
 
 
-def topk(scores, k, Tk=None, kv_len=None, idx=None, stream=None):
-    """dsa_topk: int32 [B, Tq, k] ascending, -1 padded."""
+def topk(scores, k, Tk=None, kv_len=None, idx=None, ws=None, split=True, stream=None):
+    """dsa_topk: int32 [B, Tq, k] ascending, -1 padded.  split=False passes no workspace
+    (one workgroup per row); the indices are the same either way."""
     B, Tq, ld = scores.shape
     Tk = ld if Tk is None else Tk
     if idx is None:
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=scores.device)
-    _check(lib().dsa_topk(_ptr(scores), ld, _ptr(kv_len), B, Tq, Tk, k, _ptr(idx), None, 0, _stream(stream)))
+    nbytes = workspace_size(_shape(B, Tq, Tk, 1, 1, 1, 1, k, 1.0, KV_BF16), OP_TOPK) if split else 0
+    ws = _workspace(nbytes, scores.device, ws) if nbytes else None
+    _check(lib().dsa_topk(_ptr(scores), ld, _ptr(kv_len), B, Tq, Tk, k, _ptr(idx), _ptr(ws), nbytes,
+                          _stream(stream)))
     return idx
 
 

@@ -55,6 +55,7 @@ struct IndexTopkPlan {
   bool fused;
   int rows;     // query rows per chunk
   size_t ws;    // workspace bytes
+  size_t split_off = 0;  // score route: segment lists of the split top-k (few long rows), if any
 };
 
 IndexTopkPlan plan_index_topk(const dsa_shape& s, bool force_unfused) {
@@ -72,6 +73,11 @@ IndexTopkPlan plan_index_topk(const dsa_shape& s, bool force_unfused) {
   } else {
     P.rows = chunk_rows(s);
     P.ws = (size_t)std::max(0, s.B) * P.rows * stack_ld(s.Tk) * sizeof(float);
+    const size_t lists = dsa::topk_split_workspace_bytes(s.B, P.rows, s.Tk, s.k);
+    if (lists) {
+      P.split_off = align_up(P.ws);
+      P.ws = P.split_off + lists;
+    }
   }
   return P;
 }
@@ -103,7 +109,8 @@ dsa_status run_index_topk(const IndexTopkPlan& P, const void* q_idx, const void*
         if (st != DSA_OK) return st;
       }
       // (no keys at all: every row selects nothing, and top-k reads no score)
-      dsa::TopkArgs ta{scores, ld, (int64_t)P.rows * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, idx};
+      dsa::TopkArgs ta{scores, ld, (int64_t)P.rows * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, idx,
+                       P.split_off ? reinterpret_cast<char*>(ws) + P.split_off : nullptr};
       dsa_status st = launch_status(dsa::launch_topk(ta, strm), who);
       if (st != DSA_OK) return st;
     }
@@ -253,11 +260,14 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_
 
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk, int k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   dsa_status st = check_topk(scores, ld, B, Tq, Tk, k, idx);
   if (st != DSA_OK || (int64_t)B * Tq == 0) return st;
-  dsa::TopkArgs a{scores, ld, (int64_t)Tq * ld, kv_len, B, Tq, Tk, k, 0, Tq, idx};
+  // the optional workspace: few long rows then split over the chip
+  const size_t need = dsa::topk_split_workspace_bytes(B, Tq, Tk, k);
+  if (ws && ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "topk workspace too small: need " + std::to_string(need) + " bytes");
+  if (!aligned(ws, 16)) return fail(DSA_ERR_UNSUPPORTED, "ws must be 16-byte aligned");
+  dsa::TopkArgs a{scores, ld, (int64_t)Tq * ld, kv_len, B, Tq, Tk, k, 0, Tq, idx, need ? ws : nullptr};
   return launch_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk");
 }
 
@@ -484,8 +494,8 @@ size_t dsa_workspace_size(const dsa_shape* s, dsa_op op) {
   if (s->H < 1 || s->Dv < 1 || s->k < 1) return 0;
   const bool mla = s->Hkv == 1 && s->Dqk == 576 && s->Dv == 512;
   switch (op) {
-    case DSA_OP_SCORES:
-    case DSA_OP_TOPK: return 0;
+    case DSA_OP_SCORES: return 0;
+    case DSA_OP_TOPK: return dsa::topk_split_workspace_bytes(s->B, s->Tq, s->Tk, s->k);
     case DSA_OP_ATTN: return dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, mla);
     case DSA_OP_INDEX_TOPK: return plan_index_topk(*s, false).ws;
     case DSA_OP_ATTN_PAGED: return paged_idx_bytes(*s) + dsa::attn_workspace_bytes(s->B, s->Tq, s->H, s->Dv, s->k, true);

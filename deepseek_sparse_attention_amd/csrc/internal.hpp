@@ -43,7 +43,11 @@ struct TopkArgs {
   int B, Tq, Tk, k;
   int row0, nrows;
   int32_t* idx;
+  // optional workspace of topk_split_workspace_bytes(): few long rows then split each row
+  // over the chip (segment lists, then a merge per row); null keeps one workgroup per row
+  void* ws = nullptr;
 };
+size_t topk_split_workspace_bytes(int B, int nrows, int Tk, int k);
 constexpr int kTopkMaxK = 4096;
 constexpr int64_t kTopkMaxTk = int64_t(1) << 24;
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);

@@ -259,9 +259,11 @@ __global__ __launch_bounds__(NT, 1) void topk_kernel(const float* __restrict__ s
 constexpr int kCandCap = 8192;
 constexpr int kSamples = 8;  // per thread
 
-__global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restrict__ scores, int64_t ld,
-                                                          int64_t score_bstride, const int32_t* __restrict__ kv_len,
-                                                          int Tq, int Tk, int k, int row0, int32_t* __restrict__ idx) {
+// Row r of the chunk in sequence b, by one 1024-thread workgroup (also the split route's
+// exact fallback).
+__device__ __forceinline__ void topk_fast_row(const float* __restrict__ scores, int64_t ld, int64_t score_bstride,
+                                              const int32_t* __restrict__ kv_len, int Tq, int Tk, int k, int row0,
+                                              int32_t* __restrict__ idx, int r, int b) {
   __shared__ uint32_t hist[NBINS];
   __shared__ __attribute__((aligned(8))) uint32_t sel_bits[SEG_WORDS];
   __shared__ __attribute__((aligned(8))) uint32_t tie_bits[SEG_WORDS];
@@ -271,7 +273,6 @@ __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restric
   __shared__ uint32_t state[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int r = blockIdx.x, b = blockIdx.y;
   const int64_t L = seq_len(kv_len, b, Tk);
   const int64_t p = L - Tq + row0 + r;
   int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * k;
@@ -573,6 +574,12 @@ __global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restric
       }
     }
   }
+}
+
+__global__ __launch_bounds__(NT, 1) void topk_fast_kernel(const float* __restrict__ scores, int64_t ld,
+                                                          int64_t score_bstride, const int32_t* __restrict__ kv_len,
+                                                          int Tq, int Tk, int k, int row0, int32_t* __restrict__ idx) {
+  topk_fast_row(scores, ld, score_bstride, kv_len, Tq, Tk, k, row0, idx, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1135,7 +1142,369 @@ __global__ __launch_bounds__(64 * SH_NW) void topk_short_kernel(const float* __r
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Split top-k for few long rows (decode: a few dozen rows of up to 65536 keys), so that a
+// row's load and selection spread over the chip instead of one CU.
+//
+// topk_seg_kernel: one 256-thread workgroup per 4096-position segment of a row lists every
+// key >= theta_j of its segment in position order, theta_j chosen so that the list holds
+// at least c = ceil(2k / S) keys (S = the row's segments) and at most SP_CAP: the lower
+// edge of the histogram bin of its c-th largest key (a second pass inside that bin if the
+// first overshoots).  A segment of at most SP_CAP keys lists all of them (no theta).
+// topk_merge_kernel: one workgroup per row selects the k best entries (score, then lower
+// position) of the union of the lists and emits them in position order.  That selection is
+// the row's whenever its worst entry E has key(E) >= theta_j for every segment: a key
+// missing from the lists lies below its segment's theta, so below E, and E already has
+// k entries at least as good as itself.  Rows where this fails, a list overflowed (a bin
+// of one value held by more than SP_CAP keys) or the row is too short for lists
+// (S < 4k / SP_CAP) take the one-workgroup kernel's path instead, so the output is the
+// one-workgroup result in every case.
+constexpr int SP_SEG = 4096;                // positions per segment
+constexpr int SP_NT = 256;                  // segment workgroup: 16 keys per thread
+constexpr int SP_CAP = 1024;                // list entries per segment
+constexpr int SP_MAXSEG = SEG / SP_SEG;     // segments per row, at most 16
+constexpr int SP_ROUNDS = SP_MAXSEG * SP_CAP / NT;  // union entries per merge thread
+constexpr uint32_t SP_OVERFLOW = 0xFFFFFFFFu;
+
+// Rows that use segment lists: every segment can hold its share of twice k.
+__device__ __forceinline__ bool sp_uses_lists(int n, int k) {
+  const int S = (n + SP_SEG - 1) / SP_SEG;
+  return S * (SP_CAP / 2) >= 2 * k && n > k;
+}
+
+__global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict__ scores, int64_t ld,
+                                                         int64_t score_bstride, const int32_t* __restrict__ kv_len,
+                                                         int Tq, int Tk, int k, int row0, int nrows,
+                                                         uint2* __restrict__ lists, uint2* __restrict__ meta) {
+  constexpr int SW = SP_NT / 64;
+  __shared__ uint32_t hist[kSelPadBins];
+  __shared__ uint32_t red[2 * SW];
+  __shared__ uint32_t cnt[2 * SW];
+  __shared__ uint32_t state[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int j = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
+  if (p + 1 > SEG || !sp_uses_lists((int)(p + 1), k)) return;  // the merge kernel's own path
+  const int n = (int)(p + 1);
+  const int s0 = j * SP_SEG;
+  if (s0 >= n) return;  // the merge reads the row's segments only
+  const int nv = min(SP_SEG, n - s0);
+  const int S = (n + SP_SEG - 1) / SP_SEG;
+  const int64_t slot = ((int64_t)b * nrows + r) * SP_MAXSEG + j;
+
+  // keys: thread t holds positions 1024 i + 4t + e (coalesced 16-byte loads); positions
+  // past the row read 0 through the range check and get key 0 ("none")
+  const float* row = scores + (int64_t)b * score_bstride + (int64_t)r * ld + s0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)nv * 4u);
+  uint32_t key[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = buf_load_16(rs, (uint32_t)(16 * tid), (uint32_t)(4096 * i));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * i + e] = (1024 * i + 4 * tid + e < nv) ? sel_key(__uint_as_float(v[e])) : 0u;
+  }
+
+  uint32_t theta = 1u;  // every valid key (keys are >= 1)
+  if (nv > SP_CAP) {
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      kmin = min(kmin, key[e] - 1u);  // 0 wraps to the top and drops out
+      kmax = max(kmax, key[e]);
+    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+      red[wave] = kmin;
+      red[SW + wave] = kmax;
+    }
+    for (int i = tid; i < kSelPadBins; i += SP_NT) hist[i] = 0;
+    __syncthreads();
+    uint32_t lo = red[0], hi = red[SW];
+#pragma unroll
+    for (int w = 1; w < SW; ++w) {
+      lo = min(lo, red[w]);
+      hi = max(hi, red[SW + w]);
+    }
+    lo += 1u;
+    int sh = sel_shift(lo, hi);
+    uint32_t need = (uint32_t)((2 * k + S - 1) / S), taken = 0, count;
+    for (;;) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (key[e] >= lo && key[e] <= hi) atomicAdd(&hist[sel_pad((key[e] - lo) >> sh)], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_padded(hist, need, bin, above);
+        if (lane == 0) {
+          state[0] = bin;
+          state[1] = above;
+          state[2] = hist[sel_pad(bin)];
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = state[0], above = state[1], m = state[2];
+      const uint32_t blo = lo + (bin << sh);
+      count = taken + above + m;
+      if (count <= (uint32_t)SP_CAP || sh == 0) {
+        theta = blo;
+        break;
+      }
+      // the bin overshoots the list: split it
+      taken += above;
+      need -= above;
+      hi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)hi);
+      lo = blo;
+      sh = max(0, sh - BIN_BITS);
+      for (int i = tid; i < kSelPadBins; i += SP_NT) hist[i] = 0;
+      __syncthreads();
+    }
+    if (count > (uint32_t)SP_CAP) {  // one key value held by too many positions
+      if (tid == 0) meta[slot] = make_uint2(SP_OVERFLOW, 0u);
+      return;
+    }
+  }
+
+  // the list in position order (i, then t, then e): per-thread counts of rounds 0/1 and
+  // 2/3 packed in 16-bit fields (block totals <= 1024), one block scan each
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[i] += key[4 * i + e] >= theta;
+  }
+  const uint32_t pk01 = c[0] | (c[1] << 16), pk23 = c[2] | (c[3] << 16);
+  uint32_t w01, w23;
+  const uint32_t in01 = wave_incl_scan_u32(pk01, &w01), in23 = wave_incl_scan_u32(pk23, &w23);
+  if (lane == 0) {
+    cnt[wave] = w01;
+    cnt[SW + wave] = w23;
+  }
+  __syncthreads();
+  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
+#pragma unroll
+  for (int w = 0; w < SW; ++w) {
+    pre01 += w < wave ? cnt[w] : 0u;
+    pre23 += w < wave ? cnt[SW + w] : 0u;
+    tot01 += cnt[w];
+    tot23 += cnt[SW + w];
+  }
+  const uint32_t ex01 = pre01 + in01 - pk01, ex23 = pre23 + in23 - pk23;
+  const uint32_t T0 = tot01 & 0xFFFFu, T1 = tot01 >> 16, T2 = tot23 & 0xFFFFu, T3 = tot23 >> 16;
+  uint32_t base[4] = {ex01 & 0xFFFFu, T0 + (ex01 >> 16), T0 + T1 + (ex23 & 0xFFFFu), T0 + T1 + T2 + (ex23 >> 16)};
+  uint2* lst = lists + slot * SP_CAP;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (key[4 * i + e] >= theta) {
+        lst[base[i]] = make_uint2(key[4 * i + e], (uint32_t)(s0 + 1024 * i + 4 * tid + e));
+        ++base[i];
+      }
+    }
+  }
+  if (tid == 0) meta[slot] = make_uint2(T0 + T1 + T2 + T3, nv > SP_CAP ? theta : 0u);
+}
+
+__global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restrict__ scores, int64_t ld,
+                                                           int64_t score_bstride, const int32_t* __restrict__ kv_len,
+                                                           int Tq, int Tk, int k, int row0, int nrows,
+                                                           const uint2* __restrict__ lists,
+                                                           const uint2* __restrict__ meta, int32_t* __restrict__ idx) {
+  __shared__ uint32_t mhist[kSelPadBins];
+  __shared__ uint32_t mred[2 * NWAVES];
+  __shared__ uint32_t mstate[4];
+  __shared__ uint32_t mseg[2 * SP_MAXSEG];
+  __shared__ uint32_t rbase[SP_ROUNDS * NWAVES];  // [round][wave]
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
+  bool exact = true;  // take the one-workgroup path (every branch to it is uniform)
+  do {
+    if (p + 1 > SEG || !sp_uses_lists((int)(p + 1), k)) break;
+    const int n = (int)(p + 1);
+    const int S = (n + SP_SEG - 1) / SP_SEG;
+    const int64_t slot0 = ((int64_t)b * nrows + r) * SP_MAXSEG;
+    int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * k;
+    if (tid < S) {
+      const uint2 m = meta[slot0 + tid];
+      mseg[tid] = m.x;
+      mseg[SP_MAXSEG + tid] = m.y;
+    }
+    for (int i = tid; i < kSelPadBins; i += NT) mhist[i] = 0;
+    __syncthreads();
+    // list offsets in the union (segment order = position order), the largest theta
+    uint32_t off[SP_MAXSEG + 1];
+    off[0] = 0;
+    bool ok = true;
+    uint32_t thmax = 0;
+#pragma unroll
+    for (int j = 0; j < SP_MAXSEG; ++j) {
+      const uint32_t c = j < S ? mseg[j] : 0u;
+      ok = ok && c != SP_OVERFLOW;
+      off[j + 1] = off[j] + (c == SP_OVERFLOW ? 0u : c);
+      thmax = max(thmax, j < S ? mseg[SP_MAXSEG + j] : 0u);
+    }
+    const uint32_t U = off[SP_MAXSEG];
+    if (!ok || U < (uint32_t)k) break;
+    // union entry u = tid + NT * i; rounds past nr hold none (every loop below stops there:
+    // a 1024-thread workgroup is bound by its per-lane instruction count)
+    const int nr = (int)((U + NT - 1) / NT);
+    uint32_t key[SP_ROUNDS];
+    uint32_t pos[SP_ROUNDS];
+    // branch-free range-checked loads (an entry past the union reads 0), all in flight at once
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lists + slot0 * SP_CAP, (uint32_t)(S * SP_CAP * sizeof(uint2)));
+#pragma unroll
+    for (int i = 0; i < SP_ROUNDS; ++i) {
+      key[i] = pos[i] = 0u;
+      if (i < nr) {  // (uniform)
+        const uint32_t u = (uint32_t)(tid + NT * i);
+        uint32_t jj = 0, ob = 0;
+#pragma unroll
+        for (int j = 1; j < SP_MAXSEG; ++j) {
+          const bool ge = u >= off[j];
+          jj = ge ? (uint32_t)j : jj;
+          ob = ge ? off[j] : ob;
+        }
+        const uint32_t boff = u < U ? (jj * SP_CAP + (u - ob)) * (uint32_t)sizeof(uint2) : 0x80000000u;
+        const auto e = __builtin_amdgcn_raw_buffer_load_b64(lrs, (int)boff, 0, 0);
+        key[i] = e[0];
+        pos[i] = e[1];
+      }
+    }
+    // exact radix select of the k-th best key over the union
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < SP_ROUNDS; ++i) {
+      if (i < nr) {
+        kmin = min(kmin, key[i] - 1u);
+        kmax = max(kmax, key[i]);
+      }
+    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+      mred[wave] = kmin;
+      mred[NWAVES + wave] = kmax;
+    }
+    __syncthreads();
+    uint32_t lo = mred[0], hi = mred[NWAVES];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) {
+      lo = min(lo, mred[w]);
+      hi = max(hi, mred[NWAVES + w]);
+    }
+    lo += 1u;
+    int sh = sel_shift(lo, hi);
+    uint32_t need = (uint32_t)k, blo, bhi;
+    bool whole_bin;
+    for (;;) {
+#pragma unroll
+      for (int i = 0; i < SP_ROUNDS; ++i)
+        if (i < nr && key[i] >= lo && key[i] <= hi) atomicAdd(&mhist[sel_pad((key[i] - lo) >> sh)], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin, above;
+        wave_find_bin_padded(mhist, need, bin, above);
+        if (lane == 0) {
+          mstate[0] = bin;
+          mstate[1] = above;
+          mstate[2] = mhist[sel_pad(bin)];
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = mstate[0], m = mstate[2];
+      need -= mstate[1];
+      blo = lo + (bin << sh);
+      bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)hi);
+      whole_bin = m == need;  // every member of the bin is kept
+      if (whole_bin || sh == 0) break;
+      lo = blo;
+      hi = bhi;
+      sh = max(0, sh - BIN_BITS);
+      for (int i = tid; i < kSelPadBins; i += NT) mhist[i] = 0;
+      __syncthreads();
+    }
+    // kept: keys > bhi, and the bin (all of it, or its first `need` ties by position)
+    // the worst kept key against every segment's theta
+    uint32_t kworst = blo;
+    if (whole_bin && blo < thmax) {
+      uint32_t v = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < SP_ROUNDS; ++i) v = (i < nr && key[i] >= blo) ? min(v, key[i]) : v;
+      v = wave_min_u32(v);
+      __syncthreads();  // the loop's last reads of mred are done
+      if (lane == 0) mred[wave] = v;
+      __syncthreads();
+      kworst = mred[0];
+#pragma unroll
+      for (int w = 1; w < NWAVES; ++w) kworst = min(kworst, mred[w]);
+    }
+    if (kworst < thmax) break;  // keys missing from the lists could rank
+    // emission in position order: per round and wave, the counts of kept keys above the bin
+    // (high half) and of bin members (low half); one wave scans the [round][wave] table
+#pragma unroll
+    for (int i = 0; i < SP_ROUNDS; ++i) {
+      if (i < nr) {  // (later rounds' table entries only feed later rounds)
+        const bool a = whole_bin ? key[i] >= blo : key[i] > bhi;
+        const bool t = !whole_bin && key[i] == blo;
+        const uint64_t ba = __ballot(a), bt = __ballot(t);
+        if (lane == 0) rbase[i * NWAVES + wave] = ((uint32_t)__popcll(ba) << 16) | (uint32_t)__popcll(bt);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      constexpr int PER = SP_ROUNDS * NWAVES / 64;
+      uint32_t v[PER], sum = 0;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        v[q] = rbase[PER * lane + q];
+        sum += v[q];
+      }
+      uint32_t tot;
+      uint32_t run = wave_incl_scan_u32(sum, &tot) - sum;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        rbase[PER * lane + q] = run;
+        run += v[q];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SP_ROUNDS; ++i) {
+      if (i < nr) {
+        const bool a = whole_bin ? key[i] >= blo : key[i] > bhi;
+        const bool t = !whole_bin && key[i] == blo;
+        const uint64_t ba = __ballot(a), bt = __ballot(t);
+        const uint32_t base = rbase[i * NWAVES + wave];
+        const uint32_t ap = (base >> 16) + sh_mbcnt(ba), tp = (base & 0xFFFFu) + sh_mbcnt(bt);
+        if (a) {
+          const uint32_t s = ap + min(tp, need);
+          if (s < (uint32_t)k) out[s] = (int32_t)pos[i];
+        } else if (t && tp < need) {
+          if (ap + tp < (uint32_t)k) out[ap + tp] = (int32_t)pos[i];
+        }
+      }
+    }
+    exact = false;
+  } while (false);
+  if (exact) {
+    __syncthreads();  // this kernel's LDS reads are done
+    topk_fast_row(scores, ld, score_bstride, kv_len, Tq, Tk, k, row0, idx, r, b);
+  }
+}
+
 }  // namespace
+
+size_t topk_split_workspace_bytes(int B, int nrows, int Tk, int k) {
+  // rows the one-workgroup kernel would take, with room for segment lists
+  if (B <= 0 || nrows <= 0 || Tk <= 64 * 96 || Tk > SEG || (int64_t)nrows * B >= 1024 ||
+      (int64_t)((Tk + SP_SEG - 1) / SP_SEG) * (SP_CAP / 2) < 2 * (int64_t)k)
+    return 0;
+  return (size_t)B * nrows * SP_MAXSEG * (SP_CAP + 1) * sizeof(uint2);  // lists, then (count, theta)
+}
 
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.nrows <= 0 || A.B <= 0) return hipSuccess;
@@ -1151,6 +1520,15 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
     else
       hipLaunchKernelGGL(topk_short_kernel<96>, g2, dim3(64 * SH_NW), 0, st, A.scores, A.ld, A.score_bstride,
                          A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, A.idx);
+  } else if (topk_split_workspace_bytes(A.B, A.nrows, A.Tk, A.k) && A.ws && A.ld % 4 == 0 &&
+             A.score_bstride % 4 == 0 && (reinterpret_cast<uintptr_t>(A.scores) & 15) == 0) {
+    uint2* lists = reinterpret_cast<uint2*>(A.ws);
+    uint2* meta = lists + (size_t)A.B * A.nrows * SP_MAXSEG * SP_CAP;
+    const int segs = (A.Tk + SP_SEG - 1) / SP_SEG;
+    hipLaunchKernelGGL(topk_seg_kernel, dim3(segs, A.nrows, A.B), dim3(SP_NT), 0, st, A.scores, A.ld,
+                       A.score_bstride, A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, lists, meta);
+    hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len, A.Tq,
+                       A.Tk, A.k, A.row0, A.nrows, lists, meta, A.idx);
   } else if (A.Tk <= SEG && (int64_t)A.nrows * A.B >= 1024)
     hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(ST_NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len,
                        A.Tq, A.Tk, A.k, A.row0, A.idx);

@@ -136,7 +136,14 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w_
  *          score, equal scores resolved toward the lower key index, -0.0 equal to +0.0;
  *          either way sorted ascending and padded with -1 up to k entries.
  * Scores must not be NaN.  Supported: 1 <= k <= 4096, Tk <= 65536 (rows kept in
- * registers) or Tk <= 2^24 (rows re-read per pass).  ws/ws_bytes: reserved, may be NULL/0.
+ * registers) or Tk <= 2^24 (rows re-read per pass).
+ *   ws     optional, 16-byte aligned, at least dsa_workspace_size(shape, DSA_OP_TOPK) bytes
+ *          (shape fields used: B, Tq, Tk, k; nonzero only for fewer than 1024 rows of
+ *          6145..65536 keys, about 128 KB per row).  With it such rows are split over the
+ *          chip: per-segment candidate lists, then an exact merge per row that falls back to
+ *          the whole row where the lists cannot decide; NULL runs one workgroup per row.
+ *          idx is the same either way.  A non-NULL ws smaller than the size is
+ *          DSA_ERR_WORKSPACE.
  */
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* kv_len, int B, int Tq, int Tk,
                     int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);

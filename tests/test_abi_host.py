@@ -188,8 +188,12 @@ def test_index_topk_workspace_follows_the_route(L):
     # candidate slots of 8 bytes per row; nothing of size Tq x Tk
     fused = size(1, 65536, 65536, 16, 2048, dsa.OP_INDEX_TOPK)
     assert 65536 * (4096 * 4 + 6144 * 8) <= fused <= 65536 * (4096 * 4 + 6144 * 8 + 64) + 4096
-    # few rows (decode) or 2 indexer heads: score chunks (at most 1 GiB here)
-    assert size(64, 1, 65536, 16, 2048, dsa.OP_INDEX_TOPK) == 64 * 65536 * 4
+    # few rows (decode): score chunks, then the split top-k's segment lists (16 segments of
+    # 1024 entries and a (count, theta) pair each, 8 bytes apiece)
+    lists = 64 * 16 * 1025 * 8
+    assert size(64, 1, 65536, 16, 2048, dsa.OP_INDEX_TOPK) == 64 * 65536 * 4 + lists
+    assert size(64, 1, 65536, 16, 2048, dsa.OP_TOPK) == lists
+    # 2 indexer heads: score chunks (at most 1 GiB here)
     assert size(1, 3072, 3072, 2, 512, dsa.OP_INDEX_TOPK) == 3072 * 3072 * 4
     # up to 6144 keys (every row keeps all its keys): score rows too
     assert size(1, 6144, 6144, 16, 2048, dsa.OP_INDEX_TOPK) == 6144 * 6144 * 4
@@ -197,6 +201,25 @@ def test_index_topk_workspace_follows_the_route(L):
     # the stack holds either route plus attention
     st = size(1, 65536, 65536, 16, 2048, dsa.OP_STACK)
     assert st >= fused and st >= 4096 * 65536 * 4
+
+
+def test_topk_workspace_sizes_and_checks(L):
+    def size(B, Tq, Tk, k):
+        shp = dsa.Shape(B, Tq, Tk, 16, 64, 1, 1, 1, 1, k, 1.0, 0, None)
+        return L.dsa_workspace_size(ctypes.byref(shp), dsa.OP_TOPK)
+
+    # split only for fewer than 1024 rows of 6145..65536 keys with room for 2k in the lists
+    assert size(64, 1, 65536, 2048) == 64 * 16 * 1025 * 8
+    assert size(3, 40, 65536, 4096) == 120 * 16 * 1025 * 8
+    assert size(64, 1, 6144, 2048) == 0
+    assert size(64, 1, 65537, 2048) == 0
+    assert size(1, 1024, 65536, 2048) == 0
+    assert size(1, 1, 28672, 2048) == 0 and size(1, 1, 28673, 2048) > 0
+    P = ctypes.c_void_p(256)
+    need = size(1, 2, 65536, 64)
+    assert L.dsa_topk(P, 65536, None, 1, 2, 65536, 64, P, P, need - 1, None) == 5  # small ws
+    assert b"topk workspace too small" in L.dsa_last_error()
+    assert L.dsa_topk(P, 65536, None, 1, 2, 65536, 64, P, ctypes.c_void_p(264), need, None) == 3  # ws alignment
 
 
 def test_indexer_kl_argument_checks(L):
