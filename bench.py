@@ -131,7 +131,7 @@ def summarize_mfma(pmc_csv, trace_csv, out_path=MFMA_FILE):
     for r in csv.DictReader(open(pmc_csv)):
         name = r["Kernel_Name"]
         key = ("fz_filter_kernel<16, 64>" if "fz_filter_kernel<16, 64>" in name else
-               "index_scores_kernel<16, 64, false>" if "index_scores_kernel<16, 64, false>" in name else None)
+               "index_scores_kernel<16, 64, false, 4>" if "index_scores_kernel<16, 64, false, 4>" in name else None)
         if key is None:
             continue
         agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
@@ -145,7 +145,7 @@ def summarize_mfma(pmc_csv, trace_csv, out_path=MFMA_FILE):
         "# flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; rate = flop / the dispatches' summed duration;",
         "# algorithmic indexer work of one layer: 2 x 16 x 64 x T(T+1)/2 = 4.398e12 flop",
     ]
-    for key in ("fz_filter_kernel<16, 64>", "index_scores_kernel<16, 64, false>"):
+    for key in ("fz_filter_kernel<16, 64>", "index_scores_kernel<16, 64, false, 4>"):
         if key not in agg:
             continue
         c, ids = agg[key], seen[key]
