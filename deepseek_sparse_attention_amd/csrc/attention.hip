@@ -216,7 +216,7 @@ template <int FMT, int NW>  // row format; waves per workgroup (query row)
 __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_kernel(
     const MlaLayers Ls, const int32_t* __restrict__ idx, int Tq, int Tk, int64_t kv_bstride, int H, int k,
     float scale_log2, int tiles_per_split, float* __restrict__ part_o, float* __restrict__ part_ml, int64_t part_layer,
-    const int32_t* __restrict__ tail_kv_len, int tail_Tk) {
+    const int32_t* __restrict__ tail_kv_len, int tail_Tk, int64_t nrg) {
   constexpr bool FP8 = FMT == kKvFp8;  // per-token scale on logits and probabilities
   constexpr uint32_t kRowBytes = TileStage<FMT>::kRowBytes;
   __shared__ __attribute__((aligned(16))) uint8_t kvs[NW][2][kWkSlot];  // [wave][slot]: bf16 rows once staged
@@ -235,7 +235,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int HG = H >> 4;
-  const int64_t rowh = blockIdx.x;
+  // (row, head group) pairs rowh = blockIdx.x, + gridDim.x, ... < nrg: a launch of more
+  // pairs than CUs keeps one resident workgroup per CU, which moves on to its next row
+  // instead of a new workgroup being dispatched (rows in flight stay consecutive)
+  for (int64_t rowh = blockIdx.x; rowh < nrg; rowh += gridDim.x) {
   const int64_t row = rowh / HG;
   const int hg = (int)(rowh % HG);
   const int b = (int)(row / Tq);
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
     }
     if (lse && wave == 0 && gq == 0) lse[row * H + h] = lt == 0.f ? -INFINITY : (mxr + __log2f(lt)) * kLn2;
   } else {
-    const int64_t nrowh = (int64_t)gridDim.x * 16;  // (row, head) pairs over all rows
+    const int64_t nrowh = nrg * 16;  // (row, head) pairs over all rows
     const int64_t rh = rowh * 16 + hl;
     float* po = part_o + ((int64_t)split * nrowh + rh) * kDv + 4 * gq;
     // the partial carries the exact sum: O rescaled to it from the rounded one
@@ -530,6 +533,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
       part_ml[((int64_t)split * nrowh + rh) * 2 + 1] = lt;
     }
   }
+  __syncthreads();  // the next row reuses the slots and the merge buffers
+  }  // rows
 }
 
 // Merge split-key partial results (fixed split order).  One workgroup per (row, 4 heads),
@@ -736,6 +741,18 @@ bool attn_mha_supported(const AttnArgs& a) {
          a.k >= 1 && a.k <= kMhaMaxK;
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 int attn_mla_splits(int B, int Tq, int H, int k, int nlayers) {
   // few rows (decode): split each row's key list so that one round of whole-key workgroups
   // (one per CU) covers the launch, every layer of a grouped launch alike: a lone 64-row
@@ -799,12 +816,16 @@ hipError_t launch_sparse_attn_layers(const AttnArgs& a, const AttnLayer* layers,
       part_o = reinterpret_cast<float*>(a.ws);
       part_ml = part_o + (size_t)nsplit * nrowh * kDv;
     }
-    dim3 grid((unsigned)(rows * (a.H / 16)), nsplit, nlayers);
+    // one workgroup per (row, head group) and split, or, for unsplit launches of more rows
+    // than the chip holds at once (one workgroup per CU), one per CU looping over rows
+    const int64_t nrg = rows * (a.H / 16);
+    const int64_t resident = std::max<int64_t>(1, device_cus() / nlayers);
+    dim3 grid((unsigned)(nsplit == 1 ? std::min(nrg, resident) : nrg), nsplit, nlayers);
     const int64_t bstride = a.kv_bstride < 0 ? (int64_t)a.Tk : a.kv_bstride;
     {
-#define DSA_WK_LAUNCH(F)                                                                                             \
-  hipLaunchKernelGGL((mla_attn_wk_kernel<F, kWkWaves>), grid, dim3(64 * kWkWaves), 0, st, Ls, a.idx, a.Tq, a.Tk, bstride, \
-                     a.H, a.k, sl2, per, part_o, part_ml, part_layer, a.tail_kv_len, a.tail_Tk)
+#define DSA_WK_LAUNCH(F)                                                                                           \
+  hipLaunchKernelGGL((mla_attn_wk_kernel<F, kWkWaves>), grid, dim3(64 * kWkWaves), 0, st, Ls, a.idx, a.Tq, a.Tk,   \
+                     bstride, a.H, a.k, sl2, per, part_o, part_ml, part_layer, a.tail_kv_len, a.tail_Tk, nrg)
       if (a.kv_fmt == kKvFp8)
         DSA_WK_LAUNCH(kKvFp8);
       else if (a.kv_fmt == kKvMxfp4)
