@@ -22,6 +22,7 @@
 // Multi-head form (DSA ablation card: 4 heads of width 32, RoPE'd inputs): a workgroup per
 // query row, key rows read as 16-byte chunks spread over the lanes, logits in LDS, three
 // fixed-order passes.
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -741,15 +742,19 @@ bool attn_mha_supported(const AttnArgs& a) {
          a.k >= 1 && a.k <= kMhaMaxK;
 }
 
-// Compute units of the current device (cached per device; 256 on MI355X).
+// Compute units of the current device (cached per device; 256 on MI355X).  Calls may come
+// from several host threads: the cache entries are atomic (a race only repeats the query).
 int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
