@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0, int nrows, float* __restrict__ scores,
     int64_t ld, int64_t score_bstride, int key_seg, int wave_keys, const int32_t* __restrict__ bt, int max_blocks,
     int page_shift, int64_t pool_tokens) {
-  using W = IdxWave<H_I, D_I, QP>;
+  using W = IdxWave<H_I, D_I, QP, QP == 1>;  // one query tile per wave: keys read once
   constexpr int QB = 4 * W::ROWS;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
   const int wave = wave_id();
