@@ -236,10 +236,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int HG = H >> 4;
-  // (row, head group) pairs rowh = blockIdx.x, + gridDim.x, ... < nrg: a launch of more
-  // pairs than CUs keeps one resident workgroup per CU, which moves on to its next row
-  // instead of a new workgroup being dispatched (rows in flight stay consecutive)
-  for (int64_t rowh = blockIdx.x; rowh < nrg; rowh += gridDim.x) {
+  // (row, head group) pairs: a launch of more pairs than CUs keeps one resident workgroup
+  // per CU, which takes every gridDim.x-th pair and moves on to its next one instead of a
+  // new workgroup being dispatched (rows in flight stay consecutive).  Rows whose extent
+  // comes from their position (top-k rows: the first k rows are shorter) go last to first,
+  // so the long rows keep the workgroups in step and the short ones fill the end; a
+  // front-to-back walk let the workgroups that drew short rows run ahead, which widened
+  // the window of rows in flight (T=65536: 12.8-13.1 ms against 11.9-12.4 reversed).
+  // Lists read in full (every row the same length) go front to back.
+  for (int64_t rwi = blockIdx.x; rwi < nrg; rwi += gridDim.x) {
+  const int64_t rowh = tail_Tk > 0 ? nrg - 1 - rwi : rwi;
   const int64_t row = rowh / HG;
   const int hg = (int)(rowh % HG);
   const int b = (int)(row / Tq);
