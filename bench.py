@@ -395,7 +395,10 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs) / reps
 
-    attn_ms = timed(lambda: dsa.sparse_attn(layer["q"], layer["kv"], idx_cache, w.scale(), Dv=w.Dv, out=out, lse=lse))
+    # the attention launch as the step runs it: the stack's attention over the index cache
+    # the step wrote (top-k rows, each row's extent from its position)
+    attn_ms = timed(lambda: dsa.layer_stack("S", [layer], k, w.scale(), Dv=w.Dv, index_cache=idx_cache, ws=ws,
+                                            prefilled=True, topk_rows=True))
     Tc = dsa.stack_chunk_rows(shp)
     ld = (T + 63) // 64 * 64
     chunk = torch.empty((1, Tc, ld), dtype=torch.float32, device=dev)
@@ -436,7 +439,9 @@ def main():
     attn_flops = sel * w.H * 2 * (w.Dqk + w.Dv)
     logical = attn_bytes / (attn_ms * 1e-3) / 1e9
     traffic_all = read_traffic()
-    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel<0, 4> grid={T * w.H // 16 * 256}")
+    # one resident workgroup per CU when the launch has more (row, head group) pairs
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    traffic = traffic_all.get(f"dsa::mla_attn_wk_kernel<0, 4> grid={min(T * w.H // 16, n_cu) * 256}")
     pl = probe()
     psum = torch.empty(T * 4, dtype=torch.int32, device=dev)
 
