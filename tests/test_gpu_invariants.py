@@ -6,6 +6,9 @@
     workgroup schedule takes) on sharp inputs, where a wrong gather moves outputs by O(1),
     and its exact-max recomputation when a late key's logit jumps far above the first ones;
   * duplicate index entries count twice, as in the oracle's gather form;
+  * 32 and 64 heads (several 16-head groups per row): resident workgroups walking more
+    (row, head group) pairs than they are, on plain lists and on top-k rows, and decode
+    rows with key splits;
   * decode equals prefill: a one-query step over a cache of length L gives the indices of
     prefill row L-1 bit for bit, and its outputs within the attention bar ("cached versus
     uncached" logits check, DSV2-Lite-IndexCache-Sparse-1250 card, "Validation and scope");
@@ -111,6 +114,43 @@ def test_mla_attention_bf16_unsplit_long_sharp():
     o = _host(out[:, :n]).double().numpy()
     per_row = np.max(np.abs(o - ref_bad), axis=(2, 3))[0]
     assert np.mean(per_row > 2e-2 * np.max(np.abs(ref_bad))) > 0.5
+
+
+def test_mla_attention_head_groups_and_resident_rows():
+    # 32 heads (two 16-head groups per row) over 300 query rows: 600 (row, head group)
+    # pairs, more than one launch keeps resident, so workgroups move on from row to row;
+    # the plain call walks the pairs front to back, the stack over top-k rows back to front
+    print("attention H=32, 300 rows: plain call and stack over top-k rows", flush=True)
+    Tq = Tk = 300
+    q, kv = _sharp_qkv(Tq, Tk, seed=61, H=32)
+    s = np.random.default_rng(62).standard_normal((1, Tq, Tk)).astype(np.float32)
+    idx = oracle.topk(s, 96)
+    scale = 1.0 / 24
+    ref, rlse = oracle.sparse_attn(q, kv, idx, scale, Dv=512)
+    out, lse = dsa.sparse_attn(q.to(DEV), kv.to(DEV), torch.from_numpy(idx).to(DEV), scale, Dv=512)
+    _sharp_check(out, lse, ref, rlse, "plain H=32")
+    layer = {"q": q.to(DEV), "kv": kv.to(DEV)}
+    cache = torch.from_numpy(idx).to(DEV)
+    outs, lses, _ = dsa.layer_stack("S", [layer], 96, scale, Dv=512, index_cache=cache, prefilled=True,
+                                    topk_rows=True)
+    _sharp_check(outs[0], lses[0], ref, rlse, "stack H=32")
+    assert torch.equal(outs[0], out) and torch.equal(lses[0], lse)
+
+
+def test_mla_attention_64_heads_decode_with_key_splits():
+    # 64 heads (four groups) of two decode rows: few workgroups, so the keys are split and
+    # the partials merged
+    print("attention H=64 decode rows with key splits", flush=True)
+    B, L, k = 2, 3000, 2048
+    q, kv = _sharp_qkv(1, L, B=B, seed=63, H=64)
+    s = np.random.default_rng(64).standard_normal((B, 1, L)).astype(np.float32)
+    lens = [L, 2100]
+    idx = oracle.topk(s, k, kv_len=lens, Tk=L)
+    scale = 1.0 / 24
+    assert dsa.workspace_size(dsa._shape(B, 1, L, 64, 1, 576, 512, k, scale, dsa.KV_BF16), dsa.OP_ATTN) > 0
+    ref, rlse = oracle.sparse_attn(q, kv, idx, scale, Dv=512)
+    out, lse = dsa.sparse_attn(q.to(DEV), kv.to(DEV), torch.from_numpy(idx).to(DEV), scale, Dv=512)
+    _sharp_check(out, lse, ref, rlse, "decode H=64")
 
 
 def test_mla_attention_unsplit_logit_jump_beyond_the_first_tiles():
