@@ -40,7 +40,7 @@ def probe():
         import ctypes
 
         if not os.path.exists(PROBE_LIB):
-            raise ImportError(f"{PROBE_LIB} is missing: run __graft_entry__.build()")
+            raise ImportError(f"{PROBE_LIB} is missing: run `python -m deepseek_sparse_attention_amd.build`")
         L = ctypes.CDLL(PROBE_LIB)
         P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.probe_read.argtypes = [P, SZ, P, I, P]
@@ -88,9 +88,9 @@ def summarize_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
         "# dispatch, scaled by the counts of a plain 1 GiB device copy in the same run): the T=65536,",
         "# k=2048 prefill layer, the 64 x 65536 decode step and the bench's ceiling kernels",
         "# made by (from the repository root):",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch_D -o fetch -- "
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/fetch_D -o fetch -- "
         "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-kl --copy-calibration",
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write_D -o write -- "
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/write_D -o write -- "
         "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-kl --copy-calibration",
         "#   python3 bench.py --summarize-traffic <fetch csv> <write csv>",
         f"copy_fetch_kib: {max(fc):.1f}",
@@ -140,7 +140,7 @@ def summarize_mfma(pmc_csv, trace_csv, out_path=MFMA_FILE):
         "# bf16 MFMA counters of the indexer kernels at T=65536 (16 heads x 64, workload mla_t65536_k2048_sink)",
         "# command (from the repository root):",
         f"#   rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
-        "-d gpurun_out/mfma_D -o mfma -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl",
+        "-d prof_out/mfma_D -o mfma -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-kl",
         "#   python3 bench.py --summarize-mfma <counter_collection csv> <kernel_trace csv>",
         "# flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; rate = flop / the dispatches' summed duration;",
         "# algorithmic indexer work of one layer: 2 x 16 x 64 x T(T+1)/2 = 4.398e12 flop",
@@ -187,9 +187,9 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# the 64 x 65536 decode step (FSS over 3 layers; fp8, paged fp8 and MXFP4 latent caches) and",
         "# the indexer KL objective on the ablation shape (T=3072, top-512 and dense), on one MI355X",
         "# command (from the repository root):",
-        "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_D -o trace -- "
+        "#   rocprofv3 --kernel-trace --stats --output-format csv -d prof_out/trace_D -o trace -- "
         "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "#   python3 bench.py --summarize-stats gpurun_out/trace_D/trace_kernel_stats.csv",
+        "#   python3 bench.py --summarize-stats prof_out/trace_D/trace_kernel_stats.csv",
         "# calls: 1 warmup + 3 timed layer_stack steps (fused index/top-k: fz_sample, fz_threshold,",
         "# fz_filter, fz_select, fz_exact once each, then attention), 3 event-timed launches of each",
         "# kernel group (the unfused indexer and top-k once per query chunk, the fused group, the",
