@@ -94,11 +94,12 @@ struct TileStage<kKvFp8> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
       r[c] = buf_load_16(rs, off, 0);
     }
   }
+  // bytes 2*HI and 2*HI+1 of a word as a bf16 pair (e4m3 values are exact in bf16): one
+  // scaled conversion (scale 1), which gives the same bits as widening through fp32 for all
+  // 65536 byte pairs, NaN payloads included (checked on the device)
   template <bool HI>
   __device__ __forceinline__ static uint32_t widen2(uint32_t word) {
-    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
-    // e4m3 values are exact in bf16: the low 16 bits of the fp32 pattern are zero
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
   }
   __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
 #pragma unroll
@@ -141,11 +142,13 @@ struct TileStage<kKvMxfp4> {
     r[2] = buf_load_16(rs, part0 < kBlocks - 16 ? base + 256 : kRowNone, 0);
     e = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(row + kDqk / 2 + 4 * part0), 0, 0);
   }
-  // elements 2B and 2B+1 of an 8-element word, times the scale, as a bf16 pair (low first)
+  // elements 2B and 2B+1 of an 8-element word, times the scale, as a bf16 pair (low first):
+  // one scaled conversion, which gives the same bits as converting to fp32 and keeping the
+  // upper halves for every byte value, byte position and E8M0 scale, NaNs included (e2m1
+  // times a power of two has two significant bits; checked on the device, 524288 cases)
   template <int B>
   __device__ __forceinline__ static uint32_t pair(uint32_t word, float scale) {
-    const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, B);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, B));
   }
   __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
 #pragma unroll
