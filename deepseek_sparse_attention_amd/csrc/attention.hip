@@ -306,13 +306,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
       st[g].load(kv_rs, part0);
       if (FP8) st[g].sc = buf_load_f32(sc_rs, st[g].s >= 0 ? (uint32_t)st[g].s * 4 : kOffNone, 0);
     }
-    // lanes 8r hold keys r and 8 + r
+    // lanes 8r .. 8r+7 hold keys r and 8 + r, so each byte of a ballot is 0 or 0xFF: one
+    // bit per byte, gathered by a multiply (bits 0, 8, 16, 24 land on 24 .. 27 alone)
     const uint64_t v0 = __ballot(st[0].s >= 0), v1 = __ballot(st[1].s >= 0);
-    uint32_t m = 0;
-#pragma unroll
-    for (int r2 = 0; r2 < 8; ++r2)
-      m |= (uint32_t)((v0 >> (8 * r2)) & 1u) << r2 | (uint32_t)((v1 >> (8 * r2)) & 1u) << (8 + r2);
-    rmask = m;
+    auto gather4 = [](uint32_t x) { return ((x & 0x01010101u) * 0x01020408u) >> 24; };
+    rmask = gather4((uint32_t)v0) | gather4((uint32_t)(v0 >> 32)) << 4 | gather4((uint32_t)v1) << 8 |
+            gather4((uint32_t)(v1 >> 32)) << 12;
   };
   auto stage = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
