@@ -46,6 +46,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // extra cycles per K read and 2 per V read.
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 __device__ __forceinline__ int lds_off(int r, int chunk) { return r * kRowB + ((chunk ^ swz(r)) << 4); }
+// The swizzle moves a chunk only inside its group of 8, so lds_off(r, c + 8 g) = lds_off(r, c)
+// + 128 g: a lane's reads and writes of a row take one base per chunk residue and carry the
+// rest as the LDS instruction's immediate offset (no per-access address arithmetic).
 
 // Gather of a key row: eight lanes per row, lane l owning the 16-byte parts l%8, l%8+8, ...,
 // so every load instruction reads eight full 128-byte lines.  Rows go through registers into LDS (bf16; fp8 and fp4 widened exactly).
@@ -73,8 +76,9 @@ struct TileStage<kKvBf16> {  // bf16 row: 72 parts of 16 B, 9 per lane
     for (int c = 0; c < kChunks; ++c) r[c] = buf_load_16(rs, base + 128 * c, 0);
   }
   __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
+    uint8_t* b = lds + lds_off(key, part0);  // chunk part0 + 8c
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) *reinterpret_cast<u32x4*>(lds + lds_off(key, part0 + 8 * c)) = r[c];
+    for (int c = 0; c < kChunks; ++c) *reinterpret_cast<u32x4*>(b + 128 * c) = r[c];
   }
 };
 
@@ -102,6 +106,9 @@ struct TileStage<kKvFp8> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
   }
   __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
+    // bf16 chunks 2 part and 2 part + 1, part = part0 + 8c: two bases, 256 B per c
+    uint8_t* b0 = lds + lds_off(key, 2 * part0);
+    uint8_t* b1 = lds + lds_off(key, 2 * part0 + 1);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int part = part0 + 8 * c;
@@ -115,8 +122,8 @@ struct TileStage<kKvFp8> {  // e4m3 row: 36 parts of 16 B, up to 5 per lane
       hi[1] = widen2<true>(r[c][2]);
       hi[2] = widen2<false>(r[c][3]);
       hi[3] = widen2<true>(r[c][3]);
-      *reinterpret_cast<u32x4*>(lds + lds_off(key, 2 * part)) = lo;  // bf16 chunks 2p, 2p+1
-      *reinterpret_cast<u32x4*>(lds + lds_off(key, 2 * part + 1)) = hi;
+      *reinterpret_cast<u32x4*>(b0 + 256 * c) = lo;
+      *reinterpret_cast<u32x4*>(b1 + 256 * c) = hi;
     }
   }
 };
@@ -151,6 +158,9 @@ struct TileStage<kKvMxfp4> {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, B));
   }
   __device__ __forceinline__ void store(uint8_t* lds, int key, int part0) const {
+    uint8_t* b[4];  // staged chunk 4 blk + w, blk = part0 + 8c: base w, 512 B per c
+#pragma unroll
+    for (int w = 0; w < 4; ++w) b[w] = lds + lds_off(key, 4 * part0 + w);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int blk = part0 + 8 * c;
@@ -166,7 +176,7 @@ struct TileStage<kKvMxfp4> {
         o[1] = pair<1>(r[c][w], scale);
         o[2] = pair<2>(r[c][w], scale);
         o[3] = pair<3>(r[c][w], scale);
-        *reinterpret_cast<u32x4*>(lds + lds_off(key, 4 * blk + w)) = o;
+        *reinterpret_cast<u32x4*>(b[w] + 512 * c) = o;
       }
     }
   }
@@ -337,9 +347,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
     const uint8_t* sl = kvs[wave][slot];
     // two accumulation chains (even and odd k-steps), added at the end
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    // K operand s is chunk 4s + gq of row hl: base s & 1, then 128 B per pair of steps
+    const uint8_t* kb[2] = {sl + lds_off(hl, gq), sl + lds_off(hl, 4 + gq)};
     u32x4 kr[18];  // every K operand read first, so the reads overlap
 #pragma unroll
-    for (int s = 0; s < 18; ++s) kr[s] = *reinterpret_cast<const u32x4*>(sl + lds_off(hl, 4 * s + gq));
+    for (int s = 0; s < 18; ++s) kr[s] = *reinterpret_cast<const u32x4*>(kb[s & 1] + 128 * (s >> 1));
 #pragma unroll
     for (int s = 0; s < 18; s += 2) {
       a0 = mfma16(as_bf16x8(kr[s]), qb[s], a0);
@@ -390,13 +402,18 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
   auto pv = [&](int slot, i16x4 pb) __attribute__((always_inline)) {
     const uint8_t* sl = kvs[wave][slot];
     const int r0 = 4 * gq + (hl >> 2);
+    // dims 16m + 4(hl & 3) .. +3 of row r0: chunk 2m + ((hl >> 1) & 1), byte 8 (hl & 1) in it,
+    // so base m & 3, then 128 B per four m
+    const uint8_t* vb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vb[j] = sl + lds_off(r0, 2 * j + ((hl >> 1) & 1)) + 8 * (hl & 1);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {  // sixteen operand reads, then their MFMAs
       i16x4 v[16];
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
-        const int dim = (16 * h2 + n) * 16 + 4 * (hl & 3);
-        v[n] = lds_read_tr16(sl + lds_off(r0, dim >> 3) + (dim & 7) * 2);
+        const int m = 16 * h2 + n;
+        v[n] = lds_read_tr16(vb[m & 3] + 128 * (m >> 2));
       }
 #pragma unroll
       for (int n = 0; n < 16; ++n) o_acc[16 * h2 + n] = mfma16k16(v[n], pb, o_acc[16 * h2 + n]);
