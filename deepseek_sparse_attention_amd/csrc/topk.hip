@@ -1317,7 +1317,8 @@ __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restri
   __shared__ uint32_t mred[2 * NWAVES];
   __shared__ uint32_t mstate[4];
   __shared__ uint32_t mseg[2 * SP_MAXSEG];
-  __shared__ uint32_t rbase[SP_ROUNDS * NWAVES];  // [round][wave]
+  __shared__ uint32_t rbase[NWAVES * SP_ROUNDS];  // [wave][round]
+  static_assert(NWAVES == SP_MAXSEG && SP_CAP == 64 * SP_ROUNDS, "wave j reads segment j's list");
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = blockIdx.x, b = blockIdx.y;
   const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
@@ -1335,41 +1336,32 @@ __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restri
     }
     for (int i = tid; i < kSelPadBins; i += NT) mhist[i] = 0;
     __syncthreads();
-    // list offsets in the union (segment order = position order), the largest theta
-    uint32_t off[SP_MAXSEG + 1];
-    off[0] = 0;
+    // the union's size and the largest theta
+    uint32_t U = 0, thmax = 0;
     bool ok = true;
-    uint32_t thmax = 0;
 #pragma unroll
     for (int j = 0; j < SP_MAXSEG; ++j) {
       const uint32_t c = j < S ? mseg[j] : 0u;
       ok = ok && c != SP_OVERFLOW;
-      off[j + 1] = off[j] + (c == SP_OVERFLOW ? 0u : c);
+      U += c == SP_OVERFLOW ? 0u : c;
       thmax = max(thmax, j < S ? mseg[SP_MAXSEG + j] : 0u);
     }
-    const uint32_t U = off[SP_MAXSEG];
     if (!ok || U < (uint32_t)k) break;
-    // union entry u = tid + NT * i; rounds past nr hold none (every loop below stops there:
-    // a 1024-thread workgroup is bound by its per-lane instruction count)
-    const int nr = (int)((U + NT - 1) / NT);
+    // wave j holds segment j's list: entry lane + 64 i in round i, so the union in (wave,
+    // round, lane) order is in position order.  Rounds past the wave's nr hold none (every
+    // loop below stops there: a 1024-thread workgroup is bound by its per-lane instruction
+    // count); an entry past the list has key 0 ("none").
+    const uint32_t cnt_w = wave < S ? mseg[wave] : 0u;  // (not SP_OVERFLOW: ok holds)
+    const int nr = (int)((cnt_w + 63) / 64);             // (wave-uniform)
     uint32_t key[SP_ROUNDS];
     uint32_t pos[SP_ROUNDS];
-    // branch-free range-checked loads (an entry past the union reads 0), all in flight at once
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lists + slot0 * SP_CAP, (uint32_t)(S * SP_CAP * sizeof(uint2)));
+    // branch-free range-checked loads (an entry past the list reads 0), all in flight at once
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lists + (slot0 + wave) * SP_CAP, cnt_w * (uint32_t)sizeof(uint2));
 #pragma unroll
     for (int i = 0; i < SP_ROUNDS; ++i) {
       key[i] = pos[i] = 0u;
-      if (i < nr) {  // (uniform)
-        const uint32_t u = (uint32_t)(tid + NT * i);
-        uint32_t jj = 0, ob = 0;
-#pragma unroll
-        for (int j = 1; j < SP_MAXSEG; ++j) {
-          const bool ge = u >= off[j];
-          jj = ge ? (uint32_t)j : jj;
-          ob = ge ? off[j] : ob;
-        }
-        const uint32_t boff = u < U ? (jj * SP_CAP + (u - ob)) * (uint32_t)sizeof(uint2) : 0x80000000u;
-        const auto e = __builtin_amdgcn_raw_buffer_load_b64(lrs, (int)boff, 0, 0);
+      if (i < nr) {
+        const auto e = __builtin_amdgcn_raw_buffer_load_b64(lrs, (lane + 64 * i) * (int)sizeof(uint2), 0, 0);
         key[i] = e[0];
         pos[i] = e[1];
       }
@@ -1443,16 +1435,18 @@ __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restri
       for (int w = 1; w < NWAVES; ++w) kworst = min(kworst, mred[w]);
     }
     if (kworst < thmax) break;  // keys missing from the lists could rank
-    // emission in position order: per round and wave, the counts of kept keys above the bin
-    // (high half) and of bin members (low half); one wave scans the [round][wave] table
+    // emission in position order: per wave and round, the counts of kept keys above the bin
+    // (high half) and of bin members (low half); one wave scans the [wave][round] table
 #pragma unroll
     for (int i = 0; i < SP_ROUNDS; ++i) {
-      if (i < nr) {  // (later rounds' table entries only feed later rounds)
+      uint32_t c = 0;
+      if (i < nr) {
         const bool a = whole_bin ? key[i] >= blo : key[i] > bhi;
         const bool t = !whole_bin && key[i] == blo;
         const uint64_t ba = __ballot(a), bt = __ballot(t);
-        if (lane == 0) rbase[i * NWAVES + wave] = ((uint32_t)__popcll(ba) << 16) | (uint32_t)__popcll(bt);
+        c = ((uint32_t)__popcll(ba) << 16) | (uint32_t)__popcll(bt);
       }
+      if (lane == 0) rbase[wave * SP_ROUNDS + i] = c;
     }
     __syncthreads();
     if (wave == 0) {
@@ -1478,7 +1472,7 @@ __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restri
         const bool a = whole_bin ? key[i] >= blo : key[i] > bhi;
         const bool t = !whole_bin && key[i] == blo;
         const uint64_t ba = __ballot(a), bt = __ballot(t);
-        const uint32_t base = rbase[i * NWAVES + wave];
+        const uint32_t base = rbase[wave * SP_ROUNDS + i];
         const uint32_t ap = (base >> 16) + sh_mbcnt(ba), tp = (base & 0xFFFFu) + sh_mbcnt(bt);
         if (a) {
           const uint32_t s = ap + min(tp, need);
