@@ -50,8 +50,11 @@ struct IdxWave {
   static constexpr uint32_t kTileBytes = 32 * D_I * 2;
   // key tiles in flight, and LDS tile buffers: one more than in flight, so that a buffer is
   // refilled only once the operand reads of its last tile have completed.  128-wide keys
-  // keep one tile in flight so that two workgroups still fit a CU.
-  static constexpr int DEPTH = D_I >= 128 ? 1 : 3;
+  // keep one tile in flight so that two workgroups still fit a CU.  A streaming wave (one
+  // query tile) keeps two: 48 KB of LDS per workgroup lets three workgroups share a CU
+  // (169 registers per lane allow three), which beat two workgroups with three tiles in
+  // flight each on the 64 x 65536 decode keys (101.6 against 104.3 us; four tiles: 107.7).
+  static constexpr int DEPTH = D_I >= 128 ? 1 : (STREAM ? 2 : 3);
   static constexpr int NB = DEPTH + 1;
   static constexpr uint32_t kLdsBytes = NB * kTileBytes;  // the wave's private key buffers
 
