@@ -94,10 +94,12 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   const int64_t tiles = (maxkeys + 31) / 32;
   // Aim at ~2048 workgroups per launch when query blocks are full (prefill chunks): twice
   // what the chip holds at once, with segments short enough that the causal tail of a launch
-  // stays small.  Few-row launches take ~1536 (measured on the 64 x 65536 decode key cache:
-  // 108 us against 112-116 us at 512-1024 and 109-113 us at 2048-4096); with the waves
+  // stays small.  Other few-row launches take ~1536.  A launch of one query tile (decode)
+  // streams its keys once with three workgroups per CU: one round of them, 768 on the 256
+  // CUs of MI355X (measured on the 64 x 65536 decode key cache: 99.0 us against 101.6 at
+  // 512, 104.3 at 640, 103.6 at 1024, 101.7 at 1536 and 104.9 at 2304).  With the waves
   // splitting keys (one wave's rows) a segment is a multiple of four tiles.
-  const int64_t target = A.nrows >= 8 * QB ? 2048 : 1536;
+  const int64_t target = A.nrows >= 8 * QB ? 2048 : one_tile ? 3 * (int64_t)device_cus() : 1536;
   int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, target / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
   int64_t seg_tiles = (tiles + segs - 1) / segs;
   if (wsplit) seg_tiles = (seg_tiles + 3) / 4 * 4;

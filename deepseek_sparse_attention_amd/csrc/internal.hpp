@@ -130,6 +130,8 @@ bool attn_mha_supported(const AttnArgs& a);
 // Split-key factor the MLA kernel uses for this shape in a launch of nlayers layers (1 = no
 // partial results); never more than for one layer, whose count sizes the workspace.
 int attn_mla_splits(int B, int Tq, int H, int k, int nlayers = 1);
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus();
 size_t attn_workspace_bytes(int B, int Tq, int H, int Dv, int k, bool mla);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 // Layers that share a's index list and shape in one launch (MLA form; at most
