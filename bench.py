@@ -199,7 +199,7 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# topk_seg_kernel + topk_merge_kernel: the decode rows' split top-k (segment lists, merge);",
         "# index_scores_kernel<H_I, d_I, paged, query tiles per wave>.  grid = threads of the launch",
         "# (the 64-row decode: grouped 3-layer attention 49152, one layer in 4 key splits 65536;",
-        "# decode indexer 393216)",
+        "# decode indexer 196608)",
         "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel, grid",
         "",
     ]
