@@ -52,8 +52,9 @@ __device__ __forceinline__ void wave_find_bin_from_top(const uint32_t* hist, uin
 constexpr int kSelPadBins = kSelBins + kSelBins / 32;
 __device__ __forceinline__ uint32_t sel_pad(uint32_t b) { return b + (b >> 5); }
 
+// `total`, if given, receives the histogram's total count.
 __device__ __forceinline__ void wave_find_bin_padded(const uint32_t* hist, uint32_t need, uint32_t& bin,
-                                                     uint32_t& above) {
+                                                     uint32_t& above, uint32_t* total_out = nullptr) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = kSelBins / 64;
   uint32_t sum = 0;
@@ -61,6 +62,7 @@ __device__ __forceinline__ void wave_find_bin_padded(const uint32_t* hist, uint3
   for (int i = 0; i < PER; ++i) sum += hist[sel_pad(kSelBins - 1 - (lane * PER + i))];
   uint32_t total;
   const uint32_t incl = wave_incl_scan_u32(sum, &total);
+  if (total_out) *total_out = total;
   const uint64_t hit = __ballot(incl - sum < need && need <= incl);
   const int L = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : 0);
   const uint32_t preL = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);

@@ -1150,21 +1150,25 @@ __global__ __launch_bounds__(64 * SH_NW) void topk_short_kernel(const float* __r
 // key >= theta_j of its segment in position order, theta_j chosen so that the list holds
 // at least c = ceil(2k / S) keys (S = the row's segments) and at most SP_CAP: the lower
 // edge of the histogram bin of its c-th largest key (a second pass inside that bin if the
-// first overshoots).  A segment of at most SP_CAP keys lists all of them (no theta).
-// topk_merge_kernel: one workgroup per row selects the k best entries (score, then lower
-// position) of the union of the lists and emits them in position order.  That selection is
-// the row's whenever its worst entry E has key(E) >= theta_j for every segment: a key
-// missing from the lists lies below its segment's theta, so below E, and E already has
-// k entries at least as good as itself.  Rows where this fails, a list overflowed (a bin
-// of one value held by more than SP_CAP keys) or the row is too short for lists
-// (S < 4k / SP_CAP) take the one-workgroup kernel's path instead, so the output is the
-// one-workgroup result in every case.
+// first overshoots).  A segment of at most SP_CAP keys lists all of them (theta 0).  Its
+// meta word holds the list's length, theta_j and the segment's largest key.
+// topk_merge_kernel: one workgroup per row, wave j holding segment j's list.  With
+// theta = max_j theta_j, the k best entries (score, then lower position) among the listed
+// keys >= theta are the row's k best whenever at least k listed keys are >= theta: the
+// k-th best of them, E, then has key(E) >= theta >= theta_j for every segment, so every
+// key a list lacks (below its segment's theta_j) ranks below E, while every row key
+// equal to or above E is listed (ties included, so the lowest positions among them are
+// too).  Rows where this fails, a list overflowed (a bin of one value held by more than
+// SP_CAP keys) or the row is too short for lists (S < 4k / SP_CAP) take the one-workgroup
+// kernel's path instead, so the output is the one-workgroup result in every case.
 constexpr int SP_SEG = 4096;                // positions per segment
 constexpr int SP_NT = 256;                  // segment workgroup: 16 keys per thread
 constexpr int SP_CAP = 1024;                // list entries per segment
 constexpr int SP_MAXSEG = SEG / SP_SEG;     // segments per row, at most 16
 constexpr int SP_ROUNDS = SP_MAXSEG * SP_CAP / NT;  // union entries per merge thread
 constexpr uint32_t SP_OVERFLOW = 0xFFFFFFFFu;
+constexpr int SP_SPEC = 6;                  // list rounds the merge loads before it knows the length
+constexpr int SP_PASSES = 3;                // radix passes over 32-bit keys (11 + 11 + 10 bits)
 
 // Rows that use segment lists: every segment can hold its share of twice k.
 __device__ __forceinline__ bool sp_uses_lists(int n, int k) {
@@ -1175,11 +1179,11 @@ __device__ __forceinline__ bool sp_uses_lists(int n, int k) {
 __global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict__ scores, int64_t ld,
                                                          int64_t score_bstride, const int32_t* __restrict__ kv_len,
                                                          int Tq, int Tk, int k, int row0, int nrows,
-                                                         uint2* __restrict__ lists, uint2* __restrict__ meta) {
+                                                         uint2* __restrict__ lists, uint4* __restrict__ meta) {
   constexpr int SW = SP_NT / 64;
   __shared__ uint32_t hist[kSelPadBins];
   __shared__ uint32_t red[2 * SW];
-  __shared__ uint32_t cnt[2 * SW];
+  __shared__ uint32_t cnt[3 * SW];
   __shared__ uint32_t state[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int j = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
@@ -1261,7 +1265,7 @@ __global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict
       __syncthreads();
     }
     if (count > (uint32_t)SP_CAP) {  // one key value held by too many positions
-      if (tid == 0) meta[slot] = make_uint2(SP_OVERFLOW, 0u);
+      if (tid == 0) meta[slot] = make_uint4(SP_OVERFLOW, 0u, 0u, 0u);
       return;
     }
   }
@@ -1276,20 +1280,25 @@ __global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict
     for (int e = 0; e < 4; ++e) c[i] += key[4 * i + e] >= theta;
   }
   const uint32_t pk01 = c[0] | (c[1] << 16), pk23 = c[2] | (c[3] << 16);
-  uint32_t w01, w23;
+  uint32_t w01, w23, kx = 0;
   const uint32_t in01 = wave_incl_scan_u32(pk01, &w01), in23 = wave_incl_scan_u32(pk23, &w23);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) kx = max(kx, key[e]);
+  kx = wave_max_u32(kx);
   if (lane == 0) {
     cnt[wave] = w01;
     cnt[SW + wave] = w23;
+    cnt[2 * SW + wave] = kx;
   }
   __syncthreads();
-  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0;
+  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0, segmax = 0;
 #pragma unroll
   for (int w = 0; w < SW; ++w) {
     pre01 += w < wave ? cnt[w] : 0u;
     pre23 += w < wave ? cnt[SW + w] : 0u;
     tot01 += cnt[w];
     tot23 += cnt[SW + w];
+    segmax = max(segmax, cnt[2 * SW + w]);
   }
   const uint32_t ex01 = pre01 + in01 - pk01, ex23 = pre23 + in23 - pk23;
   const uint32_t T0 = tot01 & 0xFFFFu, T1 = tot01 >> 16, T2 = tot23 & 0xFFFFu, T3 = tot23 >> 16;
@@ -1305,20 +1314,19 @@ __global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict
       }
     }
   }
-  if (tid == 0) meta[slot] = make_uint2(T0 + T1 + T2 + T3, nv > SP_CAP ? theta : 0u);
+  if (tid == 0) meta[slot] = make_uint4(T0 + T1 + T2 + T3, nv > SP_CAP ? theta : 0u, segmax, 0u);
 }
 
 __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restrict__ scores, int64_t ld,
                                                            int64_t score_bstride, const int32_t* __restrict__ kv_len,
                                                            int Tq, int Tk, int k, int row0, int nrows,
                                                            const uint2* __restrict__ lists,
-                                                           const uint2* __restrict__ meta, int32_t* __restrict__ idx) {
-  __shared__ uint32_t mhist[kSelPadBins];
-  __shared__ uint32_t mred[2 * NWAVES];
-  __shared__ uint32_t mstate[4];
-  __shared__ uint32_t mseg[2 * SP_MAXSEG];
-  __shared__ uint32_t rbase[NWAVES * SP_ROUNDS];  // [wave][round]
+                                                           const uint4* __restrict__ meta, int32_t* __restrict__ idx) {
+  __shared__ uint32_t mhist[SP_PASSES][kSelPadBins];  // one histogram per radix pass, zeroed up front
+  __shared__ uint32_t mstate[SP_PASSES][4];
+  __shared__ uint32_t wtot[NWAVES];
   static_assert(NWAVES == SP_MAXSEG && SP_CAP == 64 * SP_ROUNDS, "wave j reads segment j's list");
+  static_assert(SP_PASSES * BIN_BITS >= 32, "the last pass reaches single key values");
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = blockIdx.x, b = blockIdx.y;
   const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
@@ -1329,36 +1337,37 @@ __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restri
     const int S = (n + SP_SEG - 1) / SP_SEG;
     const int64_t slot0 = ((int64_t)b * nrows + r) * SP_MAXSEG;
     int32_t* out = idx + ((int64_t)b * Tq + row0 + r) * k;
-    if (tid < S) {
-      const uint2 m = meta[slot0 + tid];
-      mseg[tid] = m.x;
-      mseg[SP_MAXSEG + tid] = m.y;
+    // wave j holds segment j's list, entry lane + 64 i in round i, so the union in (wave,
+    // round, lane) order is in position order.  The first SP_SPEC rounds are loaded before
+    // the list's length arrives (the slot holds SP_CAP entries, so the loads stay inside
+    // it); entries past the length are masked to key 0 ("none") below.
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lists + (slot0 + wave) * SP_CAP, SP_CAP * (uint32_t)sizeof(uint2));
+    uint32_t key[SP_ROUNDS], pos[SP_ROUNDS];
+#pragma unroll
+    for (int i = 0; i < SP_SPEC; ++i) {
+      const auto e = __builtin_amdgcn_raw_buffer_load_b64(lrs, (lane + 64 * i) * (int)sizeof(uint2), 0, 0);
+      key[i] = e[0];
+      pos[i] = e[1];
     }
-    for (int i = tid; i < kSelPadBins; i += NT) mhist[i] = 0;
-    __syncthreads();
-    // the union's size and the largest theta
-    uint32_t U = 0, thmax = 0;
+    // every wave reads the row's meta words: list lengths, thetas, segment maxima
+    uint32_t U = 0, theta = 0, hi = 0, cnt_w = 0;
     bool ok = true;
 #pragma unroll
     for (int j = 0; j < SP_MAXSEG; ++j) {
-      const uint32_t c = j < S ? mseg[j] : 0u;
-      ok = ok && c != SP_OVERFLOW;
-      U += c == SP_OVERFLOW ? 0u : c;
-      thmax = max(thmax, j < S ? mseg[SP_MAXSEG + j] : 0u);
+      if (j < S) {
+        const uint4 m = meta[slot0 + j];
+        ok = ok && m.x != SP_OVERFLOW;
+        U += m.x == SP_OVERFLOW ? 0u : m.x;
+        theta = max(theta, m.y);
+        hi = max(hi, m.z);
+        cnt_w = j == wave ? m.x : cnt_w;
+      }
     }
+    for (int i = tid; i < SP_PASSES * kSelPadBins; i += NT) (&mhist[0][0])[i] = 0;
     if (!ok || U < (uint32_t)k) break;
-    // wave j holds segment j's list: entry lane + 64 i in round i, so the union in (wave,
-    // round, lane) order is in position order.  Rounds past the wave's nr hold none (every
-    // loop below stops there: a 1024-thread workgroup is bound by its per-lane instruction
-    // count); an entry past the list has key 0 ("none").
-    const uint32_t cnt_w = wave < S ? mseg[wave] : 0u;  // (not SP_OVERFLOW: ok holds)
-    const int nr = (int)((cnt_w + 63) / 64);             // (wave-uniform)
-    uint32_t key[SP_ROUNDS];
-    uint32_t pos[SP_ROUNDS];
-    // branch-free range-checked loads (an entry past the list reads 0), all in flight at once
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lists + (slot0 + wave) * SP_CAP, cnt_w * (uint32_t)sizeof(uint2));
+    const int nr = (int)((cnt_w + 63) / 64);  // (wave-uniform; cnt_w <= SP_CAP)
 #pragma unroll
-    for (int i = 0; i < SP_ROUNDS; ++i) {
+    for (int i = SP_SPEC; i < SP_ROUNDS; ++i) {
       key[i] = pos[i] = 0u;
       if (i < nr) {
         const auto e = __builtin_amdgcn_raw_buffer_load_b64(lrs, (lane + 64 * i) * (int)sizeof(uint2), 0, 0);
@@ -1366,120 +1375,79 @@ __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restri
         pos[i] = e[1];
       }
     }
-    // exact radix select of the k-th best key over the union
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-    for (int i = 0; i < SP_ROUNDS; ++i) {
-      if (i < nr) {
-        kmin = min(kmin, key[i] - 1u);
-        kmax = max(kmax, key[i]);
-      }
-    }
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    if (lane == 0) {
-      mred[wave] = kmin;
-      mred[NWAVES + wave] = kmax;
-    }
-    __syncthreads();
-    uint32_t lo = mred[0], hi = mred[NWAVES];
-#pragma unroll
-    for (int w = 1; w < NWAVES; ++w) {
-      lo = min(lo, mred[w]);
-      hi = max(hi, mred[NWAVES + w]);
-    }
-    lo += 1u;
+    for (int i = 0; i < SP_ROUNDS; ++i) key[i] = (uint32_t)(lane + 64 * i) < cnt_w ? key[i] : 0u;
+    // exact radix select of the k-th best key among the listed keys >= theta; pass 0 also
+    // counts them (fewer than k: the lists cannot decide the row)
+    uint32_t lo = max(theta, 1u), need = (uint32_t)k, blo = lo, bhi = hi;
     int sh = sel_shift(lo, hi);
-    uint32_t need = (uint32_t)k, blo, bhi;
-    bool whole_bin;
-    for (;;) {
+    bool whole_bin = false, decided = false;
+    __syncthreads();  // histograms zeroed
+#pragma unroll
+    for (int ps = 0; ps < SP_PASSES; ++ps) {
+      uint32_t* h = mhist[ps];
 #pragma unroll
       for (int i = 0; i < SP_ROUNDS; ++i)
-        if (i < nr && key[i] >= lo && key[i] <= hi) atomicAdd(&mhist[sel_pad((key[i] - lo) >> sh)], 1u);
+        if (i < nr && key[i] >= lo && key[i] <= hi) atomicAdd(&h[sel_pad((key[i] - lo) >> sh)], 1u);
       __syncthreads();
       if (wave == 0) {
-        uint32_t bin, above;
-        wave_find_bin_padded(mhist, need, bin, above);
+        uint32_t bin, above, total;
+        wave_find_bin_padded(h, need, bin, above, &total);
         if (lane == 0) {
-          mstate[0] = bin;
-          mstate[1] = above;
-          mstate[2] = mhist[sel_pad(bin)];
+          mstate[ps][0] = bin;
+          mstate[ps][1] = above;
+          mstate[ps][2] = h[sel_pad(bin)];
+          mstate[ps][3] = total;
         }
       }
       __syncthreads();
-      const uint32_t bin = mstate[0], m = mstate[2];
-      need -= mstate[1];
+      if (ps == 0 && mstate[0][3] < (uint32_t)k) break;  // decided stays false
+      const uint32_t bin = mstate[ps][0], m = mstate[ps][2];
+      need -= mstate[ps][1];
       blo = lo + (bin << sh);
       bhi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)hi);
       whole_bin = m == need;  // every member of the bin is kept
-      if (whole_bin || sh == 0) break;
+      if (whole_bin || sh == 0) {
+        decided = true;
+        break;
+      }
       lo = blo;
       hi = bhi;
       sh = max(0, sh - BIN_BITS);
-      for (int i = tid; i < kSelPadBins; i += NT) mhist[i] = 0;
-      __syncthreads();
     }
-    // kept: keys > bhi, and the bin (all of it, or its first `need` ties by position)
-    // the worst kept key against every segment's theta
-    uint32_t kworst = blo;
-    if (whole_bin && blo < thmax) {
-      uint32_t v = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < SP_ROUNDS; ++i) v = (i < nr && key[i] >= blo) ? min(v, key[i]) : v;
-      v = wave_min_u32(v);
-      __syncthreads();  // the loop's last reads of mred are done
-      if (lane == 0) mred[wave] = v;
-      __syncthreads();
-      kworst = mred[0];
-#pragma unroll
-      for (int w = 1; w < NWAVES; ++w) kworst = min(kworst, mred[w]);
-    }
-    if (kworst < thmax) break;  // keys missing from the lists could rank
-    // emission in position order: per wave and round, the counts of kept keys above the bin
-    // (high half) and of bin members (low half); one wave scans the [wave][round] table
+    if (!decided) break;
+    // kept: keys > bhi, and the bin (all of it, or its first `need` ties by position).
+    // Emission in position order: each wave's counts of kept keys above the bin (high
+    // half) and of bin members (low half), then a running count through its rounds.
+    uint32_t wsum = 0;
 #pragma unroll
     for (int i = 0; i < SP_ROUNDS; ++i) {
-      uint32_t c = 0;
       if (i < nr) {
         const bool a = whole_bin ? key[i] >= blo : key[i] > bhi;
         const bool t = !whole_bin && key[i] == blo;
-        const uint64_t ba = __ballot(a), bt = __ballot(t);
-        c = ((uint32_t)__popcll(ba) << 16) | (uint32_t)__popcll(bt);
-      }
-      if (lane == 0) rbase[wave * SP_ROUNDS + i] = c;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      constexpr int PER = SP_ROUNDS * NWAVES / 64;
-      uint32_t v[PER], sum = 0;
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        v[q] = rbase[PER * lane + q];
-        sum += v[q];
-      }
-      uint32_t tot;
-      uint32_t run = wave_incl_scan_u32(sum, &tot) - sum;
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        rbase[PER * lane + q] = run;
-        run += v[q];
+        wsum += ((uint32_t)__popcll(__ballot(a)) << 16) | (uint32_t)__popcll(__ballot(t));
       }
     }
+    if (lane == 0) wtot[wave] = wsum;
     __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += wtot[w];
+    uint32_t ap = base >> 16, tp = base & 0xFFFFu;
 #pragma unroll
     for (int i = 0; i < SP_ROUNDS; ++i) {
       if (i < nr) {
         const bool a = whole_bin ? key[i] >= blo : key[i] > bhi;
         const bool t = !whole_bin && key[i] == blo;
         const uint64_t ba = __ballot(a), bt = __ballot(t);
-        const uint32_t base = rbase[wave * SP_ROUNDS + i];
-        const uint32_t ap = (base >> 16) + sh_mbcnt(ba), tp = (base & 0xFFFFu) + sh_mbcnt(bt);
+        const uint32_t ai = ap + sh_mbcnt(ba), ti = tp + sh_mbcnt(bt);
         if (a) {
-          const uint32_t s = ap + min(tp, need);
-          if (s < (uint32_t)k) out[s] = (int32_t)pos[i];
-        } else if (t && tp < need) {
-          if (ap + tp < (uint32_t)k) out[ap + tp] = (int32_t)pos[i];
+          const uint32_t o = ai + min(ti, need);
+          if (o < (uint32_t)k) out[o] = (int32_t)pos[i];
+        } else if (t && ti < need) {
+          if (ai + ti < (uint32_t)k) out[ai + ti] = (int32_t)pos[i];
         }
+        ap += (uint32_t)__popcll(ba);
+        tp += (uint32_t)__popcll(bt);
       }
     }
     exact = false;
@@ -1497,7 +1465,7 @@ size_t topk_split_workspace_bytes(int B, int nrows, int Tk, int k) {
   if (B <= 0 || nrows <= 0 || Tk <= 64 * 96 || Tk > SEG || (int64_t)nrows * B >= 1024 ||
       (int64_t)((Tk + SP_SEG - 1) / SP_SEG) * (SP_CAP / 2) < 2 * (int64_t)k)
     return 0;
-  return (size_t)B * nrows * SP_MAXSEG * (SP_CAP + 1) * sizeof(uint2);  // lists, then (count, theta)
+  return (size_t)B * nrows * SP_MAXSEG * (SP_CAP * sizeof(uint2) + sizeof(uint4));  // lists, then meta words
 }
 
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
@@ -1517,7 +1485,7 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   } else if (topk_split_workspace_bytes(A.B, A.nrows, A.Tk, A.k) && A.ws && A.ld % 4 == 0 &&
              A.score_bstride % 4 == 0 && (reinterpret_cast<uintptr_t>(A.scores) & 15) == 0) {
     uint2* lists = reinterpret_cast<uint2*>(A.ws);
-    uint2* meta = lists + (size_t)A.B * A.nrows * SP_MAXSEG * SP_CAP;
+    uint4* meta = reinterpret_cast<uint4*>(lists + (size_t)A.B * A.nrows * SP_MAXSEG * SP_CAP);
     const int segs = (A.Tk + SP_SEG - 1) / SP_SEG;
     hipLaunchKernelGGL(topk_seg_kernel, dim3(segs, A.nrows, A.B), dim3(SP_NT), 0, st, A.scores, A.ld,
                        A.score_bstride, A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, lists, meta);
