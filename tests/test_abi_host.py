@@ -189,8 +189,8 @@ def test_index_topk_workspace_follows_the_route(L):
     fused = size(1, 65536, 65536, 16, 2048, dsa.OP_INDEX_TOPK)
     assert 65536 * (4096 * 4 + 6144 * 8) <= fused <= 65536 * (4096 * 4 + 6144 * 8 + 64) + 4096
     # few rows (decode): score chunks, then the split top-k's segment lists (16 segments of
-    # 1024 entries and a (count, theta) pair each, 8 bytes apiece)
-    lists = 64 * 16 * 1025 * 8
+    # 1024 entries of 8 bytes, and a 16-byte word each: list length, theta, largest key)
+    lists = 64 * 16 * (1024 * 8 + 16)
     assert size(64, 1, 65536, 16, 2048, dsa.OP_INDEX_TOPK) == 64 * 65536 * 4 + lists
     assert size(64, 1, 65536, 16, 2048, dsa.OP_TOPK) == lists
     # 2 indexer heads: score chunks (at most 1 GiB here)
@@ -209,8 +209,8 @@ def test_topk_workspace_sizes_and_checks(L):
         return L.dsa_workspace_size(ctypes.byref(shp), dsa.OP_TOPK)
 
     # split only for fewer than 1024 rows of 6145..65536 keys with room for 2k in the lists
-    assert size(64, 1, 65536, 2048) == 64 * 16 * 1025 * 8
-    assert size(3, 40, 65536, 4096) == 120 * 16 * 1025 * 8
+    assert size(64, 1, 65536, 2048) == 64 * 16 * (1024 * 8 + 16)
+    assert size(3, 40, 65536, 4096) == 120 * 16 * (1024 * 8 + 16)
     assert size(64, 1, 6144, 2048) == 0
     assert size(64, 1, 65537, 2048) == 0
     assert size(1, 1024, 65536, 2048) == 0
