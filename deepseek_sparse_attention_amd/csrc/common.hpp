@@ -78,6 +78,9 @@ __device__ __forceinline__ void buf_store1_b32(uint32_t v, u32x4 rs, uint32_t vo
 __device__ __forceinline__ void buf_store1_b64(u32x2 v, u32x4 rs, uint32_t voff) {
   asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(rs) : "memory");
 }
+__device__ __forceinline__ void buf_store1_b128(u32x4 v, u32x4 rs, uint32_t voff) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen" ::"v"(v), "v"(voff), "s"(rs) : "memory");
+}
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

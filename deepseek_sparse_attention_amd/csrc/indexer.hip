@@ -14,6 +14,12 @@ namespace {
 // wave_keys > 0 (launches with no more rows than one wave holds, e.g. decode): the four
 // waves share the same rows and split the workgroup's key segment, wave w taking keys
 // [w * wave_keys, (w + 1) * wave_keys) of it, so every wave streams keys.
+// A launch of one query tile per wave (QP 1: decode) with at least 8 heads stages its
+// scores in LDS and writes 1 KB of them at a time, 16 bytes per lane: stores and loads
+// share one in-order completion count, so the next key wait after a store covers the
+// store's write too, about 1 us per store burst on the 64 x 65536 decode keys (99.6 us
+// with a store per tile, 81.5 us with no stores at all); one row's scores fill 1 KB in
+// eight tiles.
 template <int H_I, int D_I, bool PAGED, int QP = idx_query_tiles<H_I, D_I>()>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ w,
@@ -63,17 +69,47 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
                    skey - rr <= pos0 ? off0 + (uint32_t)rr * row_bytes + (uint32_t)skey * 4u : kOffNone);
   };
   const int ntiles = (int)((seg_end - seg0 + 31) / 32);
-  if constexpr (PAGED) {
-    // tiles past the sequence (prefetch) clamp to its last table entry; a page id outside
-    // the pool reads zeros through the range check
-    const int32_t* btb = bt + (int64_t)b * max_blocks;
-    const int pmask = (1 << page_shift) - 1;
-    wv.template run<W::EPIS>(k_rs, wks[wave], ntiles, start, epi, [](int) {}, [&](int j) {
-      const int s0 = start(j);
-      return (btb[min(s0 >> page_shift, max_blocks - 1)] << page_shift) + (s0 & pmask);
-    });
+  // tiles past the sequence (prefetch) clamp to its last table entry; a page id outside
+  // the pool reads zeros through the range check
+  const int32_t* btb = PAGED ? bt + (int64_t)b * max_blocks : nullptr;
+  const int pmask = (1 << page_shift) - 1;
+  auto phys = [&](int j) {
+    const int s0 = start(j);
+    return PAGED ? (btb[min(s0 >> page_shift, max_blocks - 1)] << page_shift) + (s0 & pmask) : s0;
+  };
+  if constexpr (QP == 1 && W::QPT <= 4) {
+    // Scores of the wave's R real rows (its row count rounded up to a power of two) over G
+    // consecutive tiles, G = 8 / R (32 G keys), in LDS: row r of tile j at
+    // stg[wave][(r G + j % G) 32 + col] (lane group g holds rows g QPL .. g QPL + QPL - 1);
+    // flushed after the group's last tile, lane l writing keys 4 (l % 8G) .. +3 of row
+    // l / 8G: 1 KB per flush, 16 bytes per lane (rows past the wave's drop out of the range)
+    const int R = wrows <= 1 ? 1 : wrows <= 2 ? 2 : 4;  // (wrows <= QPT <= 4)
+    const int G = 8 / R;
+    __shared__ __attribute__((aligned(16))) float stg[4][256];
+    const int lane = threadIdx.x & 63, frow = lane / (8 * G), fk = 4 * (lane % (8 * G));
+    const int fpos = (int)(pos_base + wrow0) + frow;  // position of the flushed row
+    const int kend = s_first + 32 * ntiles;            // past the wave's last tile
+    auto epi1 = [&](int j, int, int, int qq, float tot) {
+      const int r = wv.g * W::QPL + qq;
+      if (r < R) stg[wave][(r * G + j % G) * 32 + col] = tot;
+    };
+    auto post1 = [&](int j) {
+      if (j % G != G - 1 && j != ntiles - 1) return;
+      const int key = start(j - j % G) + fk;  // this lane's first key (tiles are contiguous)
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&stg[wave][frow * 32 * G + fk]);
+      const uint32_t off = (uint32_t)frow * row_bytes + (uint32_t)key * 4u;
+      if (key + 3 <= fpos && key + 3 < kend) {
+        buf_store1_b128(v, s_rs, off);
+      } else {  // the causal edge, or a last group of fewer than G tiles: only computed keys
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_store1_b32(v[e], s_rs, key + e <= fpos && key + e < kend ? off + 4u * e : kOffNone);
+      }
+    };
+    // EPI_VM 0: a flush comes every G tiles, so no tile has a store to count on
+    wv.template run<0>(k_rs, wks[wave], ntiles, start, epi1, post1, phys);
   } else {
-    wv.template run<W::EPIS>(k_rs, wks[wave], ntiles, start, epi);
+    wv.template run<W::EPIS>(k_rs, wks[wave], ntiles, start, epi, [](int) {}, phys);
   }
 }
 
