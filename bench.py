@@ -453,10 +453,10 @@ def main():
     probe_ms = timed(gather_probe)
     probe_logical = attn_bytes / (probe_ms * 1e-3) / 1e9
     rbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-    rsum = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    rsum = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
 
     def read_probe():
-        rc = pl.probe_read(rbuf.data_ptr(), rbuf.numel() // 4, rsum.data_ptr(), 4096, stream.cuda_stream)
+        rc = pl.probe_read(rbuf.data_ptr(), rbuf.numel() // 4, rsum.data_ptr(), 1024, stream.cuda_stream)
         assert rc == 0, rc
 
     read_gbs = rbuf.numel() * 4 / (timed(read_probe) * 1e-3) / 1e9
