@@ -256,8 +256,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 1 : 4 / NW) void mla_attn_wk_ker
   // so the long rows keep the workgroups in step and the short ones fill the end; a
   // front-to-back walk let the workgroups that drew short rows run ahead, which widened
   // the window of rows in flight (T=65536: 12.8-13.1 ms against 11.9-12.4 reversed).
-  // Lists read in full (every row the same length) go front to back.
-  for (int64_t rwi = blockIdx.x; rwi < nrg; rwi += gridDim.x) {
+  // Lists read in full (every row the same length) go front to back.  Inside a full window
+  // of gridDim.x consecutive pairs, workgroup w takes slot (w % 8) * (gridDim.x / 8) + w / 8:
+  // workgroups are dispatched over the 8 XCDs round-robin, so each XCD's L2 then serves
+  // adjacent rows, whose top-k lists overlap most (T=65536 plain call, front to back:
+  // 12.13-12.17 against 12.65-12.75 ms with slot w; the layer stack's last-to-first walk
+  // 12.2 ms either way).  Partial windows keep slot w.
+  for (int64_t rwi0 = blockIdx.x; rwi0 < nrg; rwi0 += gridDim.x) {
+  const int64_t win0 = rwi0 - blockIdx.x;
+  const bool full = gridDim.x % 8 == 0 && win0 + gridDim.x <= nrg;
+  const int64_t rwi = full ? win0 + (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : rwi0;
   const int64_t rowh = tail_Tk > 0 ? nrg - 1 - rwi : rwi;
   const int64_t row = rowh / HG;
   const int hg = (int)(rowh % HG);
