@@ -14,13 +14,15 @@ namespace {
 // wave_keys > 0 (launches with no more rows than one wave holds, e.g. decode): the four
 // waves share the same rows and split the workgroup's key segment, wave w taking keys
 // [w * wave_keys, (w + 1) * wave_keys) of it, so every wave streams keys.
-// A launch of one query tile per wave (QP 1: decode) with at least 8 heads stages its
-// scores in LDS and writes 1 KB of them at a time, 16 bytes per lane: stores and loads
-// share one in-order completion count, so the next key wait after a store covers the
-// store's write too, about 1 us per store burst on the 64 x 65536 decode keys (99.6 us
-// with a store per tile, 81.5 us with no stores at all); one row's scores fill 1 KB in
-// eight tiles.
-template <int H_I, int D_I, bool PAGED, int QP = idx_query_tiles<H_I, D_I>()>
+// A launch of one query tile per wave (QP 1: decode) with at least 8 heads keeps its scores
+// out of the key stream: stores and loads share one in-order completion count, so the next
+// key wait after a store covers the store's write too (on the 64 x 65536 decode keys: 99.6
+// us with a store per tile, 81.5 us with no stores at all).  HOLD > 0 (the wave's rows x key
+// tiles fit HOLD): the wave keeps all its scores in LDS and writes them once its stream has
+// ended (91.0 us, two workgroups per CU for the LDS); otherwise it stages them in LDS and
+// writes 1 KB at a time, 16 bytes per lane, one row's scores every eight tiles (97.6-98.1
+// us, three workgroups per CU).
+template <int H_I, int D_I, bool PAGED, int QP = idx_query_tiles<H_I, D_I>(), int HOLD = 0>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0, int nrows, float* __restrict__ scores,
@@ -77,7 +79,38 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const int s0 = start(j);
     return PAGED ? (btb[min(s0 >> page_shift, max_blocks - 1)] << page_shift) + (s0 & pmask) : s0;
   };
-  if constexpr (QP == 1 && W::QPT <= 4) {
+  if constexpr (HOLD > 0) {
+    static_assert(QP == 1 && W::QPT <= 4, "held scores: one query tile per wave");
+    // row r of tile j at held[wave][(r ntiles + j) 32 + col]: each row's keys contiguous
+    // (the launch checks R * ntiles <= HOLD)
+    __shared__ __attribute__((aligned(16))) float held[4][HOLD * 32];
+    const int R = wrows <= 1 ? 1 : wrows <= 2 ? 2 : 4;
+    float* hw = held[wave];
+    auto epi1 = [&](int j, int, int, int qq, float tot) {
+      const int r = wv.g * W::QPL + qq;
+      if (r < R) hw[(r * ntiles + j) * 32 + col] = tot;
+    };
+    wv.template run<0>(k_rs, wks[wave], ntiles, start, epi1, [](int) {}, phys);
+    // (run ends with every key load done; this wave alone wrote hw, in program order)
+    const int lane = threadIdx.x & 63;
+    const int nchunk = 8 * ntiles;  // 16-byte chunks per row
+    const int kend = s_first + 32 * ntiles;
+    for (int r = 0; r < R; ++r) {
+      const int fpos = (int)(pos_base + wrow0) + r;  // rows past the wave's drop out of the range
+      for (int c = lane; c < nchunk; c += 64) {
+        const int key = s_first + 4 * c;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&hw[r * ntiles * 32 + 4 * c]);
+        const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)key * 4u;
+        if (key + 3 <= fpos && key + 3 < kend) {
+          buf_store1_b128(v, s_rs, off);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            buf_store1_b32(v[e], s_rs, key + e <= fpos && key + e < kend ? off + 4u * e : kOffNone);
+        }
+      }
+    }
+  } else if constexpr (QP == 1 && W::QPT <= 4) {
     // Scores of the wave's R real rows (its row count rounded up to a power of two) over G
     // consecutive tiles, G = 8 / R (32 G keys), in LDS: row r of tile j at
     // stg[wave][(r G + j % G) 32 + col] (lane group g holds rows g QPL .. g QPL + QPL - 1);
@@ -113,6 +146,10 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   }
 }
 
+// Held-score launches: tiles of scores per wave (R rows x tiles), workgroups per CU.
+constexpr int kIdxHoldTiles = 64;
+constexpr int kIdxHoldPerCu = 2;
+
 template <int H_I, int D_I>
 hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   const bool paged = A.block_table != nullptr;
@@ -131,31 +168,53 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
   // Aim at ~2048 workgroups per launch when query blocks are full (prefill chunks): twice
   // what the chip holds at once, with segments short enough that the causal tail of a launch
   // stays small.  Other few-row launches take ~1536.  A launch of one query tile (decode)
-  // streams its keys once with three workgroups per CU: one round of them, 768 on the 256
-  // CUs of MI355X (measured on the 64 x 65536 decode key cache: 99.0 us against 101.6 at
-  // 512, 104.3 at 640, 103.6 at 1024, 101.7 at 1536 and 104.9 at 2304).  With the waves
-  // splitting keys (one wave's rows) a segment is a multiple of four tiles.
-  const int64_t target = A.nrows >= 8 * QB ? 2048 : one_tile ? 3 * (int64_t)device_cus() : 1536;
-  int64_t segs = std::max<int64_t>(1, std::min<int64_t>(tiles, target / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
-  int64_t seg_tiles = (tiles + segs - 1) / segs;
-  if (wsplit) seg_tiles = (seg_tiles + 3) / 4 * 4;
-  segs = (tiles + seg_tiles - 1) / seg_tiles;
+  // streams its keys once, in one round of resident workgroups: 512 held-score workgroups
+  // (two per CU) when their scores fit, else 768 staging ones (three per CU; measured on the
+  // 64 x 65536 decode key cache before the held variant: 99.0 us against 101.6 at 512, 104.3
+  // at 640, 103.6 at 1024, 101.7 at 1536 and 104.9 at 2304).  With the waves splitting keys
+  // (one wave's rows) a segment is a multiple of four tiles.
+  auto plan = [&](int64_t target, int64_t& segs, int64_t& seg_tiles) {
+    segs = std::max<int64_t>(1, std::min<int64_t>(tiles, target / std::max<int64_t>(1, (int64_t)qblocks * A.B)));
+    seg_tiles = (tiles + segs - 1) / segs;
+    if (wsplit) seg_tiles = (seg_tiles + 3) / 4 * 4;
+    segs = (tiles + seg_tiles - 1) / seg_tiles;
+  };
+  int64_t segs, seg_tiles;
+  plan(A.nrows >= 8 * QB ? 2048 : one_tile ? 3 * (int64_t)device_cus() : 1536, segs, seg_tiles);
+  // A launch of one query tile whose waves' scores fit the held-score LDS runs the held
+  // variant instead: its LDS allows two workgroups per CU, so one round of them is 512.
+  bool hold = false;
+  if (one_tile && H_I >= 8 && D_I <= 64) {  // (128-wide keys: their tile buffers leave no room)
+    int64_t hsegs, htiles;
+    plan(kIdxHoldPerCu * (int64_t)device_cus(), hsegs, htiles);
+    const int64_t R = A.nrows <= 1 ? 1 : A.nrows <= 2 ? 2 : 4;
+    if (R * (htiles / 4) <= kIdxHoldTiles) {
+      hold = true;
+      segs = hsegs;
+      seg_tiles = htiles;
+    }
+  }
   const int wave_keys = wsplit ? (int)(seg_tiles / 4 * 32) : 0;
   dim3 grid(qblocks, (unsigned)segs, A.B);
-#define DSA_IDX_LAUNCH(PG, QP)                                                                                        \
-  hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, PG, QP>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, A.Tq, \
-                     A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys,      \
+#define DSA_IDX_LAUNCH(PG, QP, HOLD)                                                                                  \
+  hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, PG, QP, HOLD>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, \
+                     A.Tq, A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys, \
                      PG ? A.block_table : nullptr, PG ? A.max_blocks : 0, PG ? A.page_shift : 0,                    \
                      PG ? A.pool_tokens : (int64_t)0)
   constexpr int QPF = idx_query_tiles<H_I, D_I>();
-  if (paged && one_tile)
-    DSA_IDX_LAUNCH(true, 1);
+  constexpr int HT = H_I >= 8 && D_I <= 64 ? kIdxHoldTiles : 0;  // (a held instance only where it runs)
+  if (paged && hold)
+    DSA_IDX_LAUNCH(true, 1, HT);
+  else if (paged && one_tile)
+    DSA_IDX_LAUNCH(true, 1, 0);
   else if (paged)
-    DSA_IDX_LAUNCH(true, QPF);
+    DSA_IDX_LAUNCH(true, QPF, 0);
+  else if (hold)
+    DSA_IDX_LAUNCH(false, 1, HT);
   else if (one_tile)
-    DSA_IDX_LAUNCH(false, 1);
+    DSA_IDX_LAUNCH(false, 1, 0);
   else
-    DSA_IDX_LAUNCH(false, QPF);
+    DSA_IDX_LAUNCH(false, QPF, 0);
 #undef DSA_IDX_LAUNCH
   return hipGetLastError();
 }

@@ -35,7 +35,8 @@ import torch
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "tensor_seed", "normal", "bf16", "fp8_e4m3_rows", "mxfp4_rows",
-    "rope_half_split", "layer_inputs", "integer_indexer_inputs", "sharp_attention_inputs",
+    "rope_half_split", "layer_inputs", "integer_indexer_inputs", "integer_query_rows_inputs",
+    "sharp_attention_inputs",
     "decode_layer_inputs", "decode_indexer_cache",
 ]
 
@@ -207,6 +208,18 @@ def integer_indexer_inputs(B, T, H_I, d_I, seed, device="cpu", qk_max=1, w_max=2
     q = torch.randint(-qk_max, qk_max + 1, (B, T, H_I, d_I), generator=g, device=device)
     k = torch.randint(-qk_max, qk_max + 1, (B, T, d_I), generator=g, device=device)
     wt = torch.randint(-w_max, w_max + 1, (B, T, H_I), generator=g, device=device)
+    return {"q_idx": q.to(torch.bfloat16), "k_idx": k.to(torch.bfloat16), "w_idx": wt.to(torch.bfloat16)}
+
+
+def integer_query_rows_inputs(B, Tq, Tk, H_I, d_I, seed, qk_max=1, w_max=2):
+    """Integer-valued indexer inputs with Tq query rows against Tk keys per sequence (the
+    few-row shapes of decode, at many sequences or long caches): q [B,Tq,H_I,d_I], k
+    [B,Tk,d_I], w [B,Tq,H_I], drawn as int8 on the CPU (cheap at hundreds of MB of keys)."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    q = torch.randint(-qk_max, qk_max + 1, (B, Tq, H_I, d_I), generator=g, dtype=torch.int8)
+    k = torch.randint(-qk_max, qk_max + 1, (B, Tk, d_I), generator=g, dtype=torch.int8)
+    wt = torch.randint(-w_max, w_max + 1, (B, Tq, H_I), generator=g, dtype=torch.int8)
     return {"q_idx": q.to(torch.bfloat16), "k_idx": k.to(torch.bfloat16), "w_idx": wt.to(torch.bfloat16)}
 
 

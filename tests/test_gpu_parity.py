@@ -85,6 +85,27 @@ def test_indexer_few_rows_integer_inputs_bit_exact(d_I, Tq, Tk):
     assert np.all(np.isneginf(got[~c]))  # written -inf by the library
 
 
+@pytest.mark.parametrize("B,Tq,Tk", [(520, 1, 8192), (520, 1, 8300), (260, 2, 4000), (260, 2, 4300)])
+def test_indexer_one_tile_launch_held_and_flushed_scores(B, Tq, Tk):
+    # One query tile per wave (one or two rows per sequence): a wave whose rows x key tiles
+    # fit 64 keeps its scores in LDS until its key stream ends, a longer one writes them 1 KB
+    # at a time.  On 256 CUs the launch gives each wave 64 tiles at (520, 1, 8192) and 32 at
+    # (260, 2, 4000), both held at the limit, and 65 and 34 one past it.  Sampled sequences
+    # against the oracle, bit-exact; ragged lengths on some.
+    print(f"indexer one-tile launch B={B} Tq={Tq} Tk={Tk}", flush=True)
+    d = synth.integer_query_rows_inputs(B, Tq, Tk, 16, 64, seed=B + Tq + Tk)
+    kv_len = [Tk - (b % 5) * 97 for b in range(B)]
+    kl = torch.tensor(kv_len, dtype=torch.int32, device=DEV)
+    got = dsa.index_scores(d["q_idx"].to(DEV), d["k_idx"].to(DEV), d["w_idx"].to(DEV), kv_len=kl)
+    for b in (0, 1, B // 2 + 3, B - 1):
+        ref = oracle.index_scores(d["q_idx"][b:b + 1], d["k_idx"][b:b + 1], d["w_idx"][b:b + 1],
+                                  kv_len=[kv_len[b]])
+        g = _host(got[b:b + 1]).numpy()
+        c = _causal(1, Tq, Tk, [kv_len[b]])
+        assert np.array_equal(g[c], ref[c]), b
+        assert np.all(np.isneginf(g[~c])), b
+
+
 @pytest.mark.parametrize("key,T", [("A", 3072), ("B", 2057), ("D", 700)])
 def test_indexer_scores_within_tolerance(key, T):
     print(f"indexer workload {key} T={T}", flush=True)
