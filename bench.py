@@ -131,7 +131,7 @@ def summarize_mfma(pmc_csv, trace_csv, out_path=MFMA_FILE):
     for r in csv.DictReader(open(pmc_csv)):
         name = r["Kernel_Name"]
         key = ("fz_filter_kernel<16, 64>" if "fz_filter_kernel<16, 64>" in name else
-               "index_scores_kernel<16, 64, false, 4>" if "index_scores_kernel<16, 64, false, 4>" in name else None)
+               "index_scores_kernel<16, 64, false, 4, 0>" if "index_scores_kernel<16, 64, false, 4, 0>" in name else None)
         if key is None:
             continue
         agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
@@ -145,7 +145,7 @@ def summarize_mfma(pmc_csv, trace_csv, out_path=MFMA_FILE):
         "# flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; rate = flop / the dispatches' summed duration;",
         "# algorithmic indexer work of one layer: 2 x 16 x 64 x T(T+1)/2 = 4.398e12 flop",
     ]
-    for key in ("fz_filter_kernel<16, 64>", "index_scores_kernel<16, 64, false, 4>"):
+    for key in ("fz_filter_kernel<16, 64>", "index_scores_kernel<16, 64, false, 4, 0>"):
         if key not in agg:
             continue
         c, ids = agg[key], seen[key]
@@ -197,9 +197,10 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# attention launches, then the KL objective (sparse and dense, with gradients).",
         "# mla_attn_wk_kernel<f, waves>: latent rows f = 0 bf16, 1 fp8, 2 MXFP4, four waves per row;",
         "# topk_seg_kernel + topk_merge_kernel: the decode rows' split top-k (segment lists, merge);",
-        "# index_scores_kernel<H_I, d_I, paged, query tiles per wave>.  grid = threads of the launch",
-        "# (the 64-row decode: grouped 3-layer attention 49152, one layer in 4 key splits 65536;",
-        "# decode indexer 196608)",
+        "# index_scores_kernel<H_I, d_I, paged, query tiles per wave, held score tiles per wave (0:",
+        "# staged and written during the key stream)>.  grid = threads of the launch (the 64-row",
+        "# decode: grouped 3-layer attention 49152, one layer in 4 key splits 65536; decode indexer",
+        "# 131072)",
         "# columns: calls, average us, min us, max us, total ms, % of all GPU time, kernel, grid",
         "",
     ]
