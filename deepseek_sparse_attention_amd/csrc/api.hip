@@ -96,9 +96,16 @@ dsa_status run_index_topk(const IndexTopkPlan& P, const void* q_idx, const void*
     } else {
       const int64_t ld = stack_ld(s.Tk);
       float* scores = reinterpret_cast<float*>(ws);
+      dsa::TopkArgs ta{scores, ld, (int64_t)P.rows * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, idx,
+                       P.split_off ? reinterpret_cast<char*>(ws) + P.split_off : nullptr};
       if (s.Tk > 0) {
         dsa::IndexerArgs ia{(const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w_idx, s.kv_len,
                             s.B, s.Tq, s.Tk, s.H_I, s.d_I, r0, n, scores, ld, (int64_t)P.rows * ld};
+        if (dsa::topk_split_route(ta)) {  // the indexer may build the top-k's segment lists
+          ia.topk_ws = ta.ws;
+          ia.topk_k = s.k;
+          ia.lists_made = &ta.lists_ready;
+        }
         if (pages) {  // k_idx is a key pool (the fused route is never planned for pools)
           ia.block_table = pages->block_table;
           ia.max_blocks = pages->max_blocks;
@@ -109,8 +116,6 @@ dsa_status run_index_topk(const IndexTopkPlan& P, const void* q_idx, const void*
         if (st != DSA_OK) return st;
       }
       // (no keys at all: every row selects nothing, and top-k reads no score)
-      dsa::TopkArgs ta{scores, ld, (int64_t)P.rows * ld, s.kv_len, s.B, s.Tq, s.Tk, s.k, r0, n, idx,
-                       P.split_off ? reinterpret_cast<char*>(ws) + P.split_off : nullptr};
       dsa_status st = launch_status(dsa::launch_topk(ta, strm), who);
       if (st != DSA_OK) return st;
     }

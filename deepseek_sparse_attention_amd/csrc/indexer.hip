@@ -4,6 +4,7 @@
 // workgroup (4 waves) covers a block of queries against one segment of keys.
 #include "indexer_core.hpp"
 #include "internal.hpp"
+#include "seglist.hpp"
 
 namespace dsa {
 
@@ -22,12 +23,15 @@ namespace {
 // ended (91.0 us, two workgroups per CU for the LDS); otherwise it stages them in LDS and
 // writes 1 KB at a time, 16 bytes per lane, one row's scores every eight tiles (97.6-98.1
 // us, three workgroups per CU).
+// sp_lists (held launches of one row per sequence, key_seg one or two top-k segments): the
+// workgroup also builds the split top-k's segment lists and meta words (seglist.hpp) for
+// its key range from the scores it holds, so that the top-k that follows is the merge alone.
 template <int H_I, int D_I, bool PAGED, int QP = idx_query_tiles<H_I, D_I>(), int HOLD = 0>
 __global__ __launch_bounds__(256, 2) void index_scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ kv_len, int Tq, int Tk, int row0, int nrows, float* __restrict__ scores,
     int64_t ld, int64_t score_bstride, int key_seg, int wave_keys, const int32_t* __restrict__ bt, int max_blocks,
-    int page_shift, int64_t pool_tokens) {
+    int page_shift, int64_t pool_tokens, uint2* __restrict__ sp_lists, int sp_k) {
   using W = IdxWave<H_I, D_I, QP, QP == 1>;  // one query tile per wave: keys read once
   constexpr int QB = 4 * W::ROWS;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t wks[4][W::kLdsBytes];
@@ -41,7 +45,12 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
   const int wrows = min(W::ROWS, nrows - wrow0);
   const int64_t pmax = pos_base + wrow0 + wrows - 1;  // last position of this wave
   const int64_t seg0 = (int64_t)blockIdx.y * key_seg + (wsplit ? (int64_t)wave * wave_keys : 0);
-  if (pmax < 0 || seg0 > pmax) return;
+  // segment lists: a row that takes them (one row: the launch passes lists only then), and a
+  // workgroup whose key range starts inside it; every wave then stays for the lists' barriers
+  const int64_t wg_key0 = (int64_t)blockIdx.y * key_seg;
+  const bool lists = HOLD > 0 && sp_lists != nullptr && pmax >= wg_key0 && sp_uses_lists((int)min<int64_t>(pmax + 1, SP_ROW_MAX + 1), sp_k);
+  const bool live = !(pmax < 0 || seg0 > pmax);
+  if (!live && !lists) return;
   const int64_t seg_end = min((int64_t)min((int64_t)Tk, seg0 + (wsplit ? wave_keys : key_seg)), pmax + 1);
 
   W wv;
@@ -90,10 +99,10 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
       const int r = wv.g * W::QPL + qq;
       if (r < R) hw[(r * ntiles + j) * 32 + col] = tot;
     };
-    wv.template run<0>(k_rs, wks[wave], ntiles, start, epi1, [](int) {}, phys);
+    if (live) wv.template run<0>(k_rs, wks[wave], ntiles, start, epi1, [](int) {}, phys);
     // (run ends with every key load done; this wave alone wrote hw, in program order)
     const int lane = threadIdx.x & 63;
-    const int nchunk = 8 * ntiles;  // 16-byte chunks per row
+    const int nchunk = live ? 8 * ntiles : 0;  // 16-byte chunks per row
     const int kend = s_first + 32 * ntiles;
     for (int r = 0; r < R; ++r) {
       const int fpos = (int)(pos_base + wrow0) + r;  // rows past the wave's drop out of the range
@@ -108,6 +117,47 @@ __global__ __launch_bounds__(256, 2) void index_scores_kernel(
           for (int e = 0; e < 4; ++e)
             buf_store1_b32(v[e], s_rs, key + e <= fpos && key + e < kend ? off + 4u * e : kOffNone);
         }
+      }
+    }
+    if constexpr (4 * W::kLdsBytes >= 2 * sizeof(SpScratch)) {
+      if (lists) {
+        // one row (wrows 1): the workgroup's scores, key wg_key0 + w * wave_keys + o at
+        // held[w][o], become the keys of its one or two segments; the key tile buffers, free
+        // once every wave's stream has ended, hold the selection's LDS
+        __syncthreads();
+        SpScratch* sc = reinterpret_cast<SpScratch*>(&wks[0][0]);
+        const int n = (int)(pmax + 1);
+        const int S = (n + SP_SEG - 1) / SP_SEG;
+        uint4* meta = reinterpret_cast<uint4*>(sp_lists + (int64_t)gridDim.z * nrows * SP_MAXSEG * SP_CAP);
+        auto build = [&](auto nseg_tag) {
+          constexpr int NSEG = decltype(nseg_tag)::value;
+          uint32_t key[NSEG][16];
+          int nv[NSEG], s0[NSEG];
+          uint2* lst[NSEG];
+          uint4* mt[NSEG];
+          const int tid = threadIdx.x;
+#pragma unroll
+          for (int g = 0; g < NSEG; ++g) {
+            s0[g] = (int)wg_key0 + g * SP_SEG;
+            nv[g] = max(0, min(SP_SEG, n - s0[g]));
+            const int64_t slot = ((int64_t)b * nrows + wrow0) * SP_MAXSEG + s0[g] / SP_SEG;
+            lst[g] = sp_lists + slot * SP_CAP;
+            mt[g] = meta + slot;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rel = g * SP_SEG + 1024 * i + 4 * tid;  // (a multiple of 4: one wave's range)
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&held[rel / wave_keys][rel % wave_keys]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                key[g][4 * i + e] = (1024 * i + 4 * tid + e < nv[g]) ? sel_key(__uint_as_float(v[e])) : 0u;
+            }
+          }
+          sp_make_lists<NSEG>(key, nv, s0, S, sp_k, lst, mt, sc);
+        };
+        if (key_seg == 2 * SP_SEG)
+          build(std::integral_constant<int, 2>{});
+        else
+          build(std::integral_constant<int, 1>{});
       }
     }
   } else if constexpr (QP == 1 && W::QPT <= 4) {
@@ -195,12 +245,18 @@ hipError_t launch_t(const IndexerArgs& A, hipStream_t st) {
     }
   }
   const int wave_keys = wsplit ? (int)(seg_tiles / 4 * 32) : 0;
+  // the split top-k's segment lists, built by held workgroups of one row per sequence whose
+  // key range is one or two whole segments (their LDS must hold two segments' selection)
+  const bool lists = hold && A.topk_ws != nullptr && A.topk_k > 0 && A.nrows == 1 && D_I >= 32 &&
+                     A.Tk <= SP_ROW_MAX && (seg_tiles * 32 == SP_SEG || seg_tiles * 32 == 2 * SP_SEG);
+  if (A.lists_made) *A.lists_made = lists;
+  uint2* sp_lists = lists ? reinterpret_cast<uint2*>(A.topk_ws) : nullptr;
   dim3 grid(qblocks, (unsigned)segs, A.B);
 #define DSA_IDX_LAUNCH(PG, QP, HOLD)                                                                                  \
   hipLaunchKernelGGL((index_scores_kernel<H_I, D_I, PG, QP, HOLD>), grid, dim3(256), 0, st, A.q, A.k, A.w, A.kv_len, \
                      A.Tq, A.Tk, A.row0, A.nrows, A.scores, A.ld, A.score_bstride, (int)(seg_tiles * 32), wave_keys, \
                      PG ? A.block_table : nullptr, PG ? A.max_blocks : 0, PG ? A.page_shift : 0,                    \
-                     PG ? A.pool_tokens : (int64_t)0)
+                     PG ? A.pool_tokens : (int64_t)0, sp_lists, A.topk_k)
   constexpr int QPF = idx_query_tiles<H_I, D_I>();
   constexpr int HT = H_I >= 8 && D_I <= 64 ? kIdxHoldTiles : 0;  // (a held instance only where it runs)
   if (paged && hold)

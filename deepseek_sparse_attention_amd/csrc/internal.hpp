@@ -24,6 +24,13 @@ struct IndexerArgs {
   const int32_t* block_table = nullptr;
   int max_blocks = 0, page_shift = 0;
   int64_t pool_tokens = 0;
+  // optional: the split top-k's workspace (topk_split_workspace_bytes of B, nrows, Tk,
+  // topk_k) for a launch whose rows take that route; a launch of one query row per
+  // sequence that holds its scores in LDS then also builds the segment lists there and sets
+  // *lists_made (else leaves it false)
+  void* topk_ws = nullptr;
+  int topk_k = 0;
+  bool* lists_made = nullptr;
 };
 constexpr int64_t kIndexerMaxLd = int64_t(1) << 22;
 bool indexer_supported(int H_I, int d_I, int64_t ld);
@@ -46,8 +53,13 @@ struct TopkArgs {
   // optional workspace of topk_split_workspace_bytes(): few long rows then split each row
   // over the chip (segment lists, then a merge per row); null keeps one workgroup per row
   void* ws = nullptr;
+  // the segment lists in ws were built by the launch that wrote the scores (the decode
+  // indexer): only the merge runs; only with the split route
+  bool lists_ready = false;
 };
 size_t topk_split_workspace_bytes(int B, int nrows, int Tk, int k);
+// Whether launch_topk splits A's rows over the chip (segment lists in A.ws, then a merge).
+bool topk_split_route(const TopkArgs& A);
 constexpr int kTopkMaxK = 4096;
 constexpr int64_t kTopkMaxTk = int64_t(1) << 24;
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);

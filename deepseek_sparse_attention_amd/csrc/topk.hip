@@ -17,6 +17,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 #include "selection.hpp"
+#include "seglist.hpp"
 
 namespace dsa {
 
@@ -1146,12 +1147,8 @@ __global__ __launch_bounds__(64 * SH_NW) void topk_short_kernel(const float* __r
 // Split top-k for few long rows (decode: a few dozen rows of up to 65536 keys), so that a
 // row's load and selection spread over the chip instead of one CU.
 //
-// topk_seg_kernel: one 256-thread workgroup per 4096-position segment of a row lists every
-// key >= theta_j of its segment in position order, theta_j chosen so that the list holds
-// at least c = ceil(2k / S) keys (S = the row's segments) and at most SP_CAP: the lower
-// edge of the histogram bin of its c-th largest key (a second pass inside that bin if the
-// first overshoots).  A segment of at most SP_CAP keys lists all of them (theta 0).  Its
-// meta word holds the list's length, theta_j and the segment's largest key.
+// topk_seg_kernel: one 256-thread workgroup per 4096-position segment of a row builds the
+// segment's list and meta word (seglist.hpp).
 // topk_merge_kernel: one workgroup per row, wave j holding segment j's list.  With
 // theta = max_j theta_j, the k best entries (score, then lower position) among the listed
 // keys >= theta are the row's k best whenever at least k listed keys are >= theta: the
@@ -1161,31 +1158,17 @@ __global__ __launch_bounds__(64 * SH_NW) void topk_short_kernel(const float* __r
 // too).  Rows where this fails, a list overflowed (a bin of one value held by more than
 // SP_CAP keys) or the row is too short for lists (S < 4k / SP_CAP) take the one-workgroup
 // kernel's path instead, so the output is the one-workgroup result in every case.
-constexpr int SP_SEG = 4096;                // positions per segment
-constexpr int SP_NT = 256;                  // segment workgroup: 16 keys per thread
-constexpr int SP_CAP = 1024;                // list entries per segment
-constexpr int SP_MAXSEG = SEG / SP_SEG;     // segments per row, at most 16
+static_assert(SP_ROW_MAX == SEG, "a row the lists serve fits the one-workgroup kernel");
 constexpr int SP_ROUNDS = SP_MAXSEG * SP_CAP / NT;  // union entries per merge thread
-constexpr uint32_t SP_OVERFLOW = 0xFFFFFFFFu;
 constexpr int SP_SPEC = 6;                  // list rounds the merge loads before it knows the length
 constexpr int SP_PASSES = 3;                // radix passes over 32-bit keys (11 + 11 + 10 bits)
-
-// Rows that use segment lists: every segment can hold its share of twice k.
-__device__ __forceinline__ bool sp_uses_lists(int n, int k) {
-  const int S = (n + SP_SEG - 1) / SP_SEG;
-  return S * (SP_CAP / 2) >= 2 * k && n > k;
-}
 
 __global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict__ scores, int64_t ld,
                                                          int64_t score_bstride, const int32_t* __restrict__ kv_len,
                                                          int Tq, int Tk, int k, int row0, int nrows,
                                                          uint2* __restrict__ lists, uint4* __restrict__ meta) {
-  constexpr int SW = SP_NT / 64;
-  __shared__ uint32_t hist[kSelPadBins];
-  __shared__ uint32_t red[2 * SW];
-  __shared__ uint32_t cnt[3 * SW];
-  __shared__ uint32_t state[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  __shared__ SpScratch sc[1];
+  const int tid = threadIdx.x;
   const int j = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int64_t p = seq_len(kv_len, b, Tk) - Tq + row0 + r;
   if (p + 1 > SEG || !sp_uses_lists((int)(p + 1), k)) return;  // the merge kernel's own path
@@ -1200,121 +1183,17 @@ __global__ __launch_bounds__(SP_NT) void topk_seg_kernel(const float* __restrict
   // past the row read 0 through the range check and get key 0 ("none")
   const float* row = scores + (int64_t)b * score_bstride + (int64_t)r * ld + s0;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (uint32_t)nv * 4u);
-  uint32_t key[16];
+  uint32_t key[1][16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 v = buf_load_16(rs, (uint32_t)(16 * tid), (uint32_t)(4096 * i));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) key[4 * i + e] = (1024 * i + 4 * tid + e < nv) ? sel_key(__uint_as_float(v[e])) : 0u;
+    for (int e = 0; e < 4; ++e) key[0][4 * i + e] = (1024 * i + 4 * tid + e < nv) ? sel_key(__uint_as_float(v[e])) : 0u;
   }
-
-  uint32_t theta = 1u;  // every valid key (keys are >= 1)
-  if (nv > SP_CAP) {
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      kmin = min(kmin, key[e] - 1u);  // 0 wraps to the top and drops out
-      kmax = max(kmax, key[e]);
-    }
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    if (lane == 0) {
-      red[wave] = kmin;
-      red[SW + wave] = kmax;
-    }
-    for (int i = tid; i < kSelPadBins; i += SP_NT) hist[i] = 0;
-    __syncthreads();
-    uint32_t lo = red[0], hi = red[SW];
-#pragma unroll
-    for (int w = 1; w < SW; ++w) {
-      lo = min(lo, red[w]);
-      hi = max(hi, red[SW + w]);
-    }
-    lo += 1u;
-    int sh = sel_shift(lo, hi);
-    uint32_t need = (uint32_t)((2 * k + S - 1) / S), taken = 0, count;
-    for (;;) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (key[e] >= lo && key[e] <= hi) atomicAdd(&hist[sel_pad((key[e] - lo) >> sh)], 1u);
-      __syncthreads();
-      if (wave == 0) {
-        uint32_t bin, above;
-        wave_find_bin_padded(hist, need, bin, above);
-        if (lane == 0) {
-          state[0] = bin;
-          state[1] = above;
-          state[2] = hist[sel_pad(bin)];
-        }
-      }
-      __syncthreads();
-      const uint32_t bin = state[0], above = state[1], m = state[2];
-      const uint32_t blo = lo + (bin << sh);
-      count = taken + above + m;
-      if (count <= (uint32_t)SP_CAP || sh == 0) {
-        theta = blo;
-        break;
-      }
-      // the bin overshoots the list: split it
-      taken += above;
-      need -= above;
-      hi = (uint32_t)min((uint64_t)blo + ((1u << sh) - 1u), (uint64_t)hi);
-      lo = blo;
-      sh = max(0, sh - BIN_BITS);
-      for (int i = tid; i < kSelPadBins; i += SP_NT) hist[i] = 0;
-      __syncthreads();
-    }
-    if (count > (uint32_t)SP_CAP) {  // one key value held by too many positions
-      if (tid == 0) meta[slot] = make_uint4(SP_OVERFLOW, 0u, 0u, 0u);
-      return;
-    }
-  }
-
-  // the list in position order (i, then t, then e): per-thread counts of rounds 0/1 and
-  // 2/3 packed in 16-bit fields (block totals <= 1024), one block scan each
-  uint32_t c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[i] = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c[i] += key[4 * i + e] >= theta;
-  }
-  const uint32_t pk01 = c[0] | (c[1] << 16), pk23 = c[2] | (c[3] << 16);
-  uint32_t w01, w23, kx = 0;
-  const uint32_t in01 = wave_incl_scan_u32(pk01, &w01), in23 = wave_incl_scan_u32(pk23, &w23);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) kx = max(kx, key[e]);
-  kx = wave_max_u32(kx);
-  if (lane == 0) {
-    cnt[wave] = w01;
-    cnt[SW + wave] = w23;
-    cnt[2 * SW + wave] = kx;
-  }
-  __syncthreads();
-  uint32_t pre01 = 0, pre23 = 0, tot01 = 0, tot23 = 0, segmax = 0;
-#pragma unroll
-  for (int w = 0; w < SW; ++w) {
-    pre01 += w < wave ? cnt[w] : 0u;
-    pre23 += w < wave ? cnt[SW + w] : 0u;
-    tot01 += cnt[w];
-    tot23 += cnt[SW + w];
-    segmax = max(segmax, cnt[2 * SW + w]);
-  }
-  const uint32_t ex01 = pre01 + in01 - pk01, ex23 = pre23 + in23 - pk23;
-  const uint32_t T0 = tot01 & 0xFFFFu, T1 = tot01 >> 16, T2 = tot23 & 0xFFFFu, T3 = tot23 >> 16;
-  uint32_t base[4] = {ex01 & 0xFFFFu, T0 + (ex01 >> 16), T0 + T1 + (ex23 & 0xFFFFu), T0 + T1 + T2 + (ex23 >> 16)};
-  uint2* lst = lists + slot * SP_CAP;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (key[4 * i + e] >= theta) {
-        lst[base[i]] = make_uint2(key[4 * i + e], (uint32_t)(s0 + 1024 * i + 4 * tid + e));
-        ++base[i];
-      }
-    }
-  }
-  if (tid == 0) meta[slot] = make_uint4(T0 + T1 + T2 + T3, nv > SP_CAP ? theta : 0u, segmax, 0u);
+  const int nvs[1] = {nv}, s0s[1] = {s0};
+  uint2* lst[1] = {lists + slot * SP_CAP};
+  uint4* mt[1] = {meta + slot};
+  sp_make_lists<1>(key, nvs, s0s, S, k, lst, mt, sc);
 }
 
 __global__ __launch_bounds__(NT, 1) void topk_merge_kernel(const float* __restrict__ scores, int64_t ld,
@@ -1468,8 +1347,14 @@ size_t topk_split_workspace_bytes(int B, int nrows, int Tk, int k) {
   return (size_t)B * nrows * SP_MAXSEG * (SP_CAP * sizeof(uint2) + sizeof(uint4));  // lists, then meta words
 }
 
+bool topk_split_route(const TopkArgs& A) {
+  return A.nrows > 0 && A.B > 0 && A.Tk > 64 * 96 && topk_split_workspace_bytes(A.B, A.nrows, A.Tk, A.k) && A.ws &&
+         A.ld % 4 == 0 && A.score_bstride % 4 == 0 && (reinterpret_cast<uintptr_t>(A.scores) & 15) == 0;
+}
+
 hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
   if (A.nrows <= 0 || A.B <= 0) return hipSuccess;
+  if (A.lists_ready && !topk_split_route(A)) return hipErrorInvalidValue;
   dim3 grid(A.nrows, A.B);
   // rows see at most Tk keys.  Up to 6144: a wave per row.  Up to one segment (65536) they
   // stay in registers: many rows take the streaming kernel (256 threads, four rows per CU),
@@ -1482,13 +1367,13 @@ hipError_t launch_topk(const TopkArgs& A, hipStream_t st) {
     else
       hipLaunchKernelGGL(topk_short_kernel<96>, g2, dim3(64 * SH_NW), 0, st, A.scores, A.ld, A.score_bstride,
                          A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, A.idx);
-  } else if (topk_split_workspace_bytes(A.B, A.nrows, A.Tk, A.k) && A.ws && A.ld % 4 == 0 &&
-             A.score_bstride % 4 == 0 && (reinterpret_cast<uintptr_t>(A.scores) & 15) == 0) {
+  } else if (topk_split_route(A)) {
     uint2* lists = reinterpret_cast<uint2*>(A.ws);
     uint4* meta = reinterpret_cast<uint4*>(lists + (size_t)A.B * A.nrows * SP_MAXSEG * SP_CAP);
     const int segs = (A.Tk + SP_SEG - 1) / SP_SEG;
-    hipLaunchKernelGGL(topk_seg_kernel, dim3(segs, A.nrows, A.B), dim3(SP_NT), 0, st, A.scores, A.ld,
-                       A.score_bstride, A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, lists, meta);
+    if (!A.lists_ready)  // (else the scores' producer built them)
+      hipLaunchKernelGGL(topk_seg_kernel, dim3(segs, A.nrows, A.B), dim3(SP_NT), 0, st, A.scores, A.ld,
+                         A.score_bstride, A.kv_len, A.Tq, A.Tk, A.k, A.row0, A.nrows, lists, meta);
     hipLaunchKernelGGL(topk_merge_kernel, grid, dim3(NT), 0, st, A.scores, A.ld, A.score_bstride, A.kv_len, A.Tq,
                        A.Tk, A.k, A.row0, A.nrows, lists, meta, A.idx);
   } else if (A.Tk <= SEG && (int64_t)A.nrows * A.B >= 1024)

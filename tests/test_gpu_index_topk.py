@@ -109,3 +109,52 @@ def test_layer_stack_fused_and_unfused_agree():
         assert torch.equal(x, y)
     s2 = dsa.index_scores(layers[2]["q_idx"], layers[2]["k_idx"], layers[2]["w_idx"])
     assert np.array_equal(_host(a[2]).numpy(), oracle.topk(_host(s2).numpy(), w.k))
+
+
+def _decode_lists_check(q, kk, w, k, kv_len, rows):
+    # index_topk on one query row per sequence takes the score route; where the held decode
+    # indexer builds the split top-k's segment lists itself, the indices must still equal
+    # the oracle's top-k on the GPU's score rows (sampled sequences) and, on every row, the
+    # one-workgroup top-k of those rows and the segment-kernel route
+    B, Tk = q.shape[0], kk.shape[1]
+    kl = torch.tensor(kv_len, dtype=torch.int32, device=DEV)
+    got = dsa.index_topk(q, kk, w, k, kv_len=kl)
+    s = dsa.index_scores(q, kk, w, kv_len=kl)
+    assert torch.equal(got, dsa.topk(s, k, kv_len=kl, split=False))
+    assert torch.equal(got, dsa.topk(s, k, kv_len=kl))
+    for b in rows:
+        ref = oracle.topk(_host(s[b:b + 1]).numpy(), k, kv_len=[kv_len[b]], Tk=Tk)
+        assert np.array_equal(_host(got[b:b + 1]).numpy(), ref), b
+
+
+@pytest.mark.parametrize("B,Tk,k", [(64, 65536, 2048), (64, 32768, 2048), (256, 8192, 512)])
+def test_decode_index_topk_lists_from_the_indexer(B, Tk, k):
+    # on 256 CUs: two segments per indexer workgroup at (64, 65536), one at the other two;
+    # ragged lengths put some rows' last segments in part of a workgroup, and some rows
+    # too short for lists (the merge's one-workgroup path)
+    print(f"decode index_topk lists B={B} Tk={Tk} k={k}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(B + Tk + k)
+    q = (torch.randn(B, 1, 16, 64, generator=g) / 8).to(torch.bfloat16).to(DEV)
+    kk = (torch.randn(B, Tk, 64, generator=g) / 8).to(torch.bfloat16).to(DEV)
+    w = torch.randn(B, 1, 16, generator=g).to(torch.bfloat16).to(DEV)
+    kv_len = [Tk - (b % 7) * 1111 for b in range(B)]
+    kv_len[1] = k + 1
+    kv_len[2] = Tk - 4091  # a last segment of 5 keys
+    _decode_lists_check(q, kk, w, k, kv_len, rows=(0, 1, 2, 3, B - 1))
+
+
+def test_decode_index_topk_lists_cannot_decide_or_overflow():
+    # scores rising with position put a row's whole top-k in its last segments, so the
+    # lists' union above the largest segment threshold holds fewer than k keys (the merge
+    # redoes the row); small-integer scores give one value to thousands of keys, so lists
+    # overflow.  Half the sequences each.
+    print("decode index_topk lists: rising scores and massive ties", flush=True)
+    B, Tk, k = 64, 65536, 2048
+    d = synth.integer_query_rows_inputs(B, 1, Tk, 16, 64, seed=4242)
+    q, kk, w = d["q_idx"].clone(), d["k_idx"].clone(), d["w_idx"].clone()
+    ramp = (torch.arange(Tk, dtype=torch.float32) / Tk).to(torch.bfloat16)
+    kk[: B // 2] = ramp[None, :, None].expand(B // 2, Tk, 64)
+    q[: B // 2] = 1
+    w[: B // 2] = 1
+    kv_len = [Tk - (b % 3) * 4000 for b in range(B)]
+    _decode_lists_check(q.to(DEV), kk.to(DEV), w.to(DEV), k, kv_len, rows=(0, 5, B // 2, B - 1))
