@@ -196,7 +196,8 @@ def summarize_stats(stats_csv, out_path=STATS_FILE):
         "# unfused step), then the decode steps and the bench's timings of their parts, the per-layer",
         "# attention launches, then the KL objective (sparse and dense, with gradients).",
         "# mla_attn_wk_kernel<f, waves>: latent rows f = 0 bf16, 1 fp8, 2 MXFP4, four waves per row;",
-        "# topk_seg_kernel + topk_merge_kernel: the decode rows' split top-k (segment lists, merge);",
+        "# topk_seg_kernel + topk_merge_kernel: the decode rows' split top-k (segment lists, merge;",
+        "# inside the decode step the held indexer builds the lists and the merge runs alone);",
         "# index_scores_kernel<H_I, d_I, paged, query tiles per wave, held score tiles per wave (0:",
         "# staged and written during the key stream)>.  grid = threads of the launch (the 64-row",
         "# decode: grouped 3-layer attention 49152, one layer in 4 key splits 65536; decode indexer",
