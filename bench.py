@@ -319,7 +319,7 @@ def log(msg):
 
 
 LIB_SOURCES = ("api.hip", "indexer.hip", "topk.hip", "index_topk.hip", "attention.hip", "indexer_kl.hip", "common.hpp",
-               "indexer_core.hpp", "internal.hpp", "selection.hpp")
+               "indexer_core.hpp", "internal.hpp", "selection.hpp", "seglist.hpp")
 
 
 def source_hash(*names):
